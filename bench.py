@@ -1,0 +1,201 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact residue GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload wide]
+
+One step is one whole product C = A @ B on device-resident inputs: the residue
+split of both operands (kernel 1), the 29 per-prime INT8 MFMA products with
+the mod-q epilogue (kernel 2) and Garner reconstruction (kernel 3).  The
+default workload is the widest of the five: A[2048,4096] @ B[4096,2048] with
+2-limb entries uniform in [-2^100, 2^100), 29 primes, 4-limb output.
+
+Prints one JSON line: the exact-GEMM rate 2*M*N*K / t_step, the roofline of
+the dominant kernel (the per-prime INT8 products against the dense INT8 MFMA
+peak), per-stage times, and the CPU oracle timed on a bounded sample of the
+same workload on the host cores (a baseline, not a target).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "exact int GEMM ops/s (2MNK/s) + % of MI355X dense INT8 MFMA peak"
+PEAK_INT8_TOPS = 5000.0        # MI355X dense INT8 MFMA, 5.0 POP/s
+PEAK_HBM_GBPS = 8000.0         # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wide",
+                    choices=["tiny", "square", "enclosure", "dixon", "wide"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target wall time of the CPU oracle sample")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+
+    import torch
+    import exact_integer_gemm_amd as rg
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    rg.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    batched = args.workload == "dixon"
+    if batched:
+        plan = rg.plan_n(54)
+        wl = W.make("dixon", primes=list(plan.primes))
+        A_res = torch.from_numpy(wl.A_res).to(dev)
+        A = None
+    else:
+        wl = W.make(args.workload)
+        plan = rg.plan(wl.K, wl.a_bits, wl.b_bits)
+        A = torch.from_numpy(wl.A).to(dev)
+        A_res = None
+    B = torch.from_numpy(wl.B).to(dev)
+    M, N, K, n = wl.M, wl.N, wl.K, plan.n_primes
+    lc = plan.out_limbs_min
+    C = torch.empty((M, N, lc), dtype=torch.int64, device=dev)
+    ws = rg.new_workspace(plan, M, N, K, batched, dev)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        rg.split(plan, A, B, ws, M=M)
+        if evs is not None:
+            evs[1].record(stream)
+        rg.residue_products(plan, M, N, K, ws, A_res=A_res)
+        if evs is not None:
+            evs[2].record(stream)
+        rg.reconstruct(plan, M, N, K, ws, C, batched=batched)
+        if evs is not None:
+            evs[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, events on the stream the kernels run on
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s in range(args.steps):
+        step(evs[s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs])  # ms
+    split_ms, gemm_ms, garner_ms = (float(x) for x in st.mean(axis=0))
+    flags = rg.status(ws)
+
+    # rates
+    mnk2 = 2.0 * M * N * K
+    logical = mnk2 * (n if batched else 1)        # the lift step has no single product
+    value = logical / (ms_step * 1e-3)
+    gemm_ops = mnk2 * n
+    gemm_tops = gemm_ops / (gemm_ms * 1e-3) / 1e12
+    la = 0 if batched else wl.la
+    lb = wl.lb
+    split_bytes = (0 if batched else M * K * (8 * la + n)) + K * N * (8 * lb + n)
+    garner_bytes = M * N * (n + 8 * lc)
+    gemm_min_bytes = n * (M * K + N * K + M * N)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "ops/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "limbs_in": [la, lb],
+                   "limbs_out": lc, "n_primes": n, "parallelism": "single-gpu",
+                   "note": wl.note},
+        "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS,
+                     "unit": "TOP/s", "frac": gemm_tops / PEAK_INT8_TOPS, "traffic": None,
+                     "kernel": "gemm_kernel (per-prime INT8 MFMA + mod-q)",
+                     "algorithmic_ops_per_launch": gemm_ops},
+        "stages": {
+            "split_us": split_ms * 1e3, "split_GBps": split_bytes / (split_ms * 1e-3) / 1e9,
+            "gemm_us": gemm_ms * 1e3, "gemm_TOPs": gemm_tops,
+            "gemm_min_GBps": gemm_min_bytes / (gemm_ms * 1e-3) / 1e9,
+            "garner_us": garner_ms * 1e3, "garner_GBps": garner_bytes / (garner_ms * 1e-3) / 1e9,
+            "garner_share": garner_ms / (split_ms + gemm_ms + garner_ms),
+            "hbm_peak_GBps": PEAK_HBM_GBPS,
+        },
+        "status_flags": flags,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, plan, C, batched, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, plan, C_gpu, batched, target_s):
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import torch
+    from oracle import cgemm
+    from oracle import oracle as O
+
+    if batched:
+        # the lift step: numpy int64 products per prime + textbook CRT, on a
+        # sample of rows of the residue planes
+        rows = 16
+        t = time.perf_counter()
+        X = O.residue_gemm_via_crt(wl.A_res[:, :rows], wl.B[..., 0], list(plan.primes))
+        dt = time.perf_counter() - t
+        got = O.decode_array(C_gpu[:rows].cpu().numpy())
+        ops = 2.0 * rows * wl.N * wl.K * plan.n_primes
+        return {"value": ops / dt, "unit": "ops/s", "cores": 1, "kind": "oracle",
+                "sample": f"{rows} of {wl.M} rows, all 54 primes (numpy int64 products, Python CRT)",
+                "seconds": dt, "bit_exact_sample": bool(np.array_equal(got, X))}
+    cgemm.build()
+    lc = C_gpu.shape[-1]
+
+    def timed(rows):
+        t = time.perf_counter()
+        ref = cgemm.gemm(wl.A[:rows], wl.B, lc)
+        return time.perf_counter() - t, ref
+
+    # grow the sample until it takes about target_s (a few probes, capped at all rows)
+    rows = min(4, wl.M)
+    dt, ref = timed(rows)
+    while dt < 0.5 * target_s and rows < wl.M:
+        rows = int(min(wl.M, max(rows + 1, round(rows * target_s / max(dt, 1e-6)))))
+        dt, ref = timed(rows)
+    got = C_gpu[:rows].cpu().numpy()
+    ops = 2.0 * rows * wl.N * wl.K
+    return {"value": ops / dt, "unit": "ops/s", "cores": cgemm.threads_used(), "kind": "oracle",
+            "sample": f"first {rows} of {wl.M} rows of C (all of B), C schoolbook oracle",
+            "seconds": dt, "bit_exact_sample": bool(np.array_equal(got, ref))}
+
+
+if __name__ == "__main__":
+    main()

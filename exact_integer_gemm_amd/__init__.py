@@ -1,0 +1,327 @@
+"""Exact integer matrix product computed in residues, on gfx950.
+
+A thin Python binding over ``librns_gemm.so`` (C ABI: ``include/rns_gemm.h``).
+The binding only marshals arguments: every step of the product (residue split,
+prime-batched INT8 MFMA products with the mod-q epilogue, Garner
+reconstruction) runs in the library's HIP kernels.  PyTorch provides device
+memory and the current stream.
+
+    import exact_integer_gemm_amd as rg
+    plan = rg.plan(K, a_bits, b_bits)          # primes for |A|<=2^a, |B|<=2^b
+    C = rg.gemm(plan, A, B)                    # A int64 [M,K,la], B int64 [K,N,lb] on cuda
+    plan54 = rg.plan_n(54)
+    X = rg.gemm_batched_residue(plan54, A_res, r)   # A_res int8 [54,M,K]
+
+The library must be built (``python -m exact_integer_gemm_amd._build``); there
+is no fallback path: loading fails loudly when it is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import List, Optional
+
+# torch first: its HIP runtime (soname libamdhip64.so.7) must be the one the
+# library binds to, so that both share device memory and streams.
+import torch
+
+from . import _build
+
+RNS_MAX_PRIMES = 54
+RNS_K_MAX = 1 << 17
+RNS_MAX_IN_LIMBS = 4
+RNS_MAX_OUT_LIMBS = 8
+FLAG_A_RANGE = 1
+FLAG_B_RANGE = 2
+
+ERRORS = {0: "RNS_OK", -1: "RNS_E_ARG", -2: "RNS_E_K", -3: "RNS_E_CAPACITY",
+          -4: "RNS_E_OUT_LIMBS", -5: "RNS_E_WORKSPACE", -6: "RNS_E_HIP"}
+
+
+class RnsError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        self.code = code
+        super().__init__(f"{what}: {ERRORS.get(code, code)} ({error_string(code)})")
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("n_primes", ctypes.c_int32), ("out_limbs_min", ctypes.c_int32),
+                ("a_bits", ctypes.c_int32), ("b_bits", ctypes.c_int32),
+                ("k_max", ctypes.c_int64), ("log2_P", ctypes.c_double),
+                ("primes", ctypes.c_int32 * RNS_MAX_PRIMES)]
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [("m_pad", ctypes.c_int64), ("n_pad", ctypes.c_int64), ("k_pad", ctypes.c_int64),
+                ("a_off", ctypes.c_int64), ("b_off", ctypes.c_int64), ("y_off", ctypes.c_int64),
+                ("status_off", ctypes.c_int64), ("total_bytes", ctypes.c_int64),
+                ("tile_config", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load() -> ctypes.CDLL:
+    """Load librns_gemm.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        raise RuntimeError(f"{_build.LIB} is missing: build it with "
+                           "`python -m exact_integer_gemm_amd._build`")
+    lib = ctypes.CDLL(_build.LIB)
+    P, I32, I64, SZ, VP = (ctypes.POINTER(_Plan), ctypes.c_int32, ctypes.c_int64,
+                           ctypes.c_size_t, ctypes.c_void_p)
+    sig = {
+        "rns_plan": (ctypes.c_int, [I64, I32, I32, P]),
+        "rns_plan_n": (ctypes.c_int, [I32, P]),
+        "rns_workspace_size": (ctypes.c_int, [P, I64, I64, I64, I32, ctypes.POINTER(SZ)]),
+        "rns_workspace_layout": (ctypes.c_int, [P, I64, I64, I64, I32, ctypes.POINTER(_Layout)]),
+        "rns_gemm": (ctypes.c_int, [P, I64, I64, I64, VP, I32, VP, I32, VP, I32, VP, SZ, VP]),
+        "rns_gemm_batched_residue": (ctypes.c_int, [P, I64, I64, I64, VP, VP, I32, VP, I32, VP, SZ, VP]),
+        "rns_split": (ctypes.c_int, [P, I64, I64, I64, VP, I32, VP, I32, VP, SZ, VP]),
+        "rns_residue_products": (ctypes.c_int, [P, I64, I64, I64, VP, VP, SZ, VP]),
+        "rns_reconstruct": (ctypes.c_int, [P, I64, I64, I64, I32, VP, I32, VP, SZ, VP]),
+        "rns_status": (ctypes.c_int, [VP, VP, ctypes.POINTER(ctypes.c_uint32)]),
+        "rns_error_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def error_string(code: int) -> str:
+    return load().rns_error_string(int(code)).decode()
+
+
+def _check(code: int, what: str) -> None:
+    if code != 0:
+        raise RnsError(code, what)
+
+
+@dataclass(frozen=True)
+class Plan:
+    """A prime plan (a copy of the C ``rns_plan_t``)."""
+    n_primes: int
+    out_limbs_min: int
+    a_bits: int
+    b_bits: int
+    k_max: int
+    log2_P: float
+    primes: tuple
+
+    def _c(self) -> _Plan:
+        c = _Plan()
+        c.n_primes, c.out_limbs_min = self.n_primes, self.out_limbs_min
+        c.a_bits, c.b_bits, c.k_max, c.log2_P = self.a_bits, self.b_bits, self.k_max, self.log2_P
+        for i in range(RNS_MAX_PRIMES):
+            c.primes[i] = self.primes[i] if i < len(self.primes) else 0
+        return c
+
+    @staticmethod
+    def _from_c(c: _Plan) -> "Plan":
+        return Plan(c.n_primes, c.out_limbs_min, c.a_bits, c.b_bits, c.k_max, c.log2_P,
+                    tuple(int(c.primes[i]) for i in range(c.n_primes)))
+
+
+def plan(K: int, a_bits: int, b_bits: int) -> Plan:
+    """Fewest largest-first primes with product > 2*K*2^(a_bits+b_bits)."""
+    c = _Plan()
+    _check(load().rns_plan(K, a_bits, b_bits, ctypes.byref(c)), "rns_plan")
+    return Plan._from_c(c)
+
+
+def plan_n(n_primes: int) -> Plan:
+    """The n largest primes below 256, with no operand bound."""
+    c = _Plan()
+    _check(load().rns_plan_n(n_primes, ctypes.byref(c)), "rns_plan_n")
+    return Plan._from_c(c)
+
+
+def workspace_size(p: Plan, M: int, N: int, K: int, batched: bool = False) -> int:
+    c = p._c()
+    out = ctypes.c_size_t()
+    _check(load().rns_workspace_size(ctypes.byref(c), M, N, K, int(batched), ctypes.byref(out)),
+           "rns_workspace_size")
+    return out.value
+
+
+def layout(p: Plan, M: int, N: int, K: int, batched: bool = False) -> dict:
+    c = p._c()
+    out = _Layout()
+    _check(load().rns_workspace_layout(ctypes.byref(c), M, N, K, int(batched), ctypes.byref(out)),
+           "rns_workspace_layout")
+    return {f: getattr(out, f) for f, _ in _Layout._fields_}
+
+
+def new_workspace(p: Plan, M: int, N: int, K: int, batched: bool = False,
+                  device: Optional[torch.device] = None) -> torch.Tensor:
+    n = workspace_size(p, M, N, K, batched)
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device or "cuda")
+
+
+def _stream_ptr(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, dtype, ndim: int, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def gemm(p: Plan, A: torch.Tensor, B: torch.Tensor, out_limbs: Optional[int] = None,
+         workspace: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """C = A @ B exactly.  A int64 [M,K,la], B int64 [K,N,lb] -> int64 [M,N,out_limbs]."""
+    _need(A, torch.int64, 3, "A")
+    _need(B, torch.int64, 3, "B")
+    M, K, la = A.shape
+    K2, N, lb = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if B.device != A.device:
+        raise ValueError("A and B on different devices")
+    lc = p.out_limbs_min if out_limbs is None else out_limbs
+    if out is None:
+        out = torch.empty((M, N, lc), dtype=torch.int64, device=A.device)
+    _need(out, torch.int64, 3, "out")
+    if tuple(out.shape) != (M, N, lc):
+        raise ValueError("out has the wrong shape")
+    if workspace is None:
+        workspace = new_workspace(p, M, N, K, False, A.device)
+    c = p._c()
+    with torch.cuda.device(A.device):
+        rc = load().rns_gemm(ctypes.byref(c), M, N, K, A.data_ptr(), la, B.data_ptr(), lb,
+                             out.data_ptr(), lc, workspace.data_ptr(), workspace.numel(),
+                             _stream_ptr(A))
+    _check(rc, "rns_gemm")
+    return out
+
+
+def gemm_batched_residue(p: Plan, A_res: torch.Tensor, B: torch.Tensor,
+                         out_limbs: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """X = A_res[j] @ B (mod q_j) for every prime j, reconstructed in (-P/2, P/2]."""
+    _need(A_res, torch.int8, 3, "A_res")
+    _need(B, torch.int64, 3, "B")
+    n, M, K = A_res.shape
+    if n != p.n_primes:
+        raise ValueError(f"A_res has {n} planes, the plan has {p.n_primes} primes")
+    K2, N, lb = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    lc = p.out_limbs_min if out_limbs is None else out_limbs
+    if out is None:
+        out = torch.empty((M, N, lc), dtype=torch.int64, device=B.device)
+    _need(out, torch.int64, 3, "out")
+    if tuple(out.shape) != (M, N, lc):
+        raise ValueError("out has the wrong shape")
+    if workspace is None:
+        workspace = new_workspace(p, M, N, K, True, B.device)
+    c = p._c()
+    with torch.cuda.device(B.device):
+        rc = load().rns_gemm_batched_residue(ctypes.byref(c), M, N, K, A_res.data_ptr(),
+                                             B.data_ptr(), lb, out.data_ptr(), lc,
+                                             workspace.data_ptr(), workspace.numel(),
+                                             _stream_ptr(B))
+    _check(rc, "rns_gemm_batched_residue")
+    return out
+
+
+# ---- the three stages, callable one at a time (rns_gemm runs them in order) ----
+def split(p: Plan, A: Optional[torch.Tensor], B: torch.Tensor, workspace: torch.Tensor,
+          M: Optional[int] = None) -> None:
+    """Kernel 1: residue planes of A and B into ``workspace``.
+
+    A = None is the batched-residue variant (only B is split); then M, the
+    row count of the caller's residue planes, fixes the workspace layout.
+    """
+    _need(B, torch.int64, 3, "B")
+    K, N, lb = B.shape
+    if A is not None:
+        _need(A, torch.int64, 3, "A")
+        M, K2, la = A.shape
+        if K2 != K:
+            raise ValueError("inner dimensions differ")
+    else:
+        if M is None:
+            raise ValueError("the batched-residue split needs M")
+        la = 1
+    c = p._c()
+    with torch.cuda.device(B.device):
+        rc = load().rns_split(ctypes.byref(c), M, N, K,
+                              A.data_ptr() if A is not None else None, la, B.data_ptr(), lb,
+                              workspace.data_ptr(), workspace.numel(), _stream_ptr(B))
+    _check(rc, "rns_split")
+
+
+def residue_products(p: Plan, M: int, N: int, K: int, workspace: torch.Tensor,
+                     A_res: Optional[torch.Tensor] = None) -> None:
+    """Kernel 2: per-prime INT8 products mod q from the planes in ``workspace``."""
+    if A_res is not None:
+        _need(A_res, torch.int8, 3, "A_res")
+        if tuple(A_res.shape) != (p.n_primes, M, K):
+            raise ValueError("A_res must be [n_primes, M, K]")
+    c = p._c()
+    with torch.cuda.device(workspace.device):
+        rc = load().rns_residue_products(ctypes.byref(c), M, N, K,
+                                         A_res.data_ptr() if A_res is not None else None,
+                                         workspace.data_ptr(), workspace.numel(),
+                                         _stream_ptr(workspace))
+    _check(rc, "rns_residue_products")
+
+
+def reconstruct(p: Plan, M: int, N: int, K: int, workspace: torch.Tensor, out: torch.Tensor,
+                batched: bool = False) -> torch.Tensor:
+    """Kernel 3: Garner reconstruction of ``out`` (int64 [M,N,limbs]) from the Y planes."""
+    _need(out, torch.int64, 3, "out")
+    if tuple(out.shape[:2]) != (M, N):
+        raise ValueError("out has the wrong shape")
+    c = p._c()
+    with torch.cuda.device(out.device):
+        rc = load().rns_reconstruct(ctypes.byref(c), M, N, K, int(batched), out.data_ptr(),
+                                    out.shape[2], workspace.data_ptr(), workspace.numel(),
+                                    _stream_ptr(out))
+    _check(rc, "rns_reconstruct")
+    return out
+
+
+def status(workspace: torch.Tensor) -> int:
+    """Synchronises the current stream; returns the RNS_FLAG_* bits of the last call."""
+    flags = ctypes.c_uint32()
+    with torch.cuda.device(workspace.device):
+        rc = load().rns_status(workspace.data_ptr(), _stream_ptr(workspace), ctypes.byref(flags))
+    _check(rc, "rns_status")
+    return flags.value
+
+
+def workspace_planes(p: Plan, workspace: torch.Tensor, M: int, N: int, K: int,
+                     batched: bool = False) -> dict:
+    """Views of the residue planes a call left in ``workspace`` (for inspection)."""
+    L = layout(p, M, N, K, batched)
+    n = p.n_primes
+    out = {"layout": L}
+
+    def view(off, rows, cols):
+        return workspace[off:off + n * rows * cols].view(torch.int8).view(n, rows, cols)
+
+    if L["a_off"] >= 0:
+        out["A"] = view(L["a_off"], L["m_pad"], L["k_pad"])
+    out["B"] = view(L["b_off"], L["n_pad"], L["k_pad"])
+    out["Y"] = view(L["y_off"], L["m_pad"], L["n_pad"])
+    return out

@@ -1,0 +1,45 @@
+"""Compile librns_gemm.so (HIP for gfx950) in-tree with hipcc.
+
+The library is plain HIP (no PyTorch types): ``csrc/rns_host.cpp`` holds the
+C ABI and host logic, ``csrc/rns_kernels.hip`` the three device kernels.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "librns_gemm.so")
+SOURCES = [os.path.join(CSRC, "rns_host.cpp"), os.path.join(CSRC, "rns_kernels.hip")]
+HEADERS = [os.path.join(CSRC, "rns_internal.h"),
+           os.path.join(os.path.dirname(HERE), "include", "rns_gemm.h")]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+# Packed fp32 instructions are disabled for all device code; the host pass
+# warns that it does not know the feature, which is harmless.
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+         "-Wall", "-Wno-unused-function",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def build(verbose: bool = False) -> str:
+    """Always recompiles; returns the library path."""
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(s) > t for s in SOURCES + HEADERS)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

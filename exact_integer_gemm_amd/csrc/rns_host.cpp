@@ -1,0 +1,503 @@
+// Host side of librns_gemm: prime plans, per-prime constant tables, workspace
+// layout, argument validation and the C ABI declared in include/rns_gemm.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "rns_internal.h"
+
+namespace rns {
+namespace {
+
+// ---- the primes below 256, largest first ------------------------------------
+struct PrimeTable {
+    int p[kMaxPrimes];
+    PrimeTable() {
+        int cnt = 0;
+        for (int x = 255; x >= 2; x--) {
+            bool prime = true;
+            for (int d = 2; d * d <= x; d++)
+                if (x % d == 0) { prime = false; break; }
+            if (prime) p[cnt++] = x;
+        }
+    }
+};
+const PrimeTable &primes() {
+    static const PrimeTable t;
+    return t;
+}
+
+// ---- a minimal unsigned big integer (little-endian 32-bit words) ----------
+struct Big {
+    std::vector<uint32_t> w;
+    explicit Big(uint64_t v = 0) {
+        if (v) { w.push_back((uint32_t)v); if (v >> 32) w.push_back((uint32_t)(v >> 32)); }
+    }
+    void mul_small(uint32_t m) {
+        uint64_t carry = 0;
+        for (auto &x : w) {
+            uint64_t t = (uint64_t)x * m + carry;
+            x = (uint32_t)t;
+            carry = t >> 32;
+        }
+        if (carry) w.push_back((uint32_t)carry);
+    }
+    void shl(int bits) {
+        const int words = bits / 32, r = bits % 32;
+        if (w.empty()) return;
+        std::vector<uint32_t> o(w.size() + words + 1, 0);
+        for (size_t i = 0; i < w.size(); i++) {
+            uint64_t v = (uint64_t)w[i] << r;
+            o[i + words] |= (uint32_t)v;
+            o[i + words + 1] |= (uint32_t)(v >> 32);
+        }
+        w = o;
+        trim();
+    }
+    void trim() { while (!w.empty() && w.back() == 0) w.pop_back(); }
+    int bit_length() const {
+        if (w.empty()) return 0;
+        int b = 32 * (int)(w.size() - 1);
+        uint32_t top = w.back();
+        while (top) { b++; top >>= 1; }
+        return b;
+    }
+    uint16_t chunk16(int c) const {
+        const int wi = c / 2;
+        if (wi >= (int)w.size()) return 0;
+        return (uint16_t)((c & 1) ? (w[wi] >> 16) : (w[wi] & 0xffff));
+    }
+    // strict comparison a > b
+    static bool greater(Big a, Big b) {
+        a.trim(); b.trim();
+        if (a.w.size() != b.w.size()) return a.w.size() > b.w.size();
+        for (size_t i = a.w.size(); i-- > 0;)
+            if (a.w[i] != b.w[i]) return a.w[i] > b.w[i];
+        return false;
+    }
+};
+
+int64_t powmod(int64_t b, int64_t e, int64_t m) {
+    int64_t r = 1 % m;
+    b %= m;
+    if (b < 0) b += m;
+    while (e > 0) {
+        if (e & 1) r = r * b % m;
+        b = b * b % m;
+        e >>= 1;
+    }
+    return r;
+}
+int64_t inv_mod(int64_t a, int64_t q) {   // q prime, a != 0 mod q
+    a %= q;
+    if (a < 0) a += q;
+    return powmod(a, q - 2, q);
+}
+int balanced(int64_t x, int64_t q) {
+    int64_t r = x % q;
+    if (r < 0) r += q;
+    return (int)(r > q / 2 ? r - q : r);
+}
+
+void fill_common(rns_plan_t *out, int n) {
+    Big P(1);
+    double l2 = 0;
+    for (int i = 0; i < kMaxPrimes; i++) out->primes[i] = 0;
+    for (int i = 0; i < n; i++) {
+        out->primes[i] = primes().p[i];
+        P.mul_small((uint32_t)primes().p[i]);
+        l2 += std::log2((double)primes().p[i]);
+    }
+    out->n_primes = n;
+    out->log2_P = l2;
+    out->out_limbs_min = (P.bit_length() + 63) / 64;
+}
+
+bool plan_ok(const rns_plan_t *p) {
+    if (!p || p->n_primes < 1 || p->n_primes > kMaxPrimes) return false;
+    if (p->k_max < 1 || p->k_max > RNS_K_MAX) return false;
+    if (p->out_limbs_min < 1 || p->out_limbs_min > RNS_MAX_OUT_LIMBS) return false;
+    // the primes must be distinct primes below 256 (any order)
+    bool seen[256] = {false};
+    for (int i = 0; i < p->n_primes; i++) {
+        const int q = p->primes[i];
+        if (q < 2 || q > 255 || seen[q]) return false;
+        for (int d = 2; d * d <= q; d++)
+            if (q % d == 0) return false;
+        seen[q] = true;
+    }
+    return true;
+}
+
+// ---- tables -------------------------------------------------------------------
+void build_split(const rns_plan_t &pl, int la, int lb, SplitConsts &c) {
+    std::memset(&c, 0, sizeof(c));
+    c.n = pl.n_primes;
+    for (int j = 0; j < pl.n_primes; j++) {
+        const int q = pl.primes[j];
+        c.q[j] = q;
+        c.inv[j] = 1.0f / (float)q;
+        for (int w = 0; w < 2 * RNS_MAX_IN_LIMBS; w++) {
+            uint32_t packed = 0;
+            for (int b = 0; b < 4; b++) {
+                const int64_t v = powmod(256, 4 * w + b, q);   // 256^(4w+b) mod q, in [0, q)
+                packed |= (uint32_t)v << (8 * b);
+            }
+            c.w[j][w] = packed;
+        }
+        c.h_a[j] = (int32_t)powmod(2, 64 * (int64_t)(la > 0 ? la : 1) - 1, q);
+        c.h_b[j] = (int32_t)powmod(2, 64 * (int64_t)lb - 1, q);
+    }
+}
+
+void build_epi(const rns_plan_t &pl, EpiConsts &c) {
+    std::memset(&c, 0, sizeof(c));
+    for (int j = 0; j < pl.n_primes; j++) {
+        const int q = pl.primes[j];
+        c.q[j] = q;
+        c.c16[j] = balanced(65536, q);
+        c.inv[j] = 1.0f / (float)q;
+    }
+}
+
+// Garner order: 2 first when present (so that balanced mixed-radix digits land
+// in (-P/2, P/2] for even P), then the plan order.
+void build_garner(const rns_plan_t &pl, GarnerConsts &g) {
+    std::memset(&g, 0, sizeof(g));
+    const int n = pl.n_primes;
+    g.n = n;
+    int slot = 0;
+    for (int j = 0; j < n; j++)
+        if (pl.primes[j] == 2) g.plane[slot++] = (uint8_t)j;
+    for (int j = 0; j < n; j++)
+        if (pl.primes[j] != 2) g.plane[slot++] = (uint8_t)j;
+    for (int k = 0; k < kGarnerSlots; k++) {
+        if (k < n) {
+            g.q[k] = (uint8_t)pl.primes[g.plane[k]];
+            g.inv[k] = 1.0f / (float)g.q[k];
+        } else {
+            // inert padding slot: reads plane of slot 0, multiplies it by 0
+            g.plane[k] = g.plane[0];
+            g.q[k] = 1;
+            g.inv[k] = 1.0f;
+        }
+    }
+    // Q_j mod q_k for j <= k, by running products
+    for (int k = 0; k < n; k++) {
+        const int64_t qk = g.q[k];
+        int64_t Qj = 1 % qk;   // Q_0 = 1
+        std::vector<int64_t> Qmod(k + 1);
+        for (int j = 0; j <= k; j++) {
+            Qmod[j] = Qj;
+            Qj = Qj * g.q[j] % qk;
+        }
+        const int64_t Qk_inv = (qk == 2) ? 1 : inv_mod(Qmod[k], qk);
+        g.tri[tri_index(k, k)] = (int8_t)balanced(Qk_inv, qk);
+        for (int j = 0; j < k; j++)
+            g.tri[tri_index(j, k)] = (int8_t)balanced(Qmod[j] * Qk_inv, qk);
+    }
+    // 16-bit chunks of every Q_k
+    Big Q(1);
+    for (int k = 0; k < n; k++) {
+        const int nb = (Q.bit_length() + 15) / 16;
+        for (int c = 0; c < nb && c < garner_chunks(k); c++)
+            g.q16[garner_chunk_offset(k) + c] = Q.chunk16(c);
+        Q.mul_small(g.q[k]);
+    }
+}
+
+// ---- layout ------------------------------------------------------------------
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int choose_tile(int n, int64_t M, int64_t N) {
+    if (N <= 32) return kTileSkinny;
+    const int64_t big_tiles = (int64_t)n * ((M + 255) / 256) * ((N + 255) / 256);
+    if (M >= 256 && N >= 256 && big_tiles >= 256) return kTileBig;
+    return kTileSmall;
+}
+
+struct Layout {
+    rns_layout_t pub;
+    int64_t status_slots;
+    bool a_in_place;
+};
+
+Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool batched) {
+    Layout L{};
+    const int n = pl.n_primes;
+    const int cfg = choose_tile(n, M, N);
+    const TileShape ts = tile_shape(cfg);
+    L.pub.tile_config = cfg;
+    L.pub.m_pad = round_up(M, ts.bm);
+    L.pub.n_pad = round_up(N, ts.bn);
+    L.pub.k_pad = round_up(K, ts.bk);
+    L.a_in_place = batched && L.pub.m_pad == M && L.pub.k_pad == K;
+
+    SplitOperand a{}, b{};
+    a.r_pad = L.pub.m_pad; a.k_pad = L.pub.k_pad;
+    b.r_pad = L.pub.n_pad; b.k_pad = L.pub.k_pad;
+    L.status_slots = split_status_slots(batched ? nullptr : &a, &b);
+
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) { int64_t o = off; off = round_up(off + bytes, 256); return o; };
+    L.pub.status_off = take(L.status_slots * 4);
+    L.pub.a_off = L.a_in_place ? -1 : take((int64_t)n * L.pub.m_pad * L.pub.k_pad);
+    L.pub.b_off = take((int64_t)n * L.pub.n_pad * L.pub.k_pad);
+    L.pub.y_off = take((int64_t)n * L.pub.m_pad * L.pub.n_pad);
+    L.pub.total_bytes = off;
+    return L;
+}
+
+int validate(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K) {
+    if (!plan_ok(plan)) return RNS_E_ARG;
+    if (M < 0 || N < 0 || K < 0) return RNS_E_ARG;
+    if (K > RNS_K_MAX || K > plan->k_max) return RNS_E_K;
+    // index arithmetic inside the kernels is 32-bit on padded row/column counts
+    if (M > (1ll << 30) || N > (1ll << 30)) return RNS_E_ARG;
+    return RNS_OK;
+}
+
+// Shape, pointer and size checks shared by the stage calls.  Returns the
+// layout through *L when the call has work to do (rc == RNS_OK, *work = true).
+int prepare(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, bool batched,
+            void *ws, size_t ws_bytes, Layout *L, bool *work) {
+    *work = false;
+    int rc = validate(plan, M, N, K);
+    if (rc) return rc;
+    if (M == 0 || N == 0 || K == 0) return RNS_OK;
+    if (!ws) return RNS_E_ARG;
+    *L = make_layout(*plan, M, N, K, batched);
+    if (ws_bytes < (size_t)L->pub.total_bytes) return RNS_E_WORKSPACE;
+    *work = true;
+    return RNS_OK;
+}
+
+int stage_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                const int64_t *A, int32_t a_limbs, const int64_t *B, int32_t b_limbs,
+                void *ws, size_t ws_bytes, hipStream_t stream) {
+    const bool batched = A == nullptr;
+    if (!batched && (a_limbs < 1 || a_limbs > RNS_MAX_IN_LIMBS)) return RNS_E_ARG;
+    if (b_limbs < 1 || b_limbs > RNS_MAX_IN_LIMBS) return RNS_E_ARG;
+    Layout L;
+    bool work;
+    int rc = prepare(plan, M, N, K, batched, ws, ws_bytes, &L, &work);
+    if (rc || !work) return rc;
+    if (!B) return RNS_E_ARG;
+    int8_t *base = (int8_t *)ws;
+    SplitConsts sc;
+    build_split(*plan, batched ? 1 : a_limbs, b_limbs, sc);
+    SplitOperand sa{}, sb{};
+    if (!batched) {
+        sa.x = A; sa.planes = base + L.pub.a_off; sa.rows = M; sa.k = K;
+        sa.r_pad = L.pub.m_pad; sa.k_pad = L.pub.k_pad; sa.limbs = a_limbs;
+        sa.bits = (plan->a_bits >= 0 && plan->a_bits < 64 * a_limbs - 1) ? plan->a_bits : -1;
+        sa.transposed = 0;
+    }
+    sb.x = B; sb.planes = base + L.pub.b_off; sb.rows = N; sb.k = K;
+    sb.r_pad = L.pub.n_pad; sb.k_pad = L.pub.k_pad; sb.limbs = b_limbs;
+    sb.bits = (plan->b_bits >= 0 && plan->b_bits < 64 * b_limbs - 1) ? plan->b_bits : -1;
+    sb.transposed = 1;
+    return launch_split(batched ? nullptr : &sa, &sb, sc, (uint32_t *)(base + L.pub.status_off),
+                        L.status_slots, stream);
+}
+
+int stage_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, const int8_t *A_res,
+                   void *ws, size_t ws_bytes, hipStream_t stream) {
+    const bool batched = A_res != nullptr;
+    Layout L;
+    bool work;
+    int rc = prepare(plan, M, N, K, batched, ws, ws_bytes, &L, &work);
+    if (rc || !work) return rc;
+    int8_t *base = (int8_t *)ws;
+    const int n = plan->n_primes;
+    const int8_t *apl = base + L.pub.a_off;
+    if (batched) {
+        if (L.a_in_place) {
+            apl = A_res;
+        } else {
+            rc = launch_repack_residues(A_res, n, M, K, base + L.pub.a_off, L.pub.m_pad,
+                                        L.pub.k_pad, stream);
+            if (rc) return rc;
+        }
+    }
+    EpiConsts ec;
+    build_epi(*plan, ec);
+    return launch_gemm(L.pub.tile_config, n, apl, base + L.pub.b_off, base + L.pub.y_off,
+                       L.pub.m_pad, L.pub.n_pad, L.pub.k_pad, L.pub.m_pad * L.pub.k_pad,
+                       L.pub.n_pad * L.pub.k_pad, L.pub.m_pad * L.pub.n_pad, ec, stream);
+}
+
+int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, bool batched,
+                      int64_t *C, int32_t c_limbs, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int rc = validate(plan, M, N, K);
+    if (rc) return rc;
+    if (c_limbs < plan->out_limbs_min || c_limbs > RNS_MAX_OUT_LIMBS) return RNS_E_OUT_LIMBS;
+    if (M == 0 || N == 0) return RNS_OK;
+    if (!C) return RNS_E_ARG;
+    if (K == 0) return launch_zero(C, M * N * c_limbs, stream);
+    Layout L;
+    bool work;
+    rc = prepare(plan, M, N, K, batched, ws, ws_bytes, &L, &work);
+    if (rc || !work) return rc;
+    GarnerConsts gc;
+    build_garner(*plan, gc);
+    return launch_garner(gc, (const int8_t *)ws + L.pub.y_off, L.pub.m_pad * L.pub.n_pad,
+                         L.pub.n_pad, M, N, C, c_limbs, stream);
+}
+
+// Full product: every argument is checked before the first launch.
+int run(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+        const int64_t *A, int32_t a_limbs, const int8_t *A_res,
+        const int64_t *B, int32_t b_limbs, int64_t *C, int32_t c_limbs,
+        void *ws, size_t ws_bytes, hipStream_t stream) {
+    const bool batched = A_res != nullptr;
+    int rc = validate(plan, M, N, K);
+    if (rc) return rc;
+    if (!batched && (a_limbs < 1 || a_limbs > RNS_MAX_IN_LIMBS)) return RNS_E_ARG;
+    if (b_limbs < 1 || b_limbs > RNS_MAX_IN_LIMBS) return RNS_E_ARG;
+    if (c_limbs < plan->out_limbs_min || c_limbs > RNS_MAX_OUT_LIMBS) return RNS_E_OUT_LIMBS;
+    if (M == 0 || N == 0) return RNS_OK;
+    if (!C) return RNS_E_ARG;
+    // K == 0: the operands are empty (their pointers may be null); C = 0
+    if (K == 0) return launch_zero(C, M * N * c_limbs, stream);
+    if (!B || (!batched && !A) || !ws) return RNS_E_ARG;
+    const Layout L = make_layout(*plan, M, N, K, batched);
+    if (ws_bytes < (size_t)L.pub.total_bytes) return RNS_E_WORKSPACE;
+    rc = stage_split(plan, M, N, K, batched ? nullptr : A, a_limbs, B, b_limbs, ws, ws_bytes, stream);
+    if (rc) return rc;
+    rc = stage_products(plan, M, N, K, A_res, ws, ws_bytes, stream);
+    if (rc) return rc;
+    return stage_reconstruct(plan, M, N, K, batched, C, c_limbs, ws, ws_bytes, stream);
+}
+
+}  // namespace
+}  // namespace rns
+
+using namespace rns;
+
+extern "C" {
+
+int rns_plan(int64_t K, int32_t a_bits, int32_t b_bits, rns_plan_t *out) {
+    if (!out) return RNS_E_ARG;
+    if (a_bits < 0 || b_bits < 0 || a_bits > 255 || b_bits > 255) return RNS_E_ARG;
+    if (K < 0 || K > RNS_K_MAX) return RNS_E_K;
+    const int64_t Kb = K < 1 ? 1 : K;
+    Big bound((uint64_t)Kb);
+    bound.shl(a_bits + b_bits + 1);          // 2 * K * 2^(a+b)
+    Big P(1);
+    for (int n = 1; n <= kMaxPrimes; n++) {
+        P.mul_small((uint32_t)primes().p[n - 1]);
+        if (Big::greater(P, bound)) {
+            fill_common(out, n);
+            out->a_bits = a_bits;
+            out->b_bits = b_bits;
+            out->k_max = Kb;
+            return RNS_OK;
+        }
+    }
+    return RNS_E_CAPACITY;
+}
+
+int rns_plan_n(int32_t n_primes, rns_plan_t *out) {
+    if (!out || n_primes < 1 || n_primes > kMaxPrimes) return RNS_E_ARG;
+    fill_common(out, n_primes);
+    out->a_bits = -1;
+    out->b_bits = -1;
+    out->k_max = RNS_K_MAX;
+    return RNS_OK;
+}
+
+int rns_workspace_layout(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                         int32_t batched_residue, rns_layout_t *out) {
+    if (!out) return RNS_E_ARG;
+    int rc = validate(plan, M, N, K);
+    if (rc) return rc;
+    *out = make_layout(*plan, M, N, K, batched_residue != 0).pub;
+    return RNS_OK;
+}
+
+int rns_workspace_size(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                       int32_t batched_residue, size_t *bytes) {
+    if (!bytes) return RNS_E_ARG;
+    rns_layout_t l;
+    int rc = rns_workspace_layout(plan, M, N, K, batched_residue, &l);
+    if (rc) return rc;
+    *bytes = (size_t)l.total_bytes;
+    return RNS_OK;
+}
+
+int rns_gemm(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+             const int64_t *A, int32_t a_limbs, const int64_t *B, int32_t b_limbs,
+             int64_t *C, int32_t c_limbs, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return run(plan, M, N, K, A, a_limbs, nullptr, B, b_limbs, C, c_limbs, ws, ws_bytes, stream);
+}
+
+int rns_gemm_batched_residue(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                             const int8_t *A_res, const int64_t *B, int32_t b_limbs,
+                             int64_t *C, int32_t c_limbs, void *ws, size_t ws_bytes,
+                             hipStream_t stream) {
+    if (!A_res && M > 0 && N > 0 && K > 0) return RNS_E_ARG;
+    if (!A_res) {
+        // nothing to read: validate and handle the degenerate sizes only
+        int rc = validate(plan, M, N, K);
+        if (rc) return rc;
+        if (b_limbs < 1 || b_limbs > RNS_MAX_IN_LIMBS) return RNS_E_ARG;
+        if (c_limbs < plan->out_limbs_min || c_limbs > RNS_MAX_OUT_LIMBS) return RNS_E_OUT_LIMBS;
+        if (M == 0 || N == 0) return RNS_OK;
+        if (!C) return RNS_E_ARG;
+        return launch_zero(C, M * N * c_limbs, stream);
+    }
+    return run(plan, M, N, K, nullptr, 1, A_res, B, b_limbs, C, c_limbs, ws, ws_bytes, stream);
+}
+
+int rns_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+              const int64_t *A, int32_t a_limbs, const int64_t *B, int32_t b_limbs,
+              void *ws, size_t ws_bytes, hipStream_t stream) {
+    return stage_split(plan, M, N, K, A, a_limbs, B, b_limbs, ws, ws_bytes, stream);
+}
+
+int rns_residue_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                         const int8_t *A_res, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return stage_products(plan, M, N, K, A_res, ws, ws_bytes, stream);
+}
+
+int rns_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                    int32_t batched_residue, int64_t *C, int32_t c_limbs,
+                    void *ws, size_t ws_bytes, hipStream_t stream) {
+    return stage_reconstruct(plan, M, N, K, batched_residue != 0, C, c_limbs, ws, ws_bytes, stream);
+}
+
+int rns_status(const void *ws, hipStream_t stream, uint32_t *flags) {
+    if (!ws || !flags) return RNS_E_ARG;
+    if (hipStreamSynchronize(stream) != hipSuccess) return RNS_E_HIP;
+    uint32_t head[kStatusHeader] = {0, 0};
+    if (hipMemcpy(head, ws, sizeof(head), hipMemcpyDeviceToHost) != hipSuccess) return RNS_E_HIP;
+    const uint32_t nblocks = head[0];
+    // a workspace that no completed call has written fails the check word
+    if ((head[0] ^ kStatusCheck) != head[1] || nblocks > (1u << 30)) return RNS_E_ARG;
+    std::vector<uint32_t> words(nblocks);
+    if (nblocks && hipMemcpy(words.data(), (const uint32_t *)ws + kStatusHeader,
+                             4 * (size_t)nblocks, hipMemcpyDeviceToHost) != hipSuccess)
+        return RNS_E_HIP;
+    uint32_t f = 0;
+    for (uint32_t w : words) f |= w;
+    *flags = f;
+    return RNS_OK;
+}
+
+const char *rns_error_string(int code) {
+    switch (code) {
+        case RNS_OK: return "success";
+        case RNS_E_ARG: return "invalid argument";
+        case RNS_E_K: return "K exceeds 2^17 or the plan's K";
+        case RNS_E_CAPACITY: return "bound exceeds the product of the primes below 256";
+        case RNS_E_OUT_LIMBS: return "too few (or too many) output limbs";
+        case RNS_E_WORKSPACE: return "workspace too small";
+        case RNS_E_HIP: return "HIP launch or copy failed";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

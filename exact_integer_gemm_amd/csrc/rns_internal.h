@@ -1,0 +1,124 @@
+// Internal definitions shared by the host code and the gfx950 kernels of
+// librns_gemm.  Nothing here is part of the public C ABI (include/rns_gemm.h).
+//
+// The per-prime constant tables travel to the kernels by value, as kernel
+// arguments: they are read with uniform (scalar) loads, need no device
+// allocation and no host->device copy, and stay valid under stream capture.
+#pragma once
+
+#include <stdint.h>
+
+#include "../../include/rns_gemm.h"
+
+namespace rns {
+
+constexpr int kMaxPrimes = RNS_MAX_PRIMES;   // 54
+constexpr int kGarnerSlots = 56;             // kMaxPrimes rounded up to 8
+constexpr int kTriEntries = kGarnerSlots * (kGarnerSlots + 1) / 2;
+
+// 1.5 * 2^23: adding it to a float |x| < 2^22 rounds x to the nearest
+// integer j and leaves 0x4B400000 + j in the bit pattern.
+constexpr float kRoundMagic = 12582912.0f;
+constexpr int32_t kRoundMagicBits = 0x4B400000;
+
+// ---- residue split (kernel 1) ---------------------------------------------
+// An operand entry x of L limbs is read as U = x + 2^(64L-1) (its top bit
+// flipped), an unsigned 64L-bit number, so x = U - 2^(64L-1).  With U's bytes
+// u_b,  x mod q = sum_b u_b * (256^b mod q) - (2^(64L-1) mod q)  (mod q),
+// which four-byte dot products evaluate: each 32-bit word of U against a
+// word of four packed constants 256^(4w+i) mod q.
+struct SplitConsts {
+    int32_t n;
+    int32_t q[kMaxPrimes];
+    float inv[kMaxPrimes];                 // fl(1/q)
+    uint32_t w[kMaxPrimes][2 * RNS_MAX_IN_LIMBS];  // packed bytes 256^(4w+i) mod q
+    int32_t h_a[kMaxPrimes];               // 2^(64*la - 1) mod q
+    int32_t h_b[kMaxPrimes];               // 2^(64*lb - 1) mod q
+};
+
+// ---- mod-q epilogue of the residue product (kernel 2) ----------------------
+// s = hi * 2^16 + lo  ==>  s = hi * c16 + lo (mod q) with c16 = 2^16 mod q
+// (balanced), a value below 2^22 in magnitude that the float rounding step
+// reduces exactly.
+struct EpiConsts {
+    int32_t q[kMaxPrimes];
+    int32_t c16[kMaxPrimes];
+    float inv[kMaxPrimes];
+};
+
+// ---- Garner reconstruction (kernel 3) --------------------------------------
+// Slot k of the Garner order holds prime q_k; Q_k = q_0 * ... * q_{k-1}.
+// Digits: v_k = ( y_k * Q_k^-1  -  sum_{j<k} v_j * (Q_j * Q_k^-1 mod q_k) ) mod q_k,
+// balanced.  tri[T(j,k)] holds Q_j * Q_k^-1 mod q_k (balanced) for j < k and
+// Q_k^-1 mod q_k for j == k, with T(j,k) = j*(2S - j + 1)/2 + (k - j),
+// S = kGarnerSlots.  The value is X = sum_k v_k Q_k, formed from the 16-bit
+// chunks of each Q_k.  Q_k < 256^k has at most garner_chunks(k) = k/2 + 1
+// chunks; slot k's chunks start at garner_chunk_offset(k) in q16 (unused
+// chunks are zero).  Slots k >= n are padding: q = 1, inv = 1, zero tables.
+__host__ __device__ constexpr int garner_chunks(int k) { return k / 2 + 1; }
+__host__ __device__ constexpr int garner_chunk_offset(int k) {
+    // sum_{j<k} (j/2 + 1)
+    return (k / 2) * (k / 2 - 1) + (k % 2) * (k / 2) + k;
+}
+constexpr int kMaxQChunks = garner_chunk_offset(kGarnerSlots);   // 812
+
+struct GarnerConsts {
+    int32_t n;
+    uint8_t plane[kGarnerSlots];   // Garner slot -> residue plane index
+    uint8_t q[kGarnerSlots];
+    float inv[kGarnerSlots];
+    int8_t tri[kTriEntries];
+    uint16_t q16[kMaxQChunks];
+};
+
+__host__ __device__ constexpr int tri_index(int j, int k) {
+    return j * (2 * kGarnerSlots - j + 1) / 2 + (k - j);
+}
+
+// ---- GEMM tilings ----------------------------------------------------------
+enum TileConfig : int32_t {
+    kTileBig = 0,      // 256 x 256 x 64, four waves of 128 x 128
+    kTileSmall = 1,    // 64 x 64 x 64, four waves of 32 x 32
+    kTileSkinny = 2,   // 128 x 32 x 64, four waves of 32 x 32 stacked along M
+};
+
+struct TileShape { int bm, bn, bk; };
+
+__host__ __device__ constexpr TileShape tile_shape(int cfg) {
+    return cfg == kTileBig ? TileShape{256, 256, 64}
+         : cfg == kTileSmall ? TileShape{64, 64, 64}
+         : TileShape{128, 32, 64};
+}
+
+// ---- launchers (rns_kernels.hip) -------------------------------------------
+struct SplitOperand {
+    const int64_t *x;      // [rows][cols][limbs] for A, [K][N][limbs] for B
+    int8_t *planes;        // [n][r_pad][k_pad]
+    int64_t rows;          // A: M        B: N  (plane rows)
+    int64_t k;             // K
+    int64_t r_pad, k_pad;
+    int32_t limbs;
+    int32_t bits;          // declared bound, or -1 for no check
+    int32_t transposed;    // 0: A ([rows][K]), 1: B ([K][rows])
+};
+
+int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts &c,
+                 uint32_t *status, int64_t status_slots, hipStream_t s);
+int launch_repack_residues(const int8_t *src, int64_t n, int64_t M, int64_t K,
+                           int8_t *dst, int64_t m_pad, int64_t k_pad, hipStream_t s);
+int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
+                int64_t m_pad, int64_t n_pad, int64_t k_pad,
+                int64_t a_plane, int64_t b_plane, int64_t y_plane,
+                const EpiConsts &c, hipStream_t s);
+int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t n_pad,
+                  int64_t M, int64_t N, int64_t *C, int32_t c_limbs, hipStream_t s);
+int launch_zero(int64_t *C, int64_t count, hipStream_t s);
+
+// Status area written by the split kernel: word 0 = number of split blocks,
+// word 1 = that number XOR kStatusCheck, then one flag word per block.
+constexpr int kStatusHeader = 2;
+constexpr uint32_t kStatusCheck = 0x52534e53u;
+// status slots written by the split kernel: one word per block plus the header
+int64_t split_status_slots(const SplitOperand *a, const SplitOperand *b);
+
+}  // namespace rns

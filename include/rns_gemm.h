@@ -1,0 +1,223 @@
+/*
+ * rns_gemm.h -- exact integer matrix product computed in residues (gfx950).
+ *
+ * The product C = A @ B of signed multi-limb integer matrices is computed
+ * exactly: every operand entry is reduced to balanced residues modulo primes
+ * below 256, one INT8 matrix product per prime is accumulated in int32 and
+ * reduced mod that prime, and balanced Garner mixed-radix reconstruction
+ * rebuilds the exact signed result (exact-solve, "Method"; enclosure-gemm,
+ * "Method"; Ozaki Scheme II paper, §3.1: the integer products are exact and
+ * the result is reconstructed once).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Integers.  An integer of L limbs is L int64 words, little-endian two's
+ *   complement: limbs 0..L-2 are read unsigned, limb L-1 is signed
+ *   (enclosure-gemm, "Method": two's-complement integers of up to four int64
+ *   limbs).  Matrices are row-major and contiguous with the limbs innermost:
+ *   A is [M][K][a_limbs], B is [K][N][b_limbs], C is [M][N][c_limbs].
+ * Memory.  Pointers named A, B, C, A_res and ws are DEVICE pointers, owned by
+ *   the caller (e.g. allocated through PyTorch).  The library never allocates
+ *   or frees device memory.  rns_plan_t is a plain host struct owned by the
+ *   caller; it needs no release.
+ * Streams.  Every launch is asynchronous on the caller's stream; no entry
+ *   point synchronises except rns_status.  Concurrent calls are safe when
+ *   they use distinct workspaces.
+ * Errors.  0 is success, negative values are failures (RNS_E_*).  All
+ *   arguments are validated on the host before anything is launched, so on a
+ *   validation error nothing is written.  rns_error_string names a code.
+ * Sizes.  M == 0 or N == 0 is a no-op.  K == 0 writes zeros to C.
+ */
+#ifndef RNS_GEMM_H
+#define RNS_GEMM_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* There are 54 primes below 256 (2, 3, 5, ..., 251); their product P is a
+ * 335-bit number (enclosure-gemm, "Requirements and limits"). */
+#define RNS_MAX_PRIMES 54
+/* int32 accumulation of products of balanced residues (|r| <= 125) is exact
+ * for K <= 2^17 (exact-solve, "Requirements and limits"; enclosure-gemm,
+ * "Requirements and limits"). */
+#define RNS_K_MAX (1 << 17)
+/* operand limbs: up to four (a 256-bit fixed point, enclosure-gemm, "Method") */
+#define RNS_MAX_IN_LIMBS 4
+/* output limbs: the 54-prime range needs 6 (the pages' signed 384 bits) */
+#define RNS_MAX_OUT_LIMBS 8
+
+enum rns_status_code {
+    RNS_OK = 0,
+    RNS_E_ARG = -1,        /* null pointer, negative size, limbs out of range, bad plan */
+    RNS_E_K = -2,          /* K > 2^17, or K above the K the plan was made for */
+    RNS_E_CAPACITY = -3,   /* the bound 2*K*2^(a_bits+b_bits) is not below P of all 54 primes */
+    RNS_E_OUT_LIMBS = -4,  /* c_limbs < plan->out_limbs_min or > RNS_MAX_OUT_LIMBS */
+    RNS_E_WORKSPACE = -5,  /* ws_bytes smaller than rns_workspace_size reports */
+    RNS_E_HIP = -6         /* a HIP launch or copy failed */
+};
+
+/* Bits of the status word read by rns_status. */
+#define RNS_FLAG_A_RANGE 1u   /* some |A| entry exceeded 2^a_bits */
+#define RNS_FLAG_B_RANGE 2u   /* some |B| entry exceeded 2^b_bits */
+
+/* A prime plan.  Plain data, filled by rns_plan or rns_plan_n. */
+typedef struct rns_plan {
+    int32_t n_primes;        /* primes used, 1..54 */
+    int32_t out_limbs_min;   /* limbs that hold every value of (-P/2, P/2] */
+    int32_t a_bits;          /* declared |A| <= 2^a_bits; -1 when no bound is declared */
+    int32_t b_bits;          /* declared |B| <= 2^b_bits; -1 when no bound is declared */
+    int64_t k_max;           /* largest K the plan is valid for */
+    double  log2_P;          /* log2 of the product P of the primes used */
+    int32_t primes[RNS_MAX_PRIMES];  /* the primes used, largest first; rest 0 */
+} rns_plan_t;
+
+/*
+ * rns_plan -- choose the primes for |A| <= 2^a_bits, |B| <= 2^b_bits and
+ * contraction length K.
+ *
+ * The entries of C obey |C| <= K * 2^(a_bits+b_bits).  The plan takes the
+ * fewest primes, largest first (251, 241, 239, ...), whose product P strictly
+ * exceeds 2*K*2^(a_bits+b_bits), so that the balanced representative of C mod P
+ * is C itself (exact-solve, "Method": the precision must exceed twice the
+ * bound).  Accepts every case of the pages' budget
+ * a_bits + b_bits + ceil(log2 K) <= 332 (enclosure-gemm, "Requirements and
+ * limits"); the exact limit here is P of all 54 primes > 2*K*2^(a_bits+b_bits).
+ *
+ * K in 0..2^17 (K = 0 is planned as K = 1); a_bits, b_bits in 0..255.
+ * Returns RNS_OK, RNS_E_ARG (null out, bits out of range), RNS_E_K (K out of
+ * range) or RNS_E_CAPACITY.  On success out->k_max = max(K, 1).
+ */
+int rns_plan(int64_t K, int32_t a_bits, int32_t b_bits, rns_plan_t *out);
+
+/*
+ * rns_plan_n -- a plan of the n_primes largest primes below 256 (54 = all of
+ * them), with no operand bound.  The result of a GEMM under this plan is, by
+ * definition, the balanced representative in (-P/2, P/2] of the product mod
+ * P: this is the base-P digit of the lift step (exact-solve, "Method").  When
+ * P contains 2 (n_primes == 54) the range is (-P/2, P/2]; otherwise it is
+ * [-(P-1)/2, (P-1)/2].  k_max = 2^17.  Returns RNS_OK or RNS_E_ARG.
+ */
+int rns_plan_n(int32_t n_primes, rns_plan_t *out);
+
+/*
+ * rns_workspace_size -- device workspace bytes needed by rns_gemm
+ * (batched_residue == 0) or rns_gemm_batched_residue (batched_residue != 0)
+ * for this plan and shape.  The workspace holds the residue planes of both
+ * operands and of the product (about n*(M*K + N*K + M*N) bytes plus tile
+ * padding; cf. enclosure-gemm, "Requirements and limits" on working memory)
+ * and a small status area.  Writes the size to *bytes.
+ * Returns RNS_OK, RNS_E_ARG or RNS_E_K.
+ */
+int rns_workspace_size(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                       int32_t batched_residue, size_t *bytes);
+
+/*
+ * rns_gemm -- C = A @ B exactly.
+ *
+ * A: device int64 [M][K][a_limbs], B: device int64 [K][N][b_limbs],
+ * C: device int64 [M][N][c_limbs] (written in full, sign-extended),
+ * a_limbs, b_limbs in 1..4, c_limbs in plan->out_limbs_min..8,
+ * ws: device workspace of ws_bytes >= rns_workspace_size(plan, M, N, K, 0).
+ *
+ * Three kernels run on `stream`: the residue split of A and B into int8
+ * planes, the prime-batched INT8 MFMA product with a fused mod-q epilogue,
+ * and Garner reconstruction.  The result equals the integer product whenever
+ * the operands respect the plan's declared bounds; if an entry exceeds its
+ * bound, a flag is recorded for rns_status and C is unspecified.
+ * Returns RNS_OK, RNS_E_ARG, RNS_E_K (K > plan->k_max), RNS_E_OUT_LIMBS,
+ * RNS_E_WORKSPACE or RNS_E_HIP.
+ */
+int rns_gemm(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+             const int64_t *A, int32_t a_limbs,
+             const int64_t *B, int32_t b_limbs,
+             int64_t *C, int32_t c_limbs,
+             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rns_gemm_batched_residue -- the lift-step shape (exact-solve, "Method": each
+ * step's inverse mod q_j applied to the residual is one INT8 GEMM per prime,
+ * run as one batched product, and balanced Garner assembles the wide digit).
+ *
+ * A_res: device int8 [n_primes][M][K]; plane j is read as an integer matrix
+ *   mod plan->primes[j] (any int8 value is accepted; |a| <= 128 keeps the
+ *   int32 accumulation exact for K <= 2^17).
+ * B: device int64 [K][N][b_limbs], reduced per prime by the split kernel.
+ * C: device int64 [M][N][c_limbs]: the unique X in the plan's representative
+ *   range with X = A_res[j] @ B (mod primes[j]) for every j.
+ * Returns as rns_gemm.
+ */
+int rns_gemm_batched_residue(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                             const int8_t *A_res,
+                             const int64_t *B, int32_t b_limbs,
+                             int64_t *C, int32_t c_limbs,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Stage calls.  rns_gemm is exactly rns_split, then rns_residue_products,
+ * then rns_reconstruct on the same workspace and stream; the stages are
+ * exposed for callers that time them separately or keep the residue planes
+ * (for instance a lift that splits its residual once per step).  Arguments
+ * mean what they mean for rns_gemm / rns_gemm_batched_residue, and each
+ * stage validates them the same way.
+ *
+ * rns_split            -- kernel 1: the balanced int8 residue planes of A
+ *                         (skipped when A == NULL: the batched-residue
+ *                         variant) and of B, written into ws.
+ * rns_residue_products -- kernel 2: Y_j = (A_j @ B_j) mod q_j, balanced, for
+ *                         every prime; A_j from ws, or from A_res when it is
+ *                         not NULL (batched-residue variant).
+ * rns_reconstruct      -- kernel 3: Garner reconstruction of C from the Y
+ *                         planes; batched_residue selects the workspace
+ *                         layout of that variant.  K == 0 writes zeros.
+ */
+int rns_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+              const int64_t *A, int32_t a_limbs, const int64_t *B, int32_t b_limbs,
+              void *ws, size_t ws_bytes, hipStream_t stream);
+int rns_residue_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                         const int8_t *A_res, void *ws, size_t ws_bytes, hipStream_t stream);
+int rns_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                    int32_t batched_residue, int64_t *C, int32_t c_limbs,
+                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rns_status -- synchronises `stream`, then reports in *flags the
+ * RNS_FLAG_* bits recorded by the last rns_gemm / rns_gemm_batched_residue
+ * call that used workspace `ws` (0: every operand entry met its declared
+ * bound).  Returns RNS_OK, RNS_E_ARG or RNS_E_HIP.
+ */
+int rns_status(const void *ws, hipStream_t stream, uint32_t *flags);
+
+/*
+ * rns_workspace_layout -- where the residue planes live inside the
+ * workspace, for inspection by tests and for callers that reuse the planes.
+ * Plane j of an operand is the balanced residue of every entry mod
+ * plan->primes[j], stored as int8:
+ *   A planes: [n][m_pad][k_pad] at a_off   (row m, column k of A)
+ *   B planes: [n][n_pad][k_pad] at b_off   (column n, row k of B: transposed)
+ *   Y planes: [n][m_pad][n_pad] at y_off   (balanced (A_j @ B_j) mod q_j)
+ * Padding entries are zero.  In the batched-residue variant A planes are
+ * absent (a_off = -1) when the caller's A_res is used in place.
+ */
+typedef struct rns_layout {
+    int64_t m_pad, n_pad, k_pad;
+    int64_t a_off, b_off, y_off;
+    int64_t status_off;
+    int64_t total_bytes;
+    int32_t tile_config;     /* which GEMM tiling was chosen */
+} rns_layout_t;
+
+int rns_workspace_layout(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                         int32_t batched_residue, rns_layout_t *out);
+
+/* A constant string naming an RNS_* code. */
+const char *rns_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RNS_GEMM_H */

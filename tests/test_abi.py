@@ -1,0 +1,196 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every entry point ``include/rns_gemm.h``
+declares, share PyTorch's HIP runtime, plan exactly like the oracle, and turn
+every invalid argument into its error code before anything is launched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_integer_gemm_amd as rg
+from exact_integer_gemm_amd import _build
+from oracle import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rns_gemm.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if _build.is_stale():
+        _build.build()
+    return rg.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*\*?(rns_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"rns_plan", "rns_plan_n", "rns_workspace_size", "rns_gemm",
+                          "rns_gemm_batched_residue", "rns_status", "rns_error_string",
+                          "rns_workspace_layout"}
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = os.popen(f"nm -D --defined-only {_build.LIB}").read()
+    for n in names:
+        assert re.search(rf"\bT {n}\b", nm), f"{n} not exported"
+
+
+def test_one_hip_runtime_in_process(lib):
+    import torch  # noqa: F401  (already imported by the binding)
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    assert len(libs) == 1, libs
+
+
+def test_plan_struct_matches_header(lib):
+    # rns_plan_t: 4 int32, int64, double, int32[54]
+    assert ctypes.sizeof(rg._Plan) == 4 * 4 + 8 + 8 + 4 * 54
+
+
+@pytest.mark.parametrize("K,a,b", [(64, 20, 20), (1024, 31, 31), (4096, 55, 55), (4096, 100, 100),
+                                   (1, 0, 0), (2 ** 17, 1, 1), (3, 150, 170), (4096, 160, 160),
+                                   (1000, 7, 250), (0, 5, 5)])
+def test_plan_agrees_with_oracle(lib, K, a, b):
+    p = rg.plan(K, a, b)
+    ps = O.prime_set_for_bound(max(K, 1), a, b)
+    assert list(p.primes) == ps
+    assert p.n_primes == len(ps)
+    assert p.out_limbs_min == O.limbs_to_hold(O.prod(ps))
+    assert p.k_max == max(K, 1) and p.a_bits == a and p.b_bits == b
+    assert abs(p.log2_P - sum(__import__("math").log2(q) for q in ps)) < 1e-9
+
+
+def test_plan_sweep_against_oracle(lib):
+    for K in (1, 7, 64, 1000, 4096, 2 ** 17):
+        for s in range(0, 334, 9):
+            a, b = s // 2, s - s // 2
+            try:
+                ps = O.prime_set_for_bound(K, a, b)
+            except ValueError:
+                with pytest.raises(rg.RnsError) as e:
+                    rg.plan(K, a, b)
+                assert e.value.code == -3
+                continue
+            assert list(rg.plan(K, a, b).primes) == ps
+
+
+def test_plan_n(lib):
+    p = rg.plan_n(54)
+    assert list(p.primes) == O.primes_largest_first()
+    assert p.out_limbs_min == 6 and p.k_max == 2 ** 17 and p.a_bits == -1
+    assert list(rg.plan_n(10).primes) == O.primes_largest_first()[:10]
+    for bad in (0, -1, 55):
+        with pytest.raises(rg.RnsError) as e:
+            rg.plan_n(bad)
+        assert e.value.code == -1
+
+
+def test_plan_errors(lib):
+    with pytest.raises(rg.RnsError) as e:
+        rg.plan(2 ** 17 + 1, 1, 1)
+    assert e.value.code == -2
+    with pytest.raises(rg.RnsError) as e:
+        rg.plan(-1, 1, 1)
+    assert e.value.code == -2
+    with pytest.raises(rg.RnsError) as e:
+        rg.plan(4096, 170, 170)
+    assert e.value.code == -3
+    for a, b in ((-1, 3), (3, -1), (256, 0)):
+        with pytest.raises(rg.RnsError) as e:
+            rg.plan(16, a, b)
+        assert e.value.code == -1
+    assert lib.rns_plan(16, 1, 1, None) == -1
+
+
+def test_error_strings(lib):
+    for code in (0, -1, -2, -3, -4, -5, -6, 99):
+        s = rg.error_string(code)
+        assert isinstance(s, str) and s
+
+
+def test_workspace_size_and_layout(lib):
+    p = rg.plan(4096, 100, 100)
+    L = rg.layout(p, 2048, 2048, 4096)
+    n = p.n_primes
+    assert L["m_pad"] == 2048 and L["n_pad"] == 2048 and L["k_pad"] == 4096
+    assert L["y_off"] >= L["b_off"] + n * 2048 * 4096 > L["a_off"] + n * 2048 * 4096 - 1
+    assert rg.workspace_size(p, 2048, 2048, 4096) == L["total_bytes"]
+    # ragged shapes are padded to whole tiles
+    L = rg.layout(p, 65, 70, 130)
+    assert L["m_pad"] >= 65 and L["n_pad"] >= 70 and L["k_pad"] >= 130 and L["k_pad"] % 64 == 0
+    # batched residue: aligned A_res is used in place
+    p54 = rg.plan_n(54)
+    L = rg.layout(p54, 1024, 16, 1024, batched=True)
+    assert L["a_off"] == -1
+    L = rg.layout(p54, 1000, 16, 1000, batched=True)
+    assert L["a_off"] >= 0
+    with pytest.raises(rg.RnsError) as e:
+        rg.workspace_size(rg.plan(64, 20, 20), 64, 64, 65)
+    assert e.value.code == -2
+
+
+def _call_gemm(lib, plan, M, N, K, A=1 << 20, la=1, B=1 << 21, lb=1, C=1 << 22, lc=None,
+               ws=1 << 23, ws_bytes=None):
+    c = plan._c()
+    lc = plan.out_limbs_min if lc is None else lc
+    if ws_bytes is None:
+        ws_bytes = 1 << 40
+    return lib.rns_gemm(ctypes.byref(c), M, N, K, A, la, B, lb, C, lc, ws, ws_bytes, None)
+
+
+def test_gemm_validation_before_launch(lib):
+    # None of these reaches a launch: the pointers are never dereferenced.
+    p = rg.plan(64, 20, 20)
+    assert _call_gemm(lib, p, 64, 64, 64, lc=0) == -4
+    assert _call_gemm(lib, p, 64, 64, 64, lc=9) == -4
+    assert _call_gemm(lib, p, 64, 64, 64, la=0) == -1
+    assert _call_gemm(lib, p, 64, 64, 64, lb=5) == -1
+    assert _call_gemm(lib, p, -1, 64, 64) == -1
+    assert _call_gemm(lib, p, 64, 64, 65) == -2          # above the plan's K
+    assert _call_gemm(lib, p, 64, 64, 64, A=None) == -1
+    assert _call_gemm(lib, p, 64, 64, 64, ws=None) == -1
+    assert _call_gemm(lib, p, 64, 64, 64, ws_bytes=100) == -5
+    assert _call_gemm(lib, p, 0, 64, 64) == 0            # empty: no-op
+    assert _call_gemm(lib, p, 64, 0, 64, A=None, B=None, C=None, ws=None) == 0
+    bad = p._c()
+    bad.n_primes = 0
+    assert lib.rns_gemm(ctypes.byref(bad), 4, 4, 4, 1, 1, 1, 1, 1, 1, 1, 1 << 30, None) == -1
+    bad = p._c()
+    bad.primes[1] = bad.primes[0]      # repeated prime
+    assert lib.rns_gemm(ctypes.byref(bad), 4, 4, 4, 1, 1, 1, 1, 1, 1, 1, 1 << 30, None) == -1
+    bad = p._c()
+    bad.primes[0] = 250                # not a prime
+    assert lib.rns_gemm(ctypes.byref(bad), 4, 4, 4, 1, 1, 1, 1, 1, 1, 1, 1 << 30, None) == -1
+
+
+def test_batched_validation_before_launch(lib):
+    p = rg.plan_n(54)
+    c = p._c()
+    f = lib.rns_gemm_batched_residue
+    assert f(ctypes.byref(c), 8, 8, 8, None, 1, 1, 1, 6, 1, 1 << 30, None) == -1
+    assert f(ctypes.byref(c), 8, 8, 8, 1, 1, 1, 1, 5, 1, 1 << 30, None) == -4
+    assert f(ctypes.byref(c), 8, 8, 8, 1, 1, 0, 1, 6, 1, 1 << 30, None) == -1
+    assert f(ctypes.byref(c), 8, 8, 2 ** 17 + 1, 1, 1, 1, 1, 6, 1, 1 << 30, None) == -2
+    assert f(ctypes.byref(c), 8, 8, 8, 1, 1, 1, 1, 6, 1, 10, None) == -5
+    assert f(ctypes.byref(c), 0, 8, 8, None, None, 1, None, 6, None, 0, None) == 0
+
+
+def test_status_arguments(lib):
+    assert lib.rns_status(None, None, ctypes.byref(ctypes.c_uint32())) == -1
+    assert lib.rns_status(1, None, None) == -1
+
+
+def test_binding_rejects_bad_tensors(lib):
+    import torch
+    p = rg.plan(8, 4, 4)
+    A = torch.zeros((2, 8, 1), dtype=torch.int64)
+    with pytest.raises(ValueError):
+        rg.gemm(p, A, A.clone())          # CPU tensors are refused

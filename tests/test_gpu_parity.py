@@ -1,0 +1,282 @@
+"""Parity of the HIP path with the CPU oracle, element by element (GPU only).
+
+Every comparison is bit-exact: the path computes integers.  Small and medium
+shapes (several tiles plus a ragged tail in M, N and K) are compared in full
+against the C oracle; stage-level checks compare the residue planes the split
+kernel wrote, and the per-prime products the MFMA kernel wrote, with the
+oracle's stage definitions.  The full-size workloads are checked on sampled
+rows against the oracle and on the whole output by the Freivalds identity.
+"""
+import numpy as np
+import pytest
+import torch
+
+import exact_integer_gemm_amd as rg
+import workloads as W
+from oracle import oracle as O
+from oracle import cgemm
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rg.load()
+    cgemm.build()
+    yield
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def run_gemm(A, B, a_bits, b_bits, out_limbs=None, plan=None):
+    K = A.shape[1]
+    p = plan or rg.plan(K, a_bits, b_bits)
+    ws = rg.new_workspace(p, A.shape[0], B.shape[1], K)
+    C = rg.gemm(p, dev(A), dev(B), out_limbs=out_limbs, workspace=ws)
+    torch.cuda.synchronize()
+    return p, ws, C.cpu().numpy()
+
+
+def oracle_c(A, B, lc):
+    return cgemm.gemm(A, B, lc)
+
+
+SMALL = [
+    # M, N, K, la, lb, a_bits, b_bits, seed
+    (64, 64, 64, 1, 1, 20, 20, 11),       # one small tile
+    (70, 50, 130, 2, 1, 90, 40, 12),      # ragged everywhere
+    (1, 1, 1, 1, 1, 62, 62, 13),          # single entry
+    (33, 97, 65, 3, 2, 150, 100, 14),     # wide operands, ragged
+    (128, 24, 200, 1, 1, 62, 30, 15),     # skinny N (lift-step tiling)
+    (300, 280, 257, 1, 1, 40, 40, 16),    # small tiles, several per prime
+    (512, 512, 320, 2, 2, 100, 100, 17),  # big tiles
+    (513, 260, 129, 4, 4, 150, 160, 18),  # big tiles + ragged + 4 limbs
+    (17, 5, 4096, 1, 2, 60, 90, 19),      # long K, tiny output
+]
+
+
+@pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", SMALL)
+def test_product_exact_small(M, N, K, la, lb, ab, bb, seed):
+    print(f"case M={M} N={N} K={K} la={la} lb={lb} bits={ab},{bb} seed={seed}", flush=True)
+    A, B = W.random_operands(seed, M, N, K, la, lb, ab, bb)
+    p, ws, C = run_gemm(A, B, ab, bb)
+    ref = oracle_c(A, B, p.out_limbs_min)
+    assert C.shape == ref.shape
+    assert np.array_equal(C, ref)
+    assert rg.status(ws) == 0
+
+
+@pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", [SMALL[1], SMALL[3], SMALL[4], SMALL[7]])
+def test_stage_planes(M, N, K, la, lb, ab, bb, seed):
+    """Split planes and per-prime products against the oracle's stage definitions."""
+    print(f"stages M={M} N={N} K={K}", flush=True)
+    A, B = W.random_operands(seed, M, N, K, la, lb, ab, bb)
+    p, ws, C = run_gemm(A, B, ab, bb)
+    planes = rg.workspace_planes(p, ws, M, N, K)
+    Ap = planes["A"].cpu().numpy()
+    Bp = planes["B"].cpu().numpy()
+    Yp = planes["Y"].cpu().numpy()
+    Av, Bv = O.decode_array(A), O.decode_array(B)
+    refA = O.residue_planes(Av, p.primes)
+    refB = O.residue_planes(Bv.T, p.primes)
+    assert np.array_equal(Ap[:, :M, :K], refA)
+    assert not Ap[:, M:, :].any() and not Ap[:, :, K:].any()
+    assert np.array_equal(Bp[:, :N, :K], refB)
+    assert not Bp[:, N:, :].any() and not Bp[:, :, K:].any()
+    for j, q in enumerate(p.primes):
+        refY = O.residue_product(refA[j], refB[j].T, q)
+        assert np.array_equal(Yp[j, :M, :N], refY), f"prime {q}"
+
+
+def test_output_limbs_sign_extension():
+    A, B = W.random_operands(21, 40, 30, 50, 1, 1, 30, 30)
+    p, ws, C = run_gemm(A, B, 30, 30, out_limbs=5)
+    ref = oracle_c(A, B, 5)
+    assert np.array_equal(C, ref)
+
+
+def test_k_zero_and_empty():
+    p = rg.plan(0, 10, 10)
+    A = torch.zeros((5, 0, 1), dtype=torch.int64, device="cuda")
+    B = torch.zeros((0, 7, 1), dtype=torch.int64, device="cuda")
+    C = torch.full((5, 7, 1), 123, dtype=torch.int64, device="cuda")
+    rg.gemm(p, A, B, out=C, workspace=torch.empty(1, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert not C.any()
+    A = torch.zeros((0, 4, 1), dtype=torch.int64, device="cuda")
+    B = torch.zeros((4, 3, 1), dtype=torch.int64, device="cuda")
+    C = rg.gemm(rg.plan(4, 3, 3), A, B)
+    assert C.shape == (0, 3, 1)
+
+
+def test_extreme_operands_tight_bound():
+    # every entry at -2^a and -2^b: C = K * 2^(a+b) = the bound itself
+    for (K, a, b, la, lb) in [(64, 20, 20, 1, 1), (4096, 100, 100, 2, 2), (300, 62, 62, 1, 1),
+                              (1000, 200, 120, 4, 2)]:
+        M, N = 3, 5
+        Av = np.full((M, K), -(2 ** a), dtype=object)
+        Bv = np.full((K, N), -(2 ** b), dtype=object)
+        Av[1, :] = 2 ** a
+        Bv[:, 2] = 2 ** b
+        A, B = O.encode_array(Av, la), O.encode_array(Bv, lb)
+        p, ws, C = run_gemm(A, B, a, b)
+        got = O.decode_array(C)
+        assert np.array_equal(got, Av.dot(Bv))
+        assert got[0, 0] == K * 2 ** (a + b)
+        assert rg.status(ws) == 0
+
+
+def test_int32_accumulator_edge():
+    # K = 2^17 with every residue mod 251 equal to +125: the int32 sum reaches
+    # 2^17 * 125^2 = 2.048e9, the largest the accumulator must hold.
+    K = 2 ** 17
+    A = np.full((2, K, 1), 125, dtype=np.int64)
+    B = np.full((K, 3, 1), 125, dtype=np.int64)
+    B[:, 1, 0] = -125
+    A[1, ::2, 0] = 376          # 376 = 125 mod 251, other primes differ
+    p, ws, C = run_gemm(A, B, 9, 7)
+    Av, Bv = O.decode_array(A), O.decode_array(B)
+    assert np.array_equal(O.decode_array(C), Av.dot(Bv))
+
+
+def test_status_flags_out_of_bound():
+    A, B = W.random_operands(31, 20, 20, 40, 1, 1, 20, 20)
+    p = rg.plan(40, 20, 20)
+    A2 = A.copy()
+    A2[3, 7, 0] = 2 ** 20 + 1          # exceeds |a| <= 2^20
+    ws = rg.new_workspace(p, 20, 20, 40)
+    rg.gemm(p, dev(A2), dev(B), workspace=ws)
+    assert rg.status(ws) == rg.FLAG_A_RANGE
+    B2 = B.copy()
+    B2[0, 0, 0] = -(2 ** 20) - 1
+    rg.gemm(p, dev(A), dev(B2), workspace=ws)
+    assert rg.status(ws) == rg.FLAG_B_RANGE
+    A3 = A.copy()
+    A3[0, 0, 0] = 2 ** 20               # exactly at the bound: allowed
+    A3[0, 1, 0] = -(2 ** 20)
+    rg.gemm(p, dev(A3), dev(B), workspace=ws)
+    assert rg.status(ws) == 0
+
+
+def test_deterministic_bytes():
+    A, B = W.random_operands(41, 300, 300, 300, 2, 2, 100, 100)
+    p = rg.plan(300, 100, 100)
+    ws = rg.new_workspace(p, 300, 300, 300)
+    Ad, Bd = dev(A), dev(B)
+    C1 = rg.gemm(p, Ad, Bd, workspace=ws).clone()
+    C2 = rg.gemm(p, Ad, Bd, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C1, C2)
+
+
+# ---------------------------------------------------------------------------
+# batched residue (lift step)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K,n,seed", [(128, 16, 256, 54, 51), (100, 7, 70, 54, 52),
+                                          (256, 40, 192, 20, 53), (64, 1, 64, 1, 54)])
+def test_batched_residue_small(M, N, K, n, seed):
+    print(f"batched M={M} N={N} K={K} n={n}", flush=True)
+    rng = np.random.default_rng(seed)
+    p = rg.plan_n(n)
+    A_res = W.balanced_residue_planes(rng, p.primes, M, K)
+    r = rng.integers(-(1 << 34), 1 << 34, size=(K, N), endpoint=True)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None])).cpu().numpy()
+    ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
+    assert np.array_equal(O.decode_array(X), ref)
+
+
+def test_batched_residue_any_int8_and_extremes():
+    rng = np.random.default_rng(61)
+    p = rg.plan_n(54)
+    M, N, K = 8, 8, 2 ** 17
+    A_res = np.full((54, M, K), -128, dtype=np.int8)
+    A_res[:, 1::2, :] = 127
+    A_res[:, 5, :] = rng.integers(-128, 128, size=(54, K), dtype=np.int64).astype(np.int8)
+    r = np.full((K, N), 125, dtype=np.int64)
+    r[:, 3] = -(2 ** 63)
+    r[:, 4] = 2 ** 63 - 1
+    r[::3, 5] = rng.integers(-(2 ** 62), 2 ** 62, size=r[::3, 5].shape)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None])).cpu().numpy()
+    ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
+    assert np.array_equal(O.decode_array(X), ref)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at full size
+# ---------------------------------------------------------------------------
+FREIVALDS_P = 33554393   # the largest prime below 2^25: every product below 2^50, sums below 2^62
+
+
+def mod_p_limbs(x, p=FREIVALDS_P):
+    """int64 limbs [..., L] -> each value mod p (numpy int64), exactly."""
+    L = x.shape[-1]
+    acc = np.mod(x[..., L - 1], p)
+    w = (1 << 64) % p
+    for l in range(L - 2, -1, -1):
+        acc = np.mod(acc * w + np.mod(x[..., l].view(np.uint64), np.uint64(p)).astype(np.int64), p)
+    return acc
+
+
+def freivalds_mod(Am, Bm, Cm, seed, p=FREIVALDS_P):
+    """(A @ B) @ v == C @ v (mod p) for two random v; operands already reduced mod p."""
+    rng = np.random.default_rng(seed)
+    for _ in range(2):
+        v = rng.integers(0, p, size=Cm.shape[1], dtype=np.int64)
+        lhs = np.mod(Am @ np.mod(Bm @ v, p), p)
+        rhs = np.mod(Cm @ v, p)
+        if not np.array_equal(lhs, rhs):
+            return False
+    return True
+
+
+def test_freivalds_helper_catches_one_wrong_entry():
+    A, B = W.random_operands(5, 60, 50, 70, 2, 2, 100, 100)
+    C = oracle_c(A, B, 4)
+    assert freivalds_mod(mod_p_limbs(A), mod_p_limbs(B), mod_p_limbs(C), 1)
+    Cv = O.decode_array(C)
+    assert np.array_equal(mod_p_limbs(C), np.mod(Cv, FREIVALDS_P).astype(np.int64))
+    Cv[7, 9] += 1
+    assert not freivalds_mod(mod_p_limbs(A), mod_p_limbs(B), mod_p_limbs(O.encode_array(Cv, 4)), 1)
+
+
+def test_workload_tiny():
+    wl = W.make("tiny")
+    p, ws, C = run_gemm(wl.A, wl.B, wl.a_bits, wl.b_bits)
+    assert p.n_primes == 6
+    Av, Bv = O.decode_array(wl.A), O.decode_array(wl.B)
+    ref = np.array(O.int_matmul(Av.tolist(), Bv.tolist()), dtype=object)
+    assert np.array_equal(O.decode_array(C), ref)
+
+
+def test_workload_square():
+    wl = W.make("square")
+    p, ws, C = run_gemm(wl.A, wl.B, wl.a_bits, wl.b_bits)
+    assert p.n_primes == 10 and C.shape[-1] == 2
+    ref = oracle_c(wl.A, wl.B, 2)
+    assert np.array_equal(C, ref)
+
+
+@pytest.mark.parametrize("name,nprimes", [("enclosure", 16), ("wide", 29)])
+def test_workload_large_sampled(name, nprimes):
+    print(f"workload {name}", flush=True)
+    wl = W.make(name)
+    p, ws, C = run_gemm(wl.A, wl.B, wl.a_bits, wl.b_bits)
+    assert p.n_primes == nprimes
+    assert rg.status(ws) == 0
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(wl.M, size=8, replace=False))
+    ref = oracle_c(wl.A[rows], wl.B, C.shape[-1])
+    assert np.array_equal(C[rows], ref)
+    assert freivalds_mod(mod_p_limbs(wl.A), mod_p_limbs(wl.B), mod_p_limbs(C), 3)
+
+
+def test_workload_dixon():
+    p = rg.plan_n(54)
+    wl = W.make("dixon", primes=list(p.primes))
+    X = rg.gemm_batched_residue(p, dev(wl.A_res), dev(wl.B)).cpu().numpy()
+    assert X.shape == (1024, 16, 6)
+    ref = O.residue_gemm_via_crt(wl.A_res, wl.B[..., 0], O.primes_largest_first())
+    assert np.array_equal(O.decode_array(X), ref)
