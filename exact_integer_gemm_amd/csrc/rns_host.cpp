@@ -138,7 +138,7 @@ void build_split(const rns_plan_t &pl, int la, int lb, SplitConsts &c) {
     for (int j = 0; j < pl.n_primes; j++) {
         const int q = pl.primes[j];
         c.q[j] = q;
-        c.inv[j] = 1.0f / (float)q;
+        c.inv[j] = 1.0 / (double)q;
         for (int w = 0; w < 2 * RNS_MAX_IN_LIMBS; w++) {
             uint32_t packed = 0;
             for (int b = 0; b < 4; b++) {
@@ -157,8 +157,7 @@ void build_epi(const rns_plan_t &pl, EpiConsts &c) {
     for (int j = 0; j < pl.n_primes; j++) {
         const int q = pl.primes[j];
         c.q[j] = q;
-        c.c16[j] = balanced(65536, q);
-        c.inv[j] = 1.0f / (float)q;
+        c.inv[j] = 1.0 / (double)q;
     }
 }
 
@@ -176,12 +175,12 @@ void build_garner(const rns_plan_t &pl, GarnerConsts &g) {
     for (int k = 0; k < kGarnerSlots; k++) {
         if (k < n) {
             g.q[k] = (uint8_t)pl.primes[g.plane[k]];
-            g.inv[k] = 1.0f / (float)g.q[k];
+            g.inv[k] = 1.0 / (double)g.q[k];
         } else {
             // inert padding slot: reads plane of slot 0, multiplies it by 0
             g.plane[k] = g.plane[0];
             g.q[k] = 1;
-            g.inv[k] = 1.0f;
+            g.inv[k] = 1.0;
         }
     }
     // Q_j mod q_k for j <= k, by running products

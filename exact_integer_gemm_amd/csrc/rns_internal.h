@@ -16,10 +16,10 @@ constexpr int kMaxPrimes = RNS_MAX_PRIMES;   // 54
 constexpr int kGarnerSlots = 56;             // kMaxPrimes rounded up to 8
 constexpr int kTriEntries = kGarnerSlots * (kGarnerSlots + 1) / 2;
 
-// 1.5 * 2^23: adding it to a float |x| < 2^22 rounds x to the nearest
-// integer j and leaves 0x4B400000 + j in the bit pattern.
-constexpr float kRoundMagic = 12582912.0f;
-constexpr int32_t kRoundMagicBits = 0x4B400000;
+// 1.5 * 2^52: adding it to a double |x| < 2^51 rounds x to the nearest
+// integer j and leaves j in the low 32 bits of the bit pattern (two's
+// complement), because the low 32 bits of 1.5 * 2^52 are zero.
+constexpr double kRoundMagic = 6755399441055744.0;
 
 // ---- residue split (kernel 1) ---------------------------------------------
 // An operand entry x of L limbs is read as U = x + 2^(64L-1) (its top bit
@@ -30,20 +30,17 @@ constexpr int32_t kRoundMagicBits = 0x4B400000;
 struct SplitConsts {
     int32_t n;
     int32_t q[kMaxPrimes];
-    float inv[kMaxPrimes];                 // fl(1/q)
+    double inv[kMaxPrimes];                // fl(1/q) in binary64
     uint32_t w[kMaxPrimes][2 * RNS_MAX_IN_LIMBS];  // packed bytes 256^(4w+i) mod q
     int32_t h_a[kMaxPrimes];               // 2^(64*la - 1) mod q
     int32_t h_b[kMaxPrimes];               // 2^(64*lb - 1) mod q
 };
 
 // ---- mod-q epilogue of the residue product (kernel 2) ----------------------
-// s = hi * 2^16 + lo  ==>  s = hi * c16 + lo (mod q) with c16 = 2^16 mod q
-// (balanced), a value below 2^22 in magnitude that the float rounding step
-// reduces exactly.
+// The int32 accumulator s itself goes through the binary64 rounding step.
 struct EpiConsts {
     int32_t q[kMaxPrimes];
-    int32_t c16[kMaxPrimes];
-    float inv[kMaxPrimes];
+    double inv[kMaxPrimes];
 };
 
 // ---- Garner reconstruction (kernel 3) --------------------------------------
@@ -66,7 +63,7 @@ struct GarnerConsts {
     int32_t n;
     uint8_t plane[kGarnerSlots];   // Garner slot -> residue plane index
     uint8_t q[kGarnerSlots];
-    float inv[kGarnerSlots];
+    double inv[kGarnerSlots];
     int8_t tri[kTriEntries];
     uint16_t q16[kMaxQChunks];
 };
@@ -77,7 +74,7 @@ __host__ __device__ constexpr int tri_index(int j, int k) {
 
 // ---- GEMM tilings ----------------------------------------------------------
 enum TileConfig : int32_t {
-    kTileBig = 0,      // 256 x 256 x 64, four waves of 128 x 128
+    kTileBig = 0,      // 256 x 256 x 64, four waves of 128 x 128, LDS ring fed by DMA
     kTileSmall = 1,    // 64 x 64 x 64, four waves of 32 x 32
     kTileSkinny = 2,   // 128 x 32 x 64, four waves of 32 x 32 stacked along M
 };

@@ -8,11 +8,12 @@
 //   K3 garner  : balanced Garner mixed-radix digits -> signed int64 limbs
 //                (exact-solve, "Method"; enclosure-gemm, "Method").
 //
-// All reductions mod q use one exact float rounding step: for |t| < 2^22 and
-// odd q the nearest integer to t/q is computed exactly from fl(1/q) (the
-// relative error 2^-24 moves t/q by less than 1/(4q), while t/q is at least
-// 1/(2q) away from every half-integer), so t - q*round(t/q) is the balanced
-// residue.  q = 2 is handled separately (the low bit).
+// All reductions mod q use one exact rounding step in binary64: for |t| < 2^31
+// the nearest integer to t/q is computed exactly from fl(1/q) (the relative
+// error 2^-53 moves t/q by less than 2^-22, while for odd q the value t/q is
+// at least 1/(2q) away from every half-integer), so t - q*round(t/q) is the
+// balanced residue.  Adding 1.5 * 2^52 in the same fused multiply-add leaves
+// round(t/q) in the low 32 bits of the result.  q = 2 is handled separately.
 #include <hip/hip_runtime.h>
 
 #include "rns_internal.h"
@@ -23,21 +24,21 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
-// round(t / q) + 0x400000 in the low 24 bits, for |t| < 2^22
-__device__ __forceinline__ int round_q_bits(int t, float inv) {
-    return __float_as_int(__builtin_fmaf((float)t, inv, kRoundMagic));
+// round(t / q) as a 32-bit integer, for |t| < 2^31 and odd q (exact).
+__device__ __forceinline__ int round_div(int t, double inv) {
+    const double g = __builtin_fma((double)t, inv, kRoundMagic);
+    return (int)(uint32_t)__double_as_longlong(g);
 }
 
-// t - q * round(t / q): the balanced residue of t, for |t| < 2^22 and odd q.
-__device__ __forceinline__ int reduce_exact(int t, int q, float inv) {
-    int qe = round_q_bits(t, inv) - kRoundMagicBits;
-    return t - qe * q;
+// t - q * round(t / q): the balanced residue of t, exact for |t| < 2^23 and odd q.
+__device__ __forceinline__ int reduce_exact(int t, int q, double inv) {
+    return __mul24(round_div(t, inv), -q) + t;
 }
 
-// Same value minus q * 2^22: correct in its low byte (q * 2^22 = 0 mod 256),
-// one instruction shorter.  Used where only the int8 residue is stored.
-__device__ __forceinline__ int reduce_low_byte(int t, int q, float inv) {
-    return __mul24(round_q_bits(t, inv), -q) + t;
+// The same expression for any |t| < 2^31: the 24-bit product wraps, but
+// only mod 2^24, so the low byte (the int8 residue that is stored) is exact.
+__device__ __forceinline__ int reduce_low_byte(int t, int q, double inv) {
+    return __mul24(round_div(t, inv), -q) + t;
 }
 
 __device__ __forceinline__ uint32_t pack4(int b0, int b1, int b2, int b3) {
@@ -126,7 +127,7 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
                 word[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
             }
         } else {
-            const float inv = c.inv[p];
+            const double inv = c.inv[p];
             const int hp = h[p];
             int res[kRun];
 #pragma unroll
@@ -240,11 +241,17 @@ int launch_repack_residues(const int8_t *src, int64_t n, int64_t M, int64_t K,
 // Operands are K-contiguous int8 planes: A [Mp][Kp] and B^T [Np][Kp] per prime.
 // A block computes one BM x BN tile of one prime.  Tiles of BK bytes of K are
 // staged through LDS (double buffered, one barrier per step) as 16-byte
-// chunks, XOR-swizzled so that the 16-lane and 8-lane phases of ds_read_b128
-// hit distinct banks.  Each wave owns a (BM/WM) x (BN/WN) sub-tile built from
-// v_mfma_i32_32x32x32_i8.  The MFMA is fed B^T as its first operand so that
-// each lane's accumulators hold four consecutive output columns of one row,
-// which pack into one 32-bit store of int8 residues.
+// chunks, XOR-swizzled so that fragment reads are free of bank conflicts
+// (see swz).  Each wave owns a (BM/WM) x (BN/WN) sub-tile built from
+// v_mfma_i32_32x32x32_i8; the operand fragments of the next 32-wide K slice
+// are read from LDS while the MFMAs of the current one run.  The MFMA is fed
+// B^T as its first operand so that each lane's accumulators hold four
+// consecutive output columns of one row, which pack into one 32-bit store.
+//
+// Block order: the hardware hands consecutive workgroups to the 8 XCDs in
+// turn, so workgroup i is remapped to tile (i % 8) * G/8 + i / 8: each XCD
+// works through a contiguous run of tiles of the same prime, whose A rows
+// and B columns its own L2 then serves to all of them.
 struct GemmArgs {
     const int8_t *a;
     const int8_t *b;
@@ -254,9 +261,16 @@ struct GemmArgs {
     int32_t tiles_m, tiles_n;
 };
 
+// ds_read_b128 is served 32 lanes at a time from 64 banks of 4 bytes: a
+// group is conflict-free when every 16-byte bank slot (address / 16 mod 16)
+// is hit by exactly two of its lanes.  A fragment read has 32 consecutive
+// rows at one logical chunk, so the physical chunk is XORed with bits of the
+// row that, together with the row's own slot offset, spread the 32 rows
+// evenly: for 64-byte rows the slot is 4 * (row & 3) + chunk, for 128-byte
+// rows 8 * (row & 1) + chunk.
 template <int CH>
 __device__ __forceinline__ int swz(int row) {
-    if constexpr (CH == 4) return ((row >> 1) ^ (row >> 3)) & 3;
+    if constexpr (CH == 4) return (row >> 2) & 3;
     else return (row ^ (row >> 3)) & 7;
 }
 
@@ -267,20 +281,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
     constexpr int TM = BM / WM, TN = BN / WN;
     constexpr int FM = TM / 32, FN = TN / 32;
     constexpr int CH = BK / 16;
+    constexpr int KK = BK / 32;
     constexpr int A_CHUNKS = BM * CH, B_CHUNKS = BN * CH;
     constexpr int LA = (A_CHUNKS + NT - 1) / NT, LB = (B_CHUNKS + NT - 1) / NT;
-    static_assert(FM >= 1 && FN >= 1 && BK % 32 == 0, "tile shape");
+    static_assert(FM >= 1 && FN >= 1 && KK % 2 == 0, "tile shape");
 
     __shared__ v4i lds[2][A_CHUNKS + B_CHUNKS];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int wm = wave / WN, wn = wave % WN;
+    const int half = lane >> 5, l32 = lane & 31;
 
+    // XCD-aware workgroup -> tile map (a bijection on [0, G))
+    const int G = gridDim.x;
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int tile = xcd * (G >> 3) + min(xcd, G & 7) + idx;
     const int per_prime = g.tiles_m * g.tiles_n;
-    const int p = blockIdx.x / per_prime;
-    const int t = blockIdx.x - p * per_prime;
+    const int p = tile / per_prime;
+    const int t = tile - p * per_prime;
     const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
 
     const int8_t *Ap = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.kp;
@@ -291,18 +311,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
 #pragma unroll
         for (int i = 0; i < LA; i++) {
             const int c = tid + i * NT;
-            if (A_CHUNKS % NT == 0 || c < A_CHUNKS) {
-                const int row = c / CH, col = c % CH;
-                ra[i] = *(const v4i *)(Ap + (int64_t)row * g.kp + k0 + col * 16);
-            }
+            if (A_CHUNKS % NT == 0 || c < A_CHUNKS)
+                ra[i] = *(const v4i *)(Ap + (int64_t)(c / CH) * g.kp + k0 + (c % CH) * 16);
         }
 #pragma unroll
         for (int i = 0; i < LB; i++) {
             const int c = tid + i * NT;
-            if (B_CHUNKS % NT == 0 || c < B_CHUNKS) {
-                const int row = c / CH, col = c % CH;
-                rb[i] = *(const v4i *)(Bp + (int64_t)row * g.kp + k0 + col * 16);
-            }
+            if (B_CHUNKS % NT == 0 || c < B_CHUNKS)
+                rb[i] = *(const v4i *)(Bp + (int64_t)(c / CH) * g.kp + k0 + (c % CH) * 16);
         }
     };
     auto store_lds = [&](int buf) {
@@ -323,6 +339,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
             }
         }
     };
+    auto read_frags = [&](int buf, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
+        const int chunk = kk * 2 + half;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int row = wm * TM + i * 32 + l32;
+            af[i] = lds[buf][row * CH + (chunk ^ swz<CH>(row))];
+        }
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const int row = wn * TN + j * 32 + l32;
+            bf[j] = lds[buf][A_CHUNKS + row * CH + (chunk ^ swz<CH>(row))];
+        }
+    };
 
     v16i acc[FM][FN];
 #pragma unroll
@@ -330,44 +359,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
 #pragma unroll
         for (int j = 0; j < FN; j++) acc[i][j] = v16i{0};
 
+    v4i af[2][FM], bf[2][FN];
     const int KT = g.kp / BK;
     if (KT > 0) {
         load_global(0);
         store_lds(0);
     }
     __syncthreads();
-    const int half = lane >> 5, l32 = lane & 31;
+    if (KT > 0) read_frags(0, 0, af[0], bf[0]);
     for (int kt = 0; kt < KT; kt++) {
         const int buf = kt & 1;
-        if (kt + 1 < KT) load_global((kt + 1) * BK);
+        const bool more = kt + 1 < KT;
+        if (more) load_global((kt + 1) * BK);
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; kk++) {
-            const int chunk = kk * 2 + half;
-            v4i af[FM], bf[FN];
-#pragma unroll
-            for (int i = 0; i < FM; i++) {
-                const int row = wm * TM + i * 32 + l32;
-                af[i] = lds[buf][row * CH + (chunk ^ swz<CH>(row))];
-            }
-#pragma unroll
-            for (int j = 0; j < FN; j++) {
-                const int row = wn * TN + j * 32 + l32;
-                bf[j] = lds[buf][A_CHUNKS + row * CH + (chunk ^ swz<CH>(row))];
-            }
+        for (int kk = 0; kk < KK; kk++) {
+            const int cur = kk & 1;
+            if (kk + 1 < KK) read_frags(buf, kk + 1, af[cur ^ 1], bf[cur ^ 1]);
 #pragma unroll
             for (int i = 0; i < FM; i++)
 #pragma unroll
                 for (int j = 0; j < FN; j++)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[cur][j], af[cur][i],
+                                                                      acc[i][j], 0, 0, 0);
         }
-        if (kt + 1 < KT) store_lds(buf ^ 1);
+        if (more) store_lds(buf ^ 1);
         __syncthreads();
+        if (more) read_frags(buf ^ 1, 0, af[0], bf[0]);
     }
 
     // epilogue: balanced residue mod q of every accumulator, as int8
     const int q = ec.q[p];
-    const int c16 = ec.c16[p];
-    const float inv = ec.inv[p];
+    const double inv = ec.inv[p];
     int8_t *Yp = g.y + p * g.y_plane;
 #pragma unroll
     for (int i = 0; i < FM; i++) {
@@ -381,16 +403,334 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     const int s = acc[i][j][4 * gq + e];
-                    if (q == 2) {
-                        r[e] = s & 1;
-                    } else {
-                        const int tt = __mul24(s >> 16, c16) + (s & 0xffff);
-                        r[e] = reduce_low_byte(tt, q, inv);
-                    }
+                    r[e] = q == 2 ? (s & 1) : reduce_low_byte(s, q, inv);
                 }
                 *(uint32_t *)(Yp + m * g.np + n) = pack4(r[0], r[1], r[2], r[3]);
             }
         }
+    }
+}
+
+// ---- the large-tile variant: LDS fed by direct global->LDS loads -----------
+// 256 x 256 tiles, BK = 64, an S-stage LDS ring filled by global_load_lds
+// (each wave-level load writes 64 lanes x 16 bytes, contiguous in LDS, so the
+// swizzle is applied to the global addresses instead).  Tile kt + S - 1 is
+// requested while tile kt is multiplied; one barrier per step, placed half
+// way through the second MFMA slice so that the MFMA pipe has queued work
+// while waves meet.  The loads are asynchronous to the waves: each wave waits
+// (vmcnt) for its own share of the next tile before the barrier, which then
+// publishes the whole tile.
+template <int S>
+__global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g, EpiConsts ec) {
+    constexpr int BM = 256, BN = 256, BK = 64, CH = BK / 16;
+    constexpr int FM = 4, FN = 4;                  // 128 x 128 per wave
+    constexpr int TILE_CHUNKS = (BM + BN) * CH;    // 2048 chunks = 32 KB per stage
+    constexpr int LOADS = TILE_CHUNKS / 256;       // 8 wave-level loads per wave per stage
+    static_assert(S >= 2 && S * TILE_CHUNKS * 16 <= 160 * 1024, "LDS ring");
+
+    __shared__ v4i lds[S][TILE_CHUNKS];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int wm = wave >> 1, wn = wave & 1;
+    const int half = lane >> 5, l32 = lane & 31;
+
+    const int G = gridDim.x;
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int tile = xcd * (G >> 3) + min(xcd, G & 7) + idx;
+    const int per_prime = g.tiles_m * g.tiles_n;
+    const int p = tile / per_prime;
+    const int t = tile - p * per_prime;
+    const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
+    const int8_t *Ap = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.kp;
+    const int8_t *Bp = g.b + p * g.b_plane + (int64_t)(tn * BN) * g.kp;
+
+    // Load j (0..7) of this wave fills LDS slots [(j*4 + wave)*64, +64): slot
+    // s holds row s / CH (A rows first, then B rows) and physical chunk
+    // s % CH, i.e. logical chunk (s % CH) ^ swz(row) of that row.
+    const int8_t *src[LOADS];
+#pragma unroll
+    for (int j = 0; j < LOADS; j++) {
+        const int s = (j * 4 + wave) * 64 + lane;
+        const int row = s / CH;
+        const int c = (s % CH) ^ swz<CH>(row);
+        src[j] = row < BM ? Ap + (int64_t)row * g.kp + c * 16
+                          : Bp + (int64_t)(row - BM) * g.kp + c * 16;
+    }
+    auto issue = [&](int kt) {
+        v4i *dst = lds[kt % S];
+#pragma unroll
+        for (int j = 0; j < LOADS; j++)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src[j] + kt * BK),
+                (__attribute__((address_space(3))) void *)(dst + (j * 4 + wave) * 64), 16, 0, 0);
+    };
+    // wait until at most `tiles` later tiles' loads of this wave are pending
+    auto wait_tiles = [&](int tiles) {
+        // s_waitcnt vmcnt(8 * tiles), other counters untouched (gfx9 encoding)
+        if (tiles <= 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+        else if (tiles == 1) __builtin_amdgcn_s_waitcnt(0x0f78);
+        else __builtin_amdgcn_s_waitcnt(0x4f70);   // vmcnt(16)
+    };
+    auto read_frags = [&](int buf, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
+        const int chunk = kk * 2 + half;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int row = wm * 128 + i * 32 + l32;
+            af[i] = lds[buf][row * CH + (chunk ^ swz<CH>(row))];
+        }
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const int row = BM + wn * 128 + j * 32 + l32;
+            bf[j] = lds[buf][row * CH + (chunk ^ swz<CH>(row))];
+        }
+    };
+
+    v16i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = v16i{0};
+    auto mfma_rows = [&](const v4i (&af)[FM], const v4i (&bf)[FN], int i0, int i1) {
+#pragma unroll
+        for (int i = i0; i < i1; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
+    };
+
+    const int KT = g.kp / BK;
+    v4i af0[FM], bf0[FN], af1[FM], bf1[FN];
+    if (KT > 0) {
+#pragma unroll
+        for (int s = 0; s < S - 1; s++)
+            if (s < KT) issue(s);
+        wait_tiles(min(S - 2, KT - 1));
+        __syncthreads();
+        read_frags(0, 0, af0, bf0);
+    }
+    for (int kt = 0; kt < KT; kt++) {
+        const int buf = kt % S;
+        read_frags(buf, 1, af1, bf1);
+        mfma_rows(af0, bf0, 0, FM);
+        if (kt + S - 1 < KT) issue(kt + S - 1);
+        mfma_rows(af1, bf1, 0, FM / 2);
+        if (kt + 1 < KT) {
+            // tiles issued after kt + 1: kt + 2 .. min(kt + S - 1, KT - 1)
+            wait_tiles(min(kt + S - 1, KT - 1) - (kt + 1));
+            __syncthreads();
+            read_frags((kt + 1) % S, 0, af0, bf0);
+        }
+        mfma_rows(af1, bf1, FM / 2, FM);
+    }
+
+    const int q = ec.q[p];
+    const double inv = ec.inv[p];
+    int8_t *Yp = g.y + p * g.y_plane;
+#pragma unroll
+    for (int i = 0; i < FM; i++) {
+        const int64_t m = tm * BM + wm * 128 + i * 32 + l32;
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++) {
+                const int n = tn * BN + wn * 128 + j * 32 + 8 * gq + 4 * half;
+                int r[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int s = acc[i][j][4 * gq + e];
+                    r[e] = q == 2 ? (s & 1) : reduce_low_byte(s, q, inv);
+                }
+                *(uint32_t *)(Yp + m * g.np + n) = pack4(r[0], r[1], r[2], r[3]);
+            }
+        }
+    }
+}
+
+// ---- the large-tile variant: 8 waves in ping-pong ----------------------------
+// 256 x 256 tiles, BK = 64, 512 threads: two waves per SIMD (waves w and w+4
+// share SIMD w % 4).  Each wave owns a 128 x 64 sub-tile (8 accumulator
+// chains).  The waves form two groups that alternate between a compute phase
+// (16 MFMAs on fragments already in registers) and a memory phase (requesting
+// a later K step with direct global->LDS loads and reading the fragments of
+// the next step), one group in each phase at any time, so that one wave per
+// SIMD always has MFMAs to issue while its partner waits on memory.  Phases
+// end at a plain s_barrier; ordering is by explicit counter waits: in its
+// memory phase for step j a wave waits (vmcnt) for its own loads of step
+// j + 1 and (lgkmcnt) for its fragment reads, so after the next barrier step
+// j + 1 is complete in LDS and step j - 1's stage is no longer read.  The LDS
+// holds an S-stage ring; step j + S - 1 is requested during the memory phase
+// of step j, into the stage of step j - 1.
+template <int S>
+__global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g, EpiConsts ec) {
+    constexpr int BM = 256, BN = 256, BK = 64, CH = BK / 16;
+    constexpr int FM = 4, FN = 2;                  // 128 x 64 per wave
+    constexpr int STAGE = (BM + BN) * CH;          // 2048 chunks = 32 KB
+    constexpr int DPW = STAGE / 512;               // 4 loads per wave per step
+    constexpr int D = S - 1;                       // prefetch distance in steps
+    constexpr int OUT_PITCH = BN + 16;             // bytes per LDS row of the output tile
+    static_assert(S >= 2 && S <= 4 && S * STAGE * 16 <= 160 * 1024, "LDS ring");
+    static_assert(BM * OUT_PITCH <= S * STAGE * 16, "output staging fits the ring");
+
+    __shared__ v4i lds[S][STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int group = wave >> 2;
+    const int wm = wave & 1, wn = wave >> 1;       // 2 x 4 waves over the tile
+    const int half = lane >> 5, l32 = lane & 31;
+
+    const int G = gridDim.x;
+    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
+    const int tile = xcd * (G >> 3) + min(xcd, G & 7) + idx;
+    const int per_prime = g.tiles_m * g.tiles_n;
+    const int p = tile / per_prime;
+    const int t = tile - p * per_prime;
+    const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
+    const int8_t *Ap = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.kp;
+    const int8_t *Bp = g.b + p * g.b_plane + (int64_t)(tn * BN) * g.kp;
+
+    // Load j of this wave fills LDS slots [(j*8 + wave)*64, +64) of a stage.
+    const int8_t *src[DPW];
+#pragma unroll
+    for (int j = 0; j < DPW; j++) {
+        const int s = (j * 8 + wave) * 64 + lane;
+        const int row = s / CH;
+        const int c = (s % CH) ^ swz<CH>(row);
+        src[j] = row < BM ? Ap + (int64_t)row * g.kp + c * 16
+                          : Bp + (int64_t)(row - BM) * g.kp + c * 16;
+    }
+    const int KT = g.kp / BK;
+    auto issue = [&](int step) {
+        v4i *dst = lds[step % S];
+#pragma unroll
+        for (int j = 0; j < DPW; j++)
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)(src[j] + step * BK),
+                (__attribute__((address_space(3))) void *)(dst + (j * 8 + wave) * 64), 16, 0, 0);
+    };
+    // s_waitcnt vmcnt(4 * n), other counters untouched (gfx9 encoding: vmcnt
+    // in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8): at most n later steps
+    // of this wave's loads may still be pending
+    auto wait_steps = [&](int n) {
+        if (n <= 0) __builtin_amdgcn_s_waitcnt(0x0f70);
+        else if (n == 1) __builtin_amdgcn_s_waitcnt(0x0f74);
+        else __builtin_amdgcn_s_waitcnt(0x0f78);
+    };
+    auto read_frags = [&](int stage, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
+        const int chunk = kk * 2 + half;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int row = wm * 128 + i * 32 + l32;
+            af[i] = lds[stage][row * CH + (chunk ^ swz<CH>(row))];
+        }
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const int row = BM + wn * 64 + j * 32 + l32;
+            bf[j] = lds[stage][row * CH + (chunk ^ swz<CH>(row))];
+        }
+    };
+
+    v16i acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; i++)
+#pragma unroll
+        for (int j = 0; j < FN; j++) acc[i][j] = v16i{0};
+    v4i af0[FM], bf0[FN], af1[FM], bf1[FN];
+
+    // memory phase for step j: request step j + D, read the fragments of step
+    // j, then wait for own loads of step j + 1 and for the fragments
+    auto memory = [&](int j) {
+        if (j + D < KT) issue(j + D);
+        read_frags(j % S, 0, af0, bf0);
+        read_frags(j % S, 1, af1, bf1);
+        wait_steps(min(j + D, KT - 1) - (j + 1));
+        __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0)
+    };
+    auto compute = [&]() {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf0[j], af0[i], acc[i][j], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf1[j], af1[i], acc[i][j], 0, 0, 0);
+    };
+
+    if (KT > 0) {
+#pragma unroll
+        for (int s = 0; s < D; s++)
+            if (s < KT) issue(s);
+        wait_steps(min(D - 1, KT - 1));            // own loads of step 0 done
+        __builtin_amdgcn_s_barrier();               // step 0 visible
+        // Every wave runs memory(j), barrier, compute, barrier.  Group 1
+        // starts one barrier late (and group 0 ends one barrier late), so
+        // the compute phase of one group coincides with the memory phase of
+        // the other.
+        // sched_barrier(0) keeps the compiler from moving instructions
+        // across a phase boundary.
+        if (group == 1) __builtin_amdgcn_s_barrier();
+        for (int j = 0; j < KT; j++) {
+            memory(j);
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            compute();
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (group == 0) __builtin_amdgcn_s_barrier();
+    }
+
+    // epilogue: residues mod q as int8, staged through LDS (row pitch
+    // OUT_PITCH bytes) so that the tile leaves in whole 16-byte row chunks
+    __builtin_amdgcn_s_waitcnt(0x0f70);             // vmcnt(0): no load may still target LDS
+    __syncthreads();
+    int8_t *out = (int8_t *)&lds[0][0];
+    const int q = ec.q[p];
+    const double inv = ec.inv[p];
+    if (q == 2) {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
+                    const int row = wm * 128 + i * 32 + l32;
+                    const int col = wn * 64 + j * 32 + 8 * gq + 4 * half;
+                    const v16i &a = acc[i][j];
+                    *(uint32_t *)(out + row * OUT_PITCH + col) =
+                        pack4(a[4 * gq] & 1, a[4 * gq + 1] & 1, a[4 * gq + 2] & 1, a[4 * gq + 3] & 1);
+                }
+    } else {
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
+                    const int row = wm * 128 + i * 32 + l32;
+                    const int col = wn * 64 + j * 32 + 8 * gq + 4 * half;
+                    const v16i &a = acc[i][j];
+                    *(uint32_t *)(out + row * OUT_PITCH + col) =
+                        pack4(reduce_low_byte(a[4 * gq], q, inv), reduce_low_byte(a[4 * gq + 1], q, inv),
+                              reduce_low_byte(a[4 * gq + 2], q, inv), reduce_low_byte(a[4 * gq + 3], q, inv));
+                }
+    }
+    __syncthreads();
+    int8_t *Yp = g.y + p * g.y_plane + (int64_t)(tm * BM) * g.np + tn * BN;
+    // 256 rows x 256 bytes: 16 lanes per row, 32 rows per pass of 512 threads
+#pragma unroll
+    for (int pass = 0; pass < BM / 32; pass++) {
+        const int row = pass * 32 + (tid >> 4);
+        const int c = (tid & 15) * 16;
+        *(v4i *)(Yp + (int64_t)row * g.np + c) = *(const v4i *)(out + row * OUT_PITCH + c);
     }
 }
 
@@ -406,7 +746,7 @@ int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
     if (grid > 0x7fffffff || m_pad > 0x7fffffff || n_pad > 0x7fffffff) return RNS_E_ARG;
     switch (cfg) {
         case kTileBig:
-            hipLaunchKernelGGL((gemm_kernel<256, 256, 64, 2, 2>), dim3((unsigned)grid), dim3(256), 0, s, g, c);
+            hipLaunchKernelGGL((gemm_pp_kernel<4>), dim3((unsigned)grid), dim3(512), 0, s, g, c);
             break;
         case kTileSmall:
             hipLaunchKernelGGL((gemm_kernel<64, 64, 64, 2, 2>), dim3((unsigned)grid), dim3(256), 0, s, g, c);
