@@ -54,6 +54,7 @@ class _Plan(ctypes.Structure):
 
 class _Layout(ctypes.Structure):
     _fields_ = [("m_pad", ctypes.c_int64), ("n_pad", ctypes.c_int64), ("k_pad", ctypes.c_int64),
+                ("k_block", ctypes.c_int64), ("y_pitch", ctypes.c_int64),
                 ("a_off", ctypes.c_int64), ("b_off", ctypes.c_int64), ("y_off", ctypes.c_int64),
                 ("status_off", ctypes.c_int64), ("total_bytes", ctypes.c_int64),
                 ("tile_config", ctypes.c_int32)]
@@ -312,16 +313,26 @@ def status(workspace: torch.Tensor) -> int:
 
 def workspace_planes(p: Plan, workspace: torch.Tensor, M: int, N: int, K: int,
                      batched: bool = False) -> dict:
-    """Views of the residue planes a call left in ``workspace`` (for inspection)."""
+    """Views of the residue planes a call left in ``workspace`` (for inspection).
+
+    Returns int8 tensors [n, rows, cols] under keys "A" (absent when the
+    batched-residue operand was used in place), "B" (copies gathered from the
+    K-blocked planes) and "Y" (a strided view), plus the layout under "layout".
+    """
     L = layout(p, M, N, K, batched)
     n = p.n_primes
+    ws8 = workspace.view(torch.int8)
     out = {"layout": L}
+    kb = L["k_block"]
 
-    def view(off, rows, cols):
-        return workspace[off:off + n * rows * cols].view(torch.int8).view(n, rows, cols)
+    def blocked(off, rows):
+        kpad = L["k_pad"]
+        v = ws8[off:off + n * rows * kpad].view(n, kpad // kb, rows, kb)
+        return v.permute(0, 2, 1, 3).reshape(n, rows, kpad)
 
     if L["a_off"] >= 0:
-        out["A"] = view(L["a_off"], L["m_pad"], L["k_pad"])
-    out["B"] = view(L["b_off"], L["n_pad"], L["k_pad"])
-    out["Y"] = view(L["y_off"], L["m_pad"], L["n_pad"])
+        out["A"] = blocked(L["a_off"], L["m_pad"])
+    out["B"] = blocked(L["b_off"], L["n_pad"])
+    out["Y"] = ws8.as_strided((n, L["m_pad"], L["n_pad"]),
+                              (L["m_pad"] * L["y_pitch"], L["y_pitch"], 1), L["y_off"])
     return out

@@ -138,7 +138,7 @@ void build_split(const rns_plan_t &pl, int la, int lb, SplitConsts &c) {
     for (int j = 0; j < pl.n_primes; j++) {
         const int q = pl.primes[j];
         c.q[j] = q;
-        c.inv[j] = 1.0 / (double)q;
+        c.inv[j] = 1.0f / (float)q;
         for (int w = 0; w < 2 * RNS_MAX_IN_LIMBS; w++) {
             uint32_t packed = 0;
             for (int b = 0; b < 4; b++) {
@@ -217,6 +217,16 @@ int choose_tile(int n, int64_t M, int64_t N) {
     return kTileSmall;
 }
 
+// Row pitch of the product planes: at least `bytes`, a whole number of
+// 128-byte lines, and an odd number of them, so that the same column of
+// consecutive rows falls into different L2 channels (a power-of-two pitch
+// sends a whole tile's rows to one channel).
+int64_t plane_pitch(int64_t bytes) {
+    int64_t p = round_up(bytes < 1 ? 1 : bytes, 128);
+    if ((p / 128) % 2 == 0) p += 128;
+    return p;
+}
+
 struct Layout {
     rns_layout_t pub;
     int64_t status_slots;
@@ -232,6 +242,10 @@ Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool b
     L.pub.m_pad = round_up(M, ts.bm);
     L.pub.n_pad = round_up(N, ts.bn);
     L.pub.k_pad = round_up(K, ts.bk);
+    L.pub.k_block = kKBlock;
+    L.pub.y_pitch = plane_pitch(L.pub.n_pad);
+    // the caller's residue planes ([n][M][K], pitch K) serve in place when
+    // they already cover whole tiles
     L.a_in_place = batched && L.pub.m_pad == M && L.pub.k_pad == K;
 
     SplitOperand a{}, b{};
@@ -244,7 +258,7 @@ Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool b
     L.pub.status_off = take(L.status_slots * 4);
     L.pub.a_off = L.a_in_place ? -1 : take((int64_t)n * L.pub.m_pad * L.pub.k_pad);
     L.pub.b_off = take((int64_t)n * L.pub.n_pad * L.pub.k_pad);
-    L.pub.y_off = take((int64_t)n * L.pub.m_pad * L.pub.n_pad);
+    L.pub.y_off = take((int64_t)n * L.pub.m_pad * L.pub.y_pitch);
     L.pub.total_bytes = off;
     return L;
 }
@@ -312,9 +326,12 @@ int stage_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, cons
     int8_t *base = (int8_t *)ws;
     const int n = plan->n_primes;
     const int8_t *apl = base + L.pub.a_off;
+    int64_t a_row = kKBlock, a_kstep = L.pub.m_pad * kKBlock;   // K-blocked planes
     if (batched) {
         if (L.a_in_place) {
-            apl = A_res;
+            apl = A_res;                      // the caller's row-major [n][M][K]
+            a_row = K;
+            a_kstep = kKBlock;
         } else {
             rc = launch_repack_residues(A_res, n, M, K, base + L.pub.a_off, L.pub.m_pad,
                                         L.pub.k_pad, stream);
@@ -325,7 +342,8 @@ int stage_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, cons
     build_epi(*plan, ec);
     return launch_gemm(L.pub.tile_config, n, apl, base + L.pub.b_off, base + L.pub.y_off,
                        L.pub.m_pad, L.pub.n_pad, L.pub.k_pad, L.pub.m_pad * L.pub.k_pad,
-                       L.pub.n_pad * L.pub.k_pad, L.pub.m_pad * L.pub.n_pad, ec, stream);
+                       L.pub.n_pad * L.pub.k_pad, L.pub.m_pad * L.pub.y_pitch,
+                       a_row, a_kstep, kKBlock, L.pub.n_pad * kKBlock, L.pub.y_pitch, ec, stream);
 }
 
 int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, bool batched,
@@ -342,8 +360,8 @@ int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, b
     if (rc || !work) return rc;
     GarnerConsts gc;
     build_garner(*plan, gc);
-    return launch_garner(gc, (const int8_t *)ws + L.pub.y_off, L.pub.m_pad * L.pub.n_pad,
-                         L.pub.n_pad, M, N, C, c_limbs, stream);
+    return launch_garner(gc, (const int8_t *)ws + L.pub.y_off, L.pub.m_pad * L.pub.y_pitch,
+                         L.pub.y_pitch, M, N, C, c_limbs, stream);
 }
 
 // Full product: every argument is checked before the first launch.

@@ -20,6 +20,8 @@ constexpr int kTriEntries = kGarnerSlots * (kGarnerSlots + 1) / 2;
 // integer j and leaves j in the low 32 bits of the bit pattern (two's
 // complement), because the low 32 bits of 1.5 * 2^52 are zero.
 constexpr double kRoundMagic = 6755399441055744.0;
+// 1.5 * 2^23, the binary32 counterpart (for |x| < 2^22)
+constexpr float kRoundMagic32 = 12582912.0f;
 
 // ---- residue split (kernel 1) ---------------------------------------------
 // An operand entry x of L limbs is read as U = x + 2^(64L-1) (its top bit
@@ -30,7 +32,7 @@ constexpr double kRoundMagic = 6755399441055744.0;
 struct SplitConsts {
     int32_t n;
     int32_t q[kMaxPrimes];
-    double inv[kMaxPrimes];                // fl(1/q) in binary64
+    float inv[kMaxPrimes];                 // fl(1/q) in binary32
     uint32_t w[kMaxPrimes][2 * RNS_MAX_IN_LIMBS];  // packed bytes 256^(4w+i) mod q
     int32_t h_a[kMaxPrimes];               // 2^(64*la - 1) mod q
     int32_t h_b[kMaxPrimes];               // 2^(64*lb - 1) mod q
@@ -72,9 +74,14 @@ __host__ __device__ constexpr int tri_index(int j, int k) {
     return j * (2 * kGarnerSlots - j + 1) / 2 + (k - j);
 }
 
+// ---- residue plane layout ----------------------------------------------------
+// A and B^T planes are K-blocked: [n][k_pad / 64][rows][64] int8, so the
+// 64-wide K step of a tile is one contiguous run of whole cache lines.
+constexpr int kKBlock = 64;
+
 // ---- GEMM tilings ----------------------------------------------------------
 enum TileConfig : int32_t {
-    kTileBig = 0,      // 256 x 256 x 64, four waves of 128 x 128, LDS ring fed by DMA
+    kTileBig = 0,      // 256 x 256 x 64, eight waves of 128 x 64 in ping-pong, LDS ring fed by DMA
     kTileSmall = 1,    // 64 x 64 x 64, four waves of 32 x 32
     kTileSkinny = 2,   // 128 x 32 x 64, four waves of 32 x 32 stacked along M
 };
@@ -93,7 +100,7 @@ struct SplitOperand {
     int8_t *planes;        // [n][r_pad][k_pad]
     int64_t rows;          // A: M        B: N  (plane rows)
     int64_t k;             // K
-    int64_t r_pad, k_pad;
+    int64_t r_pad, k_pad;  // padded plane rows (multiple of 16); K padded to whole K blocks
     int32_t limbs;
     int32_t bits;          // declared bound, or -1 for no check
     int32_t transposed;    // 0: A ([rows][K]), 1: B ([K][rows])
@@ -106,8 +113,9 @@ int launch_repack_residues(const int8_t *src, int64_t n, int64_t M, int64_t K,
 int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
                 int64_t m_pad, int64_t n_pad, int64_t k_pad,
                 int64_t a_plane, int64_t b_plane, int64_t y_plane,
+                int64_t a_row, int64_t a_kstep, int64_t b_row, int64_t b_kstep, int64_t y_pitch,
                 const EpiConsts &c, hipStream_t s);
-int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t n_pad,
+int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t y_pitch,
                   int64_t M, int64_t N, int64_t *C, int32_t c_limbs, hipStream_t s);
 int launch_zero(int64_t *C, int64_t count, hipStream_t s);
 

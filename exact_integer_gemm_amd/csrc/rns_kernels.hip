@@ -8,12 +8,13 @@
 //   K3 garner  : balanced Garner mixed-radix digits -> signed int64 limbs
 //                (exact-solve, "Method"; enclosure-gemm, "Method").
 //
-// All reductions mod q use one exact rounding step in binary64: for |t| < 2^31
-// the nearest integer to t/q is computed exactly from fl(1/q) (the relative
-// error 2^-53 moves t/q by less than 2^-22, while for odd q the value t/q is
-// at least 1/(2q) away from every half-integer), so t - q*round(t/q) is the
-// balanced residue.  Adding 1.5 * 2^52 in the same fused multiply-add leaves
-// round(t/q) in the low 32 bits of the result.  q = 2 is handled separately.
+// Every reduction mod q is one exact rounding step: t - q * round(t / q) is
+// the balanced residue of t for odd q.  round(t / q) is formed from fl(1/q) by
+// a fused multiply-add with 1.5 * 2^52 (binary64, any int32 t: the relative
+// error 2^-53 moves t/q by less than 2^-22, while t/q stays at least 1/(2q)
+// from every half-integer) or with 1.5 * 2^23 (binary32, |t| < 2^22), which
+// leaves the rounded quotient in the low bits of the result.  q = 2 is
+// handled separately (the low bit).
 #include <hip/hip_runtime.h>
 
 #include "rns_internal.h"
@@ -23,6 +24,15 @@ namespace rns {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned v4u __attribute__((ext_vector_type(4)));
+
+// The residue split reduces values |t| < 2^22, for which binary32 suffices:
+// fl(1/q) moves t/q by less than 1/(4q), and adding 1.5 * 2^23 in the fused
+// multiply-add leaves 0x400000 + round(t/q) in the low 24 bits of the result,
+// which __mul24 reads as a signed 24-bit value.  The result is t - q *
+// round(t/q) - q * 2^22, exact in its low byte (q * 2^22 = 0 mod 256).
+__device__ __forceinline__ int reduce_low_byte_f32(int t, int q, float inv) {
+    return __mul24(__float_as_int(__builtin_fmaf((float)t, inv, kRoundMagic32)), -q) + t;
+}
 
 // round(t / q) as a 32-bit integer, for |t| < 2^31 and odd q (exact).
 __device__ __forceinline__ int round_div(int t, double inv) {
@@ -52,7 +62,8 @@ __device__ __forceinline__ uint32_t pack4(int b0, int b1, int b2, int b3) {
 // K1: residue split
 // ============================================================================
 // One thread handles a run of 16 consecutive k of one plane row (a row of A,
-// or a column of B), so each prime's 16 residues leave as one 16-byte store.
+// or a column of B), so each prime's 16 residues leave as one 16-byte store
+// into the K-blocked plane.
 constexpr int kSplitThreads = 256;
 constexpr int kRun = 16;
 
@@ -87,10 +98,14 @@ __device__ __forceinline__ bool within_bound(const uint64_t (&x)[L], int bits) {
 template <int L>
 __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const int32_t *h,
                           int64_t task, uint32_t &flag) {
-    const int64_t runs = op.k_pad / kRun;
-    const int64_t r = op.transposed ? task % op.r_pad : task / runs;
-    const int64_t run = op.transposed ? task / op.r_pad : task % runs;
-    const int64_t k0 = run * kRun;
+    // 64 consecutive tasks (one wave) cover one K block (64 k) of 16 plane
+    // rows: lane / 4 picks the row, lane % 4 the run of 16 k.  The wave's
+    // stores then fill 1 KB of the K-blocked plane contiguously.
+    const int64_t lane = task & 63, wv = task >> 6;
+    const int64_t groups = op.r_pad / 16;
+    const int64_t kb = wv / groups, rg = wv - kb * groups;
+    const int64_t r = rg * 16 + (lane >> 2);
+    const int64_t k0 = kb * kKBlock + (lane & 3) * kRun;
     const bool row_ok = r < op.rows;
 
     // U = x + 2^(64L-1) as 2L little-endian 32-bit words, per element
@@ -114,7 +129,7 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
         }
     }
 
-    int8_t *dst = op.planes + r * op.k_pad + k0;
+    int8_t *dst = op.planes + kb * (op.r_pad * kKBlock) + r * kKBlock + (lane & 3) * kRun;
     const int64_t plane = op.r_pad * op.k_pad;
     for (int p = 0; p < c.n; p++) {
         const int q = c.q[p];
@@ -127,7 +142,7 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
                 word[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
             }
         } else {
-            const double inv = c.inv[p];
+            const float inv = c.inv[p];
             const int hp = h[p];
             int res[kRun];
 #pragma unroll
@@ -136,7 +151,7 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
 #pragma unroll
                 for (int w = 0; w < 2 * L; w++)
                     t = __builtin_amdgcn_udot4(u[e][w], c.w[p][w], t, false);
-                res[e] = reduce_low_byte((int)t, q, inv);
+                res[e] = reduce_low_byte_f32((int)t, q, inv);
             }
 #pragma unroll
             for (int w = 0; w < 4; w++)
@@ -221,7 +236,8 @@ __global__ void repack_kernel(const int8_t *src, int64_t n, int64_t M, int64_t K
         const int64_t p = i / (m_pad * k_pad);
         const int64_t rem = i - p * m_pad * k_pad;
         const int64_t m = rem / k_pad, k = rem - m * k_pad;
-        dst[i] = (m < M && k < K) ? src[(p * M + m) * K + k] : (int8_t)0;
+        dst[p * m_pad * k_pad + (k / kKBlock) * (m_pad * kKBlock) + m * kKBlock + k % kKBlock] =
+            (m < M && k < K) ? src[(p * M + m) * K + k] : (int8_t)0;
     }
 }
 
@@ -231,7 +247,8 @@ int launch_repack_residues(const int8_t *src, int64_t n, int64_t M, int64_t K,
     if (total == 0) return RNS_OK;
     int64_t grid = (total + 255) / 256;
     if (grid > 65536) grid = 65536;
-    hipLaunchKernelGGL(repack_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, n, M, K, dst, m_pad, k_pad);
+    hipLaunchKernelGGL(repack_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, n, M, K, dst, m_pad,
+                       k_pad);
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 
@@ -256,8 +273,11 @@ struct GemmArgs {
     const int8_t *a;
     const int8_t *b;
     int8_t *y;
-    int64_t a_plane, b_plane, y_plane;
-    int32_t mp, np, kp;
+    int64_t a_plane, b_plane, y_plane;   // bytes between planes
+    int64_t a_row, a_kstep;              // A: bytes between rows, between K steps of BK
+    int64_t b_row, b_kstep;              // B^T: the same
+    int64_t y_pitch;                     // Y: bytes between rows
+    int32_t kt;                          // K steps of BK bytes
     int32_t tiles_m, tiles_n;
 };
 
@@ -303,22 +323,23 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
     const int t = tile - p * per_prime;
     const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
 
-    const int8_t *Ap = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.kp;
-    const int8_t *Bp = g.b + p * g.b_plane + (int64_t)(tn * BN) * g.kp;
+    const int8_t *Ap = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.a_row;
+    const int8_t *Bp = g.b + p * g.b_plane + (int64_t)(tn * BN) * g.b_row;
 
     v4i ra[LA], rb[LB];
-    auto load_global = [&](int k0) {
+    auto load_global = [&](int kt) {
+        const int8_t *As = Ap + kt * g.a_kstep, *Bs = Bp + kt * g.b_kstep;
 #pragma unroll
         for (int i = 0; i < LA; i++) {
             const int c = tid + i * NT;
             if (A_CHUNKS % NT == 0 || c < A_CHUNKS)
-                ra[i] = *(const v4i *)(Ap + (int64_t)(c / CH) * g.kp + k0 + (c % CH) * 16);
+                ra[i] = *(const v4i *)(As + (int64_t)(c / CH) * g.a_row + (c % CH) * 16);
         }
 #pragma unroll
         for (int i = 0; i < LB; i++) {
             const int c = tid + i * NT;
             if (B_CHUNKS % NT == 0 || c < B_CHUNKS)
-                rb[i] = *(const v4i *)(Bp + (int64_t)(c / CH) * g.kp + k0 + (c % CH) * 16);
+                rb[i] = *(const v4i *)(Bs + (int64_t)(c / CH) * g.b_row + (c % CH) * 16);
         }
     };
     auto store_lds = [&](int buf) {
@@ -360,7 +381,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
         for (int j = 0; j < FN; j++) acc[i][j] = v16i{0};
 
     v4i af[2][FM], bf[2][FN];
-    const int KT = g.kp / BK;
+    const int KT = g.kt;
     if (KT > 0) {
         load_global(0);
         store_lds(0);
@@ -370,7 +391,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
     for (int kt = 0; kt < KT; kt++) {
         const int buf = kt & 1;
         const bool more = kt + 1 < KT;
-        if (more) load_global((kt + 1) * BK);
+        if (more) load_global(kt + 1);
 #pragma unroll
         for (int kk = 0; kk < KK; kk++) {
             const int cur = kk & 1;
@@ -405,144 +426,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g, EpiConsts ec) {
                     const int s = acc[i][j][4 * gq + e];
                     r[e] = q == 2 ? (s & 1) : reduce_low_byte(s, q, inv);
                 }
-                *(uint32_t *)(Yp + m * g.np + n) = pack4(r[0], r[1], r[2], r[3]);
-            }
-        }
-    }
-}
-
-// ---- the large-tile variant: LDS fed by direct global->LDS loads -----------
-// 256 x 256 tiles, BK = 64, an S-stage LDS ring filled by global_load_lds
-// (each wave-level load writes 64 lanes x 16 bytes, contiguous in LDS, so the
-// swizzle is applied to the global addresses instead).  Tile kt + S - 1 is
-// requested while tile kt is multiplied; one barrier per step, placed half
-// way through the second MFMA slice so that the MFMA pipe has queued work
-// while waves meet.  The loads are asynchronous to the waves: each wave waits
-// (vmcnt) for its own share of the next tile before the barrier, which then
-// publishes the whole tile.
-template <int S>
-__global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g, EpiConsts ec) {
-    constexpr int BM = 256, BN = 256, BK = 64, CH = BK / 16;
-    constexpr int FM = 4, FN = 4;                  // 128 x 128 per wave
-    constexpr int TILE_CHUNKS = (BM + BN) * CH;    // 2048 chunks = 32 KB per stage
-    constexpr int LOADS = TILE_CHUNKS / 256;       // 8 wave-level loads per wave per stage
-    static_assert(S >= 2 && S * TILE_CHUNKS * 16 <= 160 * 1024, "LDS ring");
-
-    __shared__ v4i lds[S][TILE_CHUNKS];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
-    const int wm = wave >> 1, wn = wave & 1;
-    const int half = lane >> 5, l32 = lane & 31;
-
-    const int G = gridDim.x;
-    const int xcd = blockIdx.x & 7, idx = blockIdx.x >> 3;
-    const int tile = xcd * (G >> 3) + min(xcd, G & 7) + idx;
-    const int per_prime = g.tiles_m * g.tiles_n;
-    const int p = tile / per_prime;
-    const int t = tile - p * per_prime;
-    const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
-    const int8_t *Ap = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.kp;
-    const int8_t *Bp = g.b + p * g.b_plane + (int64_t)(tn * BN) * g.kp;
-
-    // Load j (0..7) of this wave fills LDS slots [(j*4 + wave)*64, +64): slot
-    // s holds row s / CH (A rows first, then B rows) and physical chunk
-    // s % CH, i.e. logical chunk (s % CH) ^ swz(row) of that row.
-    const int8_t *src[LOADS];
-#pragma unroll
-    for (int j = 0; j < LOADS; j++) {
-        const int s = (j * 4 + wave) * 64 + lane;
-        const int row = s / CH;
-        const int c = (s % CH) ^ swz<CH>(row);
-        src[j] = row < BM ? Ap + (int64_t)row * g.kp + c * 16
-                          : Bp + (int64_t)(row - BM) * g.kp + c * 16;
-    }
-    auto issue = [&](int kt) {
-        v4i *dst = lds[kt % S];
-#pragma unroll
-        for (int j = 0; j < LOADS; j++)
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src[j] + kt * BK),
-                (__attribute__((address_space(3))) void *)(dst + (j * 4 + wave) * 64), 16, 0, 0);
-    };
-    // wait until at most `tiles` later tiles' loads of this wave are pending
-    auto wait_tiles = [&](int tiles) {
-        // s_waitcnt vmcnt(8 * tiles), other counters untouched (gfx9 encoding)
-        if (tiles <= 0) __builtin_amdgcn_s_waitcnt(0x0f70);
-        else if (tiles == 1) __builtin_amdgcn_s_waitcnt(0x0f78);
-        else __builtin_amdgcn_s_waitcnt(0x4f70);   // vmcnt(16)
-    };
-    auto read_frags = [&](int buf, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
-        const int chunk = kk * 2 + half;
-#pragma unroll
-        for (int i = 0; i < FM; i++) {
-            const int row = wm * 128 + i * 32 + l32;
-            af[i] = lds[buf][row * CH + (chunk ^ swz<CH>(row))];
-        }
-#pragma unroll
-        for (int j = 0; j < FN; j++) {
-            const int row = BM + wn * 128 + j * 32 + l32;
-            bf[j] = lds[buf][row * CH + (chunk ^ swz<CH>(row))];
-        }
-    };
-
-    v16i acc[FM][FN];
-#pragma unroll
-    for (int i = 0; i < FM; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++) acc[i][j] = v16i{0};
-    auto mfma_rows = [&](const v4i (&af)[FM], const v4i (&bf)[FN], int i0, int i1) {
-#pragma unroll
-        for (int i = i0; i < i1; i++)
-#pragma unroll
-            for (int j = 0; j < FN; j++)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
-    };
-
-    const int KT = g.kp / BK;
-    v4i af0[FM], bf0[FN], af1[FM], bf1[FN];
-    if (KT > 0) {
-#pragma unroll
-        for (int s = 0; s < S - 1; s++)
-            if (s < KT) issue(s);
-        wait_tiles(min(S - 2, KT - 1));
-        __syncthreads();
-        read_frags(0, 0, af0, bf0);
-    }
-    for (int kt = 0; kt < KT; kt++) {
-        const int buf = kt % S;
-        read_frags(buf, 1, af1, bf1);
-        mfma_rows(af0, bf0, 0, FM);
-        if (kt + S - 1 < KT) issue(kt + S - 1);
-        mfma_rows(af1, bf1, 0, FM / 2);
-        if (kt + 1 < KT) {
-            // tiles issued after kt + 1: kt + 2 .. min(kt + S - 1, KT - 1)
-            wait_tiles(min(kt + S - 1, KT - 1) - (kt + 1));
-            __syncthreads();
-            read_frags((kt + 1) % S, 0, af0, bf0);
-        }
-        mfma_rows(af1, bf1, FM / 2, FM);
-    }
-
-    const int q = ec.q[p];
-    const double inv = ec.inv[p];
-    int8_t *Yp = g.y + p * g.y_plane;
-#pragma unroll
-    for (int i = 0; i < FM; i++) {
-        const int64_t m = tm * BM + wm * 128 + i * 32 + l32;
-#pragma unroll
-        for (int j = 0; j < FN; j++) {
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++) {
-                const int n = tn * BN + wn * 128 + j * 32 + 8 * gq + 4 * half;
-                int r[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    const int s = acc[i][j][4 * gq + e];
-                    r[e] = q == 2 ? (s & 1) : reduce_low_byte(s, q, inv);
-                }
-                *(uint32_t *)(Yp + m * g.np + n) = pack4(r[0], r[1], r[2], r[3]);
+                *(uint32_t *)(Yp + m * g.y_pitch + n) = pack4(r[0], r[1], r[2], r[3]);
             }
         }
     }
@@ -551,17 +435,17 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(GemmArgs g, EpiConsts ec)
 // ---- the large-tile variant: 8 waves in ping-pong ----------------------------
 // 256 x 256 tiles, BK = 64, 512 threads: two waves per SIMD (waves w and w+4
 // share SIMD w % 4).  Each wave owns a 128 x 64 sub-tile (8 accumulator
-// chains).  The waves form two groups that alternate between a compute phase
-// (16 MFMAs on fragments already in registers) and a memory phase (requesting
-// a later K step with direct global->LDS loads and reading the fragments of
-// the next step), one group in each phase at any time, so that one wave per
-// SIMD always has MFMAs to issue while its partner waits on memory.  Phases
-// end at a plain s_barrier; ordering is by explicit counter waits: in its
-// memory phase for step j a wave waits (vmcnt) for its own loads of step
-// j + 1 and (lgkmcnt) for its fragment reads, so after the next barrier step
-// j + 1 is complete in LDS and step j - 1's stage is no longer read.  The LDS
-// holds an S-stage ring; step j + S - 1 is requested during the memory phase
-// of step j, into the stage of step j - 1.
+// chains).  The waves form two groups that alternate between a memory phase
+// (reading the fragments of a K step from LDS) and a compute phase (16 MFMAs
+// on those fragments, with this wave's share of the direct global->LDS loads
+// of a later K step slotted between them), one group in each phase at any
+// time, so that one wave per SIMD always has MFMAs to issue while its partner
+// waits on LDS.  Phases end at a plain s_barrier; ordering is by explicit
+// counter waits: in its memory phase for step j a wave waits (vmcnt) for its
+// own loads of step j + 1 and (lgkmcnt) for its fragment reads, so after the
+// next barrier step j + 1 is complete in LDS and step j - 1's stage is no
+// longer read.  The LDS holds an S-stage ring; step j + S - 1 is requested
+// during the compute phase of step j, into the stage of step j - 1.
 template <int S>
 __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g, EpiConsts ec) {
     constexpr int BM = 256, BN = 256, BK = 64, CH = BK / 16;
@@ -589,26 +473,28 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g, EpiConsts ec) 
     const int p = tile / per_prime;
     const int t = tile - p * per_prime;
     const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
-    const int8_t *Ap = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.kp;
-    const int8_t *Bp = g.b + p * g.b_plane + (int64_t)(tn * BN) * g.kp;
+    const int8_t *Ap = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.a_row;
+    const int8_t *Bp = g.b + p * g.b_plane + (int64_t)(tn * BN) * g.b_row;
 
-    // Load j of this wave fills LDS slots [(j*8 + wave)*64, +64) of a stage.
+    // Load j of this wave fills LDS slots [(j*8 + wave)*64, +64) of a stage:
+    // loads 0, 1 carry A rows, loads 2, 3 B rows.
     const int8_t *src[DPW];
 #pragma unroll
     for (int j = 0; j < DPW; j++) {
         const int s = (j * 8 + wave) * 64 + lane;
         const int row = s / CH;
         const int c = (s % CH) ^ swz<CH>(row);
-        src[j] = row < BM ? Ap + (int64_t)row * g.kp + c * 16
-                          : Bp + (int64_t)(row - BM) * g.kp + c * 16;
+        src[j] = row < BM ? Ap + (int64_t)row * g.a_row + c * 16
+                          : Bp + (int64_t)(row - BM) * g.b_row + c * 16;
     }
-    const int KT = g.kp / BK;
+    const int KT = g.kt;
     auto issue = [&](int step) {
         v4i *dst = lds[step % S];
 #pragma unroll
         for (int j = 0; j < DPW; j++)
             __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)(src[j] + step * BK),
+                (const __attribute__((address_space(1))) void *)(
+                    src[j] + step * (j < DPW / 2 ? g.a_kstep : g.b_kstep)),
                 (__attribute__((address_space(3))) void *)(dst + (j * 8 + wave) * 64), 16, 0, 0);
     };
     // s_waitcnt vmcnt(4 * n), other counters untouched (gfx9 encoding: vmcnt
@@ -643,18 +529,26 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g, EpiConsts ec) 
     // memory phase for step j: request step j + D, read the fragments of step
     // j, then wait for own loads of step j + 1 and for the fragments
     auto memory = [&](int j) {
-        if (j + D < KT) issue(j + D);
         read_frags(j % S, 0, af0, bf0);
         read_frags(j % S, 1, af1, bf1);
-        wait_steps(min(j + D, KT - 1) - (j + 1));
+        wait_steps(min(j + D - 1, KT - 1) - (j + 1));
         __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0)
     };
-    auto compute = [&]() {
+    auto compute = [&](int jj) {
+        const bool more = jj + D < KT;
+        const int step = jj + D;
+        v4i *dst = lds[step % S];
 #pragma unroll
-        for (int i = 0; i < FM; i++)
+        for (int i = 0; i < FM; i++) {
 #pragma unroll
             for (int j = 0; j < FN; j++)
                 acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf0[j], af0[i], acc[i][j], 0, 0, 0);
+            if (more)
+                __builtin_amdgcn_global_load_lds(
+                    (const __attribute__((address_space(1))) void *)(
+                        src[i] + step * (i < DPW / 2 ? g.a_kstep : g.b_kstep)),
+                    (__attribute__((address_space(3))) void *)(dst + (i * 8 + wave) * 64), 16, 0, 0);
+        }
 #pragma unroll
         for (int i = 0; i < FM; i++)
 #pragma unroll
@@ -680,7 +574,7 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g, EpiConsts ec) 
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
-            compute();
+            compute(j);
             __builtin_amdgcn_sched_barrier(0);
             __builtin_amdgcn_s_barrier();
             __builtin_amdgcn_sched_barrier(0);
@@ -724,23 +618,24 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g, EpiConsts ec) 
                 }
     }
     __syncthreads();
-    int8_t *Yp = g.y + p * g.y_plane + (int64_t)(tm * BM) * g.np + tn * BN;
+    int8_t *Yp = g.y + p * g.y_plane + (int64_t)(tm * BM) * g.y_pitch + tn * BN;
     // 256 rows x 256 bytes: 16 lanes per row, 32 rows per pass of 512 threads
 #pragma unroll
     for (int pass = 0; pass < BM / 32; pass++) {
         const int row = pass * 32 + (tid >> 4);
         const int c = (tid & 15) * 16;
-        *(v4i *)(Yp + (int64_t)row * g.np + c) = *(const v4i *)(out + row * OUT_PITCH + c);
+        *(v4i *)(Yp + (int64_t)row * g.y_pitch + c) = *(const v4i *)(out + row * OUT_PITCH + c);
     }
 }
 
 int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
                 int64_t m_pad, int64_t n_pad, int64_t k_pad,
                 int64_t a_plane, int64_t b_plane, int64_t y_plane,
+                int64_t a_row, int64_t a_kstep, int64_t b_row, int64_t b_kstep, int64_t y_pitch,
                 const EpiConsts &c, hipStream_t s) {
     const TileShape ts = tile_shape(cfg);
-    GemmArgs g{a, b, y, a_plane, b_plane, y_plane, (int32_t)m_pad, (int32_t)n_pad, (int32_t)k_pad,
-               (int32_t)(m_pad / ts.bm), (int32_t)(n_pad / ts.bn)};
+    GemmArgs g{a, b, y, a_plane, b_plane, y_plane, a_row, a_kstep, b_row, b_kstep, y_pitch,
+               (int32_t)(k_pad / ts.bk), (int32_t)(m_pad / ts.bm), (int32_t)(n_pad / ts.bn)};
     const int64_t grid = (int64_t)n * g.tiles_m * g.tiles_n;
     if (grid == 0) return RNS_OK;
     if (grid > 0x7fffffff || m_pad > 0x7fffffff || n_pad > 0x7fffffff) return RNS_E_ARG;
@@ -773,13 +668,13 @@ int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
 // |t[c]| < 54 * 125 * 2^16 < 2^29) and carried into limbs at the end.
 template <int NB>
 __global__ __launch_bounds__(256) void garner_kernel(GarnerConsts gc, const int8_t *__restrict__ y,
-                                                     int64_t y_plane, int64_t n_pad, int64_t M,
+                                                     int64_t y_plane, int64_t y_pitch, int64_t M,
                                                      int64_t N, int64_t *__restrict__ C, int c_limbs) {
     constexpr int CB = garner_chunks(NB - 1);   // chunks of the widest Q_k
     const int64_t e = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (e >= M * N) return;
     const int64_t i = e / N, j = e - i * N;
-    const int8_t *yp = y + i * n_pad + j;
+    const int8_t *yp = y + i * y_pitch + j;
 
     int acc[NB];
 #pragma unroll
@@ -821,7 +716,7 @@ __global__ __launch_bounds__(256) void garner_kernel(GarnerConsts gc, const int8
         if (l < c_limbs) out[l] = (int64_t)(((uint64_t)words[2 * l + 1] << 32) | words[2 * l]);
 }
 
-int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t n_pad,
+int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t y_pitch,
                   int64_t M, int64_t N, int64_t *C, int32_t c_limbs, hipStream_t s) {
     const int64_t total = M * N;
     if (total == 0) return RNS_OK;
@@ -830,13 +725,13 @@ int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64
     const int nb = (g.n + 7) / 8 * 8;
     dim3 gd((unsigned)grid), bd(256);
     switch (nb) {
-        case 8: hipLaunchKernelGGL(garner_kernel<8>, gd, bd, 0, s, g, y, y_plane, n_pad, M, N, C, c_limbs); break;
-        case 16: hipLaunchKernelGGL(garner_kernel<16>, gd, bd, 0, s, g, y, y_plane, n_pad, M, N, C, c_limbs); break;
-        case 24: hipLaunchKernelGGL(garner_kernel<24>, gd, bd, 0, s, g, y, y_plane, n_pad, M, N, C, c_limbs); break;
-        case 32: hipLaunchKernelGGL(garner_kernel<32>, gd, bd, 0, s, g, y, y_plane, n_pad, M, N, C, c_limbs); break;
-        case 40: hipLaunchKernelGGL(garner_kernel<40>, gd, bd, 0, s, g, y, y_plane, n_pad, M, N, C, c_limbs); break;
-        case 48: hipLaunchKernelGGL(garner_kernel<48>, gd, bd, 0, s, g, y, y_plane, n_pad, M, N, C, c_limbs); break;
-        default: hipLaunchKernelGGL(garner_kernel<56>, gd, bd, 0, s, g, y, y_plane, n_pad, M, N, C, c_limbs); break;
+        case 8: hipLaunchKernelGGL(garner_kernel<8>, gd, bd, 0, s, g, y, y_plane, y_pitch, M, N, C, c_limbs); break;
+        case 16: hipLaunchKernelGGL(garner_kernel<16>, gd, bd, 0, s, g, y, y_plane, y_pitch, M, N, C, c_limbs); break;
+        case 24: hipLaunchKernelGGL(garner_kernel<24>, gd, bd, 0, s, g, y, y_plane, y_pitch, M, N, C, c_limbs); break;
+        case 32: hipLaunchKernelGGL(garner_kernel<32>, gd, bd, 0, s, g, y, y_plane, y_pitch, M, N, C, c_limbs); break;
+        case 40: hipLaunchKernelGGL(garner_kernel<40>, gd, bd, 0, s, g, y, y_plane, y_pitch, M, N, C, c_limbs); break;
+        case 48: hipLaunchKernelGGL(garner_kernel<48>, gd, bd, 0, s, g, y, y_plane, y_pitch, M, N, C, c_limbs); break;
+        default: hipLaunchKernelGGL(garner_kernel<56>, gd, bd, 0, s, g, y, y_plane, y_pitch, M, N, C, c_limbs); break;
     }
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }

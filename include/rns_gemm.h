@@ -196,15 +196,22 @@ int rns_status(const void *ws, hipStream_t stream, uint32_t *flags);
  * rns_workspace_layout -- where the residue planes live inside the
  * workspace, for inspection by tests and for callers that reuse the planes.
  * Plane j of an operand is the balanced residue of every entry mod
- * plan->primes[j], stored as int8:
- *   A planes: [n][m_pad][k_pad] at a_off   (row m, column k of A)
- *   B planes: [n][n_pad][k_pad] at b_off   (column n, row k of B: transposed)
- *   Y planes: [n][m_pad][n_pad] at y_off   (balanced (A_j @ B_j) mod q_j)
- * Padding entries are zero.  In the batched-residue variant A planes are
- * absent (a_off = -1) when the caller's A_res is used in place.
+ * plan->primes[j], stored as int8.  Operand planes are K-blocked in blocks
+ * of k_block (64) entries, so that a 64-wide K step of a row tile is one
+ * contiguous run of whole cache lines:
+ *   A planes at a_off: [n][k_pad / k_block][m_pad][k_block]  (row m, column k of A)
+ *   B planes at b_off: [n][k_pad / k_block][n_pad][k_block]  (column n, row k of B)
+ * Product planes are row-major with a row pitch of y_pitch bytes (an odd
+ * multiple of 128, which spreads a tile's rows over the L2 channels):
+ *   Y planes at y_off: [n][m_pad][y_pitch], entries 0..n_pad-1 of each row
+ *   (the balanced residue of (A_j @ B_j) mod q_j).
+ * Entries beyond M, N or K inside m_pad, n_pad, k_pad are zero.  In the
+ * batched-residue variant A planes are absent (a_off = -1) when the caller's
+ * A_res is used in place.
  */
 typedef struct rns_layout {
     int64_t m_pad, n_pad, k_pad;
+    int64_t k_block, y_pitch;
     int64_t a_off, b_off, y_off;
     int64_t status_off;
     int64_t total_bytes;

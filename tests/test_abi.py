@@ -121,7 +121,12 @@ def test_workspace_size_and_layout(lib):
     L = rg.layout(p, 2048, 2048, 4096)
     n = p.n_primes
     assert L["m_pad"] == 2048 and L["n_pad"] == 2048 and L["k_pad"] == 4096
-    assert L["y_off"] >= L["b_off"] + n * 2048 * 4096 > L["a_off"] + n * 2048 * 4096 - 1
+    # operand planes K-blocked by 64; product rows at an odd multiple of 128 bytes
+    assert L["k_block"] == 64
+    assert L["y_pitch"] >= 2048 and L["y_pitch"] % 128 == 0 and (L["y_pitch"] // 128) % 2 == 1
+    assert L["b_off"] >= L["a_off"] + n * 2048 * 4096
+    assert L["y_off"] >= L["b_off"] + n * 2048 * 4096
+    assert L["total_bytes"] >= L["y_off"] + n * 2048 * L["y_pitch"]
     assert rg.workspace_size(p, 2048, 2048, 4096) == L["total_bytes"]
     # ragged shapes are padded to whole tiles
     L = rg.layout(p, 65, 70, 130)
