@@ -47,7 +47,7 @@ def parse():
 TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                             "gemm_wide_hbm_traffic.txt")
 KERNEL_SOURCE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "exact_integer_gemm_amd",
-                             "csrc", "rns_kernels.hip")
+                             "csrc", "rns_gemm.hip")
 
 
 def measured_traffic(workload):

@@ -1,7 +1,9 @@
 """Compile librns_gemm.so (HIP for gfx950) in-tree with hipcc.
 
 The library is plain HIP (no PyTorch types): ``csrc/rns_host.cpp`` holds the
-C ABI and host logic, ``csrc/rns_kernels.hip`` the three device kernels.
+C ABI and host logic; ``csrc/rns_split.hip``, ``csrc/rns_gemm.hip`` and
+``csrc/rns_garner.hip`` the device kernels, with shared device helpers in
+``csrc/rns_device.h``.
 """
 from __future__ import annotations
 
@@ -11,8 +13,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librns_gemm.so")
-SOURCES = [os.path.join(CSRC, "rns_host.cpp"), os.path.join(CSRC, "rns_kernels.hip")]
-HEADERS = [os.path.join(CSRC, "rns_internal.h"),
+SOURCES = [os.path.join(CSRC, f) for f in ("rns_host.cpp", "rns_split.hip", "rns_gemm.hip", "rns_garner.hip")]
+HEADERS = [os.path.join(CSRC, "rns_internal.h"), os.path.join(CSRC, "rns_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "rns_gemm.h")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

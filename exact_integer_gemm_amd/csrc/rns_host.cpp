@@ -231,6 +231,7 @@ struct Layout {
     rns_layout_t pub;
     int64_t status_slots;
     bool a_in_place;
+    int64_t partial_off;   // split-tile residues (large tiling only, else -1)
 };
 
 Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool batched) {
@@ -259,6 +260,7 @@ Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool b
     L.pub.a_off = L.a_in_place ? -1 : take((int64_t)n * L.pub.m_pad * L.pub.k_pad);
     L.pub.b_off = take((int64_t)n * L.pub.n_pad * L.pub.k_pad);
     L.pub.y_off = take((int64_t)n * L.pub.m_pad * L.pub.y_pitch);
+    L.partial_off = cfg == kTileBig ? take(kTailUnitsMax * kTailUnitBytes) : -1;
     L.pub.total_bytes = off;
     return L;
 }
@@ -343,7 +345,8 @@ int stage_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, cons
     return launch_gemm(L.pub.tile_config, n, apl, base + L.pub.b_off, base + L.pub.y_off,
                        L.pub.m_pad, L.pub.n_pad, L.pub.k_pad, L.pub.m_pad * L.pub.k_pad,
                        L.pub.n_pad * L.pub.k_pad, L.pub.m_pad * L.pub.y_pitch,
-                       a_row, a_kstep, kKBlock, L.pub.n_pad * kKBlock, L.pub.y_pitch, ec, stream);
+                       a_row, a_kstep, kKBlock, L.pub.n_pad * kKBlock, L.pub.y_pitch,
+                       L.partial_off >= 0 ? base + L.partial_off : nullptr, ec, stream);
 }
 
 int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, bool batched,

@@ -88,13 +88,19 @@ enum TileConfig : int32_t {
 
 struct TileShape { int bm, bn, bk; };
 
+// Large tiling: tiles past the last whole round over the compute units are
+// split over K; each part leaves its 256 x 256 residues in a slot of
+// kTailUnitBytes, and a second kernel adds up the parts of each tile.
+constexpr int kTailUnitsMax = 256;
+constexpr int64_t kTailUnitBytes = 256 * 256;
+
 __host__ __device__ constexpr TileShape tile_shape(int cfg) {
     return cfg == kTileBig ? TileShape{256, 256, 64}
          : cfg == kTileSmall ? TileShape{64, 64, 64}
          : TileShape{128, 32, 64};
 }
 
-// ---- launchers (rns_kernels.hip) -------------------------------------------
+// ---- launchers (rns_split.hip, rns_gemm.hip, rns_garner.hip) ------------------
 struct SplitOperand {
     const int64_t *x;      // [rows][cols][limbs] for A, [K][N][limbs] for B
     int8_t *planes;        // [n][r_pad][k_pad]
@@ -114,7 +120,7 @@ int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
                 int64_t m_pad, int64_t n_pad, int64_t k_pad,
                 int64_t a_plane, int64_t b_plane, int64_t y_plane,
                 int64_t a_row, int64_t a_kstep, int64_t b_row, int64_t b_kstep, int64_t y_pitch,
-                const EpiConsts &c, hipStream_t s);
+                int8_t *partial, const EpiConsts &c, hipStream_t s);
 int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t y_pitch,
                   int64_t M, int64_t N, int64_t *C, int32_t c_limbs, hipStream_t s);
 int launch_zero(int64_t *C, int64_t count, hipStream_t s);

@@ -109,8 +109,10 @@ int rns_plan_n(int32_t n_primes, rns_plan_t *out);
  * (batched_residue == 0) or rns_gemm_batched_residue (batched_residue != 0)
  * for this plan and shape.  The workspace holds the residue planes of both
  * operands and of the product (about n*(M*K + N*K + M*N) bytes plus tile
- * padding; cf. enclosure-gemm, "Requirements and limits" on working memory)
- * and a small status area.  Writes the size to *bytes.
+ * padding; cf. enclosure-gemm, "Requirements and limits" on working memory),
+ * a small status area and, when the large 256 x 256 tiling is chosen, a
+ * 16 MiB area for the partial residues of tiles that are split over K to
+ * balance the last round over the compute units.  Writes the size to *bytes.
  * Returns RNS_OK, RNS_E_ARG or RNS_E_K.
  */
 int rns_workspace_size(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,

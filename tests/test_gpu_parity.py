@@ -91,6 +91,32 @@ def test_stage_planes(M, N, K, la, lb, ab, bb, seed):
         assert np.array_equal(Yp[j, :M, :N], refY), f"prime {q}"
 
 
+def test_split_tail_tiles():
+    """Tiles past the last whole round over the compute units run as K parts
+    whose residues the last part to finish combines; the result stays exact,
+    and the per-tile counters are back at zero for a second product on the
+    same workspace (no split in between)."""
+    M, N, K = 512, 768, 1024
+    p = rg.plan(K, 142, 142)
+    tiles = p.n_primes * (M // 256) * (N // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"split tail: M={M} N={N} K={K} n={p.n_primes} tiles={tiles} cus={cus}", flush=True)
+    if not (tiles > cus and tiles % cus):
+        pytest.skip("shape does not leave a partial round on this device")
+    A, B = W.random_operands(31, M, N, K, 3, 3, 142, 142)
+    ws = rg.new_workspace(p, M, N, K)
+    C = rg.gemm(p, dev(A), dev(B), workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle_c(A, B, p.out_limbs_min)
+    assert np.array_equal(C.cpu().numpy(), ref)
+    for _ in range(2):
+        rg.residue_products(p, M, N, K, ws)
+        out = torch.full_like(C, -1)
+        rg.reconstruct(p, M, N, K, ws, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref)
+
+
 def test_output_limbs_sign_extension():
     A, B = W.random_operands(21, 40, 30, 50, 1, 1, 30, 30)
     p, ws, C = run_gemm(A, B, 30, 30, out_limbs=5)
