@@ -18,9 +18,11 @@ passage of the pages it follows:
 * enclosure-gemm, "Requirements and limits": the product of the primes below
   256 is a 335-bit number, and the capacity budget follows from it.
 * Ozaki Scheme II paper, §3.1: integer products are exact and there is one
-  reconstruction at the end; §1.1: O(p) products, O(p^2) reduction and CRT.
+  reconstruction at the end; §1.1: O(p) products, O(p^2) reduction and CRT;
+  §3.5.2: the GPU reconstruction takes the centered representative by
+  rounding to nearest.
 
-Readings taken where the pages are silent (listed again in the design doc):
+Readings taken where the pages are silent:
   * the prime set for a bound is the *fewest* primes taken largest first;
   * "exceeds" is strict: P > 2 * K * 2^(a_bits + b_bits);
   * a balanced residue of x mod q lies in [-floor((q-1)/2), floor(q/2)]
@@ -214,6 +216,38 @@ def mixed_radix_value(digits: Sequence[int], primes: Sequence[int]) -> int:
     for d, q in zip(digits, primes):
         X += d * Q
         Q *= q
+    return X
+
+
+def crt_rounded_quotient(residues: Sequence[int], primes: Sequence[int],
+                         quotient_estimate=None) -> int:
+    """CRT whose centered representative comes from a rounded quotient.
+
+    Ozaki Scheme II paper, §3.5.2: the GPU reconstruction obtains the
+    centered representative by rounding to nearest.  Read plainly:
+    u_j = r_j * (M_j^-1 mod q_j) mod q_j (balanced), S = sum_j u_j * M_j with
+    M_j = P / q_j, so S = X (mod P) and S / P = sum_j u_j / q_j; the quotient
+    t = round(S / P) gives X = S - t * P.
+
+    ``quotient_estimate(u, primes)`` returns the integer t used; by default
+    the nearest integer to the exact rational sum_j u_j / q_j.  An estimate
+    off by one (a rounded floating-point sum near a half-integer) leaves
+    S - t * P one period outside (-P/2, P/2]; one exact comparison with P/2
+    moves it back, so the result is the balanced CRT value for any estimate
+    within one of the true quotient.
+    """
+    P = prod(primes)
+    u = [balanced(int(r) * pow(P // q, -1, q), q) for r, q in zip(residues, primes)]
+    if quotient_estimate is None:
+        num = sum(uj * (P // q) for uj, q in zip(u, primes))   # = S; S / P is the sum
+        t = (2 * num + P) // (2 * P)                            # nearest, ties upward
+    else:
+        t = int(quotient_estimate(u, primes))
+    X = sum(uj * (P // q) for uj, q in zip(u, primes)) - t * P
+    if 2 * X > P:
+        X -= P
+    elif 2 * X <= -P:
+        X += P
     return X
 
 

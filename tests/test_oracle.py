@@ -189,6 +189,50 @@ def test_crt_boundaries():
         assert O.crt_balanced([(top + 1) % q for q in ps], ps) == top + 1 - P
 
 
+def test_crt_rounded_quotient_against_sympy():
+    """Ozaki II §3.5.2 reading (rounded quotient) against sympy's CRT, both P
+    parities, random values and the ends of (-P/2, P/2]."""
+    rng = np.random.default_rng(17)
+    for n in (1, 6, 16, 29, 53, 54):
+        ps = O.primes_largest_first()[:n]
+        P = O.prod(ps)
+        ends = [0, 1, -1, P // 2, -((P - 1) // 2)]
+        vals = ends + [int.from_bytes(rng.bytes(48), "little") % P - P // 2 for _ in range(40)]
+        for X in vals:
+            if 2 * X <= -P:
+                X += P
+            res = [X % q for q in ps]
+            v, m = sympy_crt(ps, res)
+            v = int(v)
+            want = v - P if 2 * v > P else v
+            assert want == X
+            assert O.crt_rounded_quotient(res, ps) == X
+
+
+def test_crt_rounded_quotient_off_by_one_estimates():
+    """Any quotient estimate within one of the true one gives the same value
+    (the exact comparison with P/2 repairs it); one two away does not, so the
+    repair is a single step and not a hidden second reduction."""
+    ps = O.primes_largest_first()
+    P = O.prod(ps)
+    rng = np.random.default_rng(23)
+    for X in [P // 2, -(P // 2) + 1, 0, 5] + [int.from_bytes(rng.bytes(48), "little") % P - P // 2
+                                            for _ in range(20)]:
+        res = [X % q for q in ps]
+        u = [O.balanced(r * pow(P // q, -1, q), q) for r, q in zip(res, ps)]
+        S = sum(uj * (P // q) for uj, q in zip(u, ps))
+        t_true = (S - X) // P
+        assert (S - X) % P == 0
+        for d in (-1, 0, 1):
+            assert O.crt_rounded_quotient(res, ps, lambda u_, p_: t_true + d) == X
+        assert O.crt_rounded_quotient(res, ps, lambda u_, p_: t_true + 2) != X
+    # a binary64 estimate of sum u_j / q_j, rounded to nearest, is one such estimate
+    for X in (P // 2, -(P // 2) + 1, 12345):
+        res = [X % q for q in ps]
+        est = lambda u_, p_: round(sum(float(a) / float(b) for a, b in zip(u_, p_)))
+        assert O.crt_rounded_quotient(res, ps, est) == X
+
+
 def test_garner_digits_against_crt():
     rng = np.random.default_rng(11)
     odd = O.primes_largest_first()[:53]
