@@ -88,6 +88,7 @@ def load() -> ctypes.CDLL:
         "rns_split": (ctypes.c_int, [P, I64, I64, I64, VP, I32, VP, I32, VP, SZ, VP]),
         "rns_residue_products": (ctypes.c_int, [P, I64, I64, I64, VP, VP, SZ, VP]),
         "rns_reconstruct": (ctypes.c_int, [P, I64, I64, I64, I32, VP, I32, VP, SZ, VP]),
+        "rns_reconstruct_garner": (ctypes.c_int, [P, I64, I64, I64, I32, VP, I32, VP, SZ, VP]),
         "rns_status": (ctypes.c_int, [VP, VP, ctypes.POINTER(ctypes.c_uint32)]),
         "rns_error_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
@@ -288,17 +289,25 @@ def residue_products(p: Plan, M: int, N: int, K: int, workspace: torch.Tensor,
 
 
 def reconstruct(p: Plan, M: int, N: int, K: int, workspace: torch.Tensor, out: torch.Tensor,
-                batched: bool = False) -> torch.Tensor:
-    """Kernel 3: Garner reconstruction of ``out`` (int64 [M,N,limbs]) from the Y planes."""
+                batched: bool = False, method: str = "crt") -> torch.Tensor:
+    """Kernel 3: ``out`` (int64 [M,N,limbs]) from the Y planes.
+
+    method "crt": rns_reconstruct (centered CRT by rounded quotient, the sum
+    over primes on the matrix cores); "garner": rns_reconstruct_garner
+    (balanced Garner digits).  Both give the same exact value.
+    """
     _need(out, torch.int64, 3, "out")
     if tuple(out.shape[:2]) != (M, N):
         raise ValueError("out has the wrong shape")
+    if method not in ("crt", "garner"):
+        raise ValueError("method must be 'crt' or 'garner'")
+    name = "rns_reconstruct" if method == "crt" else "rns_reconstruct_garner"
     c = p._c()
     with torch.cuda.device(out.device):
-        rc = load().rns_reconstruct(ctypes.byref(c), M, N, K, int(batched), out.data_ptr(),
-                                    out.shape[2], workspace.data_ptr(), workspace.numel(),
-                                    _stream_ptr(out))
-    _check(rc, "rns_reconstruct")
+        rc = getattr(load(), name)(ctypes.byref(c), M, N, K, int(batched), out.data_ptr(),
+                                   out.shape[2], workspace.data_ptr(), workspace.numel(),
+                                   _stream_ptr(out))
+    _check(rc, name)
     return out
 
 

@@ -1,0 +1,238 @@
+// K3 of the exact residue GEMM on gfx950, default form: the centered CRT
+// value by rounded quotient (Ozaki Scheme II paper, §3.5.2: the GPU
+// reconstruction takes the centered representative by rounding to nearest),
+// with the sum over primes on the matrix cores.
+//
+// For an entry with residues y_k (balanced, one per plane):
+//   u_k = y_k * (M_k^-1 mod q_k) mod q_k, balanced      (M_k = P / q_k)
+//   r   = nearest integer to sum_k u_k / q_k            (binary32)
+//   X'  = sum_k u_k M_k - r P
+// X' is congruent to the product entry X mod P and, when r is the true
+// nearest integer, equal to it.  X' is formed in balanced base-256 chunks
+// by one int8 MFMA: the entry's slots (u_0 .. u_{n-1}, -r) against the
+// digits of (M_0 .. M_{n-1}, P); |chunk sum| <= 55 * 128 * 128 < 2^20.
+//
+// A wave takes 32 entries.  Lane (l32, h) holds entry l32 and slots
+// 16h .. 16h + 15 of each 32-slot K step: exactly the second-operand
+// fragment of v_mfma_i32_32x32x32_i8, whose result gives lane (l32, h) the
+// chunk sums 8*gq + 4h + e (gq, e < 4) of its entry.  The two halves swap
+// their 4-chunk groups and each carries the whole value into 32-bit words.
+#include "rns_device.h"
+
+namespace rns {
+
+// Lays the digits out as first-operand fragments: block (ks, nb), lane
+// (c32, h), byte b holds digit 32*nb + c32 of the constant of slot
+// 32*ks + 16*h + b.
+__global__ __launch_bounds__(256) void crt_table_kernel(CrtDigits d, int8_t *table) {
+    const int t = threadIdx.x;               // 4 blocks x 64 lanes
+    const int blk = t >> 6, lane = t & 63;
+    const int ks = blk >> 1, nb = blk & 1;
+    const int c = 32 * nb + (lane & 31);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; b++) {
+            const int k = 32 * ks + 16 * (lane >> 5) + 4 * i + b;
+            const int8_t dig = (k < kCrtSlots - 8 && c < kCrtDigits) ? d.d[k][c] : (int8_t)0;
+            v |= (uint32_t)(uint8_t)dig << (8 * b);
+        }
+        w[i] = v;
+    }
+    *(v4u *)(table + (int64_t)t * 16) = v4u{w[0], w[1], w[2], w[3]};
+}
+
+// u = t - q * round(t / q) for |t| < 2^22 (binary32 rounding step, ties to
+// even, so q = 2 gives u = t for t in {0, 1}).
+__device__ __forceinline__ int reduce_small(int t, int q, float inv) {
+    const int k = __float_as_int(__builtin_fmaf((float)t, inv, kRoundMagic32)) - 0x4b400000;
+    return t - q * k;
+}
+
+template <int KS, int NB>
+__global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, const int8_t *__restrict__ table,
+                                                  const int8_t *__restrict__ y, int64_t y_plane,
+                                                  int64_t y_pitch, int64_t M, int64_t N,
+                                                  int64_t *__restrict__ C, int c_limbs) {
+    constexpr int W = 8 * NB;                 // 32-bit words of X'
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+
+    v4i dig[KS][NB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+            dig[ks][nb] = *(const v4i *)(table + ((int64_t)(ks * 2 + nb) * 64 + lane) * 16);
+
+    // this lane's slot constants
+    int sq[KS][16], sw[KS][16], plane[KS][16];
+    float si[KS][16];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+        for (int b = 0; b < 16; b++) {
+            const int k0 = 32 * ks + b, k1 = k0 + 16;
+            sq[ks][b] = h ? cc.q[k1] : cc.q[k0];
+            sw[ks][b] = h ? cc.w[k1] : cc.w[k0];
+            si[ks][b] = h ? cc.inv[k1] : cc.inv[k0];
+            const int k = h ? k1 : k0;
+            plane[ks][b] = k < cc.n ? k : cc.n - 1;   // padding slots read a valid plane, weight 0
+        }
+    const int rk = cc.n;                      // the -r slot
+    const int rks = rk >> 5, rh = (rk >> 4) & 1, rb = rk & 15;
+    const int half0 = (c_limbs + 1) >> 1;     // limbs written by the lower half
+
+    const int64_t total = M * N;
+    const int64_t groups = (total + 31) >> 5;
+    for (int64_t grp = (int64_t)blockIdx.x * 4 + wave; grp < groups; grp += (int64_t)gridDim.x * 4) {
+        const int64_t e = grp * 32 + l32;
+        const bool ok = e < total;
+        const int64_t ee = ok ? e : total - 1;
+        const int64_t i = ee / N, j = ee - i * N;
+        const int8_t *yp = y + i * y_pitch + j;
+
+        float f = 0.0f;
+        v4i ua[KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++) {
+            int byte[16];
+#pragma unroll
+            for (int b = 0; b < 16; b++) {
+                const int t = (int)yp[plane[ks][b] * y_plane] * sw[ks][b];
+                const int u = reduce_small(t, sq[ks][b], si[ks][b]);
+                f = __builtin_fmaf((float)u, si[ks][b], f);
+                byte[b] = u;
+            }
+#pragma unroll
+            for (int wd = 0; wd < 4; wd++)
+                ua[ks][wd] = (int)pack4(byte[4 * wd], byte[4 * wd + 1], byte[4 * wd + 2], byte[4 * wd + 3]);
+        }
+        const float ft = f + __shfl_xor(f, 32);
+        const float rf = __builtin_rintf(ft);
+        const bool near_half = __builtin_fabsf(ft - rf) > 0.5f - 0x1p-10f;
+        const int r = (int)rf;
+        if (h == rh) {
+            // slot n carries -r (|r| <= 28); its byte was zero (weight 0)
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                if (ks == rks) {
+                    const int wd = rb >> 2, sh = 8 * (rb & 3);
+#pragma unroll
+                    for (int x = 0; x < 4; x++)
+                        if (x == wd)
+                            ua[ks][x] = (int)(((uint32_t)ua[ks][x] & ~(0xffu << sh)) |
+                                              ((uint32_t)(-r & 0xff) << sh));
+                }
+        }
+
+        v16i acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            acc[nb] = v16i{0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[ks][nb], ua[ks], acc[nb], 0, 0, 0);
+        }
+
+        // 4-chunk groups: this lane's group (nb, gq) sits at word 8*nb + 2*gq + h
+        int64_t g[NB][4], gp[NB][4];
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++) {
+                const v16i &a = acc[nb];
+                g[nb][gq] = (int64_t)a[4 * gq] + ((int64_t)a[4 * gq + 1] << 8) +
+                            ((int64_t)a[4 * gq + 2] << 16) + ((int64_t)a[4 * gq + 3] << 24);
+                const int lo = __shfl_xor((int)(uint32_t)g[nb][gq], 32);
+                const int hi = __shfl_xor((int)(g[nb][gq] >> 32), 32);
+                gp[nb][gq] = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+            }
+        uint32_t wv[W];
+        int64_t carry = 0;
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++)
+#pragma unroll
+                for (int hh = 0; hh < 2; hh++) {
+                    carry += (hh == h) ? g[nb][gq] : gp[nb][gq];
+                    wv[8 * nb + 2 * gq + hh] = (uint32_t)carry;
+                    carry >>= 32;
+                }
+        // carry is now the sign word (0 or -1): X' = wv + carry * 2^(32 W)
+
+        if (near_half) {
+            // exact: X' > P/2 <=> 2X' - P > 0;  X' <= -P/2 <=> 2X' + P <= 0
+            int64_t bm = 0, bp = 0;
+            uint32_t nzm = 0, nzp = 0;
+#pragma unroll
+            for (int w = 0; w < W; w++) {
+                const uint32_t two = (wv[w] << 1) | (w ? (wv[w - 1] >> 31) : 0u);
+                const uint32_t pw = w < 16 ? cc.P[w] : 0u;
+                const int64_t dm = (int64_t)two - pw + bm;
+                const int64_t dp = (int64_t)two + pw + bp;
+                nzm |= (uint32_t)dm;
+                nzp |= (uint32_t)dp;
+                bm = dm >> 32;
+                bp = dp >> 32;
+            }
+            const int64_t top2 = 2 * carry + (int64_t)(wv[W - 1] >> 31);
+            const int64_t tm = top2 + bm, tp = top2 + bp;
+            const bool above = tm > 0 || (tm == 0 && nzm != 0);
+            const bool below = tp < 0 || (tp == 0 && nzp == 0);
+            if (above || below) {
+                int64_t c2 = 0;
+#pragma unroll
+                for (int w = 0; w < W; w++) {
+                    const int64_t pw = w < 16 ? (int64_t)cc.P[w] : 0;
+                    c2 += (int64_t)wv[w] + (above ? -pw : pw);
+                    wv[w] = (uint32_t)c2;
+                    c2 >>= 32;
+                }
+                carry += c2;
+            }
+        }
+
+        if (ok) {
+            int64_t *ce = C + e * c_limbs;
+            const uint32_t sign = (uint32_t)carry;
+#pragma unroll
+            for (int l = 0; l < RNS_MAX_OUT_LIMBS; l++) {
+                const uint32_t lo = 2 * l < W ? wv[2 * l] : sign;
+                const uint32_t hi = 2 * l + 1 < W ? wv[2 * l + 1] : sign;
+                const bool mine = h ? (l >= half0 && l < c_limbs) : (l < half0 && l < c_limbs);
+                if (mine) ce[l] = (int64_t)(((uint64_t)hi << 32) | lo);
+            }
+        }
+    }
+}
+
+int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks, int8_t *table,
+               const int8_t *y, int64_t y_plane, int64_t y_pitch, int64_t M, int64_t N, int64_t *C,
+               int32_t c_limbs, hipStream_t s) {
+    const int64_t total = M * N;
+    if (total == 0) return RNS_OK;
+    if (c.n < 1 || c.n + 1 > 32 * ksteps || ksteps < 1 || ksteps > 2 || nblocks < 1 || nblocks > 2)
+        return RNS_E_ARG;
+    hipLaunchKernelGGL(crt_table_kernel, dim3(1), dim3(256), 0, s, d, table);
+    if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
+    const int64_t groups = (total + 31) / 32;
+    int64_t grid = (groups + 3) / 4;
+    if (grid > 8192) grid = 8192;             // grid-stride beyond 32 blocks per CU
+    const dim3 g((unsigned)grid), b(256);
+    if (ksteps == 1 && nblocks == 1)
+        hipLaunchKernelGGL((crt_kernel<1, 1>), g, b, 0, s, c, table, y, y_plane, y_pitch, M, N, C, c_limbs);
+    else if (ksteps == 1)
+        hipLaunchKernelGGL((crt_kernel<1, 2>), g, b, 0, s, c, table, y, y_plane, y_pitch, M, N, C, c_limbs);
+    else if (nblocks == 1)
+        hipLaunchKernelGGL((crt_kernel<2, 1>), g, b, 0, s, c, table, y, y_plane, y_pitch, M, N, C, c_limbs);
+    else
+        hipLaunchKernelGGL((crt_kernel<2, 2>), g, b, 0, s, c, table, y, y_plane, y_pitch, M, N, C, c_limbs);
+    return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
+}
+
+}  // namespace rns

@@ -2,6 +2,7 @@
 // layout, argument validation and the C ABI declared in include/rns_gemm.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <vector>
@@ -207,6 +208,52 @@ void build_garner(const rns_plan_t &pl, GarnerConsts &g) {
     }
 }
 
+// CRT by rounded quotient: per-slot q, (P/q)^-1 mod q and fl(1/q); P's words;
+// the balanced base-256 digits of every M_k = P / q_k and of P.  Returns the
+// MFMA K steps and N blocks through *ksteps, *nblocks.
+void build_crt(const rns_plan_t &pl, CrtConsts &c, CrtDigits &d, int *ksteps, int *nblocks) {
+    const int n = pl.n_primes;
+    std::memset(&c, 0, sizeof(c));
+    std::memset(&d, 0, sizeof(d));
+    c.n = n;
+    for (int k = 0; k < kCrtSlots; k++) { c.q[k] = 1; c.w[k] = 0; c.inv[k] = 0.0f; }
+    auto digits = [&](const Big &v, int8_t *out) {
+        // balanced base-256 digits: v = sum_c out[c] 256^c, out[c] in [-128, 127]
+        int carry = 0, last = 0;
+        const int nbytes = 4 * (int)v.w.size();
+        for (int ci = 0; ci < kCrtDigits; ci++) {
+            int byte = carry;
+            if (ci < nbytes) byte += (int)((v.w[ci / 4] >> (8 * (ci % 4))) & 0xffu);
+            carry = 0;
+            if (byte >= 128) { byte -= 256; carry = 1; }
+            out[ci] = (int8_t)byte;
+            if (byte) last = ci + 1;
+        }
+        return last;                          // digits in use
+    };
+    Big P(1);
+    for (int k = 0; k < n; k++) P.mul_small((uint32_t)pl.primes[k]);
+    int used = 0;
+    for (int k = 0; k < n; k++) {
+        const int q = pl.primes[k];
+        Big Mk(1);
+        int64_t Mk_mod = 1;
+        for (int j = 0; j < n; j++)
+            if (j != k) {
+                Mk.mul_small((uint32_t)pl.primes[j]);
+                Mk_mod = Mk_mod * pl.primes[j] % q;
+            }
+        c.q[k] = q;
+        c.w[k] = balanced(inv_mod(Mk_mod, q), q);
+        c.inv[k] = 1.0f / (float)q;
+        used = std::max(used, digits(Mk, d.d[k]));
+    }
+    used = std::max(used, digits(P, d.d[n]));
+    for (int i = 0; i < 16; i++) c.P[i] = i < (int)P.w.size() ? P.w[i] : 0u;
+    *ksteps = (n + 1 + 31) / 32;
+    *nblocks = (used + 31) / 32;
+}
+
 // ---- layout ------------------------------------------------------------------
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -232,6 +279,7 @@ struct Layout {
     int64_t status_slots;
     bool a_in_place;
     int64_t partial_off;   // split-tile residues (large tiling only, else -1)
+    int64_t crt_off;       // MFMA fragments of the CRT digits
 };
 
 Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool batched) {
@@ -261,6 +309,7 @@ Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool b
     L.pub.b_off = take((int64_t)n * L.pub.n_pad * L.pub.k_pad);
     L.pub.y_off = take((int64_t)n * L.pub.m_pad * L.pub.y_pitch);
     L.partial_off = cfg == kTileBig ? take(kTailUnitsMax * kTailUnitBytes) : -1;
+    L.crt_off = take(kCrtTableBytes);
     L.pub.total_bytes = off;
     return L;
 }
@@ -349,8 +398,11 @@ int stage_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, cons
                        L.partial_off >= 0 ? base + L.partial_off : nullptr, ec, stream);
 }
 
+enum Recon { kReconCrt = 0, kReconGarner = 1 };
+
 int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, bool batched,
-                      int64_t *C, int32_t c_limbs, void *ws, size_t ws_bytes, hipStream_t stream) {
+                      int64_t *C, int32_t c_limbs, void *ws, size_t ws_bytes, hipStream_t stream,
+                      int method = kReconCrt) {
     int rc = validate(plan, M, N, K);
     if (rc) return rc;
     if (c_limbs < plan->out_limbs_min || c_limbs > RNS_MAX_OUT_LIMBS) return RNS_E_OUT_LIMBS;
@@ -361,10 +413,18 @@ int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, b
     bool work;
     rc = prepare(plan, M, N, K, batched, ws, ws_bytes, &L, &work);
     if (rc || !work) return rc;
-    GarnerConsts gc;
-    build_garner(*plan, gc);
-    return launch_garner(gc, (const int8_t *)ws + L.pub.y_off, L.pub.m_pad * L.pub.y_pitch,
-                         L.pub.y_pitch, M, N, C, c_limbs, stream);
+    if (method == kReconGarner) {
+        GarnerConsts gc;
+        build_garner(*plan, gc);
+        return launch_garner(gc, (const int8_t *)ws + L.pub.y_off, L.pub.m_pad * L.pub.y_pitch,
+                             L.pub.y_pitch, M, N, C, c_limbs, stream);
+    }
+    CrtConsts cc;
+    CrtDigits cd;
+    int ks = 0, nb = 0;
+    build_crt(*plan, cc, cd, &ks, &nb);
+    return launch_crt(cc, cd, ks, nb, (int8_t *)ws + L.crt_off, (const int8_t *)ws + L.pub.y_off,
+                      L.pub.m_pad * L.pub.y_pitch, L.pub.y_pitch, M, N, C, c_limbs, stream);
 }
 
 // Full product: every argument is checked before the first launch.
@@ -487,6 +547,13 @@ int rns_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
                     int32_t batched_residue, int64_t *C, int32_t c_limbs,
                     void *ws, size_t ws_bytes, hipStream_t stream) {
     return stage_reconstruct(plan, M, N, K, batched_residue != 0, C, c_limbs, ws, ws_bytes, stream);
+}
+
+int rns_reconstruct_garner(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                           int32_t batched_residue, int64_t *C, int32_t c_limbs,
+                           void *ws, size_t ws_bytes, hipStream_t stream) {
+    return stage_reconstruct(plan, M, N, K, batched_residue != 0, C, c_limbs, ws, ws_bytes, stream,
+                             kReconGarner);
 }
 
 int rns_status(const void *ws, hipStream_t stream, uint32_t *flags) {

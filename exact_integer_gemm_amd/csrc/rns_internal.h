@@ -74,6 +74,33 @@ __host__ __device__ constexpr int tri_index(int j, int k) {
     return j * (2 * kGarnerSlots - j + 1) / 2 + (k - j);
 }
 
+// ---- CRT by rounded quotient (kernel 3, default) -----------------------------
+// Ozaki Scheme II paper, §3.5.2: the centered representative is taken by
+// rounding to nearest.  With M_k = P / q_k and u_k = y_k * (M_k^-1 mod q_k)
+// mod q_k (balanced), S = sum_k u_k M_k = X (mod P) and S / P = sum_k u_k /
+// q_k, so X = S - r P with r the nearest integer to sum_k u_k / q_k.  One
+// INT8 MFMA per 32 entries forms S - r P in balanced base-256 chunks: the
+// entries' slots (u_0 .. u_{n-1}, -r) times the balanced base-256 digits of
+// (M_0 .. M_{n-1}, P).  r comes from a binary32 sum (error < 2^-12); where
+// that sum is within 2^-10 of a half-integer the result is compared with
+// P/2 exactly and moved by one period if needed.
+constexpr int kCrtSlots = 64;        // n primes + the -r slot, padded to two K steps of 32
+constexpr int kCrtDigits = 48;       // balanced base-256 digits kept per constant (P < 2^336)
+constexpr int64_t kCrtTableBytes = 4 * 64 * 16;   // [K step][N block][lane][16 bytes]
+
+struct CrtConsts {
+    int32_t n;                       // primes; slot n holds -r
+    int32_t q[kCrtSlots];            // per slot; padding slots q = 1, w = 0, inv = 0
+    int32_t w[kCrtSlots];            // M_k^-1 mod q_k, balanced
+    float inv[kCrtSlots];            // fl(1/q_k)
+    uint32_t P[16];                  // P, little-endian 32-bit words
+};
+// Balanced base-256 digits of M_0 .. M_{n-1} and P (slot n), for the kernel
+// that lays them out as MFMA fragments in the workspace.
+struct CrtDigits {
+    int8_t d[kCrtSlots - 8][kCrtDigits];   // slots 0 .. 55 (n + 1 <= 55)
+};
+
 // ---- residue plane layout ----------------------------------------------------
 // A and B^T planes are K-blocked: [n][k_pad / 64][rows][64] int8, so the
 // 64-wide K step of a tile is one contiguous run of whole cache lines.
@@ -124,6 +151,10 @@ int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
 int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t y_pitch,
                   int64_t M, int64_t N, int64_t *C, int32_t c_limbs, hipStream_t s);
 int launch_zero(int64_t *C, int64_t count, hipStream_t s);
+// ksteps / nblocks: MFMA K steps (slots n + 1 in 32s) and N blocks (digits in 32s)
+int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks, int8_t *table,
+               const int8_t *y, int64_t y_plane, int64_t y_pitch, int64_t M, int64_t N, int64_t *C,
+               int32_t c_limbs, hipStream_t s);
 
 // Status area written by the split kernel: word 0 = number of split blocks,
 // word 1 = that number XOR kStatusCheck, then one flag word per block.

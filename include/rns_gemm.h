@@ -143,7 +143,7 @@ int rns_gemm(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
 /*
  * rns_gemm_batched_residue -- the lift-step shape (exact-solve, "Method": each
  * step's inverse mod q_j applied to the residual is one INT8 GEMM per prime,
- * run as one batched product, and balanced Garner assembles the wide digit).
+ * run as one batched product, and the CRT assembles the wide digit).
  *
  * A_res: device int8 [n_primes][M][K]; plane j is read as an integer matrix
  *   mod plan->primes[j] (any int8 value is accepted; |a| <= 128 keeps the
@@ -173,9 +173,24 @@ int rns_gemm_batched_residue(const rns_plan_t *plan, int64_t M, int64_t N, int64
  * rns_residue_products -- kernel 2: Y_j = (A_j @ B_j) mod q_j, balanced, for
  *                         every prime; A_j from ws, or from A_res when it is
  *                         not NULL (batched-residue variant).
- * rns_reconstruct      -- kernel 3: Garner reconstruction of C from the Y
- *                         planes; batched_residue selects the workspace
- *                         layout of that variant.  K == 0 writes zeros.
+ * rns_reconstruct      -- kernel 3: C from the Y planes, the centered CRT
+ *                         value by rounded quotient (Ozaki Scheme II paper,
+ *                         §3.5.2: the centered representative by rounding to
+ *                         nearest): u_j = y_j * (M_j^-1 mod q_j) balanced,
+ *                         M_j = P / q_j, X = sum_j u_j M_j - r P with r the
+ *                         nearest integer to sum_j u_j / q_j, the sum over
+ *                         primes formed on the matrix cores; where the
+ *                         binary32 estimate of r is near a half-integer the
+ *                         result is compared with P/2 exactly and moved by one
+ *                         period, so C is the same exact value as Garner's.
+ *                         batched_residue selects the workspace layout of that
+ *                         variant.  K == 0 writes zeros.
+ * rns_reconstruct_garner -- the same C by balanced Garner mixed-radix digits
+ *                         (exact-solve, "Method"; enclosure-gemm, "Method":
+ *                         balanced-Garner digits assembled in signed
+ *                         arithmetic), one thread per entry; the O(n^2) digit
+ *                         recurrence (Ozaki Scheme II paper, §1.1).  Same
+ *                         arguments, layout and errors as rns_reconstruct.
  */
 int rns_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
               const int64_t *A, int32_t a_limbs, const int64_t *B, int32_t b_limbs,
@@ -185,6 +200,9 @@ int rns_residue_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K
 int rns_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
                     int32_t batched_residue, int64_t *C, int32_t c_limbs,
                     void *ws, size_t ws_bytes, hipStream_t stream);
+int rns_reconstruct_garner(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                           int32_t batched_residue, int64_t *C, int32_t c_limbs,
+                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * rns_status -- synchronises `stream`, then reports in *flags the

@@ -214,6 +214,70 @@ def test_batched_residue_small(M, N, K, n, seed):
     assert np.array_equal(O.decode_array(X), ref)
 
 
+def _planted(n, values):
+    """Batched call with K = 1 and B = 1: entry m of the output is the CRT
+    value of the residues planted in A_res[:, m, 0], i.e. values[m]."""
+    p = rg.plan_n(n)
+    ps = list(p.primes)
+    M = len(values)
+    A_res = np.zeros((n, M, 1), dtype=np.int8)
+    for j, q in enumerate(ps):
+        for m, X in enumerate(values):
+            A_res[j, m, 0] = O.balanced(X, q)
+    B = np.ones((1, 1, 1), dtype=np.int64)
+    return p, ps, dev(A_res), dev(B)
+
+
+def _boundary_values(ps, rng, count=40):
+    P = O.prod(ps)
+    lo = -(P // 2) + (1 if P % 2 == 0 else 0)      # the smallest value of (-P/2, P/2]
+    hi = P // 2
+    vals = [0, 1, -1, hi, lo, hi - 1, lo + 1, hi - 2, lo + 2, P // 3, -(P // 3), P // 4, -(P // 4)]
+    assert all(2 * v <= P and 2 * v > -P for v in vals)
+    for _ in range(count):
+        d = int(rng.integers(0, min(1 << 20, (P - 1) // 2)))
+        vals += [hi - d, lo + d]
+        x = int.from_bytes(rng.bytes(48), "little") % P - P // 2
+        vals.append(x if 2 * x > -P else x + P)
+    assert all(2 * v <= P and 2 * v > -P for v in vals)
+    return vals
+
+
+@pytest.mark.parametrize("n", [1, 2, 6, 16, 29, 30, 31, 32, 33, 47, 53, 54])
+def test_reconstruct_planted_values(n):
+    """Both reconstructions return the planted value, including both ends of
+    (-P/2, P/2] and values next to them, for prime counts around the CRT
+    kernel's one/two K-step and N-block sizes (odd and even P)."""
+    rng = np.random.default_rng(1000 + n)
+    ps = rg.plan_n(n).primes
+    vals = _boundary_values(list(ps), rng)
+    print(f"planted n={n} entries={len(vals)}", flush=True)
+    p, ps, A_res, B = _planted(n, vals)
+    M = len(vals)
+    for method in ("crt", "garner"):
+        ws = rg.new_workspace(p, M, 1, 1, True, B.device)
+        rg.split(p, None, B, ws, M=M)
+        rg.residue_products(p, M, 1, 1, ws, A_res=A_res)
+        out = torch.full((M, 1, p.out_limbs_min + 1), 7, dtype=torch.int64, device=B.device)
+        rg.reconstruct(p, M, 1, 1, ws, out, batched=True, method=method)
+        got = O.decode_array(out.cpu().numpy())[:, 0]
+        assert [int(v) for v in got] == vals, method
+
+
+@pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", [SMALL[1], SMALL[3], SMALL[7],
+                                                    (200, 150, 96, 3, 3, 150, 160, 71)])
+def test_crt_matches_garner(M, N, K, la, lb, ab, bb, seed):
+    """The two reconstructions agree bit for bit on the same Y planes."""
+    print(f"crt vs garner M={M} N={N} K={K}", flush=True)
+    A, B = W.random_operands(seed, M, N, K, la, lb, ab, bb)
+    p, ws, C = run_gemm(A, B, ab, bb, out_limbs=8)
+    out = torch.zeros((M, N, 8), dtype=torch.int64, device="cuda")
+    rg.reconstruct(p, M, N, K, ws, out, method="garner")
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), C)
+    assert np.array_equal(C, oracle_c(A, B, 8))
+
+
 def test_batched_residue_any_int8_and_extremes():
     rng = np.random.default_rng(61)
     p = rg.plan_n(54)
