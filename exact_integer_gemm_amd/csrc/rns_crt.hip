@@ -21,29 +21,6 @@
 
 namespace rns {
 
-// Lays the digits out as first-operand fragments: block (ks, nb), lane
-// (c32, h), byte b holds digit 32*nb + c32 of the constant of slot
-// 32*ks + 16*h + b.
-__global__ __launch_bounds__(256) void crt_table_kernel(CrtDigits d, int8_t *table) {
-    const int t = threadIdx.x;               // 4 blocks x 64 lanes
-    const int blk = t >> 6, lane = t & 63;
-    const int ks = blk >> 1, nb = blk & 1;
-    const int c = 32 * nb + (lane & 31);
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int b = 0; b < 4; b++) {
-            const int k = 32 * ks + 16 * (lane >> 5) + 4 * i + b;
-            const int8_t dig = (k < kCrtSlots - 8 && c < kCrtDigits) ? d.d[k][c] : (int8_t)0;
-            v |= (uint32_t)(uint8_t)dig << (8 * b);
-        }
-        w[i] = v;
-    }
-    *(v4u *)(table + (int64_t)t * 16) = v4u{w[0], w[1], w[2], w[3]};
-}
-
 // u = t - q * round(t / q) for |t| < 2^22 (binary32 rounding step, ties to
 // even, so q = 2 gives u = t for t in {0, 1}).
 __device__ __forceinline__ int reduce_small(int t, int q, float inv) {
@@ -52,7 +29,7 @@ __device__ __forceinline__ int reduce_small(int t, int q, float inv) {
 }
 
 template <int KS, int NB>
-__global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, const int8_t *__restrict__ table,
+__global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
                                                   const int8_t *__restrict__ y, int64_t y_plane,
                                                   int64_t y_pitch, int64_t M, int64_t N,
                                                   int64_t *__restrict__ C, int c_limbs) {
@@ -61,12 +38,26 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, const int8_t *__
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = lane >> 5, l32 = lane & 31;
 
+    // first-operand fragments of the digits: block (ks, nb), lane (c32, h),
+    // byte b = digit 32*nb + c32 of the constant of slot 32*ks + 16*h + b
     v4i dig[KS][NB];
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++)
-            dig[ks][nb] = *(const v4i *)(table + ((int64_t)(ks * 2 + nb) * 64 + lane) * 16);
+        for (int nb = 0; nb < NB; nb++) {
+            const int c = 32 * nb + l32;
+#pragma unroll
+            for (int x = 0; x < 4; x++) {
+                uint32_t v = 0;
+#pragma unroll
+                for (int b = 0; b < 4; b++) {
+                    const int k = 32 * ks + 16 * h + 4 * x + b;
+                    const int8_t dd = (k < kCrtSlots - 8 && c < kCrtDigits) ? cd.d[k][c] : (int8_t)0;
+                    v |= (uint32_t)(uint8_t)dd << (8 * b);
+                }
+                dig[ks][nb][x] = (int)v;
+            }
+        }
 
     // this lane's slot constants
     int sq[KS][16], sw[KS][16], plane[KS][16];
@@ -211,27 +202,25 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, const int8_t *__
     }
 }
 
-int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks, int8_t *table,
+int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
                const int8_t *y, int64_t y_plane, int64_t y_pitch, int64_t M, int64_t N, int64_t *C,
                int32_t c_limbs, hipStream_t s) {
     const int64_t total = M * N;
     if (total == 0) return RNS_OK;
     if (c.n < 1 || c.n + 1 > 32 * ksteps || ksteps < 1 || ksteps > 2 || nblocks < 1 || nblocks > 2)
         return RNS_E_ARG;
-    hipLaunchKernelGGL(crt_table_kernel, dim3(1), dim3(256), 0, s, d, table);
-    if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
     const int64_t groups = (total + 31) / 32;
     int64_t grid = (groups + 3) / 4;
     if (grid > 8192) grid = 8192;             // grid-stride beyond 32 blocks per CU
     const dim3 g((unsigned)grid), b(256);
     if (ksteps == 1 && nblocks == 1)
-        hipLaunchKernelGGL((crt_kernel<1, 1>), g, b, 0, s, c, table, y, y_plane, y_pitch, M, N, C, c_limbs);
+        hipLaunchKernelGGL((crt_kernel<1, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);
     else if (ksteps == 1)
-        hipLaunchKernelGGL((crt_kernel<1, 2>), g, b, 0, s, c, table, y, y_plane, y_pitch, M, N, C, c_limbs);
+        hipLaunchKernelGGL((crt_kernel<1, 2>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);
     else if (nblocks == 1)
-        hipLaunchKernelGGL((crt_kernel<2, 1>), g, b, 0, s, c, table, y, y_plane, y_pitch, M, N, C, c_limbs);
+        hipLaunchKernelGGL((crt_kernel<2, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);
     else
-        hipLaunchKernelGGL((crt_kernel<2, 2>), g, b, 0, s, c, table, y, y_plane, y_pitch, M, N, C, c_limbs);
+        hipLaunchKernelGGL((crt_kernel<2, 2>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 

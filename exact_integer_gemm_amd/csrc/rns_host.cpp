@@ -279,7 +279,6 @@ struct Layout {
     int64_t status_slots;
     bool a_in_place;
     int64_t partial_off;   // split-tile residues (large tiling only, else -1)
-    int64_t crt_off;       // MFMA fragments of the CRT digits
 };
 
 Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool batched) {
@@ -300,7 +299,7 @@ Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool b
     SplitOperand a{}, b{};
     a.r_pad = L.pub.m_pad; a.k_pad = L.pub.k_pad;
     b.r_pad = L.pub.n_pad; b.k_pad = L.pub.k_pad;
-    L.status_slots = split_status_slots(batched ? nullptr : &a, &b);
+    L.status_slots = split_status_slots(batched ? nullptr : &a, &b, n);
 
     int64_t off = 0;
     auto take = [&](int64_t bytes) { int64_t o = off; off = round_up(off + bytes, 256); return o; };
@@ -309,7 +308,6 @@ Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool b
     L.pub.b_off = take((int64_t)n * L.pub.n_pad * L.pub.k_pad);
     L.pub.y_off = take((int64_t)n * L.pub.m_pad * L.pub.y_pitch);
     L.partial_off = cfg == kTileBig ? take(kTailUnitsMax * kTailUnitBytes) : -1;
-    L.crt_off = take(kCrtTableBytes);
     L.pub.total_bytes = off;
     return L;
 }
@@ -423,7 +421,7 @@ int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, b
     CrtDigits cd;
     int ks = 0, nb = 0;
     build_crt(*plan, cc, cd, &ks, &nb);
-    return launch_crt(cc, cd, ks, nb, (int8_t *)ws + L.crt_off, (const int8_t *)ws + L.pub.y_off,
+    return launch_crt(cc, cd, ks, nb, (const int8_t *)ws + L.pub.y_off,
                       L.pub.m_pad * L.pub.y_pitch, L.pub.y_pitch, M, N, C, c_limbs, stream);
 }
 

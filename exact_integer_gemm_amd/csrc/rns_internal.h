@@ -86,7 +86,6 @@ __host__ __device__ constexpr int tri_index(int j, int k) {
 // P/2 exactly and moved by one period if needed.
 constexpr int kCrtSlots = 64;        // n primes + the -r slot, padded to two K steps of 32
 constexpr int kCrtDigits = 48;       // balanced base-256 digits kept per constant (P < 2^336)
-constexpr int64_t kCrtTableBytes = 4 * 64 * 16;   // [K step][N block][lane][16 bytes]
 
 struct CrtConsts {
     int32_t n;                       // primes; slot n holds -r
@@ -95,8 +94,8 @@ struct CrtConsts {
     float inv[kCrtSlots];            // fl(1/q_k)
     uint32_t P[16];                  // P, little-endian 32-bit words
 };
-// Balanced base-256 digits of M_0 .. M_{n-1} and P (slot n), for the kernel
-// that lays them out as MFMA fragments in the workspace.
+// Balanced base-256 digits of M_0 .. M_{n-1} and P (slot n); the kernel
+// takes them as an argument and lays out its MFMA fragments itself.
 struct CrtDigits {
     int8_t d[kCrtSlots - 8][kCrtDigits];   // slots 0 .. 55 (n + 1 <= 55)
 };
@@ -152,7 +151,7 @@ int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64
                   int64_t M, int64_t N, int64_t *C, int32_t c_limbs, hipStream_t s);
 int launch_zero(int64_t *C, int64_t count, hipStream_t s);
 // ksteps / nblocks: MFMA K steps (slots n + 1 in 32s) and N blocks (digits in 32s)
-int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks, int8_t *table,
+int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
                const int8_t *y, int64_t y_plane, int64_t y_pitch, int64_t M, int64_t N, int64_t *C,
                int32_t c_limbs, hipStream_t s);
 
@@ -161,6 +160,6 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks, 
 constexpr int kStatusHeader = 2;
 constexpr uint32_t kStatusCheck = 0x52534e53u;
 // status slots written by the split kernel: one word per block plus the header
-int64_t split_status_slots(const SplitOperand *a, const SplitOperand *b);
+int64_t split_status_slots(const SplitOperand *a, const SplitOperand *b, int n_primes);
 
 }  // namespace rns

@@ -14,10 +14,18 @@ namespace rns {
 constexpr int kSplitThreads = 256;
 constexpr int kRun = 16;
 
+// Small problems (a few hundred blocks or fewer) would leave most compute
+// units idle while each thread loops over every prime; their grid repeats
+// the task blocks for groups of primes instead (the entries are loaded once
+// per group).
+constexpr int64_t kSplitTargetBlocks = 1024;
+
 struct SplitArgs {
     SplitOperand op[2];
     int64_t tasks[2];      // r_pad * (k_pad / 16) per operand
-    int32_t blocks0;       // blocks that serve operand 0
+    int32_t blocks0;       // task blocks that serve operand 0
+    int32_t task_blocks;   // task blocks of both operands
+    int32_t prime_groups;  // the grid is prime_groups x task_blocks
     uint32_t flag_bit[2];  // RNS_FLAG_* recorded for an out-of-bound entry of each operand
     uint32_t *status;      // [2 + gridDim.x] words
 };
@@ -44,7 +52,7 @@ __device__ __forceinline__ bool within_bound(const uint64_t (&x)[L], int bits) {
 
 template <int L>
 __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const int32_t *h,
-                          int64_t task, uint32_t &flag) {
+                          int64_t task, int p_begin, int p_end, uint32_t &flag) {
     // 64 consecutive tasks (one wave) cover one K block (64 k) of 16 plane
     // rows: lane / 4 picks the row, lane % 4 the run of 16 k.  The wave's
     // stores then fill 1 KB of the K-blocked plane contiguously.
@@ -78,7 +86,7 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
 
     int8_t *dst = op.planes + kb * (op.r_pad * kKBlock) + r * kKBlock + (lane & 3) * kRun;
     const int64_t plane = op.r_pad * op.k_pad;
-    for (int p = 0; p < c.n; p++) {
+    for (int p = p_begin; p < p_end; p++) {
         const int q = c.q[p];
         uint32_t word[4];
         if (q == 2) {
@@ -110,18 +118,20 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
 }
 
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs args, SplitConsts c) {
-    const int which = (int)blockIdx.x < args.blocks0 ? 0 : 1;
-    const int64_t block = which == 0 ? blockIdx.x : blockIdx.x - args.blocks0;
+    const int tb = (int)blockIdx.x % args.task_blocks, pg = (int)blockIdx.x / args.task_blocks;
+    const int p_begin = pg * c.n / args.prime_groups, p_end = (pg + 1) * c.n / args.prime_groups;
+    const int which = tb < args.blocks0 ? 0 : 1;
+    const int64_t block = which == 0 ? tb : tb - args.blocks0;
     const int64_t task = block * kSplitThreads + threadIdx.x;
     const SplitOperand &op = args.op[which];
     const int32_t *h = which == 0 ? c.h_a : c.h_b;
     uint32_t flag = 0;
     if (task < args.tasks[which]) {
         switch (op.limbs) {
-            case 1: split_run<1>(op, c, h, task, flag); break;
-            case 2: split_run<2>(op, c, h, task, flag); break;
-            case 3: split_run<3>(op, c, h, task, flag); break;
-            default: split_run<4>(op, c, h, task, flag); break;
+            case 1: split_run<1>(op, c, h, task, p_begin, p_end, flag); break;
+            case 2: split_run<2>(op, c, h, task, p_begin, p_end, flag); break;
+            case 3: split_run<3>(op, c, h, task, p_begin, p_end, flag); break;
+            default: split_run<4>(op, c, h, task, p_begin, p_end, flag); break;
         }
     }
     // one status word per block, written unconditionally (no clearing pass);
@@ -137,11 +147,17 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs args, Sp
     }
 }
 
-int64_t split_status_slots(const SplitOperand *a, const SplitOperand *b) {
+static int split_prime_groups(int64_t task_blocks, int n) {
+    if (task_blocks >= kSplitTargetBlocks / 2) return 1;
+    const int64_t g = (kSplitTargetBlocks + task_blocks - 1) / task_blocks;
+    return (int)(g < n ? g : n);
+}
+
+int64_t split_status_slots(const SplitOperand *a, const SplitOperand *b, int n) {
     int64_t ta = a ? a->r_pad * (a->k_pad / kRun) : 0;
     int64_t tb = b->r_pad * (b->k_pad / kRun);
-    return kStatusHeader + (ta + kSplitThreads - 1) / kSplitThreads +
-           (tb + kSplitThreads - 1) / kSplitThreads;
+    const int64_t blocks = (ta + kSplitThreads - 1) / kSplitThreads + (tb + kSplitThreads - 1) / kSplitThreads;
+    return kStatusHeader + blocks * split_prime_groups(blocks, n);
 }
 
 int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts &c,
@@ -156,10 +172,15 @@ int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts
         args.tasks[i] = ops[i]->r_pad * (ops[i]->k_pad / kRun);
         blocks[i] = (args.tasks[i] + kSplitThreads - 1) / kSplitThreads;
     }
-    const int64_t grid = blocks[0] + blocks[1];
-    if (grid <= 0) return RNS_OK;
+    const int64_t task_blocks = blocks[0] + blocks[1];
+    if (task_blocks <= 0) return RNS_OK;
+    if (c.n < 1 || c.n > kMaxPrimes) return RNS_E_ARG;
+    const int groups = split_prime_groups(task_blocks, c.n);
+    const int64_t grid = task_blocks * groups;
     if (grid + kStatusHeader > status_slots || grid > 0x7fffffff) return RNS_E_ARG;
     args.blocks0 = (int32_t)blocks[0];
+    args.task_blocks = (int32_t)task_blocks;
+    args.prime_groups = groups;
     args.flag_bit[0] = a ? RNS_FLAG_A_RANGE : RNS_FLAG_B_RANGE;
     args.flag_bit[1] = RNS_FLAG_B_RANGE;
     args.status = status;
