@@ -76,6 +76,21 @@ def measured_traffic(workload):
         return None
 
 
+def gemm_kernel_name(n, M, N):
+    """The product kernels the library launches for this shape (its tile choice)."""
+    import torch
+    if N <= 32:
+        return "gemm_kernel<128,32,64,4,1> (skinny tiles)"
+    tiles = n * ((M + 255) // 256) * ((N + 255) // 256)
+    if M < 256 or N < 256 or tiles < 256:
+        return "gemm_kernel<64,64,64,2,2> (small tiles)"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if tiles > cus and cus % 8 == 0:
+        return ("gemm_ps_kernel<4> (persistent, one workgroup per CU) + gemm_tail_kernel<8> "
+                "when tiles past the last whole round are split over K")
+    return "gemm_pp_kernel<4> (one 256x256 tile per workgroup)"
+
+
 def copy_probe():
     """A plain streaming kernel over 1 GiB (reads 1 GiB, writes 1 GiB), for counter scaling."""
     import torch
@@ -204,7 +219,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS,
                      "unit": "TOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,
                      "traffic": measured_traffic(args.workload),
-                     "kernel": "gemm_pp_kernel<4> (per-prime INT8 MFMA + mod-q epilogue)",
+                     "kernel": gemm_kernel_name(n, M, N),
                      "algorithmic_ops_per_launch": gemm_ops},
         "stages": {
             "split_us": split_ms * 1e3, "split_GBps": split_bytes / (split_ms * 1e-3) / 1e9,

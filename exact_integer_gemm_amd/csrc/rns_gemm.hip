@@ -38,6 +38,7 @@ struct GemmArgs {
     // per workgroup), which gemm_tail_kernel combines.
     int32_t full_tiles, split;
     int8_t *partial;
+    int32_t tiles;                       // all tiles of all primes
 };
 
 // ds_read_b128 is served 32 lanes at a time from 64 banks of 4 bytes: a
@@ -247,10 +248,15 @@ __device__ __forceinline__ void store_big_tile(v16i (&acc)[4][16 / NW], int q, d
 // A part of a split tile leaves its residues for gemm_tail_kernel: thread
 // tid's 64 * FN values as 4 * FN runs of 16 bytes, run c = i * FN + j at
 // [c][tid][16] of the part's kTailUnitBytes slot.
+// For q = 2 the rounding step leaves s - 2 round(s / 2) in {-1, 0, 1}, whose
+// low bit is the residue: `keep` masks each byte to it.
+__device__ __forceinline__ uint32_t residue_keep_mask(int q) { return q == 2 ? 0x01010101u : 0xffffffffu; }
+
 template <int NW>
 __device__ __forceinline__ void store_part(v16i (&acc)[4][16 / NW], int q, double inv, int8_t *slot,
                                            int tid) {
     constexpr int FN = 16 / NW;
+    const uint32_t keep = residue_keep_mask(q);
 #pragma unroll
     for (int i = 0; i < 4; i++)
 #pragma unroll
@@ -258,14 +264,12 @@ __device__ __forceinline__ void store_part(v16i (&acc)[4][16 / NW], int q, doubl
             const v16i &a = acc[i][j];
             uint32_t w[4];
 #pragma unroll
-            for (int gq = 0; gq < 4; gq++) {
-                int r[4];
-#pragma unroll
-                for (int e = 0; e < 4; e++)
-                    r[e] = q == 2 ? (a[4 * gq + e] & 1) : reduce_low_byte(a[4 * gq + e], q, inv);
-                w[gq] = pack4(r[0], r[1], r[2], r[3]);
-            }
+            for (int gq = 0; gq < 4; gq++)
+                w[gq] = pack4(reduce_low_byte(a[4 * gq], q, inv), reduce_low_byte(a[4 * gq + 1], q, inv),
+                              reduce_low_byte(a[4 * gq + 2], q, inv), reduce_low_byte(a[4 * gq + 3], q, inv)) &
+                        keep;
             *(v4u *)(slot + ((i * FN + j) * 64 * NW + tid) * 16) = v4u{w[0], w[1], w[2], w[3]};
+            __builtin_amdgcn_sched_barrier(0);          // one block at a time: bounded registers
         }
 }
 
@@ -443,6 +447,260 @@ __global__ __launch_bounds__(512) void gemm_pp_kernel(GemmArgs g, EpiConsts ec) 
                       g.y + p * g.y_plane + (int64_t)(tm * BM) * g.y_pitch + tn * BN, g.y_pitch, tid);
 }
 
+// ---- the persistent variant ---------------------------------------------------
+// gemm_pp_kernel's ping-pong with one workgroup per compute unit (G of them, G
+// a multiple of 8), each running a fixed list of items: the whole tiles b, b +
+// G, b + 2G, ... in the same XCD-aware order (G = 0 mod 8 keeps every item of
+// workgroup b on XCD b % 8), then K part b of the split tiles, if there is
+// one.  The LDS ring and the direct loads run on across items: a workgroup
+// counts its K steps globally, and the first steps of its next item are
+// requested during the last compute phases of the current one, so no item
+// starts by waiting for operands.  Each wave reduces and stores its own
+// 128 x 64 sub-tile right after its last compute phase of an item (no LDS, no
+// barrier), while the other group's waves keep the matrix cores busy; the
+// first compute phase of the next item starts its chains from zero.
+template <int S>
+__global__ __launch_bounds__(512) void gemm_ps_kernel(GemmArgs g, EpiConsts ec) {
+    constexpr int BM = 256, BN = 256, BK = 64, CH = BK / 16;
+    constexpr int FM = 4, FN = 2;                  // 128 x 64 per wave
+    constexpr int STAGE = (BM + BN) * CH;          // 2048 chunks = 32 KB
+    constexpr int DPW = STAGE / 512;               // 4 loads per wave per step
+    constexpr int D = S - 1;                       // prefetch distance in steps
+    constexpr int NST = FM * FN;                   // stores per wave per item
+    static_assert(S >= 2 && S <= 4 && S * STAGE * 16 <= 160 * 1024, "LDS ring");
+    static_assert(DPW == FM, "one direct load after each of the first FM MFMA rows");
+
+    __shared__ v4i lds[S][STAGE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
+    const int group = wave >> 2;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int half = lane >> 5, l32 = lane & 31;
+
+    const int G = gridDim.x, b = blockIdx.x;
+    const int nfull = b < g.full_tiles ? (g.full_tiles - 1 - b) / G + 1 : 0;
+    const bool has_part = b < (g.tiles - g.full_tiles) * g.split;
+    const int kt_part = g.kt / g.split;
+    const int items = nfull + (has_part ? 1 : 0);
+    const int KT = nfull * g.kt + (has_part ? kt_part : 0);
+    const int per_prime = g.tiles_m * g.tiles_n;
+
+    // item -> prime, tile row and column, first K step
+    auto locate = [&](int item, int &p, int &tm, int &tn, int &k_first) {
+        int tile;
+        k_first = 0;
+        if (item < nfull) {
+            const int F = g.full_tiles, v = b + item * G;
+            const int xcd = v & 7, idx = v >> 3;
+            tile = xcd * (F >> 3) + min(xcd, F & 7) + idx;
+        } else {
+            tile = g.full_tiles + b / g.split;
+            k_first = (b % g.split) * kt_part;
+        }
+        p = tile / per_prime;
+        const int t = tile - p * per_prime;
+        tm = t / g.tiles_n;
+        tn = t - tm * g.tiles_n;
+    };
+
+    // Load j of this wave fills LDS slots [(j*8 + wave)*64, +64) of a stage:
+    // loads 0, 1 carry A rows, loads 2, 3 B rows; off[j] is this lane's byte
+    // offset from the tile's first row at the current K step.
+    uint32_t off[DPW];
+#pragma unroll
+    for (int j = 0; j < DPW; j++) {
+        const int s = (j * 8 + wave) * 64 + lane;
+        const int row = s / CH;
+        const int c = (s % CH) ^ swz<CH>(row);
+        off[j] = row < BM ? (uint32_t)(row * g.a_row + c * 16) : (uint32_t)((row - BM) * g.b_row + c * 16);
+    }
+    // the load cursor: item and remaining steps of the next step to request
+    int d_item = 0, d_left = 0;
+    const int8_t *dA = g.a, *dB = g.b;
+    auto d_start = [&](int item) {
+        int p, tm, tn, kf;
+        locate(item, p, tm, tn, kf);
+        dA = g.a + p * g.a_plane + (int64_t)(tm * BM) * g.a_row + kf * g.a_kstep;
+        dB = g.b + p * g.b_plane + (int64_t)(tn * BN) * g.b_row + kf * g.b_kstep;
+        d_left = item < nfull ? g.kt : kt_part;
+    };
+    auto d_load = [&](int j, v4i *dst) {
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void *)((j < DPW / 2 ? dA : dB) + off[j]),
+            (__attribute__((address_space(3))) void *)(dst + (j * 8 + wave) * 64), 16, 0, 0);
+    };
+    auto d_advance = [&]() {
+        dA += g.a_kstep;
+        dB += g.b_kstep;
+        if (--d_left == 0 && ++d_item < items) d_start(d_item);
+    };
+    // s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding: vmcnt in
+    // bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).  Vector memory
+    // operations, the direct loads and the output stores alike, complete in
+    // the order they were issued.
+    auto wait_vm = [&](int n) {
+        switch (n) {
+            case 0: __builtin_amdgcn_s_waitcnt(0x0f70); break;
+            case 4: __builtin_amdgcn_s_waitcnt(0x0f74); break;
+            case 8: __builtin_amdgcn_s_waitcnt(0x0f78); break;
+            case 12: __builtin_amdgcn_s_waitcnt(0x0f7c); break;
+            default: __builtin_amdgcn_s_waitcnt(0x4f70); break;   // 16
+        }
+    };
+    auto read_frags = [&](int stage, int kk, v4i (&af)[FM], v4i (&bf)[FN]) {
+        const int chunk = kk * 2 + half;
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+            const int row = wm * 128 + i * 32 + l32;
+            af[i] = lds[stage][row * CH + (chunk ^ swz<CH>(row))];
+        }
+#pragma unroll
+        for (int j = 0; j < FN; j++) {
+            const int row = BM + wn * 64 + j * 32 + l32;
+            bf[j] = lds[stage][row * CH + (chunk ^ swz<CH>(row))];
+        }
+    };
+
+    v16i acc[FM][FN];
+    v4i af0[FM], bf0[FN], af1[FM], bf1[FN];
+
+    // memory phase for global step j: read the fragments of step j, then wait
+    // for the fragments and for own loads of step j + 1, behind which n later
+    // steps of loads may stay pending (and, in the first D - 1 steps of an
+    // item, the previous item's output stores)
+    auto pending = [&](int j) { return max(min(j + D - 1, KT - 1) - (j + 1), 0); };
+    auto memory = [&](int j, int n, bool after_store) {
+        read_frags(j % S, 0, af0, bf0);
+        read_frags(j % S, 1, af1, bf1);
+        wait_vm(4 * n + (after_store ? NST : 0));
+        __builtin_amdgcn_s_waitcnt(0xc07f);        // lgkmcnt(0)
+    };
+    // compute phase for global step j: 16 MFMAs, the loads of step j + D
+    // between them; FIRST starts the chains from zero; CHECK: step j + D may
+    // be past the end or in the next item
+    auto compute = [&](auto first, auto check, int jj) {
+        constexpr bool FIRST = decltype(first)::value, CHECK = decltype(check)::value;
+        const bool more = !CHECK || jj + D < KT;
+        v4i *dst = lds[(jj + D) % S];
+#pragma unroll
+        for (int i = 0; i < FM; i++) {
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf0[j], af0[i], FIRST ? v16i{0} : acc[i][j],
+                                                                  0, 0, 0);
+            if (more) d_load(i, dst);
+        }
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf1[j], af1[i], acc[i][j], 0, 0, 0);
+        if (more) {
+            dA += g.a_kstep;
+            dB += g.b_kstep;
+            --d_left;
+            if (CHECK && d_left == 0 && ++d_item < items) d_start(d_item);
+        }
+    };
+    // one K step: memory phase, barrier, compute phase, barrier
+    auto step = [&](auto first, auto check, int j, int n, bool after_store) {
+        memory(j, n, after_store);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        compute(first, check, j);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // The lane index, read afresh where an item ends: values derived from it
+    // there are not kept live (or spilled) across the whole item loop.
+    auto lane_now = []() {
+        int l;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+        return l;
+    };
+    // this wave's 128 x 64 sub-tile of item `item`: balanced residues mod q;
+    // the two half-waves swap 4-byte runs so that each lane stores 16 bytes
+    // of one row
+    auto store_tile = [&](int item) {
+        int p, tm, tn, kf;
+        locate(item, p, tm, tn, kf);
+        const int q = ec.q[p];
+        const double inv = ec.inv[p];
+        const uint32_t keep = residue_keep_mask(q);
+        // a uniform base per accumulator block plus this lane's 32-bit offset
+        const int ln = lane_now();
+        const uint32_t yl = (uint32_t)((wm * 128 + (ln & 31)) * g.y_pitch + wn * 64 + 16 * (ln >> 5));
+        int8_t *Yt = g.y + p * g.y_plane + (int64_t)(tm * BM) * g.y_pitch + tn * BN;
+#pragma unroll
+        for (int i = 0; i < FM; i++)
+#pragma unroll
+            for (int j = 0; j < FN; j++) {
+                const v16i &a = acc[i][j];
+                uint32_t w[4];
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++)
+                    w[gq] = pack4(reduce_low_byte(a[4 * gq], q, inv), reduce_low_byte(a[4 * gq + 1], q, inv),
+                                  reduce_low_byte(a[4 * gq + 2], q, inv), reduce_low_byte(a[4 * gq + 3], q, inv)) &
+                            keep;
+                // w[gq] holds columns 8gq + 4 half .. + 3.  v_permlane32_swap
+                // trades the upper half-wave of its first operand for the
+                // lower half-wave of its second: lane (l32, 0) gets columns
+                // 0 .. 15, lane (l32, 1) columns 16 .. 31.
+                const auto s02 = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+                const auto s13 = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+                int8_t *Yb = Yt + (int64_t)(i * 32) * g.y_pitch + j * 32;
+                *(v4u *)(Yb + yl) = v4u{s02[0], s02[1], s13[0], s13[1]};
+                __builtin_amdgcn_sched_barrier(0);      // one block at a time: bounded registers
+            }
+    };
+    auto epilogue = [&](int item) {
+        int p, tm, tn, kf;
+        locate(item, p, tm, tn, kf);
+        if (item >= nfull)
+            store_part<8>(acc, ec.q[p], ec.inv[p], g.partial + (int64_t)b * kTailUnitBytes, wave * 64 + lane_now());
+        else
+            store_tile(item);
+    };
+
+    if (KT == 0) return;
+    d_start(0);
+#pragma unroll
+    for (int s = 0; s < D; s++)
+        if (s < KT) {
+            v4i *dst = lds[s % S];
+#pragma unroll
+            for (int j = 0; j < DPW; j++) d_load(j, dst);
+            d_advance();
+        }
+    wait_vm(4 * min(D - 1, KT - 1));               // own loads of step 0 done
+    __builtin_amdgcn_s_barrier();                   // step 0 visible
+    // As in gemm_pp_kernel: group 1 runs one barrier behind group 0, so the
+    // compute phase of one group coincides with the memory phase (and the
+    // item epilogue) of the other.
+    if (group == 1) __builtin_amdgcn_s_barrier();
+    const std::true_type yes;
+    const std::false_type no;
+    int gs = 0;                                     // global K step
+    for (int item = 0; item < items; item++) {
+        const int len = item < nfull ? g.kt : kt_part;
+        const bool after = item > 0;
+        // the first D - 1 steps may wait behind the previous item's stores;
+        // the loads of the last D + 1 steps may reach into the next item
+        int j = 0;
+        step(yes, yes, gs, pending(gs), after);
+        for (j = 1, gs++; j < len && j < D - 1; j++, gs++) step(no, yes, gs, pending(gs), after);
+        for (; j < len - D - 1; j++, gs++) step(no, no, gs, D - 2, false);
+        for (; j < len; j++, gs++) step(no, yes, gs, pending(gs), false);
+        epilogue(item);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (group == 0) __builtin_amdgcn_s_barrier();
+}
+
 // The split tiles: block b sums the residues the `split` parts of tile
 // full_tiles + b left in their slots (|sum| <= split * 128, exact in int32),
 // reduces the sum mod q and stores the tile like the product kernel does.
@@ -521,17 +779,27 @@ int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
     if (tiles == 0) return RNS_OK;
     if (tiles > 0x7fffffff || m_pad > 0x7fffffff || n_pad > 0x7fffffff) return RNS_E_ARG;
     int64_t grid = tiles;
+    g.tiles = (int32_t)tiles;
     g.full_tiles = (int32_t)tiles;
+    const int cus = device_cus();
     if (cfg == kTileBig && partial) {
         int sp = 1;
-        g.full_tiles = tail_split(tiles, g.kt, device_cus(), &sp);
+        g.full_tiles = tail_split(tiles, g.kt, cus, &sp);
         g.split = sp;
         grid = g.full_tiles + (tiles - g.full_tiles) * sp;
         if (grid - g.full_tiles > kTailUnitsMax || (sp > 1 && g.kt % sp)) return RNS_E_ARG;
     }
+    // One persistent workgroup per compute unit once there is more than a
+    // round of tiles (its per-lane load offsets are 32-bit); a single round
+    // runs as before, one tile per workgroup.
+    const bool persistent = cfg == kTileBig && cus >= 8 && cus % 8 == 0 && tiles > cus &&
+                            256 * a_row < (int64_t)1 << 32 && 256 * b_row < (int64_t)1 << 32;
     switch (cfg) {
         case kTileBig:
-            hipLaunchKernelGGL((gemm_pp_kernel<4>), dim3((unsigned)grid), dim3(512), 0, s, g, c);
+            if (persistent)
+                hipLaunchKernelGGL((gemm_ps_kernel<4>), dim3((unsigned)cus), dim3(512), 0, s, g, c);
+            else
+                hipLaunchKernelGGL((gemm_pp_kernel<4>), dim3((unsigned)grid), dim3(512), 0, s, g, c);
             if (g.split > 1) {
                 if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
                 hipLaunchKernelGGL((gemm_tail_kernel<8>), dim3((unsigned)(tiles - g.full_tiles)), dim3(512), 0,

@@ -117,6 +117,45 @@ def test_split_tail_tiles():
         assert np.array_equal(out.cpu().numpy(), ref)
 
 
+def test_persistent_rounds():
+    """Two whole rounds of 256 x 256 tiles per compute unit, then K parts of
+    the remaining tiles: each workgroup walks its list of tiles with the
+    operand ring running on from one tile into the next."""
+    M, N, K = 1024, 1024, 1024
+    p = rg.plan(K, 113, 113)
+    tiles = p.n_primes * (M // 256) * (N // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"persistent: M={M} N={N} K={K} n={p.n_primes} tiles={tiles} cus={cus}", flush=True)
+    assert tiles > 2 * cus or cus > 256
+    A, B = W.random_operands(37, M, N, K, 2, 2, 113, 113)
+    p, ws, C = run_gemm(A, B, 113, 113)
+    assert rg.status(ws) == 0
+    assert np.array_equal(C, oracle_c(A, B, p.out_limbs_min))
+
+
+def test_persistent_uneven_rounds_all_primes():
+    """54 primes (q = 2 among them) on large tiles, with a last round that
+    only some workgroups run: the per-prime products against the oracle's
+    stage definition for q = 2 and a spread of other primes."""
+    M, N, K = 768, 768, 256
+    rng = np.random.default_rng(71)
+    p = rg.plan_n(54)
+    ps = list(p.primes)
+    print(f"persistent batched: M={M} N={N} K={K} tiles={54 * 9}", flush=True)
+    A_res = W.balanced_residue_planes(rng, ps, M, K)
+    r = rng.integers(-(1 << 34), 1 << 34, size=(K, N), endpoint=True)
+    ws = rg.new_workspace(p, M, N, K, True, "cuda")
+    B = dev(r[..., None])
+    rg.split(p, None, B, ws, M=M)
+    rg.residue_products(p, M, N, K, ws, A_res=dev(A_res))
+    torch.cuda.synchronize()
+    Yp = rg.workspace_planes(p, ws, M, N, K, batched=True)["Y"].cpu().numpy()
+    for j in (0, 1, 17, 30, 52, 53):
+        q = ps[j]
+        refB = O.residue_planes(r.T, [q])[0]
+        assert np.array_equal(Yp[j, :M, :N], O.residue_product(A_res[j], refB.T, q)), f"prime {q}"
+
+
 def test_output_limbs_sign_extension():
     A, B = W.random_operands(21, 40, 30, 50, 1, 1, 30, 30)
     p, ws, C = run_gemm(A, B, 30, 30, out_limbs=5)
