@@ -211,7 +211,7 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
         return RNS_E_ARG;
     const int64_t groups = (total + 31) / 32;
     int64_t grid = (groups + 3) / 4;
-    if (grid > 8192) grid = 8192;             // grid-stride beyond 32 blocks per CU
+    if (grid > 1536) grid = 1536;             // grid-stride: each wave amortises its set-up
     const dim3 g((unsigned)grid), b(256);
     if (ksteps == 1 && nblocks == 1)
         hipLaunchKernelGGL((crt_kernel<1, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);

@@ -63,17 +63,28 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
     const int64_t k0 = kb * kKBlock + (lane & 3) * kRun;
     const bool row_ok = r < op.rows;
 
+    // All 16 L limbs are requested before any is used: a padding entry reads
+    // entry 0 (the operand is not empty when there are tasks) and is then
+    // replaced by zero, so no load sits behind a branch and a wait.
+    uint64_t xs[kRun][L];
+#pragma unroll
+    for (int e = 0; e < kRun; e++) {
+        const int64_t k = k0 + e;
+        const bool ok = row_ok && k < op.k;
+        const int64_t idx = !ok ? 0 : op.transposed ? (k * op.rows + r) : (r * op.k + k);
+#pragma unroll
+        for (int l = 0; l < L; l++) xs[e][l] = (uint64_t)op.x[idx * L + l];
+    }
     // U = x + 2^(64L-1) as 2L little-endian 32-bit words, per element
     uint32_t u[kRun][2 * L];
     uint32_t lowbit = 0;   // bit e: x_e is odd (residue mod 2)
 #pragma unroll
     for (int e = 0; e < kRun; e++) {
         const int64_t k = k0 + e;
-        uint64_t x[L];
         const bool ok = row_ok && k < op.k;
-        const int64_t idx = op.transposed ? (k * op.rows + r) : (r * op.k + k);
+        uint64_t x[L];
 #pragma unroll
-        for (int l = 0; l < L; l++) x[l] = ok ? (uint64_t)op.x[idx * L + l] : 0ull;
+        for (int l = 0; l < L; l++) x[l] = ok ? xs[e][l] : 0ull;
         if (op.bits >= 0 && !within_bound<L>(x, op.bits)) flag = 1;
         lowbit |= (uint32_t)(x[0] & 1u) << e;
 #pragma unroll
