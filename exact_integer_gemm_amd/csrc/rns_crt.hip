@@ -16,7 +16,8 @@
 // 16h .. 16h + 15 of each 32-slot K step: exactly the second-operand
 // fragment of v_mfma_i32_32x32x32_i8, whose result gives lane (l32, h) the
 // chunk sums 8*gq + 4h + e (gq, e < 4) of its entry.  The two halves swap
-// their 4-chunk groups and each carries the whole value into 32-bit words.
+// their 4-chunk groups and each carries the whole value into 32-bit words;
+// each then stores half of the entry's limbs.
 #include "rns_device.h"
 
 namespace rns {
@@ -28,11 +29,21 @@ __device__ __forceinline__ int reduce_small(int t, int q, float inv) {
     return t - q * k;
 }
 
+// The value x of the lane in the other half-wave (lane l xor 32), by
+// v_permlane32_swap: swapping x with itself gives the lower half-wave the
+// upper half's values in the second result and vice versa in the first.
+__device__ __forceinline__ uint32_t partner_u32(uint32_t x, int h) {
+    const auto s = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return h ? s[0] : s[1];
+}
+
+// pair_stores: C is 16-byte aligned and c_limbs is even, so the two limbs
+// of a lane leave as one 16-byte store
 template <int KS, int NB>
 __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
                                                   const int8_t *__restrict__ y, int64_t y_plane,
                                                   int64_t y_pitch, int64_t M, int64_t N,
-                                                  int64_t *__restrict__ C, int c_limbs) {
+                                                  int64_t *__restrict__ C, int c_limbs, int pair_stores) {
     constexpr int W = 8 * NB;                 // 32-bit words of X'
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -75,7 +86,6 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
         }
     const int rk = cc.n;                      // the -r slot
     const int rks = rk >> 5, rh = (rk >> 4) & 1, rb = rk & 15;
-    const int half0 = (c_limbs + 1) >> 1;     // limbs written by the lower half
 
     const int64_t total = M * N;
     const int64_t groups = (total + 31) >> 5;
@@ -102,7 +112,7 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
             for (int wd = 0; wd < 4; wd++)
                 ua[ks][wd] = (int)pack4(byte[4 * wd], byte[4 * wd + 1], byte[4 * wd + 2], byte[4 * wd + 3]);
         }
-        const float ft = f + __shfl_xor(f, 32);
+        const float ft = f + __uint_as_float(partner_u32(__float_as_uint(f), h));
         const float rf = __builtin_rintf(ft);
         const bool near_half = __builtin_fabsf(ft - rf) > 0.5f - 0x1p-10f;
         const int r = (int)rf;
@@ -138,9 +148,9 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
                 const v16i &a = acc[nb];
                 g[nb][gq] = (int64_t)a[4 * gq] + ((int64_t)a[4 * gq + 1] << 8) +
                             ((int64_t)a[4 * gq + 2] << 16) + ((int64_t)a[4 * gq + 3] << 24);
-                const int lo = __shfl_xor((int)(uint32_t)g[nb][gq], 32);
-                const int hi = __shfl_xor((int)(g[nb][gq] >> 32), 32);
-                gp[nb][gq] = (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+                const uint32_t lo = partner_u32((uint32_t)g[nb][gq], h);
+                const uint32_t hi = partner_u32((uint32_t)((uint64_t)g[nb][gq] >> 32), h);
+                gp[nb][gq] = (int64_t)(((uint64_t)hi << 32) | lo);
             }
         uint32_t wv[W];
         int64_t carry = 0;
@@ -189,14 +199,25 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
         }
 
         if (ok) {
+            // lane (l32, h) writes limbs 4t + 2h and 4t + 2h + 1 of its entry
             int64_t *ce = C + e * c_limbs;
             const uint32_t sign = (uint32_t)carry;
 #pragma unroll
-            for (int l = 0; l < RNS_MAX_OUT_LIMBS; l++) {
-                const uint32_t lo = 2 * l < W ? wv[2 * l] : sign;
-                const uint32_t hi = 2 * l + 1 < W ? wv[2 * l + 1] : sign;
-                const bool mine = h ? (l >= half0 && l < c_limbs) : (l < half0 && l < c_limbs);
-                if (mine) ce[l] = (int64_t)(((uint64_t)hi << 32) | lo);
+            for (int t = 0; t < RNS_MAX_OUT_LIMBS / 4; t++) {
+                uint32_t wd[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int i0 = 8 * t + i, i1 = 8 * t + 4 + i;
+                    const uint32_t a0 = i0 < W ? wv[i0] : sign, a1 = i1 < W ? wv[i1] : sign;
+                    wd[i] = h ? a1 : a0;
+                }
+                const int l = 4 * t + 2 * h;
+                if (pair_stores) {
+                    if (l < c_limbs) *(v4u *)(ce + l) = v4u{wd[0], wd[1], wd[2], wd[3]};
+                } else {
+                    if (l < c_limbs) ce[l] = (int64_t)(((uint64_t)wd[1] << 32) | wd[0]);
+                    if (l + 1 < c_limbs) ce[l + 1] = (int64_t)(((uint64_t)wd[3] << 32) | wd[2]);
+                }
             }
         }
     }
@@ -213,14 +234,15 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
     int64_t grid = (groups + 3) / 4;
     if (grid > 1536) grid = 1536;             // grid-stride: each wave amortises its set-up
     const dim3 g((unsigned)grid), b(256);
+    const int pairs = (reinterpret_cast<uintptr_t>(C) % 16 == 0 && c_limbs % 2 == 0) ? 1 : 0;
     if (ksteps == 1 && nblocks == 1)
-        hipLaunchKernelGGL((crt_kernel<1, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);
+        hipLaunchKernelGGL((crt_kernel<1, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs);
     else if (ksteps == 1)
-        hipLaunchKernelGGL((crt_kernel<1, 2>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);
+        hipLaunchKernelGGL((crt_kernel<1, 2>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs);
     else if (nblocks == 1)
-        hipLaunchKernelGGL((crt_kernel<2, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);
+        hipLaunchKernelGGL((crt_kernel<2, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs);
     else
-        hipLaunchKernelGGL((crt_kernel<2, 2>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs);
+        hipLaunchKernelGGL((crt_kernel<2, 2>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs);
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 

@@ -163,6 +163,22 @@ def test_output_limbs_sign_extension():
     assert np.array_equal(C, ref)
 
 
+def test_output_only_8_byte_aligned():
+    """An output that starts 8 bytes into its allocation (even limb count):
+    the reconstruction falls back from 16-byte to 8-byte limb stores."""
+    A, B = W.random_operands(23, 70, 45, 60, 2, 2, 90, 90)
+    p = rg.plan(60, 90, 90)
+    lc = 4
+    assert p.out_limbs_min <= lc
+    buf = torch.full((70 * 45 * lc + 1,), 5, dtype=torch.int64, device="cuda")
+    out = buf[1:].view(70, 45, lc)
+    assert out.data_ptr() % 16 == 8
+    rg.gemm(p, dev(A), dev(B), out_limbs=lc, out=out)
+    torch.cuda.synchronize()
+    assert int(buf[0]) == 5
+    assert np.array_equal(out.cpu().numpy(), oracle_c(A, B, lc))
+
+
 def test_k_zero_and_empty():
     p = rg.plan(0, 10, 10)
     A = torch.zeros((5, 0, 1), dtype=torch.int64, device="cuda")
