@@ -36,7 +36,7 @@ FLAG_A_RANGE = 1
 FLAG_B_RANGE = 2
 
 ERRORS = {0: "RNS_OK", -1: "RNS_E_ARG", -2: "RNS_E_K", -3: "RNS_E_CAPACITY",
-          -4: "RNS_E_OUT_LIMBS", -5: "RNS_E_WORKSPACE", -6: "RNS_E_HIP"}
+          -4: "RNS_E_OUT_LIMBS", -5: "RNS_E_WORKSPACE", -6: "RNS_E_HIP", -7: "RNS_E_NONFINITE"}
 
 
 class RnsError(RuntimeError):
@@ -58,6 +58,19 @@ class _Layout(ctypes.Structure):
                 ("a_off", ctypes.c_int64), ("b_off", ctypes.c_int64), ("y_off", ctypes.c_int64),
                 ("status_off", ctypes.c_int64), ("total_bytes", ctypes.c_int64),
                 ("tile_config", ctypes.c_int32)]
+
+
+class _FpStats(ctypes.Structure):
+    _fields_ = [("max_msb", ctypes.c_int32), ("min_lsb", ctypes.c_int32),
+                ("nonzero", ctypes.c_int32), ("nonfinite", ctypes.c_int32)]
+
+
+class _EnclosePlan(ctypes.Structure):
+    _fields_ = [("plan", _Plan), ("fa", ctypes.c_int32), ("fb", ctypes.c_int32),
+                ("a_bits", ctypes.c_int32), ("b_bits", ctypes.c_int32),
+                ("a_limbs", ctypes.c_int32), ("b_limbs", ctypes.c_int32),
+                ("c_limbs", ctypes.c_int32), ("q", ctypes.c_int32),
+                ("out_format", ctypes.c_int32), ("zero", ctypes.c_int32)]
 
 
 _lib = None
@@ -91,6 +104,15 @@ def load() -> ctypes.CDLL:
         "rns_reconstruct_garner": (ctypes.c_int, [P, I64, I64, I64, I32, VP, I32, VP, SZ, VP]),
         "rns_status": (ctypes.c_int, [VP, VP, ctypes.POINTER(ctypes.c_uint32)]),
         "rns_error_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "rns_fp64_stats": (ctypes.c_int, [VP, I64, VP, VP, SZ, VP]),
+        "rns_enclose_plan": (ctypes.c_int, [I64, ctypes.POINTER(_FpStats), ctypes.POINTER(_FpStats), I32,
+                                            ctypes.POINTER(_EnclosePlan)]),
+        "rns_enclose_workspace_size": (ctypes.c_int, [ctypes.POINTER(_EnclosePlan), I64, I64, I64,
+                                                      ctypes.POINTER(SZ)]),
+        "rns_mm_enclose": (ctypes.c_int, [ctypes.POINTER(_EnclosePlan), I64, I64, I64, VP, VP, VP, VP, VP,
+                                          SZ, VP]),
+        "rns_fp64_to_limbs": (ctypes.c_int, [VP, I64, I32, I32, VP, VP]),
+        "rns_round_outward": (ctypes.c_int, [VP, I64, I32, I32, I32, VP, VP, VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -345,3 +367,7 @@ def workspace_planes(p: Plan, workspace: torch.Tensor, M: int, N: int, K: int,
     out["Y"] = ws8.as_strided((n, L["m_pad"], L["n_pad"]),
                               (L["m_pad"] * L["y_pitch"], L["y_pitch"], 1), L["y_off"])
     return out
+
+
+from .enclose import (EnclosePlan, digest, enclose_plan, fp64_stats, fp64_to_limbs,  # noqa: E402
+                      mm_enclose, round_outward, width_ulps)

@@ -581,6 +581,7 @@ const char *rns_error_string(int code) {
         case RNS_E_OUT_LIMBS: return "too few (or too many) output limbs";
         case RNS_E_WORKSPACE: return "workspace too small";
         case RNS_E_HIP: return "HIP launch or copy failed";
+        case -7: return "non-finite operand";
         default: return "unknown error code";
     }
 }

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs args, Sp
 }
 
 static int split_prime_groups(int64_t task_blocks, int n) {
-    if (task_blocks >= kSplitTargetBlocks / 2) return 1;
+    if (task_blocks <= 0 || task_blocks >= kSplitTargetBlocks / 2) return 1;
     const int64_t g = (kSplitTargetBlocks + task_blocks - 1) / task_blocks;
     return (int)(g < n ? g : n);
 }

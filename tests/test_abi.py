@@ -1,7 +1,6 @@
 """Host-side checks of the C ABI (no GPU needed).
 
-The library must load, export every entry point ``include/rns_gemm.h``
-declares, share PyTorch's HIP runtime, plan exactly like the oracle, and turn
+The library must load, export every entry point ``include/*.h`` declares, share PyTorch's HIP runtime, plan exactly like the oracle, and turn
 every invalid argument into its error code before anything is launched.
 """
 import ctypes
@@ -15,7 +14,8 @@ from exact_integer_gemm_amd import _build
 from oracle import oracle as O
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rns_gemm.h")
+HEADERS = [os.path.join(ROOT, "include", h) for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 
 @pytest.fixture(scope="module")
@@ -26,16 +26,20 @@ def lib():
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*\*?(rns_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:int|const char \*)\s*\*?(rns_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
     assert set(names) >= {"rns_plan", "rns_plan_n", "rns_workspace_size", "rns_gemm",
                           "rns_gemm_batched_residue", "rns_status", "rns_error_string",
-                          "rns_workspace_layout"}
+                          "rns_workspace_layout", "rns_fp64_stats", "rns_enclose_plan",
+                          "rns_enclose_workspace_size", "rns_mm_enclose", "rns_fp64_to_limbs",
+                          "rns_round_outward"}
     for n in names:
         assert hasattr(lib, n), n
     nm = os.popen(f"nm -D --defined-only {_build.LIB}").read()
@@ -53,6 +57,9 @@ def test_one_hip_runtime_in_process(lib):
 def test_plan_struct_matches_header(lib):
     # rns_plan_t: 4 int32, int64, double, int32[54]
     assert ctypes.sizeof(rg._Plan) == 4 * 4 + 8 + 8 + 4 * 54
+    # rns_fp_stats_t: 4 int32; rns_enclose_plan_t: rns_plan_t then 10 int32
+    assert ctypes.sizeof(rg._FpStats) == 16
+    assert ctypes.sizeof(rg._EnclosePlan) == ctypes.sizeof(rg._Plan) + 10 * 4
 
 
 @pytest.mark.parametrize("K,a,b", [(64, 20, 20), (1024, 31, 31), (4096, 55, 55), (4096, 100, 100),
@@ -199,3 +206,66 @@ def test_binding_rejects_bad_tensors(lib):
     A = torch.zeros((2, 8, 1), dtype=torch.int64)
     with pytest.raises(ValueError):
         rg.gemm(p, A, A.clone())          # CPU tensors are refused
+
+
+# ---------------------------------------------------------------------------
+# enclosure planner (host logic; enclosure-gemm, "Method")
+# ---------------------------------------------------------------------------
+def _stats_of(X):
+    """The four planner reductions of an array, from the oracle's definitions."""
+    import math
+    import numpy as np
+    from oracle import enclose as E
+    vals = [float(x) for x in np.asarray(X, dtype=np.float64).ravel()]
+    nonfinite = int(any(not math.isfinite(v) for v in vals))
+    nz = [v for v in vals if math.isfinite(v) and v != 0]
+    if not nz:
+        return (-2 ** 31, 2 ** 31 - 1, 0, nonfinite)
+    msb = max(math.frexp(v)[1] - 1 for v in nz)
+    lsb = min(E.lowest_set_bit_exponent(v) for v in nz)
+    return (msb, lsb, 1, nonfinite)
+
+
+def test_enclose_plan_scales_like_the_oracle(lib):
+    import numpy as np
+    from oracle import enclose as E
+    rng = np.random.default_rng(11)
+    A = rng.standard_normal((6, 9)) * 2.0 ** rng.integers(-20, 20, size=(6, 9))
+    B = rng.standard_normal((9, 4))
+    ep = rg.enclose_plan(9, _stats_of(A), _stats_of(B), 64)
+    assert ep.fa == E.coarsest_lossless_scale(A) and ep.fb == E.coarsest_lossless_scale(B)
+    SA = E.scaled_integers(A, ep.fa)
+    SB = E.scaled_integers(B, ep.fb)
+    assert max(abs(int(v)) for v in SA.ravel()) < 2 ** ep.c.a_bits
+    assert max(abs(int(v)) for v in SB.ravel()) < 2 ** ep.c.b_bits
+    assert ep.q == ep.fa + ep.fb and not ep.zero
+    ps = O.prime_set_for_bound(9, ep.c.a_bits, ep.c.b_bits)
+    assert ep.n_primes == len(ps)
+
+
+def test_enclose_plan_errors_and_zero(lib):
+    import numpy as np
+    with pytest.raises(rg.RnsError) as e:
+        rg.enclose_plan(4, _stats_of([1.0, np.inf]), _stats_of([1.0]), 64)
+    assert e.value.code == -7
+    with pytest.raises(rg.RnsError) as e:
+        rg.enclose_plan(4, _stats_of([2.0 ** 300, 2.0 ** -300]), _stats_of([1.0]), 64)
+    assert e.value.code == -3
+    with pytest.raises(rg.RnsError) as e:     # each fits 4 limbs, the product does not fit P
+        rg.enclose_plan(4096, _stats_of([2.0 ** 100, 2.0 ** -90]), _stats_of([2.0 ** 100, 2.0 ** -90]), 64)
+    assert e.value.code == -3
+    with pytest.raises(rg.RnsError) as e:
+        rg.enclose_plan(2 ** 17 + 1, _stats_of([1.0]), _stats_of([1.0]), 64)
+    assert e.value.code == -2
+    with pytest.raises(rg.RnsError) as e:
+        rg.enclose_plan(4, _stats_of([1.0]), _stats_of([1.0]), 16)
+    assert e.value.code == -1
+    ep = rg.enclose_plan(5, _stats_of(np.zeros(6)), _stats_of([3.0, 1e300]), 32)
+    assert ep.zero and ep.c.out_format == 32
+
+
+def test_workspace_size_with_empty_contraction(lib):
+    """K == 0 (no split work at all) still has a workspace size."""
+    for M, N in ((2, 5), (300, 300), (1, 40)):
+        assert rg.workspace_size(rg.plan(0, 0, 0), M, N, 0) >= 0
+        assert rg.workspace_size(rg.plan_n(54), M, N, 0, True) >= 0
