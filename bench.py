@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wide",
-                    choices=["tiny", "square", "enclosure", "dixon", "wide"])
+                    choices=["tiny", "square", "enclosure", "dixon", "wide", "enclosure_fp64"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
@@ -103,6 +103,108 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes_read": n, "copy_probe_bytes_written": n}), flush=True)
 
 
+def enclosure_fp64(args):
+    """The enclosure product on binary64 operands: A[1024,4096] @ B[4096,1024]
+    of N(0,1) entries, (lo, hi) rounded outward.  One step is a whole
+    mm_enclose call: the planner's reductions and their host synchronisation,
+    the scaling into limbs, the exact product and the rounding."""
+    import ctypes
+    import torch
+    import exact_integer_gemm_amd as rg
+    from exact_integer_gemm_amd import enclose as EN
+
+    rg.load()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    M, K, N = 1024, 4096, 1024
+    rng = np.random.default_rng(3)
+    A_h = rng.standard_normal((M, K))
+    B_h = rng.standard_normal((K, N))
+    A = torch.from_numpy(A_h).to(dev)
+    B = torch.from_numpy(B_h).to(dev)
+    lo, hi, ep = rg.mm_enclose(A, B, return_plan=True)
+    ws = torch.empty(EN.workspace_size(ep, M, N, K), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        rg.mm_enclose(A, B, workspace=ws)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(args.steps):
+        lo, hi = rg.mm_enclose(A, B, workspace=ws)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+
+    # device stages of the same call, each timed alone (events on the stream)
+    a_l, b_l, c_l = ep.limbs
+    plan = rg.Plan._from_c(ep.c.plan)
+    gws = rg.new_workspace(plan, M, N, K, False, dev)
+    Ai = torch.empty((M, K, a_l), dtype=torch.int64, device=dev)
+    Bi = torch.empty((K, N, b_l), dtype=torch.int64, device=dev)
+    S = torch.empty((M, N, c_l), dtype=torch.int64, device=dev)
+    stats = torch.empty(8, dtype=torch.int32, device=dev)
+    sws = torch.empty(EN.FP_STATS_WS_BYTES, dtype=torch.uint8, device=dev)
+    # the products and the reconstruction are the integer path's kernels on
+    # the same planes: the split of the integer copies prepares them once
+    rg.load().rns_fp64_to_limbs(A.data_ptr(), M * K, ep.fa, a_l, Ai.data_ptr(), stream.cuda_stream)
+    rg.load().rns_fp64_to_limbs(B.data_ptr(), K * N, ep.fb, b_l, Bi.data_ptr(), stream.cuda_stream)
+    rg.split(plan, Ai, Bi, gws, M=M)
+    stages = {
+        "stats_us": lambda: (EN.fp64_stats(A, stats[0:4], sws), EN.fp64_stats(B, stats[4:8], sws)),
+        "mm_enclose_device_us": lambda: rg.load().rns_mm_enclose(
+            ctypes.byref(ep.c), M, N, K, A.data_ptr(), B.data_ptr(), lo.data_ptr(), hi.data_ptr(),
+            ws.data_ptr(), ws.numel(), stream.cuda_stream),
+        "gemm_us": lambda: rg.residue_products(plan, M, N, K, gws),
+        "reconstruct_us": lambda: rg.reconstruct(plan, M, N, K, gws, S),
+        "round_us": lambda: rg.load().rns_round_outward(S.data_ptr(), M * N, c_l, ep.q, 64, lo.data_ptr(),
+                                                        hi.data_ptr(), stream.cuda_stream),
+    }
+    out_st = {}
+    for name, fn in stages.items():
+        fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out_st[name] = e0.elapsed_time(e1) / 10 * 1e3
+    gemm_ops = 2.0 * M * N * K * ep.n_primes
+    gemm_tops = gemm_ops / (out_st["gemm_us"] * 1e-6) / 1e12
+    width = rg.width_ulps(lo, hi)
+    out = {
+        "metric": "enclosure product rate (2MNK/s, lo <= A@B <= hi exactly)",
+        "value": 2.0 * M * N * K / (ms_step * 1e-3), "unit": "ops/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": "enclosure_fp64", "M": M, "N": N, "K": K, "operands": "binary64 N(0,1)",
+                   "fa": ep.fa, "fb": ep.fb, "limbs": [a_l, b_l, c_l], "n_primes": ep.n_primes,
+                   "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                     "frac": gemm_tops / PEAK_INT8_TOPS, "traffic": None,
+                     "kernel": gemm_kernel_name(ep.n_primes, M, N)},
+        "stages": out_st,
+        "width_ulps_max": int(width.max()), "width_ulps_zero_frac": float((width == 0).float().mean()),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import enclose as E
+        t = time.perf_counter()
+        rows, cols = 2, 32
+        rlo, rhi = E.enclose(A_h[:rows], B_h[:, :cols])
+        dt = time.perf_counter() - t
+        same = (np.array_equal(rlo.view(np.uint64), lo[:rows, :cols].cpu().numpy().view(np.uint64)) and
+                np.array_equal(rhi.view(np.uint64), hi[:rows, :cols].cpu().numpy().view(np.uint64)))
+        out["cpu_baseline"] = {"value": 2.0 * rows * cols * K / dt, "unit": "ops/s", "cores": 1,
+                               "kind": "oracle", "bit_exact_sample": bool(same),
+                               "sample": f"{rows}x{cols} entries of the product (all of K), Python Fraction "
+                                         f"oracle ({dt:.1f} s)"}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -112,6 +214,9 @@ def main():
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.workload == "enclosure_fp64":
+        enclosure_fp64(args)
+        return
 
     import torch
     import exact_integer_gemm_amd as rg

@@ -46,6 +46,52 @@ __device__ __forceinline__ int reduce_low_byte(int t, int q, double inv) {
     return __mul24(round_div(t, inv), -q) + t;
 }
 
+// floor(x * 2^F) for the binary64 value with bit pattern `bits`, as L
+// little-endian two's-complement limbs (the caller guarantees the result
+// fits).  A finite x is m * 2^e2 with m < 2^53 (hidden bit for normal
+// numbers; subnormals share the smallest normal exponent), so the magnitude
+// is m shifted by e2 + F; a right shift that drops set bits moves the floor of
+// a negative value one further from zero.
+template <int L>
+__device__ __forceinline__ void fp64_floor_scaled(uint64_t bits, int F, uint64_t (&limb)[L]) {
+    const uint64_t a = bits & 0x7fffffffffffffffull;
+    const int ef = (int)(a >> 52);
+    const uint64_t frac = a & ((1ull << 52) - 1);
+    const uint64_t m = ef ? (frac | (1ull << 52)) : frac;
+    const int e2 = ef ? ef - 1075 : -1074;
+#pragma unroll
+    for (int l = 0; l < L; l++) limb[l] = 0;
+    bool dropped = false;
+    if (a != 0) {
+        const int shift = e2 + F;
+        if (shift >= 0) {
+            const int li = shift >> 6, off = shift & 63;
+#pragma unroll
+            for (int l = 0; l < L; l++) {
+                uint64_t w = 0;
+                if (l == li) w = m << off;
+                if (l == li + 1 && off) w = m >> (64 - off);
+                limb[l] = w;
+            }
+        } else if (shift > -64) {
+            limb[0] = m >> -shift;
+            dropped = (m & ((1ull << -shift) - 1)) != 0;
+        } else {
+            dropped = true;
+        }
+    }
+    if (bits >> 63) {
+        // -(magnitude + dropped) = ~magnitude + 1 - dropped
+        uint64_t carry = dropped ? 0 : 1;
+#pragma unroll
+        for (int l = 0; l < L; l++) {
+            const uint64_t w = ~limb[l] + carry;
+            carry = (carry && w == 0) ? 1 : 0;
+            limb[l] = w;
+        }
+    }
+}
+
 __device__ __forceinline__ uint32_t pack4(int b0, int b1, int b2, int b3) {
     // low bytes of four ints -> one word (byte 0 = b0)
     uint32_t lo = __builtin_amdgcn_perm((uint32_t)b1, (uint32_t)b0, 0x0c0c0400u);

@@ -12,7 +12,7 @@
 
 namespace rns {
 
-constexpr int kStatsBlocks = 256;
+constexpr int kStatsBlocks = 1024;     // 4 per CU: enough loads in flight to stream X
 constexpr int kStatsThreads = 256;
 static_assert(kStatsBlocks * 4 * 4 <= RNS_FP_STATS_WS_BYTES, "stats workspace");
 
@@ -64,9 +64,8 @@ __global__ __launch_bounds__(kStatsThreads) void fp_stats_kernel(const uint64_t 
                                                                  int *__restrict__ partial) {
     __shared__ int sh[4][kStatsThreads];
     int v[4] = {INT_MIN, INT_MAX, 0, 0};
-    for (int64_t i = (int64_t)blockIdx.x * kStatsThreads + threadIdx.x; i < count;
-         i += (int64_t)gridDim.x * kStatsThreads) {
-        const Fp64Fields f = fp64_fields(x[i]);
+    auto take = [&](uint64_t b) {
+        const Fp64Fields f = fp64_fields(b);
         if (!f.finite) {
             v[3] = 1;
         } else if (!f.zero) {
@@ -74,7 +73,18 @@ __global__ __launch_bounds__(kStatsThreads) void fp_stats_kernel(const uint64_t 
             v[0] = max(v[0], f.e2 + 63 - __clzll((long long)f.m));
             v[1] = min(v[1], f.e2 + __ffsll((long long)f.m) - 1);
         }
+    };
+    // four loads in flight per thread, then the tail one by one
+    const int64_t stride = (int64_t)gridDim.x * kStatsThreads;
+    int64_t i = (int64_t)blockIdx.x * kStatsThreads + threadIdx.x;
+    for (; i + 3 * stride < count; i += 4 * stride) {
+        uint64_t b[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) b[u] = x[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; u++) take(b[u]);
     }
+    for (; i < count; i += stride) take(x[i]);
     block_reduce4(v, sh);
     if (threadIdx.x == 0) {
         int4 *o = reinterpret_cast<int4 *>(partial) + blockIdx.x;
@@ -105,46 +115,12 @@ __global__ __launch_bounds__(kStatsThreads) void fp_stats_final_kernel(const int
 }
 
 // ---- scaling into integer limbs ------------------------------------------------
-// floor(x * 2^F) as L little-endian two's-complement limbs.  x = m * 2^e2, so
-// the magnitude is m shifted by e2 + F; a right shift that drops set bits
-// makes the floor of a negative value one further from zero.
 template <int L>
 __global__ __launch_bounds__(256) void fp64_to_limbs_kernel(const uint64_t *__restrict__ x, int64_t count, int F,
                                                             int64_t *__restrict__ out) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count; i += (int64_t)gridDim.x * 256) {
-        const Fp64Fields f = fp64_fields(x[i]);
         uint64_t limb[L];
-#pragma unroll
-        for (int l = 0; l < L; l++) limb[l] = 0;
-        bool dropped = false;
-        if (!f.zero) {
-            const int shift = f.e2 + F;
-            if (shift >= 0) {
-                const int li = shift >> 6, off = shift & 63;
-#pragma unroll
-                for (int l = 0; l < L; l++) {
-                    uint64_t w = 0;
-                    if (l == li) w = f.m << off;
-                    if (l == li + 1 && off) w = f.m >> (64 - off);
-                    limb[l] = w;
-                }
-            } else if (shift > -64) {
-                limb[0] = f.m >> -shift;
-                dropped = (f.m & ((1ull << -shift) - 1)) != 0;
-            } else {
-                dropped = true;
-            }
-        }
-        if (f.neg) {
-            // -(magnitude + dropped) = ~magnitude + 1 - dropped
-            uint64_t carry = dropped ? 0 : 1;
-#pragma unroll
-            for (int l = 0; l < L; l++) {
-                const uint64_t w = ~limb[l] + carry;
-                carry = (carry && w == 0) ? 1 : 0;
-                limb[l] = w;
-            }
-        }
+        fp64_floor_scaled<L>(x[i], F, limb);
         int64_t *o = out + i * L;
 #pragma unroll
         for (int l = 0; l < L; l++) o[l] = (int64_t)limb[l];
@@ -254,8 +230,10 @@ int limbs_for_bits(int bits) { return (bits + 1 + 63) / 64; }
 
 int64_t round_up256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// The exact product S, then rns_gemm's workspace (the split reads the
+// binary64 operands directly, so no integer copy of them is kept).
 struct EncloseLayout {
-    int64_t a_off, b_off, s_off, gemm_off, gemm_bytes, total;
+    int64_t s_off, gemm_off, gemm_bytes, total;
 };
 
 int enclose_layout(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K, EncloseLayout *L) {
@@ -263,10 +241,6 @@ int enclose_layout(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K
     const int rc = rns_workspace_size(&ep->plan, M, N, K, 0, &gb);
     if (rc != RNS_OK) return rc;
     int64_t off = 0;
-    L->a_off = off;
-    off = round_up256(off + M * K * ep->a_limbs * 8);
-    L->b_off = off;
-    off = round_up256(off + K * N * ep->b_limbs * 8);
     L->s_off = off;
     off = round_up256(off + M * N * ep->c_limbs * 8);
     L->gemm_off = off;
@@ -390,13 +364,9 @@ int rns_mm_enclose(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K
     if (rc != RNS_OK) return rc;
     if ((int64_t)ws_bytes < L.total) return RNS_E_WORKSPACE;
     int8_t *base = static_cast<int8_t *>(ws);
-    int64_t *Ai = reinterpret_cast<int64_t *>(base + L.a_off);
-    int64_t *Bi = reinterpret_cast<int64_t *>(base + L.b_off);
     int64_t *Si = reinterpret_cast<int64_t *>(base + L.s_off);
-    if ((rc = rns_fp64_to_limbs(A, M * K, ep->fa, ep->a_limbs, Ai, stream)) != RNS_OK) return rc;
-    if ((rc = rns_fp64_to_limbs(B, K * N, ep->fb, ep->b_limbs, Bi, stream)) != RNS_OK) return rc;
-    if ((rc = rns_gemm(&ep->plan, M, N, K, Ai, ep->a_limbs, Bi, ep->b_limbs, Si, ep->c_limbs, base + L.gemm_off,
-                       (size_t)L.gemm_bytes, stream)) != RNS_OK)
+    if ((rc = gemm_fp64_scaled(&ep->plan, M, N, K, A, ep->a_limbs, B, ep->b_limbs, Fp64Scales{ep->fa, ep->fb}, Si,
+                               ep->c_limbs, base + L.gemm_off, (size_t)L.gemm_bytes, stream)) != RNS_OK)
         return rc;
     return rns_round_outward(Si, M * N, ep->c_limbs, ep->q, ep->out_format, lo, hi, stream);
 }

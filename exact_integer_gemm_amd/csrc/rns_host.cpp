@@ -338,7 +338,7 @@ int prepare(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, bool batche
 
 int stage_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
                 const int64_t *A, int32_t a_limbs, const int64_t *B, int32_t b_limbs,
-                void *ws, size_t ws_bytes, hipStream_t stream) {
+                void *ws, size_t ws_bytes, hipStream_t stream, const Fp64Scales *fp = nullptr) {
     const bool batched = A == nullptr;
     if (!batched && (a_limbs < 1 || a_limbs > RNS_MAX_IN_LIMBS)) return RNS_E_ARG;
     if (b_limbs < 1 || b_limbs > RNS_MAX_IN_LIMBS) return RNS_E_ARG;
@@ -356,11 +356,13 @@ int stage_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
         sa.r_pad = L.pub.m_pad; sa.k_pad = L.pub.k_pad; sa.limbs = a_limbs;
         sa.bits = (plan->a_bits >= 0 && plan->a_bits < 64 * a_limbs - 1) ? plan->a_bits : -1;
         sa.transposed = 0;
+        if (fp) { sa.fp64 = 1; sa.scale = fp->fa; }
     }
     sb.x = B; sb.planes = base + L.pub.b_off; sb.rows = N; sb.k = K;
     sb.r_pad = L.pub.n_pad; sb.k_pad = L.pub.k_pad; sb.limbs = b_limbs;
     sb.bits = (plan->b_bits >= 0 && plan->b_bits < 64 * b_limbs - 1) ? plan->b_bits : -1;
     sb.transposed = 1;
+    if (fp) { sb.fp64 = 1; sb.scale = fp->fb; }
     return launch_split(batched ? nullptr : &sa, &sb, sc, (uint32_t *)(base + L.pub.status_off),
                         L.status_slots, stream);
 }
@@ -429,7 +431,7 @@ int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, b
 int run(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
         const int64_t *A, int32_t a_limbs, const int8_t *A_res,
         const int64_t *B, int32_t b_limbs, int64_t *C, int32_t c_limbs,
-        void *ws, size_t ws_bytes, hipStream_t stream) {
+        void *ws, size_t ws_bytes, hipStream_t stream, const Fp64Scales *fp = nullptr) {
     const bool batched = A_res != nullptr;
     int rc = validate(plan, M, N, K);
     if (rc) return rc;
@@ -443,7 +445,7 @@ int run(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
     if (!B || (!batched && !A) || !ws) return RNS_E_ARG;
     const Layout L = make_layout(*plan, M, N, K, batched);
     if (ws_bytes < (size_t)L.pub.total_bytes) return RNS_E_WORKSPACE;
-    rc = stage_split(plan, M, N, K, batched ? nullptr : A, a_limbs, B, b_limbs, ws, ws_bytes, stream);
+    rc = stage_split(plan, M, N, K, batched ? nullptr : A, a_limbs, B, b_limbs, ws, ws_bytes, stream, fp);
     if (rc) return rc;
     rc = stage_products(plan, M, N, K, A_res, ws, ws_bytes, stream);
     if (rc) return rc;
@@ -451,6 +453,16 @@ int run(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
 }
 
 }  // namespace
+
+int gemm_fp64_scaled(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                     const double *A, int32_t a_limbs, const double *B, int32_t b_limbs,
+                     const Fp64Scales &scales, int64_t *C, int32_t c_limbs,
+                     void *ws, size_t ws_bytes, hipStream_t stream) {
+    // the split reads each binary64 operand as one 64-bit word per entry
+    return run(plan, M, N, K, reinterpret_cast<const int64_t *>(A), a_limbs, nullptr,
+               reinterpret_cast<const int64_t *>(B), b_limbs, C, c_limbs, ws, ws_bytes, stream, &scales);
+}
+
 }  // namespace rns
 
 using namespace rns;

@@ -136,10 +136,24 @@ struct SplitOperand {
     int32_t limbs;
     int32_t bits;          // declared bound, or -1 for no check
     int32_t transposed;    // 0: A ([rows][K]), 1: B ([K][rows])
+    int32_t fp64;          // 1: x holds binary64 values (one word per entry), read as
+                           //    `limbs` limbs of floor(x * 2^scale)
+    int32_t scale;
 };
 
 int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts &c,
                  uint32_t *status, int64_t status_slots, hipStream_t s);
+
+// Binary64 operands read by the split as floor(A * 2^fa), floor(B * 2^fb).
+struct Fp64Scales {
+    int32_t fa, fb;
+};
+// rns_gemm on binary64 operands A [M][K], B [K][N], scaled into a_limbs /
+// b_limbs limbs inside the split (same checks, layout and errors as rns_gemm).
+int gemm_fp64_scaled(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                     const double *A, int32_t a_limbs, const double *B, int32_t b_limbs,
+                     const Fp64Scales &scales, int64_t *C, int32_t c_limbs,
+                     void *ws, size_t ws_bytes, hipStream_t stream);
 int launch_repack_residues(const int8_t *src, int64_t n, int64_t M, int64_t K,
                            int8_t *dst, int64_t m_pad, int64_t k_pad, hipStream_t s);
 int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,

@@ -50,7 +50,7 @@ __device__ __forceinline__ bool within_bound(const uint64_t (&x)[L], int bits) {
     return below || is_pow;
 }
 
-template <int L>
+template <int L, bool FP>
 __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const int32_t *h,
                           int64_t task, int p_begin, int p_end, uint32_t &flag) {
     // 64 consecutive tasks (one wave) cover one K block (64 k) of 16 plane
@@ -66,14 +66,16 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
     // All 16 L limbs are requested before any is used: a padding entry reads
     // entry 0 (the operand is not empty when there are tasks) and is then
     // replaced by zero, so no load sits behind a branch and a wait.
-    uint64_t xs[kRun][L];
+    // (binary64 operands: one word per entry, scaled into L limbs here)
+    constexpr int W = FP ? 1 : L;
+    uint64_t xs[kRun][W];
 #pragma unroll
     for (int e = 0; e < kRun; e++) {
         const int64_t k = k0 + e;
         const bool ok = row_ok && k < op.k;
         const int64_t idx = !ok ? 0 : op.transposed ? (k * op.rows + r) : (r * op.k + k);
 #pragma unroll
-        for (int l = 0; l < L; l++) xs[e][l] = (uint64_t)op.x[idx * L + l];
+        for (int l = 0; l < W; l++) xs[e][l] = (uint64_t)op.x[idx * W + l];
     }
     // U = x + 2^(64L-1) as 2L little-endian 32-bit words, per element
     uint32_t u[kRun][2 * L];
@@ -83,8 +85,12 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
         const int64_t k = k0 + e;
         const bool ok = row_ok && k < op.k;
         uint64_t x[L];
+        if constexpr (FP) {
+            fp64_floor_scaled<L>(ok ? xs[e][0] : 0ull, op.scale, x);
+        } else {
 #pragma unroll
-        for (int l = 0; l < L; l++) x[l] = ok ? xs[e][l] : 0ull;
+            for (int l = 0; l < L; l++) x[l] = ok ? xs[e][l] : 0ull;
+        }
         if (op.bits >= 0 && !within_bound<L>(x, op.bits)) flag = 1;
         lowbit |= (uint32_t)(x[0] & 1u) << e;
 #pragma unroll
@@ -128,6 +134,9 @@ __device__ void split_run(const SplitOperand &op, const SplitConsts &c, const in
     }
 }
 
+// FP: both operands are binary64 (one kernel per operand kind keeps the
+// register allocation of each path separate)
+template <bool FP>
 __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs args, SplitConsts c) {
     const int tb = (int)blockIdx.x % args.task_blocks, pg = (int)blockIdx.x / args.task_blocks;
     const int p_begin = pg * c.n / args.prime_groups, p_end = (pg + 1) * c.n / args.prime_groups;
@@ -139,10 +148,10 @@ __global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs args, Sp
     uint32_t flag = 0;
     if (task < args.tasks[which]) {
         switch (op.limbs) {
-            case 1: split_run<1>(op, c, h, task, p_begin, p_end, flag); break;
-            case 2: split_run<2>(op, c, h, task, p_begin, p_end, flag); break;
-            case 3: split_run<3>(op, c, h, task, p_begin, p_end, flag); break;
-            default: split_run<4>(op, c, h, task, p_begin, p_end, flag); break;
+            case 1: split_run<1, FP>(op, c, h, task, p_begin, p_end, flag); break;
+            case 2: split_run<2, FP>(op, c, h, task, p_begin, p_end, flag); break;
+            case 3: split_run<3, FP>(op, c, h, task, p_begin, p_end, flag); break;
+            default: split_run<4, FP>(op, c, h, task, p_begin, p_end, flag); break;
         }
     }
     // one status word per block, written unconditionally (no clearing pass);
@@ -200,7 +209,12 @@ int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts
         // operand 0 is B: its offset constant lives in h_a's place
         for (int p = 0; p < kMaxPrimes; p++) cc.h_a[p] = c.h_b[p];
     }
-    hipLaunchKernelGGL(split_kernel, dim3((unsigned)grid), dim3(kSplitThreads), 0, s, args, cc);
+    const bool fp = ops[0]->fp64 != 0;
+    if (ops[1] && (ops[1]->fp64 != 0) != fp) return RNS_E_ARG;
+    if (fp)
+        hipLaunchKernelGGL(split_kernel<true>, dim3((unsigned)grid), dim3(kSplitThreads), 0, s, args, cc);
+    else
+        hipLaunchKernelGGL(split_kernel<false>, dim3((unsigned)grid), dim3(kSplitThreads), 0, s, args, cc);
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 

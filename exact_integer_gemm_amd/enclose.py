@@ -20,7 +20,7 @@ import torch
 
 from . import (RnsError, _EnclosePlan, _FpStats, _check, _stream_ptr, load)
 
-FP_STATS_WS_BYTES = 8192
+FP_STATS_WS_BYTES = 16384
 
 
 @dataclass(frozen=True)

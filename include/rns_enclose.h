@@ -42,7 +42,7 @@ extern "C" {
 #define RNS_E_NONFINITE (-7)
 
 /* Device workspace of rns_fp64_stats, in bytes. */
-#define RNS_FP_STATS_WS_BYTES 8192
+#define RNS_FP_STATS_WS_BYTES 16384
 
 /* The exponent-field reductions that plan one operand (enclosure-gemm,
  * "Method": planning an operand reads reductions over its exponent field). */
@@ -86,7 +86,7 @@ int rns_enclose_plan(int64_t K, const rns_fp_stats_t *a, const rns_fp_stats_t *b
 
 /*
  * rns_enclose_workspace_size -- device bytes needed by rns_mm_enclose: the
- * integer operands and product plus rns_gemm's workspace.  Returns RNS_OK,
+ * exact integer product plus rns_gemm's workspace.  Returns RNS_OK,
  * RNS_E_ARG or RNS_E_K.
  */
 int rns_enclose_workspace_size(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K,
@@ -97,8 +97,9 @@ int rns_enclose_workspace_size(const rns_enclose_plan_t *ep, int64_t M, int64_t 
  * ep->out_format) with lo <= A @ B <= hi exactly, lo the largest and hi the
  * smallest such format values; lo == hi when the product is representable.
  * An exact zero gives +0.0 in both.  ep must come from rns_enclose_plan on
- * the stats of these very operands.  Four steps on `stream`: the scaling of
- * A and B into integer limbs, rns_gemm, and the outward rounding.
+ * the stats of these very operands.  The steps of rns_gemm on `stream`, with
+ * the residue split reading the binary64 entries and scaling them into
+ * integer limbs itself, then the outward rounding.
  * Returns RNS_OK, RNS_E_ARG, RNS_E_K, RNS_E_WORKSPACE or RNS_E_HIP.
  */
 int rns_mm_enclose(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K,
