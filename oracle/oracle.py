@@ -59,6 +59,20 @@ def primes_largest_first(bound: int = 256) -> List[int]:
     return sorted(primes_below(bound), reverse=True)
 
 
+def prime_power_moduli(bound: int = 256) -> List[int]:
+    """For every prime p < bound, the largest power of p not above ``bound``;
+    largest first (256, 251, 243, 241, ...).  Their product is lcm(1..256),
+    whose log2 is the 362.8-bit INT8 CRT capacity of the Ozaki Scheme II
+    paper (§1.2, §4.2.2)."""
+    out = []
+    for p in primes_below(bound):
+        q = p
+        while q * p <= bound:
+            q *= p
+        out.append(q)
+    return sorted(out, reverse=True)
+
+
 def prod(xs: Iterable[int]) -> int:
     r = 1
     for x in xs:
@@ -86,6 +100,26 @@ def prime_set_for_bound(K: int, a_bits: int, b_bits: int) -> List[int]:
         if P > bound2:
             return ps
     raise ValueError("bound exceeds the product of all primes below 256")
+
+
+def moduli_set_for_bound(K: int, a_bits: int, b_bits: int, prime_powers: bool = False) -> List[int]:
+    """``prime_set_for_bound``, or with ``prime_powers`` the same rule over the
+    prime-power moduli (256 first).  Balanced residues mod 256 reach -128, so
+    int32 accumulation of K products of them is exact only for K <= 2^17 - 1
+    (K * 2^14 <= 2^31 - 1)."""
+    if not prime_powers:
+        return prime_set_for_bound(K, a_bits, b_bits)
+    if not (0 <= K <= K_MAX - 1):
+        raise ValueError("K outside 0..2^17-1")
+    bound2 = 2 * max(K, 1) * (1 << (a_bits + b_bits))
+    ms: List[int] = []
+    P = 1
+    for q in prime_power_moduli():
+        ms.append(q)
+        P *= q
+        if P > bound2:
+            return ms
+    raise ValueError("bound exceeds the product of the prime-power moduli")
 
 
 def limbs_to_hold(P: int) -> int:

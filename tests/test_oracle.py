@@ -400,3 +400,45 @@ def test_batched_residue_step_invariants():
         rhs = np.mod(Ares[j].astype(object).dot(r.astype(object).dot(v.astype(object))), q)
         assert np.array_equal(lhs, rhs)
     assert np.all(2 * X <= P) and np.all(2 * X > -P)
+
+
+# ---------------------------------------------------------------------------
+# prime-power moduli (Ozaki Scheme II paper, §1.2 / §4.2.2: 362.8-bit capacity)
+# ---------------------------------------------------------------------------
+def test_prime_power_moduli_product_is_lcm():
+    import math as _m
+    ms = O.prime_power_moduli()
+    assert len(ms) == 54 and ms[0] == 256 and ms[2] == 243
+    assert O.prod(ms) == _m.lcm(*range(1, 257))
+    assert abs(_m.log2(O.prod(ms)) - 362.8) < 0.05
+    for a in ms:
+        for b in ms:
+            assert a == b or _m.gcd(a, b) == 1
+
+
+def test_moduli_set_for_bound_prime_powers():
+    import math as _m
+    ms = O.moduli_set_for_bound(4096, 170, 170, prime_powers=True)   # beyond the 335-bit primes
+    assert O.prod(ms) > 2 * 4096 * 2 ** 340 and O.prod(ms[:-1]) <= 2 * 4096 * 2 ** 340
+    with pytest.raises(ValueError):
+        O.prime_set_for_bound(4096, 170, 170)
+    with pytest.raises(ValueError):
+        O.moduli_set_for_bound(2 ** 17, 1, 1, prime_powers=True)
+    with pytest.raises(ValueError):
+        O.moduli_set_for_bound(8, 180, 180, prime_powers=True)
+
+
+def test_crt_with_prime_power_moduli():
+    """CRT and Garner over the composite (coprime) moduli against sympy, at
+    both ends of (-P/2, P/2] for the even P that contains 256."""
+    from sympy.ntheory.modular import crt as sympy_crt
+    rng = np.random.default_rng(31)
+    ms = O.prime_power_moduli()[:12]
+    P = O.prod(ms)
+    for X in [0, 1, -1, P // 2, -(P // 2) + 1, P // 3, -(P // 7)] + [int(v) for v in rng.integers(-2 ** 62, 2 ** 62, 20)]:
+        res = [O.balanced(X, q) for q in ms]
+        assert O.crt_balanced(res, ms) == X
+        assert O.crt_rounded_quotient(res, ms) == X
+        r0, _ = sympy_crt(ms, [r % q for r, q in zip(res, ms)])
+        assert (int(r0) - X) % P == 0
+        assert O.mixed_radix_value(O.garner_digits(res, ms), ms) == X
