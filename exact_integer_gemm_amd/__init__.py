@@ -94,6 +94,8 @@ def load() -> ctypes.CDLL:
     sig = {
         "rns_plan": (ctypes.c_int, [I64, I32, I32, P]),
         "rns_plan_n": (ctypes.c_int, [I32, P]),
+        "rns_plan_moduli": (ctypes.c_int, [I64, I32, I32, I32, P]),
+        "rns_plan_n_moduli": (ctypes.c_int, [I32, I32, P]),
         "rns_workspace_size": (ctypes.c_int, [P, I64, I64, I64, I32, ctypes.POINTER(SZ)]),
         "rns_workspace_layout": (ctypes.c_int, [P, I64, I64, I64, I32, ctypes.POINTER(_Layout)]),
         "rns_gemm": (ctypes.c_int, [P, I64, I64, I64, VP, I32, VP, I32, VP, I32, VP, SZ, VP]),
@@ -156,17 +158,25 @@ class Plan:
                     tuple(int(c.primes[i]) for i in range(c.n_primes)))
 
 
-def plan(K: int, a_bits: int, b_bits: int) -> Plan:
-    """Fewest largest-first primes with product > 2*K*2^(a_bits+b_bits)."""
+MODULI_PRIMES = 0
+MODULI_PRIME_POWERS = 1
+
+
+def plan(K: int, a_bits: int, b_bits: int, prime_powers: bool = False) -> Plan:
+    """Fewest largest-first moduli with product > 2*K*2^(a_bits+b_bits): the
+    primes below 256, or with ``prime_powers`` the factors of lcm(1..256)
+    (up to 362.8 bits; K <= 2^17 - 1)."""
     c = _Plan()
-    _check(load().rns_plan(K, a_bits, b_bits, ctypes.byref(c)), "rns_plan")
+    kind = MODULI_PRIME_POWERS if prime_powers else MODULI_PRIMES
+    _check(load().rns_plan_moduli(K, a_bits, b_bits, kind, ctypes.byref(c)), "rns_plan_moduli")
     return Plan._from_c(c)
 
 
-def plan_n(n_primes: int) -> Plan:
-    """The n largest primes below 256, with no operand bound."""
+def plan_n(n_primes: int, prime_powers: bool = False) -> Plan:
+    """The n largest moduli (primes below 256, or prime powers), with no operand bound."""
     c = _Plan()
-    _check(load().rns_plan_n(n_primes, ctypes.byref(c)), "rns_plan_n")
+    kind = MODULI_PRIME_POWERS if prime_powers else MODULI_PRIMES
+    _check(load().rns_plan_n_moduli(n_primes, kind, ctypes.byref(c)), "rns_plan_n_moduli")
     return Plan._from_c(c)
 
 

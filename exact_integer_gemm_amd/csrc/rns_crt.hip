@@ -84,6 +84,9 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
             const int k = h ? k1 : k0;
             plane[ks][b] = k < cc.n ? k : cc.n - 1;   // padding slots read a valid plane, weight 0
         }
+    // a modulus 256 (always slot 0, the largest) can round to u = 128, whose
+    // int8 byte reads as -128: its quotient term must use the byte's value
+    const bool wrap0 = cc.q[0] == 256;
     const int rk = cc.n;                      // the -r slot
     const int rks = rk >> 5, rh = (rk >> 4) & 1, rb = rk & 15;
 
@@ -104,7 +107,8 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
 #pragma unroll
             for (int b = 0; b < 16; b++) {
                 const int t = (int)yp[plane[ks][b] * y_plane] * sw[ks][b];
-                const int u = reduce_small(t, sq[ks][b], si[ks][b]);
+                int u = reduce_small(t, sq[ks][b], si[ks][b]);
+                if (ks == 0 && b == 0) u = (wrap0 && h == 0) ? (int)(int8_t)u : u;
                 f = __builtin_fmaf((float)u, si[ks][b], f);
                 byte[b] = u;
             }

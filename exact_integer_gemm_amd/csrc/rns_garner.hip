@@ -11,11 +11,13 @@ namespace rns {
 // One thread per output entry.  NB (a multiple of 8, >= n) bounds the fully
 // unrolled digit loops, so every digit and partial sum lives in registers.
 // Slots k >= n are padding that the tables make inert (q = 1, all constants
-// zero), so the loops carry no guards.  Slot 0 holds the prime 2 when the
-// plan has it.
+// zero), so the loops carry no guards.  Slot 0 holds the even modulus (2 or
+// 256) when the plan has one; its digit is taken in (-q/2, q/2], which puts
+// the mixed-radix value in (-P/2, P/2].
 //
 // acc[k] starts at y_k * Q_k^-1 and loses v_j * (Q_j Q_k^-1 mod q_k) for every
-// earlier digit j; |acc| <= 54 * 125^2 < 2^20 keeps the rounding step exact.
+// earlier digit j; |acc| <= 128 + 54 * 128 * 125 < 2^20 keeps the rounding
+// step exact.
 // The value X = sum_k v_k Q_k is gathered in 16-bit chunks t[c] (signed,
 // |t[c]| < 54 * 125 * 2^16 < 2^29) and carried into limbs at the end.
 template <int NB>
@@ -39,6 +41,7 @@ __global__ __launch_bounds__(256) void garner_kernel(GarnerConsts gc, const int8
     for (int k = 0; k < NB; k++) {
         int v;
         if (k == 0 && gc.q[0] == 2) v = acc[0] & 1;
+        else if (k == 0 && gc.q[0] == 256) v = ((acc[0] + 127) & 255) - 127;   // digit in [-127, 128]
         else v = reduce_exact(acc[k], gc.q[k], gc.inv[k]);
 #pragma unroll
         for (int kk = k + 1; kk < NB; kk++) acc[kk] -= __mul24(v, (int)gc.tri[tri_index(k, kk)]);

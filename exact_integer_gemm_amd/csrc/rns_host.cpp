@@ -12,22 +12,33 @@
 namespace rns {
 namespace {
 
-// ---- the primes below 256, largest first ------------------------------------
-struct PrimeTable {
+// ---- the moduli, largest first ----------------------------------------------
+// kind RNS_MODULI_PRIMES: the primes below 256.  kind RNS_MODULI_PRIME_POWERS:
+// for each of those primes its largest power not above 256 (256, 243, 169,
+// 125, 121, 49 and the primes from 17 up), the factors of lcm(1..256).
+bool is_prime(int x) {
+    if (x < 2) return false;
+    for (int d = 2; d * d <= x; d++)
+        if (x % d == 0) return false;
+    return true;
+}
+struct ModuliTable {
     int p[kMaxPrimes];
-    PrimeTable() {
+    explicit ModuliTable(bool powers) {
         int cnt = 0;
         for (int x = 255; x >= 2; x--) {
-            bool prime = true;
-            for (int d = 2; d * d <= x; d++)
-                if (x % d == 0) { prime = false; break; }
-            if (prime) p[cnt++] = x;
+            if (!is_prime(x)) continue;
+            int q = x;
+            if (powers)
+                while (q * x <= 256) q *= x;
+            p[cnt++] = q;
         }
+        std::sort(p, p + cnt, [](int a, int b) { return a > b; });
     }
 };
-const PrimeTable &primes() {
-    static const PrimeTable t;
-    return t;
+const ModuliTable &moduli(int kind) {
+    static const ModuliTable primes(false), powers(true);
+    return kind == RNS_MODULI_PRIME_POWERS ? powers : primes;
 }
 
 // ---- a minimal unsigned big integer (little-endian 32-bit words) ----------
@@ -91,10 +102,14 @@ int64_t powmod(int64_t b, int64_t e, int64_t m) {
     }
     return r;
 }
-int64_t inv_mod(int64_t a, int64_t q) {   // q prime, a != 0 mod q
-    a %= q;
-    if (a < 0) a += q;
-    return powmod(a, q - 2, q);
+int64_t inv_mod(int64_t a, int64_t q) {   // gcd(a, q) = 1 (extended Euclid)
+    int64_t r0 = q, r1 = ((a % q) + q) % q, t0 = 0, t1 = 1;
+    while (r1 != 0) {
+        const int64_t k = r0 / r1;
+        int64_t r = r0 - k * r1; r0 = r1; r1 = r;
+        int64_t t = t0 - k * t1; t0 = t1; t1 = t;
+    }
+    return ((t0 % q) + q) % q;
 }
 int balanced(int64_t x, int64_t q) {
     int64_t r = x % q;
@@ -102,32 +117,47 @@ int balanced(int64_t x, int64_t q) {
     return (int)(r > q / 2 ? r - q : r);
 }
 
-void fill_common(rns_plan_t *out, int n) {
+void fill_common(rns_plan_t *out, int n, int kind) {
     Big P(1);
     double l2 = 0;
     for (int i = 0; i < kMaxPrimes; i++) out->primes[i] = 0;
     for (int i = 0; i < n; i++) {
-        out->primes[i] = primes().p[i];
-        P.mul_small((uint32_t)primes().p[i]);
-        l2 += std::log2((double)primes().p[i]);
+        const int q = moduli(kind).p[i];
+        out->primes[i] = q;
+        P.mul_small((uint32_t)q);
+        l2 += std::log2((double)q);
     }
     out->n_primes = n;
     out->log2_P = l2;
     out->out_limbs_min = (P.bit_length() + 63) / 64;
 }
 
+// the prime of a prime power q <= 256, or 0 when q is not one
+int prime_of(int q) {
+    for (int d = 2; d <= q; d++)
+        if (q % d == 0) {
+            int r = q;
+            while (r % d == 0) r /= d;
+            return (r == 1 && is_prime(d)) ? d : 0;
+        }
+    return 0;
+}
+
 bool plan_ok(const rns_plan_t *p) {
     if (!p || p->n_primes < 1 || p->n_primes > kMaxPrimes) return false;
     if (p->k_max < 1 || p->k_max > RNS_K_MAX) return false;
     if (p->out_limbs_min < 1 || p->out_limbs_min > RNS_MAX_OUT_LIMBS) return false;
-    // the primes must be distinct primes below 256 (any order)
-    bool seen[256] = {false};
+    // the moduli must be prime powers up to 256 over distinct primes (so
+    // pairwise coprime), in any order; 256 (residues down to -128) needs
+    // K <= 2^17 - 1 for exact int32 accumulation
+    bool seen[257] = {false};
     for (int i = 0; i < p->n_primes; i++) {
         const int q = p->primes[i];
-        if (q < 2 || q > 255 || seen[q]) return false;
-        for (int d = 2; d * d <= q; d++)
-            if (q % d == 0) return false;
-        seen[q] = true;
+        if (q < 2 || q > 256) return false;
+        const int pr = prime_of(q);
+        if (!pr || seen[pr]) return false;
+        seen[pr] = true;
+        if (q == 256 && p->k_max > RNS_K_MAX - 1) return false;
     }
     return true;
 }
@@ -170,12 +200,12 @@ void build_garner(const rns_plan_t &pl, GarnerConsts &g) {
     g.n = n;
     int slot = 0;
     for (int j = 0; j < n; j++)
-        if (pl.primes[j] == 2) g.plane[slot++] = (uint8_t)j;
+        if (pl.primes[j] % 2 == 0) g.plane[slot++] = (uint8_t)j;
     for (int j = 0; j < n; j++)
-        if (pl.primes[j] != 2) g.plane[slot++] = (uint8_t)j;
+        if (pl.primes[j] % 2 != 0) g.plane[slot++] = (uint8_t)j;
     for (int k = 0; k < kGarnerSlots; k++) {
         if (k < n) {
-            g.q[k] = (uint8_t)pl.primes[g.plane[k]];
+            g.q[k] = (uint16_t)pl.primes[g.plane[k]];
             g.inv[k] = 1.0 / (double)g.q[k];
         } else {
             // inert padding slot: reads plane of slot 0, multiplies it by 0
@@ -193,7 +223,7 @@ void build_garner(const rns_plan_t &pl, GarnerConsts &g) {
             Qmod[j] = Qj;
             Qj = Qj * g.q[j] % qk;
         }
-        const int64_t Qk_inv = (qk == 2) ? 1 : inv_mod(Qmod[k], qk);
+        const int64_t Qk_inv = inv_mod(Qmod[k], qk);
         g.tri[tri_index(k, k)] = (int8_t)balanced(Qk_inv, qk);
         for (int j = 0; j < k; j++)
             g.tri[tri_index(j, k)] = (int8_t)balanced(Qmod[j] * Qk_inv, qk);
@@ -469,18 +499,19 @@ using namespace rns;
 
 extern "C" {
 
-int rns_plan(int64_t K, int32_t a_bits, int32_t b_bits, rns_plan_t *out) {
-    if (!out) return RNS_E_ARG;
+int rns_plan_moduli(int64_t K, int32_t a_bits, int32_t b_bits, int32_t kind, rns_plan_t *out) {
+    if (!out || (kind != RNS_MODULI_PRIMES && kind != RNS_MODULI_PRIME_POWERS)) return RNS_E_ARG;
     if (a_bits < 0 || b_bits < 0 || a_bits > 255 || b_bits > 255) return RNS_E_ARG;
-    if (K < 0 || K > RNS_K_MAX) return RNS_E_K;
+    const int64_t kmax = kind == RNS_MODULI_PRIME_POWERS ? RNS_K_MAX - 1 : RNS_K_MAX;
+    if (K < 0 || K > kmax) return RNS_E_K;
     const int64_t Kb = K < 1 ? 1 : K;
     Big bound((uint64_t)Kb);
     bound.shl(a_bits + b_bits + 1);          // 2 * K * 2^(a+b)
     Big P(1);
     for (int n = 1; n <= kMaxPrimes; n++) {
-        P.mul_small((uint32_t)primes().p[n - 1]);
+        P.mul_small((uint32_t)moduli(kind).p[n - 1]);
         if (Big::greater(P, bound)) {
-            fill_common(out, n);
+            fill_common(out, n, kind);
             out->a_bits = a_bits;
             out->b_bits = b_bits;
             out->k_max = Kb;
@@ -490,13 +521,22 @@ int rns_plan(int64_t K, int32_t a_bits, int32_t b_bits, rns_plan_t *out) {
     return RNS_E_CAPACITY;
 }
 
-int rns_plan_n(int32_t n_primes, rns_plan_t *out) {
-    if (!out || n_primes < 1 || n_primes > kMaxPrimes) return RNS_E_ARG;
-    fill_common(out, n_primes);
+int rns_plan(int64_t K, int32_t a_bits, int32_t b_bits, rns_plan_t *out) {
+    return rns_plan_moduli(K, a_bits, b_bits, RNS_MODULI_PRIMES, out);
+}
+
+int rns_plan_n_moduli(int32_t n, int32_t kind, rns_plan_t *out) {
+    if (!out || n < 1 || n > kMaxPrimes || (kind != RNS_MODULI_PRIMES && kind != RNS_MODULI_PRIME_POWERS))
+        return RNS_E_ARG;
+    fill_common(out, n, kind);
     out->a_bits = -1;
     out->b_bits = -1;
-    out->k_max = RNS_K_MAX;
+    out->k_max = kind == RNS_MODULI_PRIME_POWERS ? RNS_K_MAX - 1 : RNS_K_MAX;
     return RNS_OK;
+}
+
+int rns_plan_n(int32_t n_primes, rns_plan_t *out) {
+    return rns_plan_n_moduli(n_primes, RNS_MODULI_PRIMES, out);
 }
 
 int rns_workspace_layout(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,

@@ -64,7 +64,7 @@ constexpr int kMaxQChunks = garner_chunk_offset(kGarnerSlots);   // 812
 struct GarnerConsts {
     int32_t n;
     uint8_t plane[kGarnerSlots];   // Garner slot -> residue plane index
-    uint8_t q[kGarnerSlots];
+    uint16_t q[kGarnerSlots];      // moduli up to 256
     double inv[kGarnerSlots];
     int8_t tri[kTriEntries];
     uint16_t q16[kMaxQChunks];

@@ -105,6 +105,36 @@ int rns_plan(int64_t K, int32_t a_bits, int32_t b_bits, rns_plan_t *out);
 int rns_plan_n(int32_t n_primes, rns_plan_t *out);
 
 /*
+ * Moduli of a plan.  RNS_MODULI_PRIMES: the 54 primes below 256 (P up to
+ * 2^334.9).  RNS_MODULI_PRIME_POWERS: for each of those primes its largest
+ * power not above 256 -- 256, 251, 243, 241, ..., 169, ..., 125, 121, ...,
+ * 49, ..., 17 -- whose product is lcm(1..256), about 2^362.8: the INT8 CRT
+ * capacity of the Ozaki Scheme II paper (§1.2, §4.2.2).  The moduli are
+ * pairwise coprime; residues mod 256 are the int8 values themselves, in
+ * [-128, 127], so K <= 2^17 - 1 keeps the int32 accumulation exact
+ * (2^17 * 128^2 would reach 2^31).  The other moduli keep their balanced
+ * residues (|r| <= 125).  The field `primes` of a plan lists its moduli.
+ */
+#define RNS_MODULI_PRIMES 0
+#define RNS_MODULI_PRIME_POWERS 1
+
+/*
+ * rns_plan_moduli -- rns_plan over either modulus set: the fewest moduli,
+ * largest first, whose product exceeds 2*K*2^(a_bits+b_bits).  K in 0..2^17
+ * (0..2^17-1 for prime powers).  rns_plan(K, a, b, out) is
+ * rns_plan_moduli(K, a, b, RNS_MODULI_PRIMES, out).  Returns as rns_plan,
+ * and RNS_E_ARG for an unknown kind.
+ */
+int rns_plan_moduli(int64_t K, int32_t a_bits, int32_t b_bits, int32_t kind, rns_plan_t *out);
+
+/*
+ * rns_plan_n_moduli -- rns_plan_n over either modulus set (k_max = 2^17, or
+ * 2^17 - 1 for prime powers).  With all 54 prime powers the representative
+ * range is (-P/2, P/2] for P = lcm(1..256).  Returns RNS_OK or RNS_E_ARG.
+ */
+int rns_plan_n_moduli(int32_t n, int32_t kind, rns_plan_t *out);
+
+/*
  * rns_workspace_size -- device workspace bytes needed by rns_gemm
  * (batched_residue == 0) or rns_gemm_batched_residue (batched_residue != 0)
  * for this plan and shape.  The workspace holds the residue planes of both

@@ -269,3 +269,29 @@ def test_workspace_size_with_empty_contraction(lib):
     for M, N in ((2, 5), (300, 300), (1, 40)):
         assert rg.workspace_size(rg.plan(0, 0, 0), M, N, 0) >= 0
         assert rg.workspace_size(rg.plan_n(54), M, N, 0, True) >= 0
+
+
+@pytest.mark.parametrize("K,a,b", [(64, 20, 20), (4096, 100, 100), (4096, 170, 170), (131071, 170, 170),
+                                   (3, 180, 178), (0, 5, 5)])
+def test_prime_power_plan_agrees_with_oracle(lib, K, a, b):
+    p = rg.plan(K, a, b, prime_powers=True)
+    ms = O.moduli_set_for_bound(max(K, 1), a, b, prime_powers=True)
+    assert list(p.primes) == ms
+    assert p.out_limbs_min == O.limbs_to_hold(O.prod(ms))
+    assert p.k_max == max(K, 1)
+
+
+def test_prime_power_plan_limits(lib):
+    with pytest.raises(rg.RnsError) as e:
+        rg.plan(2 ** 17, 1, 1, prime_powers=True)       # 256 needs K <= 2^17 - 1
+    assert e.value.code == -2
+    with pytest.raises(rg.RnsError) as e:
+        rg.plan(8, 181, 181, prime_powers=True)
+    assert e.value.code == -3
+    p = rg.plan_n(54, prime_powers=True)
+    assert p.k_max == 2 ** 17 - 1 and p.out_limbs_min == 6 and abs(p.log2_P - 362.828) < 1e-3
+    # a plan whose 256 claims K up to 2^17 is refused by every entry point
+    bad = rg.Plan(p.n_primes, p.out_limbs_min, -1, -1, 2 ** 17, p.log2_P, p.primes)
+    with pytest.raises(rg.RnsError) as e:
+        rg.workspace_size(bad, 4, 4, 4)
+    assert e.value.code == -1

@@ -269,16 +269,16 @@ def test_batched_residue_small(M, N, K, n, seed):
     assert np.array_equal(O.decode_array(X), ref)
 
 
-def _planted(n, values):
+def _planted(n, values, prime_powers=False):
     """Batched call with K = 1 and B = 1: entry m of the output is the CRT
     value of the residues planted in A_res[:, m, 0], i.e. values[m]."""
-    p = rg.plan_n(n)
+    p = rg.plan_n(n, prime_powers=prime_powers)
     ps = list(p.primes)
     M = len(values)
     A_res = np.zeros((n, M, 1), dtype=np.int8)
     for j, q in enumerate(ps):
         for m, X in enumerate(values):
-            A_res[j, m, 0] = O.balanced(X, q)
+            A_res[j, m, 0] = (O.balanced(X, q) + 128) % 256 - 128   # as an int8 byte (128 -> -128 mod 256)
     B = np.ones((1, 1, 1), dtype=np.int64)
     return p, ps, dev(A_res), dev(B)
 
@@ -317,6 +317,70 @@ def test_reconstruct_planted_values(n):
         rg.reconstruct(p, M, 1, 1, ws, out, batched=True, method=method)
         got = O.decode_array(out.cpu().numpy())[:, 0]
         assert [int(v) for v in got] == vals, method
+
+
+@pytest.mark.parametrize("n", [1, 2, 17, 31, 32, 33, 53, 54])
+def test_reconstruct_planted_values_prime_powers(n):
+    """The same with the prime-power moduli (256 first; P even): both ends
+    of (-P/2, P/2] through the CRT kernel and Garner."""
+    rng = np.random.default_rng(2000 + n)
+    ps = rg.plan_n(n, prime_powers=True).primes
+    vals = _boundary_values(list(ps), rng)
+    print(f"planted prime powers n={n} entries={len(vals)}", flush=True)
+    p, ps, A_res, B = _planted(n, vals, prime_powers=True)
+    M = len(vals)
+    for method in ("crt", "garner"):
+        ws = rg.new_workspace(p, M, 1, 1, True, B.device)
+        rg.split(p, None, B, ws, M=M)
+        rg.residue_products(p, M, 1, 1, ws, A_res=A_res)
+        out = torch.full((M, 1, p.out_limbs_min + 1), 7, dtype=torch.int64, device=B.device)
+        rg.reconstruct(p, M, 1, 1, ws, out, batched=True, method=method)
+        got = O.decode_array(out.cpu().numpy())[:, 0]
+        assert [int(v) for v in got] == vals, method
+
+
+@pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", [(40, 33, 512, 3, 3, 170, 170, 81),
+                                                    (300, 270, 200, 3, 3, 172, 168, 82),
+                                                    (64, 64, 64, 2, 2, 100, 100, 83)])
+def test_prime_power_products_beyond_the_primes(M, N, K, la, lb, ab, bb, seed):
+    """Bounds beyond the 335-bit capacity of the primes, on the prime-power
+    moduli (up to 362.8 bits): exact against the oracle, CRT and Garner."""
+    print(f"prime powers M={M} N={N} K={K} bits={ab},{bb}", flush=True)
+    p = rg.plan(K, ab, bb, prime_powers=True)
+    assert p.primes[0] == 256 and list(p.primes) == O.moduli_set_for_bound(K, ab, bb, prime_powers=True)
+    A, B = W.random_operands(seed, M, N, K, la, lb, ab, bb)
+    ws = rg.new_workspace(p, M, N, K)
+    C = rg.gemm(p, dev(A), dev(B), workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle_c(A, B, p.out_limbs_min)
+    assert np.array_equal(C.cpu().numpy(), ref)
+    assert rg.status(ws) == 0
+    out = torch.zeros_like(C)
+    rg.reconstruct(p, M, N, K, ws, out, method="garner")
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy(), ref)
+    planes = rg.workspace_planes(p, ws, M, N, K)
+    Av, Bv = O.decode_array(A), O.decode_array(B)
+    refA = O.residue_planes(Av, [256])[0]
+    assert np.array_equal(planes["A"].cpu().numpy()[0, :M, :K], refA)
+    refB = O.residue_planes(Bv.T, [256])[0]
+    refY = O.residue_product(refA, refB.T, 256)
+    assert np.array_equal(planes["Y"].cpu().numpy()[0, :M, :N], refY)
+
+
+def test_prime_power_int32_edge():
+    """K = 2^17 - 1 with every residue mod 256 equal to -128: the int32
+    accumulator of that plane reaches 2^31 - 2^14."""
+    K = 2 ** 17 - 1
+    p = rg.plan_n(3, prime_powers=True)
+    assert p.primes[0] == 256 and p.k_max == K
+    M, N = 4, 3
+    A_res = np.full((3, M, K), -128, dtype=np.int8)
+    A_res[1:] = 5
+    r = np.full((K, N), -128, dtype=np.int64)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None])).cpu().numpy()
+    ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
+    assert np.array_equal(O.decode_array(X), ref)
 
 
 @pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", [SMALL[1], SMALL[3], SMALL[7],
