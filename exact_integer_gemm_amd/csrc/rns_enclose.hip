@@ -297,7 +297,11 @@ int rns_enclose_plan(int64_t K, const rns_fp_stats_t *a, const rns_fp_stats_t *b
     ep.b_limbs = limbs_for_bits(ep.b_bits);
     if (ep.a_limbs > RNS_MAX_IN_LIMBS || ep.b_limbs > RNS_MAX_IN_LIMBS || ep.a_bits > 255 || ep.b_bits > 255)
         return RNS_E_CAPACITY;
-    const int rc = rns_plan(K, ep.a_bits, ep.b_bits, &ep.plan);
+    // the primes below 256 first; past their 334.9 bits, the prime-power
+    // moduli (362.8 bits, K <= 2^17 - 1)
+    int rc = rns_plan(K, ep.a_bits, ep.b_bits, &ep.plan);
+    if (rc == RNS_E_CAPACITY && K <= RNS_K_MAX - 1)
+        rc = rns_plan_moduli(K, ep.a_bits, ep.b_bits, RNS_MODULI_PRIME_POWERS, &ep.plan);
     if (rc != RNS_OK) return rc;
     ep.c_limbs = ep.plan.out_limbs_min;
     ep.q = ep.fa + ep.fb;

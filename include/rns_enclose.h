@@ -77,9 +77,11 @@ typedef struct rns_enclose_plan {
 
 /*
  * rns_enclose_plan -- plan A @ B from host copies of both operands' stats.
- * K in 0..2^17, out_format 64 or 32.  Returns RNS_OK, RNS_E_ARG, RNS_E_K,
- * RNS_E_NONFINITE, or RNS_E_CAPACITY when the scaled operands need more than
- * four limbs or their product exceeds the residue range of all 54 primes.
+ * K in 0..2^17, out_format 64 or 32.  The residue plan takes the primes below
+ * 256 when they suffice, else the prime-power moduli (rns_gemm.h; up to 362.8
+ * bits, K <= 2^17 - 1).  Returns RNS_OK, RNS_E_ARG, RNS_E_K, RNS_E_NONFINITE,
+ * or RNS_E_CAPACITY when the scaled operands need more than four limbs or
+ * their product exceeds the range of all 54 prime powers.
  */
 int rns_enclose_plan(int64_t K, const rns_fp_stats_t *a, const rns_fp_stats_t *b,
                      int32_t out_format, rns_enclose_plan_t *out);

@@ -295,3 +295,14 @@ def test_prime_power_plan_limits(lib):
     with pytest.raises(rg.RnsError) as e:
         rg.workspace_size(bad, 4, 4, 4)
     assert e.value.code == -1
+
+
+def test_enclose_plan_falls_back_to_prime_powers(lib):
+    """Spreads whose product needs more than the primes' 334.9 bits take the
+    prime-power moduli (lossless up to 362.8 bits)."""
+    import numpy as np
+    A = np.array([2.0 ** 100, 2.0 ** -70])       # 171-bit integers
+    B = np.array([2.0 ** 90, 2.0 ** -70])        # 161-bit integers
+    ep = rg.enclose_plan(64, _stats_of(A), _stats_of(B), 64)
+    assert ep.c.plan.primes[0] == 256
+    assert ep.c.a_bits + ep.c.b_bits + 7 > 335

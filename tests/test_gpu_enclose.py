@@ -134,6 +134,19 @@ def test_zero_operand_and_empty_contraction():
     assert same_bits(lo, np.zeros((2, 5))) and same_bits(hi, np.zeros((2, 5)))
 
 
+def test_wide_spread_on_prime_power_moduli():
+    """Exponent spreads whose exact product needs more than the primes'
+    334.9 bits run on the prime-power moduli and stay bit-exact."""
+    rng = np.random.default_rng(12)
+    A = rng.standard_normal((9, 64)) * 2.0 ** rng.integers(-64, 64, size=(9, 64))
+    B = rng.standard_normal((64, 7)) * 2.0 ** rng.integers(-54, 54, size=(64, 7))
+    lo, hi, ep = rg.mm_enclose(dev(A), dev(B), return_plan=True)
+    torch.cuda.synchronize()
+    assert ep.c.plan.primes[0] == 256, "this case is meant to need the prime powers"
+    rlo, rhi = E.enclose(A, B)
+    assert same_bits(lo.cpu().numpy(), rlo) and same_bits(hi.cpu().numpy(), rhi)
+
+
 def test_rejected_operands():
     with pytest.raises(rg.RnsError) as e:
         rg.mm_enclose(dev(np.array([[1.0, np.nan]])), dev(np.ones((2, 2))))
