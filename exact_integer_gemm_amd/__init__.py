@@ -113,6 +113,8 @@ def load() -> ctypes.CDLL:
                                                       ctypes.POINTER(SZ)]),
         "rns_mm_enclose": (ctypes.c_int, [ctypes.POINTER(_EnclosePlan), I64, I64, I64, VP, VP, VP, VP, VP,
                                           SZ, VP]),
+        "rns_mm_enclose_nt": (ctypes.c_int, [ctypes.POINTER(_EnclosePlan), I64, I64, I64, VP, VP, VP, VP, VP,
+                                             SZ, VP]),
         "rns_fp64_to_limbs": (ctypes.c_int, [VP, I64, I32, I32, VP, VP]),
         "rns_round_outward": (ctypes.c_int, [VP, I64, I32, I32, I32, VP, VP, VP]),
     }
@@ -379,5 +381,5 @@ def workspace_planes(p: Plan, workspace: torch.Tensor, M: int, N: int, K: int,
     return out
 
 
-from .enclose import (EnclosePlan, digest, enclose_plan, fp64_stats, fp64_to_limbs,  # noqa: E402
-                      mm_enclose, round_outward, width_ulps)
+from .enclose import (EnclosePlan, bmm_enclose, digest, enclose_plan, fp64_stats,  # noqa: E402
+                      fp64_to_limbs, mm_enclose, mm_enclose_nt, round_outward, width_ulps)

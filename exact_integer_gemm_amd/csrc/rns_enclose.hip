@@ -347,8 +347,9 @@ int rns_round_outward(const int64_t *S, int64_t count, int32_t s_limbs, int32_t 
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 
-int rns_mm_enclose(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K, const double *A,
-                   const double *B, void *lo, void *hi, void *ws, size_t ws_bytes, hipStream_t stream) {
+static int mm_enclose(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K, const double *A,
+                      const double *B, int b_rows_n, void *lo, void *hi, void *ws, size_t ws_bytes,
+                      hipStream_t stream) {
     if (!plan_ok(ep) || M < 0 || N < 0 || K < 0) return RNS_E_ARG;
     if (K > ep->plan.k_max && !(K == 0)) return RNS_E_K;
     if (M == 0 || N == 0) return RNS_OK;
@@ -369,10 +370,21 @@ int rns_mm_enclose(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K
     if ((int64_t)ws_bytes < L.total) return RNS_E_WORKSPACE;
     int8_t *base = static_cast<int8_t *>(ws);
     int64_t *Si = reinterpret_cast<int64_t *>(base + L.s_off);
-    if ((rc = gemm_fp64_scaled(&ep->plan, M, N, K, A, ep->a_limbs, B, ep->b_limbs, Fp64Scales{ep->fa, ep->fb}, Si,
-                               ep->c_limbs, base + L.gemm_off, (size_t)L.gemm_bytes, stream)) != RNS_OK)
+    if ((rc = gemm_fp64_scaled(&ep->plan, M, N, K, A, ep->a_limbs, B, ep->b_limbs,
+                               Fp64Scales{ep->fa, ep->fb, b_rows_n}, Si, ep->c_limbs, base + L.gemm_off,
+                               (size_t)L.gemm_bytes, stream)) != RNS_OK)
         return rc;
     return rns_round_outward(Si, M * N, ep->c_limbs, ep->q, ep->out_format, lo, hi, stream);
+}
+
+int rns_mm_enclose(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K, const double *A,
+                   const double *B, void *lo, void *hi, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return mm_enclose(ep, M, N, K, A, B, 0, lo, hi, ws, ws_bytes, stream);
+}
+
+int rns_mm_enclose_nt(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K, const double *A,
+                      const double *Bt, void *lo, void *hi, void *ws, size_t ws_bytes, hipStream_t stream) {
+    return mm_enclose(ep, M, N, K, A, Bt, 1, lo, hi, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -392,7 +392,11 @@ int stage_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
     sb.r_pad = L.pub.n_pad; sb.k_pad = L.pub.k_pad; sb.limbs = b_limbs;
     sb.bits = (plan->b_bits >= 0 && plan->b_bits < 64 * b_limbs - 1) ? plan->b_bits : -1;
     sb.transposed = 1;
-    if (fp) { sb.fp64 = 1; sb.scale = fp->fb; }
+    if (fp) {
+        sb.fp64 = 1;
+        sb.scale = fp->fb;
+        if (fp->b_rows_n) sb.transposed = 0;   // B^T [N][K]: plane rows are its rows
+    }
     return launch_split(batched ? nullptr : &sa, &sb, sc, (uint32_t *)(base + L.pub.status_off),
                         L.status_slots, stream);
 }

@@ -147,6 +147,7 @@ int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts
 // Binary64 operands read by the split as floor(A * 2^fa), floor(B * 2^fb).
 struct Fp64Scales {
     int32_t fa, fb;
+    int32_t b_rows_n;      // 1: B is given as B^T, [N][K] row-major
 };
 // rns_gemm on binary64 operands A [M][K], B [K][N], scaled into a_limbs /
 // b_limbs limbs inside the split (same checks, layout and errors as rns_gemm).

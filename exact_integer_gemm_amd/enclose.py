@@ -53,15 +53,6 @@ class EnclosePlan:
         return bool(self.c.zero)
 
 
-def _need_float(t: torch.Tensor, name: str) -> None:
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
-        raise ValueError(f"{name} must be a tensor on a GPU device")
-    if t.dtype not in (torch.float32, torch.float64):
-        raise TypeError(f"{name} must be float32 or float64, got {t.dtype}")
-    if t.dim() != 2:
-        raise ValueError(f"{name} must be a matrix, got shape {tuple(t.shape)}")
-
-
 def fp64_stats(X: torch.Tensor, out: Optional[torch.Tensor] = None,
                workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """int32 [4] on the device: max leading-bit exponent, min lowest-set-bit
@@ -101,40 +92,92 @@ def workspace_size(ep: EnclosePlan, M: int, N: int, K: int) -> int:
     return out.value
 
 
-def mm_enclose(A: torch.Tensor, B: torch.Tensor, workspace: Optional[torch.Tensor] = None,
-               return_plan: bool = False):
-    """(lo, hi) with lo <= A @ B <= hi exactly (float32 pair if both operands
-    are float32, else float64)."""
-    _need_float(A, "A")
-    _need_float(B, "B")
-    M, K = A.shape
-    K2, N = B.shape
-    if K2 != K:
-        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
-    if B.device != A.device:
-        raise ValueError("A and B on different devices")
-    fmt = 32 if (A.dtype == torch.float32 and B.dtype == torch.float32) else 64
-    A64 = A.to(torch.float64).contiguous()      # binary32 -> binary64 is exact
-    B64 = B.to(torch.float64).contiguous()
-    dev = A.device
+def _plan_for(A64: torch.Tensor, B64: torch.Tensor, K: int, fmt: int) -> EnclosePlan:
+    """Both operands' reductions, one host synchronisation, the plan."""
+    dev = A64.device
     stats = torch.empty(8, dtype=torch.int32, device=dev)
     sws = torch.empty(FP_STATS_WS_BYTES, dtype=torch.uint8, device=dev)
     fp64_stats(A64, stats[0:4], sws)
     fp64_stats(B64, stats[4:8], sws)
     host = stats.cpu().tolist()                 # the one synchronisation
-    ep = enclose_plan(K, host[0:4], host[4:8], fmt)
-    dt = torch.float32 if fmt == 32 else torch.float64
-    lo = torch.empty((M, N), dtype=dt, device=dev)
-    hi = torch.empty((M, N), dtype=dt, device=dev)
+    return enclose_plan(K, host[0:4], host[4:8], fmt)
+
+
+def _operands(A: torch.Tensor, B: torch.Tensor, ndim: int = 2):
+    for t, name in ((A, "A"), (B, "B")):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+            raise ValueError(f"{name} must be a tensor on a GPU device")
+        if t.dtype not in (torch.float32, torch.float64):
+            raise TypeError(f"{name} must be float32 or float64, got {t.dtype}")
+        if t.dim() != ndim:
+            raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if B.device != A.device:
+        raise ValueError("A and B on different devices")
+    fmt = 32 if (A.dtype == torch.float32 and B.dtype == torch.float32) else 64
+    # binary32 -> binary64 is exact
+    return A.to(torch.float64).contiguous(), B.to(torch.float64).contiguous(), fmt
+
+
+def _run(fn_name: str, ep: EnclosePlan, M: int, N: int, K: int, A64, B64, lo, hi, workspace, stream) -> None:
+    with torch.cuda.device(A64.device):
+        rc = getattr(load(), fn_name)(ctypes.byref(ep.c), M, N, K, A64.data_ptr(), B64.data_ptr(),
+                                      lo.data_ptr(), hi.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                      stream)
+    _check(rc, fn_name)
+
+
+def _outputs(ep: EnclosePlan, shape, dev, M, N, K, workspace):
+    dt = torch.float32 if ep.c.out_format == 32 else torch.float64
+    lo = torch.empty(shape, dtype=dt, device=dev)
+    hi = torch.empty(shape, dtype=dt, device=dev)
     need = workspace_size(ep, M, N, K)
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    with torch.cuda.device(dev):
-        rc = load().rns_mm_enclose(ctypes.byref(ep.c), M, N, K, A64.data_ptr(), B64.data_ptr(),
-                                   lo.data_ptr(), hi.data_ptr(), workspace.data_ptr(), workspace.numel(),
-                                   _stream_ptr(A))
-    _check(rc, "rns_mm_enclose")
+    return lo, hi, workspace
+
+
+def mm_enclose(A: torch.Tensor, B: torch.Tensor, workspace: Optional[torch.Tensor] = None,
+               return_plan: bool = False):
+    """(lo, hi) with lo <= A @ B <= hi exactly (float32 pair if both operands
+    are float32, else float64)."""
+    A64, B64, fmt = _operands(A, B)
+    M, K = A64.shape
+    K2, N = B64.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    ep = _plan_for(A64, B64, K, fmt)
+    lo, hi, workspace = _outputs(ep, (M, N), A64.device, M, N, K, workspace)
+    _run("rns_mm_enclose", ep, M, N, K, A64, B64, lo, hi, workspace, _stream_ptr(A64))
     return (lo, hi, ep) if return_plan else (lo, hi)
+
+
+def mm_enclose_nt(A: torch.Tensor, Bt: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """(lo, hi) enclosing A @ Bt.T, Bt given as [N, K] (no transposed copy)."""
+    A64, B64, fmt = _operands(A, Bt)
+    M, K = A64.shape
+    N, K2 = B64.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    ep = _plan_for(A64, B64, K, fmt)
+    lo, hi, workspace = _outputs(ep, (M, N), A64.device, M, N, K, workspace)
+    _run("rns_mm_enclose_nt", ep, M, N, K, A64, B64, lo, hi, workspace, _stream_ptr(A64))
+    return lo, hi
+
+
+def bmm_enclose(A: torch.Tensor, B: torch.Tensor, workspace: Optional[torch.Tensor] = None):
+    """[b, M, K] @ [b, K, N]: one plan for the whole batch (one host
+    synchronisation), then one enclosure product per matrix on the stream."""
+    A64, B64, fmt = _operands(A, B, 3)
+    nb, M, K = A64.shape
+    nb2, K2, N = B64.shape
+    if nb2 != nb or K2 != K:
+        raise ValueError(f"batch shapes differ: {tuple(A.shape)} and {tuple(B.shape)}")
+    ep = _plan_for(A64, B64, K, fmt)
+    lo, hi, workspace = _outputs(ep, (nb, M, N), A64.device, M, N, K, workspace)
+    s = _stream_ptr(A64)
+    for i in range(nb):
+        _run("rns_mm_enclose", ep, M, N, K, A64[i], B64[i], lo[i], hi[i], workspace, s)
+    return lo, hi
 
 
 def fp64_to_limbs(X: torch.Tensor, F: int, limbs: int) -> torch.Tensor:
@@ -188,5 +231,5 @@ def digest(lo: torch.Tensor, hi: torch.Tensor) -> str:
     return h.hexdigest()
 
 
-__all__ = ["EnclosePlan", "RnsError", "digest", "enclose_plan", "fp64_stats", "fp64_to_limbs",
-           "mm_enclose", "round_outward", "width_ulps"]
+__all__ = ["EnclosePlan", "RnsError", "bmm_enclose", "digest", "enclose_plan", "fp64_stats",
+           "fp64_to_limbs", "mm_enclose", "mm_enclose_nt", "round_outward", "width_ulps"]

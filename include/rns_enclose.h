@@ -109,6 +109,15 @@ int rns_mm_enclose(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K
                    void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * rns_mm_enclose_nt -- the same for A @ Bt^T with Bt given as double [N][K]
+ * row-major (no transposed copy is made; enclosure-gemm, "Usage").  Stats
+ * and plan as for rns_mm_enclose, with Bt's stats standing for B's.
+ */
+int rns_mm_enclose_nt(const rns_enclose_plan_t *ep, int64_t M, int64_t N, int64_t K,
+                      const double *A, const double *Bt, void *lo, void *hi,
+                      void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * rns_fp64_to_limbs -- floor(X * 2^F) for `count` doubles as `limbs` int64
  * limbs each (device [count][limbs], two's complement).  The caller
  * guarantees |floor(X * 2^F)| < 2^(64 limbs - 1).  limbs in 1..4.

@@ -147,6 +147,31 @@ def test_wide_spread_on_prime_power_moduli():
     assert same_bits(lo.cpu().numpy(), rlo) and same_bits(hi.cpu().numpy(), rhi)
 
 
+def test_nt_variant():
+    """A @ Bt.T with Bt given as [N, K] (enclosure-gemm, "Usage")."""
+    rng = np.random.default_rng(13)
+    A = rng.standard_normal((13, 70))
+    Bt = rng.standard_normal((21, 70)) * 2.0 ** 20
+    lo, hi = rg.mm_enclose_nt(dev(A), dev(Bt))
+    torch.cuda.synchronize()
+    rlo, rhi = E.enclose(A, Bt.T.copy())
+    assert same_bits(lo.cpu().numpy(), rlo) and same_bits(hi.cpu().numpy(), rhi)
+
+
+def test_batched_shares_one_plan():
+    """Five 20x256x12 products under one plan (enclosure-gemm, "Measured":
+    the batch pays one plan and one synchronisation)."""
+    rng = np.random.default_rng(14)
+    A = rng.standard_normal((5, 20, 256))
+    B = rng.standard_normal((5, 256, 12))
+    A[3] *= 2.0 ** -30
+    lo, hi = rg.bmm_enclose(dev(A), dev(B))
+    torch.cuda.synchronize()
+    for i in range(5):
+        rlo, rhi = E.enclose(A[i], B[i])
+        assert same_bits(lo[i].cpu().numpy(), rlo) and same_bits(hi[i].cpu().numpy(), rhi), i
+
+
 def test_rejected_operands():
     with pytest.raises(rg.RnsError) as e:
         rg.mm_enclose(dev(np.array([[1.0, np.nan]])), dev(np.ones((2, 2))))
