@@ -116,6 +116,13 @@ def load() -> ctypes.CDLL:
         "rns_mm_enclose_nt": (ctypes.c_int, [ctypes.POINTER(_EnclosePlan), I64, I64, I64, VP, VP, VP, VP, VP,
                                              SZ, VP]),
         "rns_fp64_to_limbs": (ctypes.c_int, [VP, I64, I32, I32, VP, VP]),
+        "rns_inverse_workspace_size": (ctypes.c_int, [I32, I64, ctypes.POINTER(SZ)]),
+        "rns_batched_inverse": (ctypes.c_int, [ctypes.POINTER(I32), I32, I64, VP, VP, VP, SZ, VP]),
+        "rns_inverse_planes": (ctypes.c_int, [ctypes.POINTER(I32), I32, I64, ctypes.POINTER(I32), I32, VP, VP,
+                                              SZ, VP]),
+        "rns_plan_from_moduli": (ctypes.c_int, [ctypes.POINTER(I32), I32, I64, P]),
+        "rns_lift_workspace_size": (ctypes.c_int, [P, I64, I64, ctypes.POINTER(SZ)]),
+        "rns_dixon_lift": (ctypes.c_int, [P, I64, I64, VP, VP, VP, I32, VP, I32, VP, SZ, VP]),
         "rns_round_outward": (ctypes.c_int, [VP, I64, I32, I32, I32, VP, VP, VP]),
     }
     for name, (res, args) in sig.items():
@@ -383,3 +390,5 @@ def workspace_planes(p: Plan, workspace: torch.Tensor, M: int, N: int, K: int,
 
 from .enclose import (EnclosePlan, bmm_enclose, digest, enclose_plan, fp64_stats,  # noqa: E402
                       fp64_to_limbs, mm_enclose, mm_enclose_nt, round_outward, width_ulps)
+from .exact_solve import (batched_inverse, dixon_lift, inverse_planes, plan_from_moduli,  # noqa: E402
+                    solve)

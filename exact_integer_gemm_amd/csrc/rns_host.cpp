@@ -488,6 +488,27 @@ int run(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
 
 }  // namespace
 
+int plan_from_moduli(const int32_t *moduli, int n, int64_t k_max, rns_plan_t *out) {
+    rns_plan_t pl{};
+    Big P(1);
+    double l2 = 0;
+    for (int i = 0; i < n; i++) {
+        if (moduli[i] < 2 || moduli[i] > 256) return RNS_E_ARG;
+        pl.primes[i] = moduli[i];
+        P.mul_small((uint32_t)moduli[i]);
+        l2 += std::log2((double)moduli[i]);
+    }
+    pl.n_primes = n;
+    pl.log2_P = l2;
+    pl.out_limbs_min = (P.bit_length() + 63) / 64;
+    pl.a_bits = -1;
+    pl.b_bits = -1;
+    pl.k_max = k_max;
+    if (!plan_ok(&pl)) return RNS_E_ARG;
+    *out = pl;
+    return RNS_OK;
+}
+
 int gemm_fp64_scaled(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
                      const double *A, int32_t a_limbs, const double *B, int32_t b_limbs,
                      const Fp64Scales &scales, int64_t *C, int32_t c_limbs,

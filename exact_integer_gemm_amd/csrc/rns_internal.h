@@ -144,6 +144,9 @@ struct SplitOperand {
 int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts &c,
                  uint32_t *status, int64_t status_slots, hipStream_t s);
 
+// A plan over explicit moduli (validated like any plan), no operand bound.
+int plan_from_moduli(const int32_t *moduli, int n, int64_t k_max, rns_plan_t *out);
+
 // Binary64 operands read by the split as floor(A * 2^fa), floor(B * 2^fb).
 struct Fp64Scales {
     int32_t fa, fb;

@@ -1,0 +1,223 @@
+"""Exact rational solve A x = b by Dixon p-adic lifting (C ABI: ``include/rns_solve.h``).
+
+``X = solve(A, b)`` returns the exact solution as lists of ``fractions.Fraction``
+(None if A is singular), following exact-solve, "Method": the batched modular
+inverse (Gauss-Jordan mod every odd prime below 256 at once) and the lift (one
+batched INT8 product per prime per step, the wide digit by the CRT, the
+residual in one limb) run in the library's HIP kernels; the rational
+reconstruction of x mod P^m runs on the host, as the page's CPU stage does.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from fractions import Fraction
+from typing import List, Optional, Sequence
+
+import numpy as np
+import torch
+
+from . import Plan, RnsError, _check, _Plan, _stream_ptr, load
+
+# the odd primes below 256, largest first (P must be odd for the residual update)
+ODD_PRIMES = [q for q in range(255, 2, -1) if q % 2 and all(q % d for d in range(3, int(q ** 0.5) + 1, 2))]
+
+
+def _i32_array(vals: Sequence[int]):
+    arr = (ctypes.c_int32 * len(vals))(*[int(v) for v in vals])
+    return arr
+
+
+def _need_int64(t: torch.Tensor, ndim: int, name: str) -> None:
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dtype != torch.int64:
+        raise ValueError(f"{name} must be an int64 tensor on a GPU device")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+def plan_from_moduli(moduli: Sequence[int], k_max: int) -> Plan:
+    c = _Plan()
+    _check(load().rns_plan_from_moduli(_i32_array(moduli), len(moduli), k_max, ctypes.byref(c)),
+           "rns_plan_from_moduli")
+    return Plan._from_c(c)
+
+
+def batched_inverse(A: torch.Tensor, primes: Sequence[int] = ODD_PRIMES):
+    """Gauss-Jordan inverses of A mod every prime.  Returns (singular flags
+    (int32 [E] on the device), workspace holding the inverses)."""
+    _need_int64(A, 2, "A")
+    n = A.shape[0]
+    if A.shape[1] != n:
+        raise ValueError("A must be square")
+    sz = ctypes.c_size_t()
+    _check(load().rns_inverse_workspace_size(len(primes), n, ctypes.byref(sz)), "rns_inverse_workspace_size")
+    ws = torch.empty(sz.value, dtype=torch.uint8, device=A.device)
+    singular = torch.empty(len(primes), dtype=torch.int32, device=A.device)
+    with torch.cuda.device(A.device):
+        rc = load().rns_batched_inverse(_i32_array(primes), len(primes), n, A.data_ptr(), singular.data_ptr(),
+                                        ws.data_ptr(), ws.numel(), _stream_ptr(A))
+    _check(rc, "rns_batched_inverse")
+    return singular, ws
+
+
+def inverse_planes(ws: torch.Tensor, n: int, select: Sequence[int], primes: Sequence[int] = ODD_PRIMES):
+    """Balanced int8 planes [len(select), n, n] of the inverses mod primes[select]."""
+    planes = torch.empty((len(select), n, n), dtype=torch.int8, device=ws.device)
+    with torch.cuda.device(ws.device):
+        rc = load().rns_inverse_planes(_i32_array(primes), len(primes), n, _i32_array(select), len(select),
+                                       planes.data_ptr(), ws.data_ptr(), ws.numel(),
+                                       torch.cuda.current_stream(ws.device).cuda_stream)
+    _check(rc, "rns_inverse_planes")
+    return planes
+
+
+def dixon_lift(p: Plan, A: torch.Tensor, b: torch.Tensor, planes: torch.Tensor, steps: int) -> torch.Tensor:
+    """Digits int64 [steps, n, c, out_limbs_min]: x_i = B r_i mod P, balanced."""
+    _need_int64(A, 2, "A")
+    _need_int64(b, 2, "b")
+    n, c = b.shape
+    c_plan = p._c()
+    sz = ctypes.c_size_t()
+    _check(load().rns_lift_workspace_size(ctypes.byref(c_plan), n, c, ctypes.byref(sz)), "rns_lift_workspace_size")
+    ws = torch.empty(sz.value, dtype=torch.uint8, device=A.device)
+    dl = p.out_limbs_min
+    digits = torch.empty((steps, n, c, dl), dtype=torch.int64, device=A.device)
+    with torch.cuda.device(A.device):
+        rc = load().rns_dixon_lift(ctypes.byref(c_plan), n, c, planes.data_ptr(), A.data_ptr(), b.data_ptr(), steps,
+                                   digits.data_ptr(), dl, ws.data_ptr(), ws.numel(), _stream_ptr(A))
+    _check(rc, "rns_dixon_lift")
+    return digits
+
+
+# ---- host stage: bounds and rational reconstruction --------------------------------
+def _ceil_sqrt(v: int) -> int:
+    r = math.isqrt(v)
+    return r if r * r == v else r + 1
+
+
+def _bounds(A: np.ndarray, b: np.ndarray):
+    """Hadamard: |det A| <= prod of row norms; a Cramer numerator replaces a
+    column by one of b, so each of its rows is bounded by sqrt(|a_i|^2 + b_ik^2)."""
+    rows2 = [sum(int(v) * int(v) for v in row) for row in A.tolist()]
+    D = 1
+    for r2 in rows2:
+        D *= _ceil_sqrt(r2)
+    N = 1
+    for k in range(b.shape[1]):
+        Nk = 1
+        for i, r2 in enumerate(rows2):
+            Nk *= _ceil_sqrt(r2 + int(b[i, k]) ** 2)
+        N = max(N, Nk)
+    return N, max(D, 1)
+
+
+def _limbs_to_int(limbs: np.ndarray) -> List[int]:
+    """int64 [..., L] two's-complement limbs -> Python ints (flattened)."""
+    L = limbs.shape[-1]
+    flat = limbs.reshape(-1, L)
+    u = flat.astype(np.uint64)
+    out = []
+    for row in u.tolist():
+        v = 0
+        for l in range(L - 1, -1, -1):
+            v = (v << 64) | int(row[l])
+        if row[L - 1] >> 63:
+            v -= 1 << (64 * L)
+        out.append(v)
+    return out
+
+
+def _ratrec(u: int, M: int, Nb: int, Db: int) -> Optional[Fraction]:
+    r0, r1, t0, t1 = M, u % M, 0, 1
+    while r1 > Nb:
+        qt = r0 // r1
+        r0, r1 = r1, r0 - qt * r1
+        t0, t1 = t1, t0 - qt * t1
+    if t1 == 0 or abs(t1) > Db or (r1 - t1 * u) % M:
+        return None
+    return Fraction(r1, t1)
+
+
+def lift_steps_for(P: int, Nb: int, Db: int) -> int:
+    """The least m with P^m > 2 Nb Db (Db + 1): enough for one rational
+    reconstruction per denominator and a rigorous one-multiply test for every
+    other component."""
+    target = 2 * Nb * Db * (Db + 1)
+    m, Pm = 1, P
+    while Pm <= target:
+        m += 1
+        Pm *= P
+    return m
+
+
+def reconstruct(per_step: Sequence[Sequence[int]], P: int, m: int, Nb: int, Db: int):
+    """(numerators, common denominator) from the lift digits per_step[s][idx].
+
+    x = sum_s digits[s] P^s mod P^m per component.  Common denominator D:
+    w = D u mod P^m (balanced) is the numerator over D when |w| <= D Nb --
+    rigorous, since a wrong w would give |w e - D a| < P^m for the true a/e,
+    so e | D.  Otherwise the component is reconstructed alone (unique for
+    P^m > 2 Nb Db) and D grows."""
+    Pm = P ** m
+    count = len(per_step[0])
+    D = 1
+    nums: List[int] = []
+    half = Pm // 2
+    for idx in range(count):
+        v = 0
+        for s in range(m - 1, -1, -1):
+            v = v * P + per_step[s][idx]
+        u = v % Pm
+        w = D * u % Pm
+        if w > half:
+            w -= Pm
+        if abs(w) > D * Nb:
+            f = _ratrec(u, Pm, Nb, Db)
+            if f is None:
+                raise RnsError(-3, "rational reconstruction failed")
+            g = f.denominator // math.gcd(D, f.denominator)
+            nums = [x * g for x in nums]
+            D *= g
+            w = D * u % Pm
+            if w > half:
+                w -= Pm
+        nums.append(w)
+    return nums, D
+
+
+def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
+    """Exact x with A x = b as [n][c] lists of Fraction; None if A is singular."""
+    _need_int64(A, 2, "A")
+    if b.dim() == 1:
+        b = b.reshape(-1, 1)
+    _need_int64(b.contiguous(), 2, "b")
+    b = b.contiguous()
+    n = A.shape[0]
+    if A.shape != (n, n) or b.shape[0] != n:
+        raise ValueError("A must be [n, n] and b [n, c]")
+    An = A.cpu().numpy()
+    bn = b.cpu().numpy()
+    amax = int(np.abs(An.astype(object)).max()) if n else 0
+    if n * amax >= 1 << 63:
+        raise ValueError("n * max|A| must stay below 2^63 (the residual is one signed limb)")
+    singular, ws = batched_inverse(A)
+    sing = singular.cpu().tolist()                     # synchronises
+    sel = [i for i, s in enumerate(sing) if not s]
+    if not sel:
+        return None
+    moduli = [ODD_PRIMES[i] for i in sel]
+    p = plan_from_moduli(moduli, max(n, 1))
+    planes = inverse_planes(ws, n, sel)
+    del ws
+    Nb, Db = _bounds(An, bn)
+    P = math.prod(moduli)
+    m = lift_steps_for(P, Nb, Db)
+    digits = dixon_lift(p, A, b, planes, m).cpu().numpy()  # synchronises
+    c = bn.shape[1]
+    per_step = [_limbs_to_int(digits[s]) for s in range(m)]
+    nums, D = reconstruct(per_step, P, m, Nb, Db)
+    out = [[Fraction(nums[i * c + k], D) for k in range(c)] for i in range(n)]
+    if return_info:
+        return out, {"primes": moduli, "steps": m, "log2_P": math.log2(P), "denominator_bits": D.bit_length(),
+                     "numerators": nums, "denominator": D}
+    return out

@@ -1,0 +1,97 @@
+/*
+ * rns_solve.h -- the GPU part of the exact rational solve A x = b by Dixon
+ * p-adic lifting on the residue engine (exact-solve).
+ *
+ * The method (exact-solve, "Method"): with B = A^-1 mod P for a squarefree
+ * product P of primes below 256, r_0 = b, x_i = B r_i mod P and
+ * r_{i+1} = (r_i - A x_i) / P, the digits x_i give x mod P^m, from which the
+ * rational solution is reconstructed once P^m exceeds twice the Hadamard
+ * bound on numerator and denominator.  Two parts run here:
+ *   - the batched modular inverse: A^-1 mod q_j for every prime by
+ *     Gauss-Jordan elimination of the augmented matrix [A | I], one launch
+ *     per elimination step spanning all primes, Barrett reduction in place of
+ *     a hardware modulo;
+ *   - the lift: per step, x_i = B r_i mod P as one batched INT8 product per
+ *     prime with the wide digit assembled by rns_gemm_batched_residue, and the
+ *     residual update in one limb as (r_i - A x_i) * P^-1 mod 2^64 (P odd).
+ * The rational reconstruction of x mod P^m runs on the host (exact-solve,
+ * "Method": a CPU stage).
+ *
+ * Conventions of rns_gemm.h: device pointers owned by the caller,
+ * asynchronous launches on the caller's stream, 0 on success and a negative
+ * RNS_E_* code on failure with nothing written.  A is int64 [n][n], b and r
+ * int64 [n][c], row-major.  Range (exact-solve, "Requirements and limits"):
+ * n * max|A_ij| < 2^63 keeps the residual in one signed limb; n <= 2^17.
+ */
+#ifndef RNS_SOLVE_H
+#define RNS_SOLVE_H
+
+#include "rns_gemm.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/*
+ * rns_inverse_workspace_size -- device bytes of rns_batched_inverse for
+ * n_primes primes and an n x n matrix: the augmented matrices as bytes
+ * ([n_primes][n][2n], residues in [0, q)) plus per-step pivot rows and
+ * columns.  Returns RNS_OK or RNS_E_ARG.
+ */
+int rns_inverse_workspace_size(int32_t n_primes, int64_t n, size_t *bytes);
+
+/*
+ * rns_batched_inverse -- Gauss-Jordan elimination of [A mod q_j | I] for every
+ * prime q_j = primes[j] (host array of n_primes distinct primes below 256).
+ * A: device int64 [n][n].  singular: device int32 [n_primes], set to 1 where
+ * A is singular mod q_j (that prime's inverse is then unspecified), else 0.
+ * The inverses stay in ws for rns_inverse_planes.  2n + 2 launches.
+ * Returns RNS_OK, RNS_E_ARG, RNS_E_K (n > 2^17), RNS_E_WORKSPACE or RNS_E_HIP.
+ */
+int rns_batched_inverse(const int32_t *primes, int32_t n_primes, int64_t n, const int64_t *A,
+                        int32_t *singular, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rns_inverse_planes -- the balanced int8 residue planes of the inverses left
+ * in ws by rns_batched_inverse (same primes, n, ws): plane t of `planes`
+ * (device int8 [n_sel][n][n]) is A^-1 mod primes[select[t]], select a host
+ * array of n_sel indices.  The planes are in the layout of A_res of
+ * rns_gemm_batched_residue.  Returns RNS_OK, RNS_E_ARG or RNS_E_HIP.
+ */
+int rns_inverse_planes(const int32_t *primes, int32_t n_primes, int64_t n, const int32_t *select,
+                       int32_t n_sel, int8_t *planes, const void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rns_plan_from_moduli -- a plan over the given moduli (host array, any
+ * order, distinct prime powers up to 256), with no operand bound and the
+ * given k_max (1..2^17, 2^17 - 1 with 256).  For the lift: the primes for
+ * which A is invertible.  Returns RNS_OK or RNS_E_ARG.
+ */
+int rns_plan_from_moduli(const int32_t *moduli, int32_t n, int64_t k_max, rns_plan_t *out);
+
+/*
+ * rns_lift_workspace_size -- device bytes of rns_dixon_lift: the residual and
+ * the batched-residue product's workspace.  Returns RNS_OK, RNS_E_ARG or
+ * RNS_E_K.
+ */
+int rns_lift_workspace_size(const rns_plan_t *plan, int64_t n, int64_t c, size_t *bytes);
+
+/*
+ * rns_dixon_lift -- `steps` Dixon steps from r_0 = b.
+ * plan: odd primes only (P odd), k_max >= n.  Binv: device int8
+ * [plan->n_primes][n][n], the balanced residues of A^-1 mod each prime in
+ * plan order (rns_inverse_planes).  digits: device int64
+ * [steps][n][c][d_limbs], d_limbs >= plan->out_limbs_min: digit i is the
+ * balanced representative of B r_i mod P.  Returns RNS_OK, RNS_E_ARG (also
+ * for an even modulus), RNS_E_K, RNS_E_OUT_LIMBS, RNS_E_WORKSPACE or
+ * RNS_E_HIP.
+ */
+int rns_dixon_lift(const rns_plan_t *plan, int64_t n, int64_t c, const int8_t *Binv, const int64_t *A,
+                   const int64_t *b, int32_t steps, int64_t *digits, int32_t d_limbs,
+                   void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RNS_SOLVE_H */

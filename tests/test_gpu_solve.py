@@ -1,0 +1,151 @@
+"""Parity of the Dixon-lift path (batched modular inverse, lift steps, exact
+solve) with the oracle (oracle/dixon.py) (GPU only).
+
+Cases follow exact-solve, "Correctness": bitwise against an exact Fraction
+Gaussian elimination on small systems, a planted integer solution, a scaled
+Hilbert system with dense denominators, the order-30 Pascal system, and the
+integer identity A @ N == d * b at a larger size.
+"""
+import math
+import random
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import exact_integer_gemm_amd as rg
+from exact_integer_gemm_amd.exact_solve import ODD_PRIMES
+from oracle import dixon as D
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    rg.load()
+    yield
+
+
+def dev(x):
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x, dtype=np.int64))).cuda()
+
+
+def _system(seed, n, c, amax, bmax):
+    rng = random.Random(seed)
+    A = [[rng.randint(-amax, amax) for _ in range(n)] for _ in range(n)]
+    b = [[rng.randint(-bmax, bmax) for _ in range(c)] for _ in range(n)]
+    return A, b
+
+
+def test_batched_inverse_matches_oracle():
+    """Inverses mod all 53 odd primes, with A singular mod 3 and mod 7."""
+    n = 37
+    A, _ = _system(1, n, 1, 1000, 1)
+    A[0] = [21 * v for v in A[0]]          # det A becomes a multiple of 3 and 7
+    print(f"batched inverse n={n}", flush=True)
+    singular, ws = rg.batched_inverse(dev(A))
+    sing = singular.cpu().tolist()
+    for e, q in enumerate(ODD_PRIMES):
+        assert bool(sing[e]) == (D.inverse_mod(A, q) is None), q
+    assert sing[ODD_PRIMES.index(3)] and sing[ODD_PRIMES.index(7)]
+    sel = [i for i, s in enumerate(sing) if not s]
+    planes = rg.inverse_planes(ws, n, sel).cpu().numpy()
+    for t in (0, 1, 2, len(sel) // 2, len(sel) - 1):
+        q = ODD_PRIMES[sel[t]]
+        ref = D.inverse_mod(A, q)
+        ref_bal = [[v - q if v > q // 2 else v for v in row] for row in ref]
+        assert np.array_equal(planes[t], np.array(ref_bal, dtype=np.int8)), q
+
+
+def test_lift_digits_match_oracle():
+    n, c = 12, 3
+    A, b = _system(2, n, c, 10 ** 6, 10 ** 6)
+    singular, ws = rg.batched_inverse(dev(A))
+    sel = [i for i, s in enumerate(singular.cpu().tolist()) if not s]
+    moduli = [ODD_PRIMES[i] for i in sel]
+    p = rg.plan_from_moduli(moduli, n)
+    planes = rg.inverse_planes(ws, n, sel)
+    digits = rg.dixon_lift(p, dev(A), dev(b), planes, 4).cpu().numpy()
+    from oracle import oracle as O
+    ref = D.dixon_digits(A, b, moduli, 4)
+    for s in range(4):
+        got = O.decode_array(digits[s])
+        assert [[int(v) for v in row] for row in got] == ref[s], s
+
+
+@pytest.mark.parametrize("seed,n,c", [(3, 5, 1), (4, 16, 3), (5, 40, 2), (6, 1, 1)])
+def test_solve_matches_fraction_elimination(seed, n, c):
+    print(f"solve n={n} c={c}", flush=True)
+    A, b = _system(seed, n, c, 1000, 1000)
+    X = rg.solve(dev(A), dev(b))
+    assert X == D.solve_fraction(A, b)
+
+
+def test_planted_integer_solution():
+    n = 128
+    rng = np.random.default_rng(7)
+    A = rng.integers(-2 ** 23, 2 ** 23, size=(n, n))
+    x = rng.integers(-10 ** 6, 10 ** 6, size=(n, 1))
+    b = A @ x
+    print(f"planted n={n}", flush=True)
+    X, info = rg.solve(dev(A), dev(b), return_info=True)
+    assert info["denominator"] == 1
+    assert [[int(v) for v in row] for row in X] == x.tolist()
+
+
+def test_scaled_hilbert_dense_denominators():
+    n = 9
+    L = math.lcm(*range(1, 2 * n))
+    A = [[L // (i + j + 1) for j in range(n)] for i in range(n)]
+    b = [[1], [0], [-1], [2], [0], [3], [1], [-2], [5]]
+    X = rg.solve(dev(A), dev(b))
+    assert X == D.solve_fraction(A, b)
+    assert max(v[0].denominator for v in X) > 1
+
+
+def test_pascal_order_30():
+    """The page's example: the order-30 Pascal matrix is unimodular, so the
+    solution is integral; A x == b in integer arithmetic."""
+    n = 30
+    A = [[math.comb(i + j, i) for j in range(n)] for i in range(n)]
+    rng = random.Random(8)
+    b = [[rng.randint(-10 ** 6, 10 ** 6)] for _ in range(n)]
+    X = rg.solve(dev(A), dev(b))
+    assert all(v[0].denominator == 1 for v in X)
+    xs = [int(v[0]) for v in X]
+    assert [sum(A[i][j] * xs[j] for j in range(n)) for i in range(n)] == [r[0] for r in b]
+
+
+def test_singular_system():
+    A, b = _system(9, 10, 1, 100, 100)
+    A[9] = [A[0][j] - 3 * A[4][j] for j in range(10)]
+    assert rg.solve(dev(A), dev(b)) is None
+
+
+def test_identity_at_larger_size():
+    """n = 256, 24-bit entries, two right-hand sides: A @ N == d * b."""
+    n, c = 256, 2
+    rng = np.random.default_rng(10)
+    A = rng.integers(-2 ** 23, 2 ** 23, size=(n, n))
+    b = rng.integers(-2 ** 23, 2 ** 23, size=(n, c))
+    print(f"identity n={n}", flush=True)
+    X, info = rg.solve(dev(A), dev(b), return_info=True)
+    d = info["denominator"]
+    N = np.array(info["numerators"], dtype=object).reshape(n, c)
+    AN = A.astype(object).dot(N)
+    assert np.array_equal(AN, d * b.astype(object))
+    assert d > 1
+
+
+def test_lift_rejects_even_modulus():
+    p = rg.plan_n(3)               # 251, 241, 239: odd, accepted
+    A = dev(np.eye(4, dtype=np.int64))
+    b = dev(np.ones((4, 1), dtype=np.int64))
+    planes = torch.zeros((3, 4, 4), dtype=torch.int8, device="cuda")
+    rg.dixon_lift(p, A, b, planes, 1)
+    p2 = rg.plan_from_moduli([256, 251], 4)
+    with pytest.raises(rg.RnsError) as e:
+        rg.dixon_lift(p2, A, b, torch.zeros((2, 4, 4), dtype=torch.int8, device="cuda"), 1)
+    assert e.value.code == -1
