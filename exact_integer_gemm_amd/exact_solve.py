@@ -204,7 +204,11 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
     sing = singular.cpu().tolist()                     # synchronises
     sel = [i for i, s in enumerate(sing) if not s]
     if not sel:
-        return None
+        # det A vanishes mod every odd prime below 256, hence mod their product; below that product
+        # (Hadamard) it is zero, so A is singular over the rationals.
+        if _bounds(An, bn)[1] < math.prod(ODD_PRIMES):
+            return None
+        raise RnsError(-3, "A is singular modulo every odd prime below 256, but det A may be nonzero")
     moduli = [ODD_PRIMES[i] for i in sel]
     p = plan_from_moduli(moduli, max(n, 1))
     planes = inverse_planes(ws, n, sel)

@@ -149,3 +149,23 @@ def test_lift_rejects_even_modulus():
     with pytest.raises(rg.RnsError) as e:
         rg.dixon_lift(p2, A, b, torch.zeros((2, 4, 4), dtype=torch.int8, device="cuda"), 1)
     assert e.value.code == -1
+
+
+def test_nonsingular_but_singular_mod_every_prime():
+    """det A is a multiple of all 53 odd primes below 256 yet nonzero: the lift has no prime left,
+    and the solve must raise rather than report a singular system."""
+    n = 10
+    groups, cur = [], 1
+    for q in ODD_PRIMES:
+        if cur * q * n >= 1 << 62:
+            groups.append(cur)
+            cur = 1
+        cur *= q
+    groups.append(cur)
+    assert len(groups) <= n
+    diag = groups + [1] * (n - len(groups))
+    A = np.diag(np.array(diag, dtype=np.int64))
+    b = np.ones((n, 1), dtype=np.int64)
+    with pytest.raises(rg.RnsError) as e:
+        rg.solve(dev(A), dev(b))
+    assert e.value.code == -3
