@@ -36,7 +36,8 @@ FLAG_A_RANGE = 1
 FLAG_B_RANGE = 2
 
 ERRORS = {0: "RNS_OK", -1: "RNS_E_ARG", -2: "RNS_E_K", -3: "RNS_E_CAPACITY",
-          -4: "RNS_E_OUT_LIMBS", -5: "RNS_E_WORKSPACE", -6: "RNS_E_HIP", -7: "RNS_E_NONFINITE"}
+          -4: "RNS_E_OUT_LIMBS", -5: "RNS_E_WORKSPACE", -6: "RNS_E_HIP", -7: "RNS_E_NONFINITE",
+          -8: "RNS_E_RECONSTRUCT", -9: "RNS_E_HOSTLIB"}
 
 
 class RnsError(RuntimeError):
@@ -124,6 +125,10 @@ def load() -> ctypes.CDLL:
         "rns_lift_workspace_size": (ctypes.c_int, [P, I64, I64, ctypes.POINTER(SZ)]),
         "rns_dixon_lift": (ctypes.c_int, [P, I64, I64, VP, VP, VP, I32, VP, I32, VP, SZ, VP]),
         "rns_round_outward": (ctypes.c_int, [VP, I64, I32, I32, I32, VP, VP, VP]),
+        "rns_host_bigint_available": (ctypes.c_int, []),
+        "rns_padic_numerators": (ctypes.c_int, [VP, I32, I64, I32, VP, I64, VP, I32, VP, I32, VP, I32, VP,
+                                                I32, VP, I32]),
+        "rns_rational_reconstruct": (ctypes.c_int, [VP, I32, VP, I32, VP, I32, VP, I32, VP, I32, VP, I32]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)

@@ -4,7 +4,8 @@ The library is plain HIP (no PyTorch types): ``csrc/rns_host.cpp`` holds the
 C ABI and host logic; ``csrc/rns_split.hip``, ``csrc/rns_gemm.hip``, ``csrc/rns_crt.hip``,
 ``csrc/rns_garner.hip``, ``csrc/rns_enclose.hip`` and ``csrc/rns_solve.hip`` the
 device kernels, with shared device helpers in
-``csrc/rns_device.h``.
+``csrc/rns_device.h``; ``csrc/rns_ratrec.cpp`` the host stage of the exact solve
+(big integers through the system's libgmp.so.10, opened at run time).
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librns_gemm.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("rns_host.cpp", "rns_split.hip", "rns_gemm.hip", "rns_crt.hip", "rns_garner.hip",
-                                                    "rns_enclose.hip", "rns_solve.hip")]
+                                                    "rns_enclose.hip", "rns_solve.hip", "rns_ratrec.cpp")]
 HEADERS = [os.path.join(CSRC, "rns_internal.h"), os.path.join(CSRC, "rns_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "rns_gemm.h"),
            os.path.join(os.path.dirname(HERE), "include", "rns_enclose.h"),
@@ -25,7 +26,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Packed fp32 instructions are disabled for all device code; the host pass
 # warns that it does not know the feature, which is harmless.
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
-         "-Wall", "-Wno-unused-function",
+         "-Wall", "-Wno-unused-function", "-pthread",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 

@@ -659,6 +659,8 @@ const char *rns_error_string(int code) {
         case RNS_E_WORKSPACE: return "workspace too small";
         case RNS_E_HIP: return "HIP launch or copy failed";
         case -7: return "non-finite operand";
+        case -8: return "no fraction within the bounds matches the residue";
+        case -9: return "the host big-integer library (libgmp.so.10) is not available";
         default: return "unknown error code";
     }
 }

@@ -1,0 +1,286 @@
+// rns_ratrec.cpp -- the host stage of the exact solve (exact-solve, "Method":
+// the final rational reconstruction runs on the CPU): the p-adic value of the
+// lift digits, the numerators over a common denominator, and rational
+// reconstruction by the extended Euclidean algorithm.
+//
+// Big integers go through GMP, opened at first use from the system's
+// libgmp.so.10 (its documented mpz interface, declared below).  Components are
+// spread over host threads; GMP is reentrant and the shared values are only
+// read.  No device memory is touched here.
+#include <dlfcn.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <type_traits>
+#include <thread>
+#include <vector>
+
+#include "../../include/rns_solve.h"
+
+namespace {
+
+// ---- GMP, opened at run time ------------------------------------------------------
+struct Mpz {
+    int alloc;
+    int size;  // |size| limbs, sign of the value
+    uint64_t *d;
+};
+using mpz_ptr = Mpz *;
+using mpz_srcptr = const Mpz *;
+
+struct Gmp {
+    void (*init)(mpz_ptr);
+    void (*clear)(mpz_ptr);
+    void (*import_)(mpz_ptr, size_t, int, size_t, int, size_t, const void *);
+    void *(*export_)(void *, size_t *, int, size_t, int, size_t, mpz_srcptr);
+    void (*mul)(mpz_ptr, mpz_srcptr, mpz_srcptr);
+    void (*add)(mpz_ptr, mpz_srcptr, mpz_srcptr);
+    void (*sub)(mpz_ptr, mpz_srcptr, mpz_srcptr);
+    void (*submul)(mpz_ptr, mpz_srcptr, mpz_srcptr);
+    void (*fdiv_r)(mpz_ptr, mpz_srcptr, mpz_srcptr);
+    void (*tdiv_qr)(mpz_ptr, mpz_ptr, mpz_srcptr, mpz_srcptr);
+    int (*cmp)(mpz_srcptr, mpz_srcptr);
+    int (*cmpabs)(mpz_srcptr, mpz_srcptr);
+    void (*set)(mpz_ptr, mpz_srcptr);
+    void (*set_ui)(mpz_ptr, unsigned long);
+    void (*neg)(mpz_ptr, mpz_srcptr);
+    void (*swap)(mpz_ptr, mpz_ptr);
+    void (*fdiv_q_2exp)(mpz_ptr, mpz_srcptr, unsigned long);
+    size_t (*sizeinbase)(mpz_srcptr, int);
+    bool ok = false;
+};
+
+const Gmp *gmp() {
+    static Gmp g;
+    static std::once_flag once;
+    std::call_once(once, [] {
+        void *h = dlopen("libgmp.so.10", RTLD_NOW | RTLD_LOCAL);
+        if (!h) return;
+        bool all = true;
+        auto get = [&](auto &fn, const char *name) {
+            fn = reinterpret_cast<std::remove_reference_t<decltype(fn)>>(dlsym(h, name));
+            all = all && fn != nullptr;
+        };
+        get(g.init, "__gmpz_init");
+        get(g.clear, "__gmpz_clear");
+        get(g.import_, "__gmpz_import");
+        get(g.export_, "__gmpz_export");
+        get(g.mul, "__gmpz_mul");
+        get(g.add, "__gmpz_add");
+        get(g.sub, "__gmpz_sub");
+        get(g.submul, "__gmpz_submul");
+        get(g.fdiv_r, "__gmpz_fdiv_r");
+        get(g.tdiv_qr, "__gmpz_tdiv_qr");
+        get(g.cmp, "__gmpz_cmp");
+        get(g.cmpabs, "__gmpz_cmpabs");
+        get(g.set, "__gmpz_set");
+        get(g.set_ui, "__gmpz_set_ui");
+        get(g.neg, "__gmpz_neg");
+        get(g.swap, "__gmpz_swap");
+        get(g.fdiv_q_2exp, "__gmpz_fdiv_q_2exp");
+        get(g.sizeinbase, "__gmpz_sizeinbase");
+        g.ok = all;
+    });
+    return g.ok ? &g : nullptr;
+}
+
+// An mpz that clears itself.
+struct Z {
+    Mpz v;
+    const Gmp *g;
+    explicit Z(const Gmp *g_) : g(g_) { g->init(&v); }
+    ~Z() { g->clear(&v); }
+    Z(const Z &) = delete;
+    Z &operator=(const Z &) = delete;
+    mpz_ptr operator&() { return &v; }
+    mpz_srcptr c() const { return &v; }
+};
+
+int sign(mpz_srcptr x) { return x->size > 0 ? 1 : (x->size < 0 ? -1 : 0); }
+
+// magnitude limbs (least significant first) -> x
+void from_mag(const Gmp *g, mpz_ptr x, const uint64_t *mag, int32_t n) {
+    g->import_(x, (size_t)n, -1, sizeof(uint64_t), 0, 0, mag);
+}
+
+// two's-complement int64 limbs (top limb signed) -> x
+void from_twos(const Gmp *g, mpz_ptr x, const int64_t *l, int32_t n, uint64_t *tmp) {
+    const bool neg = l[n - 1] < 0;
+    uint64_t carry = 1;
+    for (int32_t i = 0; i < n; i++) {
+        const uint64_t w = (uint64_t)l[i];
+        if (neg) {
+            const uint64_t t = ~w + carry;
+            carry = (carry && t == 0) ? 1 : 0;
+            tmp[i] = t;
+        } else {
+            tmp[i] = w;
+        }
+    }
+    from_mag(g, x, tmp, n);
+    if (neg) g->neg(x, x);
+}
+
+// |x| < 2^(64n - 1) is required (checked by the callers' bounds); x -> n limbs.
+bool to_twos(const Gmp *g, int64_t *out, int32_t n, mpz_srcptr x) {
+    std::memset(out, 0, sizeof(int64_t) * (size_t)n);
+    if (sign(x) == 0) return true;
+    if (g->sizeinbase(x, 2) >= (size_t)64 * (size_t)n) return false;
+    size_t cnt = 0;
+    g->export_(out, &cnt, -1, sizeof(uint64_t), 0, 0, x);
+    if (sign(x) < 0) {
+        uint64_t carry = 1;
+        for (int32_t i = 0; i < n; i++) {
+            const uint64_t t = ~(uint64_t)out[i] + carry;
+            carry = (carry && t == 0) ? 1 : 0;
+            out[i] = (int64_t)t;
+        }
+    }
+    return true;
+}
+
+bool to_mag(const Gmp *g, uint64_t *out, int32_t n, mpz_srcptr x) {
+    std::memset(out, 0, sizeof(uint64_t) * (size_t)n);
+    if (sign(x) == 0) return true;
+    if (g->sizeinbase(x, 2) > (size_t)64 * (size_t)n) return false;
+    size_t cnt = 0;
+    g->export_(out, &cnt, -1, sizeof(uint64_t), 0, 0, x);
+    return true;
+}
+
+bool mag_positive(const uint64_t *m, int32_t n) {
+    for (int32_t i = 0; i < n; i++)
+        if (m[i]) return true;
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rns_host_bigint_available(void) { return gmp() ? 1 : 0; }
+
+int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, int32_t d_limbs,
+                         const int64_t *index, int64_t n_index, const uint64_t *P, int32_t p_limbs,
+                         const uint64_t *D, int32_t den_limbs, const uint64_t *bound, int32_t b_limbs,
+                         int64_t *num, int32_t w_limbs, int32_t *ok, int32_t threads) {
+    if (steps < 1 || count < 0 || n_index < 0 || d_limbs < 1 || d_limbs > 64 || p_limbs < 1 || den_limbs < 1 ||
+        b_limbs < 1 || w_limbs < 1 || threads < 0)
+        return RNS_E_ARG;
+    if (!P || !D || !bound || (n_index > 0 && (!digits || !index || !num || !ok))) return RNS_E_ARG;
+    for (int64_t t = 0; t < n_index; t++)
+        if (index[t] < 0 || index[t] >= count) return RNS_E_ARG;
+    if (!mag_positive(D, den_limbs) || !(P[0] & 1) || (p_limbs == 1 && P[0] < 3)) return RNS_E_ARG;
+    const Gmp *g = gmp();
+    if (!g) return RNS_E_HOSTLIB;
+    Z Pz(g), Dz(g), Bz(g), Pm(g), half(g);
+    from_mag(g, &Pz, P, p_limbs);
+    from_mag(g, &Dz, D, den_limbs);
+    from_mag(g, &Bz, bound, b_limbs);
+    if (g->sizeinbase(Bz.c(), 2) >= (size_t)64 * (size_t)w_limbs) return RNS_E_OUT_LIMBS;
+    if (n_index == 0) return RNS_OK;
+
+    // P^(2^j) for the pairwise assembly, and P^steps
+    int levels = 0;
+    while ((1LL << levels) < steps) levels++;
+    std::vector<Mpz> pw((size_t)levels + 1);
+    for (auto &z : pw) g->init(&z);
+    g->set(&pw[0], Pz.c());
+    for (int j = 1; j <= levels; j++) g->mul(&pw[j], &pw[j - 1], &pw[j - 1]);
+    g->set_ui(&Pm, 1);
+    for (int j = 0; j <= levels; j++)
+        if ((steps >> j) & 1) g->mul(&Pm, Pm.c(), &pw[j]);
+    g->fdiv_q_2exp(&half, Pm.c(), 1);  // (P^m - 1) / 2, P odd
+
+    int nt = threads ? threads : (int)std::min<unsigned>(std::max(1u, std::thread::hardware_concurrency()), 16u);
+    nt = (int)std::max<int64_t>(1, std::min<int64_t>(nt, n_index));
+    std::atomic<int64_t> next{0};
+    auto work = [&]() {
+        std::vector<Mpz> v((size_t)steps);
+        for (auto &z : v) g->init(&z);
+        Z tmp(g), w(g);
+        std::vector<uint64_t> scratch((size_t)d_limbs);
+        for (;;) {
+            const int64_t t = next.fetch_add(1);
+            if (t >= n_index) break;
+            const int64_t idx = index[t];
+            for (int32_t s = 0; s < steps; s++)
+                from_twos(g, &v[s], digits + ((int64_t)s * count + idx) * d_limbs, d_limbs, scratch.data());
+            // X = sum_s x_s P^s: adjacent pairs joined level by level
+            int64_t n = steps;
+            for (int j = 0; n > 1; j++) {
+                for (int64_t i = 0; i < n / 2; i++) {
+                    g->mul(&tmp, &v[2 * i + 1], &pw[j]);
+                    g->add(&v[i], &v[2 * i], tmp.c());
+                }
+                if (n & 1) g->swap(&v[n / 2], &v[n - 1]);
+                n = (n + 1) / 2;
+            }
+            // w = D X mod P^m, balanced
+            g->mul(&w, Dz.c(), &v[0]);
+            g->fdiv_r(&w, w.c(), Pm.c());
+            if (g->cmp(w.c(), half.c()) > 0) g->sub(&w, w.c(), Pm.c());
+            int64_t *out = num + t * w_limbs;
+            if (g->cmpabs(w.c(), Bz.c()) <= 0) {
+                to_twos(g, out, w_limbs, w.c());  // fits: |w| <= bound < 2^(64 w_limbs - 1)
+                ok[t] = 1;
+            } else {
+                std::memset(out, 0, sizeof(int64_t) * (size_t)w_limbs);
+                ok[t] = 0;
+            }
+        }
+        for (auto &z : v) g->clear(&z);
+    };
+    std::vector<std::thread> pool;
+    for (int i = 1; i < nt; i++) pool.emplace_back(work);
+    work();
+    for (auto &th : pool) th.join();
+    for (auto &z : pw) g->clear(&z);
+    return RNS_OK;
+}
+
+int rns_rational_reconstruct(const uint64_t *u, int32_t u_limbs, const uint64_t *M, int32_t m_limbs,
+                             const uint64_t *Nb, int32_t nb_limbs, const uint64_t *Db, int32_t db_limbs,
+                             int64_t *num, int32_t num_limbs, uint64_t *den, int32_t den_limbs) {
+    if (!u || !M || !Nb || !Db || !num || !den || u_limbs < 1 || m_limbs < 1 || nb_limbs < 1 || db_limbs < 1 ||
+        num_limbs < 1 || den_limbs < 1)
+        return RNS_E_ARG;
+    if (!mag_positive(M, m_limbs)) return RNS_E_ARG;
+    const Gmp *g = gmp();
+    if (!g) return RNS_E_HOSTLIB;
+    Z Mz(g), uz(g), Nz(g), Dz(g), r0(g), r1(g), t0(g), t1(g), q(g), r(g), chk(g);
+    from_mag(g, &Mz, M, m_limbs);
+    from_mag(g, &uz, u, u_limbs);
+    from_mag(g, &Nz, Nb, nb_limbs);
+    from_mag(g, &Dz, Db, db_limbs);
+    g->fdiv_r(&uz, uz.c(), Mz.c());
+    // r_i = t_i u (mod M) along the remainder sequence of (M, u); stop at the
+    // first remainder within the numerator bound
+    g->set(&r0, Mz.c());
+    g->set(&r1, uz.c());
+    g->set_ui(&t0, 0);
+    g->set_ui(&t1, 1);
+    while (g->cmp(r1.c(), Nz.c()) > 0) {
+        g->tdiv_qr(&q, &r, r0.c(), r1.c());
+        g->swap(&r0, &r1);
+        g->swap(&r1, &r);
+        g->submul(&t0, q.c(), t1.c());  // t0 - q t1
+        g->swap(&t0, &t1);
+    }
+    if (sign(t1.c()) == 0 || g->cmpabs(t1.c(), Dz.c()) > 0) return RNS_E_RECONSTRUCT;
+    g->mul(&chk, t1.c(), uz.c());
+    g->sub(&chk, r1.c(), chk.c());
+    g->fdiv_r(&chk, chk.c(), Mz.c());
+    if (sign(chk.c()) != 0) return RNS_E_RECONSTRUCT;
+    if (sign(t1.c()) < 0) {
+        g->neg(&t1, t1.c());
+        g->neg(&r1, r1.c());
+    }
+    if (!to_twos(g, num, num_limbs, r1.c()) || !to_mag(g, den, den_limbs, t1.c())) return RNS_E_OUT_LIMBS;
+    return RNS_OK;
+}
+
+}  // extern "C"

@@ -114,17 +114,61 @@ def _bounds(A: np.ndarray, b: np.ndarray):
 def _limbs_to_int(limbs: np.ndarray) -> List[int]:
     """int64 [..., L] two's-complement limbs -> Python ints (flattened)."""
     L = limbs.shape[-1]
-    flat = limbs.reshape(-1, L)
-    u = flat.astype(np.uint64)
-    out = []
-    for row in u.tolist():
-        v = 0
-        for l in range(L - 1, -1, -1):
-            v = (v << 64) | int(row[l])
-        if row[L - 1] >> 63:
-            v -= 1 << (64 * L)
-        out.append(v)
-    return out
+    flat = np.ascontiguousarray(limbs.reshape(-1, L), dtype=np.int64)
+    raw = flat.tobytes()
+    w = 8 * L
+    return [int.from_bytes(raw[i * w:(i + 1) * w], "little", signed=True) for i in range(flat.shape[0])]
+
+
+def _mag(v: int):
+    """A non-negative int as little-endian uint64 limbs (at least one)."""
+    n = max(1, (v.bit_length() + 63) // 64)
+    return np.frombuffer(v.to_bytes(8 * n, "little"), dtype=np.uint64).copy(), n
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def host_bigint_available() -> bool:
+    """Whether the native host stage (GMP through the library) can run."""
+    return bool(load().rns_host_bigint_available())
+
+
+def padic_numerators(digits: np.ndarray, P: int, D: int, bound: int, index: Optional[Sequence[int]] = None,
+                     threads: int = 0):
+    """For the components ``index`` of digits int64 [steps, count, L]: w = D * X mod P^steps (balanced),
+    X = sum_s digits[s] P^s; returns (ok bool [len(index)], w as ints, 0 where not ok)."""
+    digits = np.ascontiguousarray(digits, dtype=np.int64)
+    steps, count, L = digits.shape
+    idx = np.arange(count, dtype=np.int64) if index is None else np.ascontiguousarray(index, dtype=np.int64)
+    Pl, pn = _mag(P)
+    Dl, dn = _mag(D)
+    Bl, bn = _mag(bound)
+    wl = bound.bit_length() // 64 + 1
+    num = np.zeros((max(len(idx), 1), wl), dtype=np.int64)
+    ok = np.zeros(max(len(idx), 1), dtype=np.int32)
+    rc = load().rns_padic_numerators(_ptr(digits), steps, count, L, _ptr(idx), len(idx), _ptr(Pl), pn, _ptr(Dl), dn,
+                                     _ptr(Bl), bn, _ptr(num), wl, _ptr(ok), threads)
+    _check(rc, "rns_padic_numerators")
+    return ok[:len(idx)].astype(bool), _limbs_to_int(num[:len(idx)])
+
+
+def rational_reconstruct(u: int, M: int, Nb: int, Db: int) -> Optional[Fraction]:
+    """N/d with |N| <= Nb, 0 < d <= Db, N = d u (mod M) (native extended Euclid); None if none."""
+    ul, un = _mag(u % M)
+    Ml, mn = _mag(M)
+    Nl, nn = _mag(Nb)
+    Dl, dn = _mag(Db)
+    numl = Nb.bit_length() // 64 + 1
+    num = np.zeros(numl, dtype=np.int64)
+    den = np.zeros(dn, dtype=np.uint64)
+    rc = load().rns_rational_reconstruct(_ptr(ul), un, _ptr(Ml), mn, _ptr(Nl), nn, _ptr(Dl), dn, _ptr(num), numl,
+                                         _ptr(den), dn)
+    if rc == -8:
+        return None
+    _check(rc, "rns_rational_reconstruct")
+    return Fraction(_limbs_to_int(num.reshape(1, -1))[0], int.from_bytes(den.tobytes(), "little"))
 
 
 def _ratrec(u: int, M: int, Nb: int, Db: int) -> Optional[Fraction]:
@@ -174,7 +218,7 @@ def reconstruct(per_step: Sequence[Sequence[int]], P: int, m: int, Nb: int, Db: 
         if abs(w) > D * Nb:
             f = _ratrec(u, Pm, Nb, Db)
             if f is None:
-                raise RnsError(-3, "rational reconstruction failed")
+                raise RnsError(-8, "rational reconstruction failed")
             g = f.denominator // math.gcd(D, f.denominator)
             nums = [x * g for x in nums]
             D *= g
@@ -183,6 +227,37 @@ def reconstruct(per_step: Sequence[Sequence[int]], P: int, m: int, Nb: int, Db: 
                 w -= Pm
         nums.append(w)
     return nums, D
+
+
+def reconstruct_digits(digits: np.ndarray, P: int, m: int, Nb: int, Db: int, threads: int = 0):
+    """(numerators, common denominator) from the lift digits int64 [m, count, L], in native code.
+
+    The first component still pending is reconstructed alone (its p-adic value, then the extended
+    Euclidean algorithm); the common denominator D takes its denominator, and one pass over every
+    pending component computes w = D u mod P^m and keeps those with |w| <= D Nb (rigorous for
+    P^m > 2 Nb Db (Db + 1), as in ``reconstruct``).  Components that fail wait for the next
+    denominator; each pass at least doubles D, so there are at most log2 Db + 1 passes."""
+    digits = np.ascontiguousarray(digits, dtype=np.int64)
+    count = digits.shape[1]
+    Pm = P ** m
+    D = 1
+    nums: List[Optional[int]] = [None] * count
+    at: List[int] = [1] * count
+    todo = np.arange(count, dtype=np.int64)
+    while len(todo):
+        _, (u,) = padic_numerators(digits, P, 1, Pm // 2, todo[:1], threads=1)
+        f = rational_reconstruct(u, Pm, Nb, Db)
+        if f is None:
+            raise RnsError(-8, "rational reconstruction failed")
+        D *= f.denominator // math.gcd(D, f.denominator)
+        ok, w = padic_numerators(digits, P, D, D * Nb, todo, threads=threads)
+        if not ok[0]:
+            raise RnsError(-8, "a reconstructed component failed the common-denominator test")
+        for t in np.flatnonzero(ok):
+            nums[todo[t]] = w[t]
+            at[todo[t]] = D
+        todo = todo[~ok]
+    return [v * (D // a) for v, a in zip(nums, at)], D
 
 
 def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
@@ -218,8 +293,11 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
     m = lift_steps_for(P, Nb, Db)
     digits = dixon_lift(p, A, b, planes, m).cpu().numpy()  # synchronises
     c = bn.shape[1]
-    per_step = [_limbs_to_int(digits[s]) for s in range(m)]
-    nums, D = reconstruct(per_step, P, m, Nb, Db)
+    if host_bigint_available():
+        nums, D = reconstruct_digits(digits.reshape(m, n * c, -1), P, m, Nb, Db)
+    else:
+        per_step = [_limbs_to_int(digits[s]) for s in range(m)]
+        nums, D = reconstruct(per_step, P, m, Nb, Db)
     out = [[Fraction(nums[i * c + k], D) for k in range(c)] for i in range(n)]
     if return_info:
         return out, {"primes": moduli, "steps": m, "log2_P": math.log2(P), "denominator_bits": D.bit_length(),

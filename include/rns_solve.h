@@ -15,7 +15,7 @@
  *     prime with the wide digit assembled by rns_gemm_batched_residue, and the
  *     residual update in one limb as (r_i - A x_i) * P^-1 mod 2^64 (P odd).
  * The rational reconstruction of x mod P^m runs on the host (exact-solve,
- * "Method": a CPU stage).
+ * "Method": a CPU stage), declared at the end of this header.
  *
  * Conventions of rns_gemm.h: device pointers owned by the caller,
  * asynchronous launches on the caller's stream, 0 on success and a negative
@@ -31,6 +31,10 @@
 #ifdef __cplusplus
 extern "C" {
 #endif
+
+/* Errors of the host stage, beside those of rns_gemm.h. */
+#define RNS_E_RECONSTRUCT (-8) /* no fraction within the bounds matches the residue */
+#define RNS_E_HOSTLIB (-9)     /* the host big-integer library (libgmp.so.10) is not available */
 
 /*
  * rns_inverse_workspace_size -- device bytes of rns_batched_inverse for
@@ -89,6 +93,52 @@ int rns_lift_workspace_size(const rns_plan_t *plan, int64_t n, int64_t c, size_t
 int rns_dixon_lift(const rns_plan_t *plan, int64_t n, int64_t c, const int8_t *Binv, const int64_t *A,
                    const int64_t *b, int32_t steps, int64_t *digits, int32_t d_limbs,
                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * ---- host stage (exact-solve, "Method": the final rational reconstruction is
+ * a CPU stage: a common denominator, then one modular multiply per numerator).
+ * Host pointers only; no device memory is touched.  Big integers cross as
+ * little-endian uint64 magnitudes (unsigned) or two's-complement int64 limbs
+ * with a signed top limb (signed).  Big-integer arithmetic is GMP's, opened at
+ * first use from libgmp.so.10; without it these calls return RNS_E_HOSTLIB.
+ */
+
+/* rns_host_bigint_available -- 1 when libgmp.so.10 could be opened, else 0. */
+int rns_host_bigint_available(void);
+
+/*
+ * rns_padic_numerators -- for each t < n_index, the component idx = index[t]:
+ *   X = sum_{s < steps} digits[s][idx] * P^s   (digits: host int64
+ *       [steps][count][d_limbs], two's complement, the layout rns_dixon_lift
+ *       writes for [n][c] components),
+ *   w = D * X mod P^steps, taken in (-P^steps/2, P^steps/2),
+ * and ok[t] = 1 with num[t] = w (int64 [n_index][w_limbs], two's complement)
+ * when |w| <= bound, else ok[t] = 0 and num[t] = 0.  With D = 1 and bound =
+ * (P^steps - 1)/2 every X is returned as is.  Accepting |w| <= bound is the
+ * common-denominator test: if X = a/e (mod P^steps) with |D a| <= bound and
+ * P^steps > bound * (e + 1), an accepted w satisfies |w e - D a| < P^steps
+ * and w e = D a (mod P^steps), so w e = D a exactly.  P: odd, > 1 (magnitude, p_limbs); D > 0 (den_limbs); bound
+ * (b_limbs) must satisfy bound < 2^(64 w_limbs - 1).  threads = 0 uses up to
+ * 16 host threads.  Returns RNS_OK, RNS_E_ARG, RNS_E_OUT_LIMBS (bound too
+ * wide for w_limbs) or RNS_E_HOSTLIB.
+ */
+int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, int32_t d_limbs,
+                         const int64_t *index, int64_t n_index, const uint64_t *P, int32_t p_limbs,
+                         const uint64_t *D, int32_t den_limbs, const uint64_t *bound, int32_t b_limbs,
+                         int64_t *num, int32_t w_limbs, int32_t *ok, int32_t threads);
+
+/*
+ * rns_rational_reconstruct -- the fraction N/d with |N| <= Nb, 0 < d <= Db and
+ * N = d * u (mod M), from the remainder sequence of the extended Euclidean
+ * algorithm on (M, u mod M), stopped at the first remainder not above Nb; it
+ * is unique when M > 2 * Nb * Db.  u, M (> 0), Nb, Db: magnitudes.  Writes N
+ * (two's complement, num_limbs) and d (magnitude, den_limbs), not necessarily
+ * in lowest terms.  Returns RNS_OK, RNS_E_ARG, RNS_E_RECONSTRUCT (no such
+ * fraction), RNS_E_OUT_LIMBS or RNS_E_HOSTLIB.
+ */
+int rns_rational_reconstruct(const uint64_t *u, int32_t u_limbs, const uint64_t *M, int32_t m_limbs,
+                             const uint64_t *Nb, int32_t nb_limbs, const uint64_t *Db, int32_t db_limbs,
+                             int64_t *num, int32_t num_limbs, uint64_t *den, int32_t den_limbs);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,7 @@
 """The host stage of the exact solve (bounds, step count, rational
 reconstruction of the lift digits) against the oracle, on the CPU: the digits
 come from the oracle's own recurrence."""
+import math
 import random
 
 import numpy as np
@@ -42,3 +43,140 @@ def test_limbs_to_int_matches_the_oracle():
 
 def test_odd_primes():
     assert S.ODD_PRIMES == [q for q in O.primes_largest_first() if q % 2]
+
+
+# ---- the native host stage (GMP through the library; host pointers only) -------------------
+
+def _native():
+    import exact_integer_gemm_amd as rg
+    try:
+        rg.load()
+    except Exception as e:          # the library is missing: nothing native to test
+        pytest.skip(f"library not built: {e}")
+    if not S.host_bigint_available():
+        pytest.skip("libgmp.so.10 is not available")
+
+
+def _digit_array(digits_per_step, L):
+    """Python-int digits [m][count] -> int64 [m][count][L] two's-complement limbs."""
+    m, cnt = len(digits_per_step), len(digits_per_step[0])
+    out = np.zeros((m, cnt, L), dtype=np.int64)
+    for s in range(m):
+        for i in range(cnt):
+            out[s, i] = O.to_limbs(int(digits_per_step[s][i]), L)
+    return out
+
+
+@pytest.mark.parametrize("seed,n,c", [(1, 6, 1), (2, 9, 3), (5, 12, 2)])
+def test_native_reconstruction_from_oracle_digits(seed, n, c):
+    _native()
+    A, b = _system(seed, n, c)
+    ps = D.lift_primes(A)
+    P = O.prod(ps)
+    Nb, Db = D.hadamard_bounds(A, b)
+    m = S.lift_steps_for(P, Nb, Db)
+    digits = D.dixon_digits(A, b, ps, m)
+    per_step = [[digits[s][i][k] for i in range(n) for k in range(c)] for s in range(m)]
+    L = (P.bit_length() + 64) // 64
+    nums, den = S.reconstruct_digits(_digit_array(per_step, L), P, m, Nb, Db)
+    ref = D.solve_fraction(A, b)
+    assert [[S.Fraction(nums[i * c + k], den) for k in range(c)] for i in range(n)] == ref
+
+
+def test_native_padic_value_matches_the_oracle():
+    """D = 1 and the widest bound give X = sum_s digits[s] P^s itself."""
+    _native()
+    rng = random.Random(6)
+    for ps, m, cnt in ((O.primes_largest_first()[1:9], 7, 11), ([3], 1, 4), ([251, 241, 239], 33, 5)):
+        P = O.prod(ps)
+        per_step = [[rng.randint(-(P // 2), P // 2) for _ in range(cnt)] for _ in range(m)]
+        L = (P.bit_length() + 64) // 64
+        ok, X = S.padic_numerators(_digit_array(per_step, L), P, 1, P ** m // 2)
+        ref = D.padic_value([[[v] for v in row] for row in per_step], P)
+        assert ok.all() and X == [r[0] for r in ref]
+
+
+def test_native_common_denominator_test():
+    """Planted fractions a/e: with D a multiple of every e the numerator D a / e is accepted; with
+    D = 1 only the integer components are (the rest exceed the bound), never a wrong value."""
+    _native()
+    rng = random.Random(7)
+    ps = [q for q in O.primes_largest_first() if q % 2][:10]
+    P = O.prod(ps)
+    m = 9
+    Pm = P ** m
+    Nb = 2 ** 60
+    es = [2 ** 50 + 1, 1, 3 ** 20, 2 ** 40 + 3, 1]
+    assert all(math.gcd(e, P) == 1 for e in es)
+    comps = [(rng.randint(-Nb, Nb), e) for e in es]
+    vals = [a * pow(e, -1, Pm) % Pm for a, e in comps]
+    vals = [u - Pm if u > Pm // 2 else u for u in vals]
+    per_step = []
+    for _ in range(m):
+        row = []
+        for i, v in enumerate(vals):
+            d = O.balanced(v, P)
+            vals[i] = (v - d) // P
+            row.append(d)
+        per_step.append(row)
+    dig = _digit_array(per_step, (P.bit_length() + 64) // 64)
+    Dfull = math.lcm(*es)
+    assert Pm > 2 * Dfull * Nb * (Dfull + 1)
+    ok, w = S.padic_numerators(dig, P, Dfull, Dfull * Nb)
+    assert ok.all() and w == [a * (Dfull // e) for a, e in comps]
+    ok1, w1 = S.padic_numerators(dig, P, 1, Nb)
+    assert list(ok1) == [e == 1 for _, e in comps]
+    assert [w1[i] for i in range(len(es)) if ok1[i]] == [a for a, e in comps if e == 1]
+    ok_t, w_t = S.padic_numerators(dig, P, Dfull, Dfull * Nb, threads=1)
+    assert list(ok_t) == list(ok) and w_t == w
+    nums, den = S.reconstruct_digits(dig, P, m, Nb, Dfull)
+    assert [S.Fraction(v, den) for v in nums] == [S.Fraction(a, e) for a, e in comps]
+    assert den == math.lcm(*[S.Fraction(a, e).denominator for a, e in comps])   # lowest terms
+
+
+def test_native_rational_reconstruction_matches_the_oracle():
+    _native()
+    rng = random.Random(8)
+    M = O.prod(O.primes_largest_first()[1:12])
+    Nb = Db = math.isqrt(M // 2) - 1
+    for _ in range(150):
+        d = rng.randint(1, Db)
+        while math.gcd(d, M) != 1:
+            d = rng.randint(1, Db)
+        a = rng.randint(-Nb, Nb)
+        u = a * pow(d, -1, M) % M
+        assert S.rational_reconstruct(u, M, Nb, Db) == D.rational_reconstruct(u, M, Nb, Db) == S.Fraction(a, d)
+    # tight bounds: residues with no small fraction; both sides agree on None or the value
+    for _ in range(150):
+        u = rng.randrange(M)
+        assert S.rational_reconstruct(u, M, 2 ** 20, 2 ** 20) == D.rational_reconstruct(u, M, 2 ** 20, 2 ** 20)
+
+
+def test_native_host_stage_argument_errors():
+    _native()
+    import ctypes
+    import exact_integer_gemm_amd as rg
+    lib = rg.load()
+    dig = np.zeros((2, 3, 1), dtype=np.int64)
+    one = np.ones(1, dtype=np.uint64)
+    P = np.array([15], dtype=np.uint64)
+    Peven = np.array([16], dtype=np.uint64)
+    big = np.array([0, 1], dtype=np.uint64)          # 2^64
+    num = np.zeros((3, 1), dtype=np.int64)
+    ok = np.zeros(3, dtype=np.int32)
+    p = lambda a: a.ctypes.data
+
+    def call(idx, Pv=P, bound=one, bl=1, wl=1):
+        ix = np.array(idx, dtype=np.int64)
+        return lib.rns_padic_numerators(p(dig), 2, 3, 1, p(ix), len(ix), p(Pv), 1, p(one), 1, p(bound), bl,
+                                        p(num), wl, p(ok), 1)
+    assert call([0, 1, 2]) == 0
+    assert call([3]) == -1                             # index beyond count
+    assert call([-1]) == -1
+    assert call([0], Pv=Peven) == -1                   # P must be odd
+    assert call([0], bound=big, bl=2) == -4            # bound does not fit one signed limb
+    assert call([0], bound=big, bl=2, wl=2) == 0
+    assert lib.rns_error_string(-8).decode() and lib.rns_error_string(-9).decode()
+    d = np.zeros(1, dtype=np.uint64)
+    assert lib.rns_rational_reconstruct(p(one), 1, p(np.zeros(1, dtype=np.uint64)), 1, p(one), 1, p(one), 1,
+                                        p(num), 1, p(d), 1) == -1  # M = 0
