@@ -161,6 +161,252 @@ __global__ __launch_bounds__(64) void gj_update_kernel(GjConsts gc, uint8_t *__r
     }
 }
 
+// ---- blocked elimination: a panel of B columns in LDS, then one rank-B update --------
+// Gauss-Jordan on the B panel columns, with every row operation also applied to
+// a companion block Y (unit column j placed at the pivot row when step j
+// begins), leaves Y = X + S^T, where the panel's whole transformation is
+// T = (I + X S) Pi: Pi the row interchanges, S the selection of the B pivot
+// rows kb..kb+B-1 of Pi W.  So the rest of the matrix is updated at once as
+//   W'[i][c] = W[perm(i)][c] + sum_j X[i][j] * W[perm(kb + j)][c]  (mod q),
+// a product of depth B done with byte dot products.  The rows the update reads
+// in another row's place (the pivot rows, and rows moved by an interchange,
+// whose old contents all come from rows kb..kb+B-1) are copied out first, so
+// the update runs in place.
+
+// bytes of a (value in [0, q)) row as balanced int8 packed in a dword
+__device__ __forceinline__ uint32_t balanced4(uint32_t w, uint32_t q) {
+    uint32_t o = 0;
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+        const uint32_t v = (w >> (8 * b)) & 0xffu;
+        o |= ((v > q / 2 ? v - q : v) & 0xffu) << (8 * b);
+    }
+    return o;
+}
+
+template <int B, int NMAX>
+__global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8_t *__restrict__ W, int64_t n,
+                                                        int64_t pitch, int64_t kb, int bw, int8_t *__restrict__ Xb,
+                                                        int8_t *__restrict__ Rb, uint8_t *__restrict__ Oc,
+                                                        int32_t *__restrict__ perm, int32_t *__restrict__ singular) {
+    constexpr int S = 2 * B + 4;        // LDS row: B panel bytes, B bytes of Y, 4 bytes of padding
+    constexpr int WD = B / 4 + 1;       // dwords of the window a step touches
+    __shared__ uint32_t rows[NMAX * S / 4];
+    __shared__ int16_t pl[NMAX];
+    __shared__ int32_t piv_sh[2];
+    const int e = blockIdx.x;
+    if (singular[e]) return;
+    const int t = threadIdx.x;
+    const uint32_t q = gc.q[e], mq = gc.mq[e], qq = q * q;
+    const uint8_t *We = W + (int64_t)e * n * pitch;
+    uint8_t *lb = reinterpret_cast<uint8_t *>(rows);
+
+    // the panel columns of every row; Y and the padding start at zero
+    for (int64_t it = t; it < n * (S / 4); it += 1024) {
+        const int64_t i = it / (S / 4);
+        const int d = (int)(it - i * (S / 4));
+        uint32_t v = 0;
+        if (4 * d < bw) {
+            v = *reinterpret_cast<const uint32_t *>(We + i * pitch + kb + 4 * d);
+            const int keep = bw - 4 * d;                   // bytes of this dword inside the panel
+            if (keep < 4) v &= (1u << (8 * keep)) - 1u;
+        }
+        rows[it] = v;
+    }
+    for (int64_t i = t; i < n; i += 1024) pl[i] = (int16_t)i;
+    if (t < 2) piv_sh[t] = (int32_t)n;
+    __syncthreads();
+
+    for (int j = 0; j < bw; j++) {
+        const int64_t r0 = kb + j;
+        // the first row at or below r0 with a nonzero entry in column j
+        int32_t mine = (int32_t)n;
+        for (int64_t i = r0 + t; i < n; i += 1024)
+            if (lb[i * S + j]) { mine = (int32_t)i; break; }
+        if (mine < n) atomicMin(&piv_sh[j & 1], mine);
+        if (t == 0) piv_sh[(j + 1) & 1] = (int32_t)n;      // read last at step j - 1, before the barrier above
+        __syncthreads();
+        const int64_t p = piv_sh[j & 1];
+        if (p >= n) {
+            if (t == 0) singular[e] = 1;
+            return;
+        }
+        // interchange rows r0 and p, put Y's unit in column j, scale by the pivot's inverse
+        if (t < S / 4) {
+            const uint32_t a = lb[p * S + j];
+            uint32_t inv = 1, base = a, ex = q - 2;
+            while (ex) {
+                if (ex & 1) inv = barrett(inv * base, q, mq);
+                base = barrett(base * base, q, mq);
+                ex >>= 1;
+            }
+            uint32_t x = rows[p * (S / 4) + t];
+            const uint32_t y = rows[r0 * (S / 4) + t];
+            if (t == (B + j) / 4) x |= 1u << (8 * ((B + j) % 4));
+            uint32_t o = 0;
+#pragma unroll
+            for (int b = 0; b < 4; b++) o |= barrett(((x >> (8 * b)) & 0xffu) * inv, q, mq) << (8 * b);
+            if (p != r0) rows[p * (S / 4) + t] = y;
+            rows[r0 * (S / 4) + t] = o;
+            if (t == 0 && p != r0) {
+                const int16_t s = pl[p];
+                pl[p] = pl[r0];
+                pl[r0] = s;
+            }
+        }
+        __syncthreads();
+        // eliminate column j from every other row over the window j+1 .. B+j
+        const int d0 = (j + 1) / 4;
+        for (int64_t it = t; it < n * WD; it += 1024) {
+            const int64_t i = it / WD;
+            const int d = d0 + (int)(it - i * WD);
+            if (i == r0 || d >= S / 4) continue;
+            const uint32_t f = lb[i * S + j];
+            if (!f) continue;
+            const uint32_t pv = rows[r0 * (S / 4) + d], wv = rows[i * (S / 4) + d];
+            uint32_t o = 0;
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                const uint32_t a = (wv >> (8 * b)) & 0xffu, c = (pv >> (8 * b)) & 0xffu;
+                o |= barrett(a + qq - f * c, q, mq) << (8 * b);
+            }
+            // bytes of columns <= j stay: column j holds f, which the other threads of this row read
+            const int keep = j + 1 - 4 * d;
+            if (keep > 0) {
+                const uint32_t m = (1u << (8 * keep)) - 1u;
+                o = (o & ~m) | (wv & m);
+            }
+            rows[i * (S / 4) + d] = o;
+        }
+        __syncthreads();
+    }
+
+    // X = Y - S^T as balanced int8 [n][B] (columns bw.. zero); the permutation
+    int8_t *Xe = Xb + (int64_t)e * n * B;
+    for (int64_t it = t; it < n * (B / 4); it += 1024) {
+        const int64_t i = it / (B / 4);
+        const int d = (int)(it - i * (B / 4));
+        uint32_t y = rows[i * (S / 4) + B / 4 + d];
+        const int64_t jj = i - kb;                      // the unit sits at row kb + jj, column jj
+        if (jj >= 4 * d && jj < 4 * d + 4 && jj < bw) {
+            const int b = (int)(jj - 4 * d);
+            const uint32_t v = (y >> (8 * b)) & 0xffu;
+            y = (y & ~(0xffu << (8 * b))) | ((v == 0 ? q - 1 : v - 1) << (8 * b));
+        }
+        if (4 * d + 4 > bw) y &= (4 * d >= bw) ? 0u : (1u << (8 * (bw - 4 * d))) - 1u;
+        reinterpret_cast<uint32_t *>(Xe)[it] = balanced4(y, q);
+    }
+    for (int64_t i = t; i < n; i += 1024) perm[(int64_t)e * n + i] = pl[i];
+    // copies of the rows the update reads in another row's place, columns cs..pitch
+    const int64_t cs = (kb + bw) & ~(int64_t)15;
+    const int64_t cw = (pitch - cs) / 4;
+    int8_t *Re = Rb + (int64_t)e * B * pitch;
+    uint8_t *Oe = Oc + (int64_t)e * B * pitch;
+    for (int64_t it = t; it < (int64_t)bw * cw; it += 1024) {
+        const int64_t jr = it / cw;
+        const int64_t c = cs + 4 * (it - jr * cw);
+        const uint32_t src = *reinterpret_cast<const uint32_t *>(We + (int64_t)pl[kb + jr] * pitch + c);
+        *reinterpret_cast<uint32_t *>(Re + jr * pitch + c) = balanced4(src, q);
+        *reinterpret_cast<uint32_t *>(Oe + jr * pitch + c) =
+            *reinterpret_cast<const uint32_t *>(We + (kb + jr) * pitch + c);
+    }
+    for (int64_t it = t; it < (int64_t)(B - bw) * cw; it += 1024) {      // rows bw..B of R: zero
+        const int64_t jr = bw + it / cw;
+        const int64_t c = cs + 4 * (it % cw);
+        *reinterpret_cast<uint32_t *>(Re + jr * pitch + c) = 0u;
+    }
+}
+
+// W[i][c] <- W[perm(i)][c] + sum_j X[i][j] R[j][c] (mod q) for columns c >= cs:
+// 64 rows x 256 columns per block of 256 threads, 16 rows x 4 columns each.
+template <int B>
+__global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8_t *__restrict__ W, int64_t n,
+                                                              int64_t pitch, int64_t kb, int bw, int64_t cs,
+                                                              int64_t row_tiles, int64_t col_tiles,
+                                                              const int8_t *__restrict__ Xb,
+                                                              const int8_t *__restrict__ Rb,
+                                                              const uint8_t *__restrict__ Oc,
+                                                              const int32_t *__restrict__ perm,
+                                                              const int32_t *__restrict__ singular) {
+    constexpr int KC = B / 4;           // dword chunks of the depth
+    __shared__ uint32_t xs[64][KC];
+    __shared__ uint32_t rt[KC][256];
+    const int64_t per = row_tiles * col_tiles;
+    const int e = (int)(blockIdx.x / per);
+    if (singular[e]) return;
+    const int64_t tile = blockIdx.x - (int64_t)e * per;
+    const int64_t i0 = (tile / col_tiles) * 64;
+    const int64_t c0 = cs + (tile % col_tiles) * 256;
+    const int t = threadIdx.x, cg = t & 63, rg = t >> 6;
+    const uint32_t q = gc.q[e], mq = gc.mq[e];
+    const int8_t *Xe = Xb + (int64_t)e * n * B;
+    const int8_t *Re = Rb + (int64_t)e * B * pitch;
+    const int64_t c = c0 + 4 * cg;
+    const bool col_ok = c < pitch;
+
+    for (int it = t; it < 64 * KC; it += 256) {
+        const int r = it / KC, d = it - r * KC;
+        xs[r][d] = (i0 + r < n) ? reinterpret_cast<const uint32_t *>(Xe + (i0 + r) * B)[d] : 0u;
+    }
+    // R^T: four depth rows of this thread's four columns, transposed in registers
+    for (int jc = rg; jc < KC; jc += 4) {
+        uint32_t r4[4];
+#pragma unroll
+        for (int k = 0; k < 4; k++)
+            r4[k] = col_ok ? *reinterpret_cast<const uint32_t *>(Re + (int64_t)(4 * jc + k) * pitch + c) : 0u;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {           // column k: byte r is depth row 4 jc + r
+            uint32_t v = 0;
+#pragma unroll
+            for (int r = 0; r < 4; r++) v |= ((r4[r] >> (8 * k)) & 0xffu) << (8 * r);
+            rt[jc][4 * cg + k] = v;
+        }
+    }
+    __syncthreads();
+    int acc[16][4];
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+#pragma unroll
+        for (int k = 0; k < 4; k++) acc[r][k] = 0;
+#pragma unroll
+    for (int jc = 0; jc < KC; jc++) {
+        const v4u rv = *reinterpret_cast<const v4u *>(&rt[jc][4 * cg]);
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int x = (int)xs[16 * rg + r][jc];
+#pragma unroll
+            for (int k = 0; k < 4; k++) acc[r][k] = __builtin_amdgcn_sdot4(x, (int)rv[k], acc[r][k], false);
+        }
+    }
+    if (!col_ok) return;
+    const uint32_t off = q * ((1u << 21) / q + 1);   // > |acc| + 255, keeps the sum positive
+    uint8_t *We = W + (int64_t)e * n * pitch;
+    const uint8_t *Oe = Oc + (int64_t)e * B * pitch;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+        const int64_t i = i0 + 16 * rg + r;
+        if (i >= n) break;
+        uint32_t s;
+        bool sgn = false;
+        if (i >= kb && i < kb + bw) {
+            s = *reinterpret_cast<const uint32_t *>(Re + (i - kb) * pitch + c);
+            sgn = true;
+        } else {
+            const int64_t pi = perm[(int64_t)e * n + i];
+            s = (pi == i) ? *reinterpret_cast<const uint32_t *>(We + i * pitch + c)
+                          : *reinterpret_cast<const uint32_t *>(Oe + (pi - kb) * pitch + c);
+        }
+        uint32_t o = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+            const uint32_t sb = (s >> (8 * k)) & 0xffu;
+            const int sv = sgn ? (int)(int8_t)sb : (int)sb;
+            o |= barrett((uint32_t)(acc[r][k] + sv + (int)off), q, mq) << (8 * k);
+        }
+        *reinterpret_cast<uint32_t *>(We + i * pitch + c) = o;
+    }
+}
+
 // ---- the inverses as balanced int8 planes ---------------------------------------
 struct PlaneSelect {
     int32_t n_sel;
@@ -234,13 +480,21 @@ namespace {
 int64_t pad16(int64_t x) { return (x + 15) / 16 * 16; }
 int64_t pad256(int64_t x) { return (x + 255) / 256 * 256; }
 
+// Panel width of the blocked elimination: the panel and its companion block
+// of n rows sit in LDS (n * (2B + 4) bytes plus the permutation).  Above
+// 4096 rows the elimination runs unblocked, one step per launch pair.
+int panel_width(int64_t n) { return n <= 2048 ? 32 : (n <= 4096 ? 16 : 0); }
+
 struct InvLayout {
-    int64_t pitch, w_off, prow_off, mcol_off, piv_off, total;
+    int64_t pitch, w_off, prow_off, mcol_off, piv_off;
+    int B;                                   // panel width (0: unblocked)
+    int64_t xb_off, rb_off, oc_off, perm_off, total;
 };
 
 InvLayout inv_layout(int32_t E, int64_t n) {
     InvLayout L;
     L.pitch = pad16(2 * n);
+    L.B = panel_width(n);
     int64_t off = 0;
     L.w_off = off;
     off = pad256(off + (int64_t)E * n * L.pitch);
@@ -250,8 +504,37 @@ InvLayout inv_layout(int32_t E, int64_t n) {
     off = pad256(off + (int64_t)E * n);
     L.piv_off = off;
     off = pad256(off + (int64_t)E * 4);
+    L.xb_off = off;                          // X: [E][n][B] int8
+    off = pad256(off + (int64_t)E * n * L.B);
+    L.rb_off = off;                          // pivot rows: [E][B][pitch] int8
+    off = pad256(off + (int64_t)E * L.B * L.pitch);
+    L.oc_off = off;                          // old rows kb..kb+B-1: [E][B][pitch]
+    off = pad256(off + (int64_t)E * L.B * L.pitch);
+    L.perm_off = off;                        // [E][n] int32
+    off = pad256(off + (L.B ? (int64_t)E * n * 4 : 0));
     L.total = off;
     return L;
+}
+
+template <int B, int NMAX>
+int blocked_inverse(const GjConsts &gc, int32_t E, int64_t n, const InvLayout &L, uint8_t *base, int32_t *singular,
+                    hipStream_t stream) {
+    uint8_t *W = base + L.w_off;
+    int8_t *Xb = reinterpret_cast<int8_t *>(base + L.xb_off);
+    int8_t *Rb = reinterpret_cast<int8_t *>(base + L.rb_off);
+    uint8_t *Oc = base + L.oc_off;
+    int32_t *perm = reinterpret_cast<int32_t *>(base + L.perm_off);
+    const int64_t row_tiles = (n + 63) / 64;
+    for (int64_t kb = 0; kb < n; kb += B) {
+        const int bw = (int)(n - kb < B ? n - kb : B);
+        hipLaunchKernelGGL((gj_panel_kernel<B, NMAX>), dim3((unsigned)E), dim3(1024), 0, stream, gc, W, n, L.pitch, kb,
+                           bw, Xb, Rb, Oc, perm, singular);
+        const int64_t cs = (kb + bw) & ~(int64_t)15;
+        const int64_t col_tiles = (L.pitch - cs + 255) / 256;
+        hipLaunchKernelGGL((gj_block_update_kernel<B>), dim3((unsigned)(E * row_tiles * col_tiles)), dim3(256), 0,
+                           stream, gc, W, n, L.pitch, kb, bw, cs, row_tiles, col_tiles, Xb, Rb, Oc, perm, singular);
+    }
+    return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 
 bool small_prime(int q) {
@@ -312,6 +595,8 @@ int rns_batched_inverse(const int32_t *primes, int32_t n_primes, int64_t n, cons
     // singular flags start at 0 (a fill kernel: no memset node in a captured graph)
     hipLaunchKernelGGL(zero_i32_kernel, dim3(1), dim3(64), 0, stream, singular, (int64_t)n_primes);
     if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
+    if (L.B == 32) return blocked_inverse<32, 2048>(gc, n_primes, n, L, base, singular, stream);
+    if (L.B == 16) return blocked_inverse<16, 4096>(gc, n_primes, n, L, base, singular, stream);
     for (int64_t k = 0; k < n; k++) {
         hipLaunchKernelGGL(gj_pivot_kernel, dim3(n_primes), dim3(256), 0, stream, gc, W, n, L.pitch, k, prow, mcol,
                            piv, singular);

@@ -169,3 +169,40 @@ def test_nonsingular_but_singular_mod_every_prime():
     with pytest.raises(rg.RnsError) as e:
         rg.solve(dev(A), dev(b))
     assert e.value.code == -3
+
+
+def _planted_lu(n, seed, diag_factor_rows):
+    """A = L U with L unit lower triangular (entries in {-1, 0, 1}) and U upper triangular with
+    entries in [-3, 3]: det A = prod(diag U), so A is singular exactly mod the primes dividing
+    some diagonal entry.  diag_factor_rows: {row: diagonal value}."""
+    rng = np.random.default_rng(seed)
+    L = np.tril(rng.integers(-1, 2, size=(n, n)), -1) + np.eye(n, dtype=np.int64)
+    U = np.triu(rng.integers(-3, 4, size=(n, n)), 1) + np.eye(n, dtype=np.int64)
+    for r, v in diag_factor_rows.items():
+        U[r, r] = v
+    return (L.astype(np.float64) @ U.astype(np.float64)).astype(np.int64)   # exact: |sums| < 2^53
+
+
+def _check_inverses(A, planes, sel, primes_to_check):
+    Af = A.astype(np.float64)
+    n = A.shape[0]
+    for t in primes_to_check:
+        q = ODD_PRIMES[sel[t]]
+        Bq = planes[t].astype(np.float64)
+        prod = np.mod(np.mod(Af, q) @ Bq, q)     # exact: n * 255 * 127 < 2^53
+        assert np.array_equal(prod, np.eye(n)), q
+
+
+@pytest.mark.parametrize("n", [300, 2100, 4097])
+def test_batched_inverse_larger_sizes(n):
+    """The blocked elimination (panels of 32 columns up to 2048 rows, 16 up to 4096, ragged last
+    panel) and the unblocked one above 4096: A B = I mod q, and the singular flags match the
+    planted determinant (diagonal entries 3 * 7 and 5 * 11)."""
+    A = _planted_lu(n, 11 + n, {n // 3: 21, n - 1: 55})
+    print(f"batched inverse n={n}", flush=True)
+    singular, ws = rg.batched_inverse(dev(A))
+    sing = singular.cpu().tolist()
+    assert [ODD_PRIMES[e] for e, s in enumerate(sing) if s] == [11, 7, 5, 3]
+    sel = [i for i, s in enumerate(sing) if not s]
+    planes = rg.inverse_planes(ws, n, sel).cpu().numpy()
+    _check_inverses(A, planes, sel, (0, len(sel) - 1) if n > 4096 else (0, 1, len(sel) // 2, len(sel) - 1))
