@@ -50,6 +50,9 @@ struct Gmp {
     void (*swap)(mpz_ptr, mpz_ptr);
     void (*fdiv_q_2exp)(mpz_ptr, mpz_srcptr, unsigned long);
     size_t (*sizeinbase)(mpz_srcptr, int);
+    void (*mul_si)(mpz_ptr, mpz_srcptr, long);
+    void (*addmul_ui)(mpz_ptr, mpz_srcptr, unsigned long);
+    void (*submul_ui)(mpz_ptr, mpz_srcptr, unsigned long);
     bool ok = false;
 };
 
@@ -82,6 +85,9 @@ const Gmp *gmp() {
         get(g.swap, "__gmpz_swap");
         get(g.fdiv_q_2exp, "__gmpz_fdiv_q_2exp");
         get(g.sizeinbase, "__gmpz_sizeinbase");
+        get(g.mul_si, "__gmpz_mul_si");
+        get(g.addmul_ui, "__gmpz_addmul_ui");
+        get(g.submul_ui, "__gmpz_submul_ui");
         g.ok = all;
     });
     return g.ok ? &g : nullptr;
@@ -149,6 +155,23 @@ bool to_mag(const Gmp *g, uint64_t *out, int32_t n, mpz_srcptr x) {
     size_t cnt = 0;
     g->export_(out, &cnt, -1, sizeof(uint64_t), 0, 0, x);
     return true;
+}
+
+// floor(|x| / 2^h) for a value known to be below 2^(h + 63), from the limbs
+uint64_t top_bits(mpz_srcptr x, size_t h) {
+    const size_t n = (size_t)(x->size < 0 ? -x->size : x->size);
+    const size_t w = h / 64, b = h % 64;
+    const uint64_t lo = w < n ? x->d[w] : 0, hi = w + 1 < n ? x->d[w + 1] : 0;
+    return b ? (lo >> b) | (hi << (64 - b)) : lo;
+}
+
+// dst = a * x + b * y with single-word signed cofactors
+void lincomb(const Gmp *g, mpz_ptr dst, int64_t a, mpz_srcptr x, int64_t b, mpz_srcptr y) {
+    g->mul_si(dst, x, (long)a);
+    if (b >= 0)
+        g->addmul_ui(dst, y, (unsigned long)b);
+    else
+        g->submul_ui(dst, y, (unsigned long)(-(b + 1)) + 1ul);
 }
 
 bool mag_positive(const uint64_t *m, int32_t n) {
@@ -263,13 +286,54 @@ int rns_rational_reconstruct(const uint64_t *u, int32_t u_limbs, const uint64_t 
     g->set(&r1, uz.c());
     g->set_ui(&t0, 0);
     g->set_ui(&t1, 1);
-    while (g->cmp(r1.c(), Nz.c()) > 0) {
+    auto euclid_step = [&]() {
         g->tdiv_qr(&q, &r, r0.c(), r1.c());
         g->swap(&r0, &r1);
         g->swap(&r1, &r);
         g->submul(&t0, q.c(), t1.c());  // t0 - q t1
         g->swap(&t0, &t1);
+    };
+    // Lehmer's method (Knuth, TAOCP vol. 2, 4.5.2, Algorithm L) while the remainders are far above
+    // the bound: Euclid on the leading 62 bits yields the next quotients, exactly where the two
+    // bracketing single-word quotients agree, as one 2x2 cofactor matrix applied at once.  A batch
+    // shrinks r1 by at most 64 bits (its matrix entries are below 2^62), so it cannot step past
+    // the first remainder within the bound.
+    const size_t nb_bits = g->sizeinbase(Nz.c(), 2);
+    Z u0(g), u1(g), v0(g), v1(g);
+    while (sign(r1.c()) != 0 && g->sizeinbase(r1.c(), 2) > nb_bits + 70) {
+        const size_t h = g->sizeinbase(r0.c(), 2) - 62;
+        int64_t x = (int64_t)top_bits(r0.c(), h), y = (int64_t)top_bits(r1.c(), h);
+        int64_t A = 1, B = 0, C = 0, D = 1;
+        for (;;) {
+            if (y + C <= 0 || y + D <= 0 || x + A < 0 || x + B < 0) break;
+            const int64_t q1 = (x + A) / (y + C), q2 = (x + B) / (y + D);
+            if (q1 != q2) break;
+            const __int128 nC = (__int128)A - (__int128)q1 * C, nD = (__int128)B - (__int128)q1 * D;
+            if (nC > ((__int128)1 << 62) || nC < -((__int128)1 << 62) || nD > ((__int128)1 << 62) ||
+                nD < -((__int128)1 << 62))
+                break;
+            A = C;
+            C = (int64_t)nC;
+            B = D;
+            D = (int64_t)nD;
+            const int64_t ny = x - q1 * y;
+            x = y;
+            y = ny;
+        }
+        if (B == 0) {
+            euclid_step();
+            continue;
+        }
+        lincomb(g, &u0, A, r0.c(), B, r1.c());
+        lincomb(g, &u1, C, r0.c(), D, r1.c());
+        lincomb(g, &v0, A, t0.c(), B, t1.c());
+        lincomb(g, &v1, C, t0.c(), D, t1.c());
+        g->swap(&r0, &u0);
+        g->swap(&r1, &u1);
+        g->swap(&t0, &v0);
+        g->swap(&t1, &v1);
     }
+    while (g->cmp(r1.c(), Nz.c()) > 0) euclid_step();
     if (sign(t1.c()) == 0 || g->cmpabs(t1.c(), Dz.c()) > 0) return RNS_E_RECONSTRUCT;
     g->mul(&chk, t1.c(), uz.c());
     g->sub(&chk, r1.c(), chk.c());

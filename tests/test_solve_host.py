@@ -180,3 +180,28 @@ def test_native_host_stage_argument_errors():
     d = np.zeros(1, dtype=np.uint64)
     assert lib.rns_rational_reconstruct(p(one), 1, p(np.zeros(1, dtype=np.uint64)), 1, p(one), 1, p(one), 1,
                                         p(num), 1, p(d), 1) == -1  # M = 0
+
+
+def test_native_rational_reconstruction_long_remainder_sequences():
+    """Moduli of thousands of bits with bounds far below them, so that the reconstruction runs
+    through its batched (Lehmer) steps before the last single divisions: the fraction equals the
+    oracle's, for planted fractions and for residues with no fraction within the bounds."""
+    _native()
+    rng = random.Random(9)
+    ps = [q for q in O.primes_largest_first() if q % 2]
+    for bits, nb_bits, trials in ((4000, 1500, 12), (20000, 9000, 3), (600, 100, 30)):
+        M = 1
+        while M.bit_length() < bits:
+            M *= ps[rng.randrange(len(ps))]
+        Nb = rng.getrandbits(nb_bits) | (1 << (nb_bits - 1))
+        Db = (M // (2 * Nb)) - 1
+        for _ in range(trials):
+            d = rng.randint(1, Db)
+            while math.gcd(d, M) != 1:
+                d = rng.randint(1, Db)
+            a = rng.randint(-Nb, Nb)
+            u = a * pow(d, -1, M) % M
+            assert S.rational_reconstruct(u, M, Nb, Db) == D.rational_reconstruct(u, M, Nb, Db) == S.Fraction(a, d)
+            v = rng.randrange(M)
+            small = 2 ** (nb_bits // 2)
+            assert S.rational_reconstruct(v, M, small, small) == D.rational_reconstruct(v, M, small, small)
