@@ -53,6 +53,8 @@ struct Gmp {
     void (*mul_si)(mpz_ptr, mpz_srcptr, long);
     void (*addmul_ui)(mpz_ptr, mpz_srcptr, unsigned long);
     void (*submul_ui)(mpz_ptr, mpz_srcptr, unsigned long);
+    void (*mul_2exp)(mpz_ptr, mpz_srcptr, unsigned long);
+    void (*tdiv_q)(mpz_ptr, mpz_srcptr, mpz_srcptr);
     bool ok = false;
 };
 
@@ -88,6 +90,8 @@ const Gmp *gmp() {
         get(g.mul_si, "__gmpz_mul_si");
         get(g.addmul_ui, "__gmpz_addmul_ui");
         get(g.submul_ui, "__gmpz_submul_ui");
+        get(g.mul_2exp, "__gmpz_mul_2exp");
+        get(g.tdiv_q, "__gmpz_tdiv_q");
         g.ok = all;
     });
     return g.ok ? &g : nullptr;
@@ -217,6 +221,15 @@ int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, in
     for (int j = 0; j <= levels; j++)
         if ((steps >> j) & 1) g->mul(&Pm, Pm.c(), &pw[j]);
     g->fdiv_q_2exp(&half, Pm.c(), 1);  // (P^m - 1) / 2, P odd
+    // Barrett reduction by P^m for y = D X with |X| <= (P^m - 1)/2 < 2^(L-1): the quotient is
+    // below 2^kd (kd = bits of D), and mu = floor(2^(L+kd+1) / P^m) has kd + 2 bits, so the
+    // estimate floor(floor(|y| / 2^(L-1)) mu / 2^(kd+2)) is at most the quotient and a few short
+    const unsigned long L = (unsigned long)g->sizeinbase(Pm.c(), 2);
+    const unsigned long kd = (unsigned long)g->sizeinbase(Dz.c(), 2);
+    Z mu(g);
+    g->set_ui(&mu, 1);
+    g->mul_2exp(&mu, mu.c(), L + kd + 1);
+    g->tdiv_q(&mu, mu.c(), Pm.c());
 
     int nt = threads ? threads : (int)std::min<unsigned>(std::max(1u, std::thread::hardware_concurrency()), 16u);
     nt = (int)std::max<int64_t>(1, std::min<int64_t>(nt, n_index));
@@ -243,8 +256,16 @@ int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, in
                 n = (n + 1) / 2;
             }
             // w = D X mod P^m, balanced
-            g->mul(&w, Dz.c(), &v[0]);
-            g->fdiv_r(&w, w.c(), Pm.c());
+            const bool neg = sign(&v[0]) < 0;
+            if (neg) g->neg(&v[0], &v[0]);
+            g->mul(&w, Dz.c(), &v[0]);                  // |y|
+            g->fdiv_q_2exp(&tmp, w.c(), L - 1);
+            g->mul(&tmp, tmp.c(), mu.c());
+            g->fdiv_q_2exp(&tmp, tmp.c(), kd + 2);
+            g->mul(&tmp, tmp.c(), Pm.c());
+            g->sub(&w, w.c(), tmp.c());
+            while (g->cmp(w.c(), Pm.c()) >= 0) g->sub(&w, w.c(), Pm.c());
+            if (neg && sign(w.c()) != 0) g->sub(&w, Pm.c(), w.c());
             if (g->cmp(w.c(), half.c()) > 0) g->sub(&w, w.c(), Pm.c());
             int64_t *out = num + t * w_limbs;
             if (g->cmpabs(w.c(), Bz.c()) <= 0) {

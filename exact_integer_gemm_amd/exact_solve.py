@@ -98,16 +98,20 @@ def _ceil_sqrt(v: int) -> int:
 def _bounds(A: np.ndarray, b: np.ndarray):
     """Hadamard: |det A| <= prod of row norms; a Cramer numerator replaces a
     column by one of b, so each of its rows is bounded by sqrt(|a_i|^2 + b_ik^2)."""
-    rows2 = [sum(int(v) * int(v) for v in row) for row in A.tolist()]
-    D = 1
-    for r2 in rows2:
-        D *= _ceil_sqrt(r2)
+    n = A.shape[0]
+    big = max([max(int(x.max()), -int(x.min())) for x in (A, b) if x.size] or [0])
+    if (n + 1) * big * big < 1 << 63:           # the squared norms are exact in int64
+        A64 = A.astype(np.int64, copy=False)
+        b64 = b.astype(np.int64, copy=False)
+        rows2 = np.einsum("ij,ij->i", A64, A64).tolist()
+        b2 = (b64 * b64).tolist()
+    else:
+        rows2 = [sum(int(v) * int(v) for v in row) for row in A.tolist()]
+        b2 = [[int(v) * int(v) for v in row] for row in b.tolist()]
+    D = math.prod(_ceil_sqrt(r2) for r2 in rows2)
     N = 1
     for k in range(b.shape[1]):
-        Nk = 1
-        for i, r2 in enumerate(rows2):
-            Nk *= _ceil_sqrt(r2 + int(b[i, k]) ** 2)
-        N = max(N, Nk)
+        N = max(N, math.prod(_ceil_sqrt(r2 + b2[i][k]) for i, r2 in enumerate(rows2)))
     return N, max(D, 1)
 
 
