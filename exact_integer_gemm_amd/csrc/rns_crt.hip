@@ -26,7 +26,7 @@ namespace rns {
 // even, so q = 2 gives u = t for t in {0, 1}).
 __device__ __forceinline__ int reduce_small(int t, int q, float inv) {
     const int k = __float_as_int(__builtin_fmaf((float)t, inv, kRoundMagic32)) - 0x4b400000;
-    return t - q * k;
+    return __mul24(k, -q) + t;                // |k| < 2^15, q <= 256: 24-bit operands
 }
 
 // The value x of the lane in the other half-wave (lane l xor 32), by
@@ -39,11 +39,14 @@ __device__ __forceinline__ uint32_t partner_u32(uint32_t x, int h) {
 
 // pair_stores: C is 16-byte aligned and c_limbs is even, so the two limbs
 // of a lane leave as one 16-byte store
-template <int KS, int NB>
+// OFF32: every Y byte lies within 2^32 of y, so addresses are 32-bit offsets
+// from the (uniform) base.
+template <int KS, int NB, bool OFF32, bool ROWS>
 __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
                                                   const int8_t *__restrict__ y, int64_t y_plane,
                                                   int64_t y_pitch, int64_t M, int64_t N,
                                                   int64_t *__restrict__ C, int c_limbs, int pair_stores) {
+    constexpr bool rows_mode = ROWS;
     constexpr int W = 8 * NB;                 // 32-bit words of X'
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -73,6 +76,7 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
     // this lane's slot constants
     int sq[KS][16], sw[KS][16], plane[KS][16];
     float si[KS][16];
+    uint32_t poff[KS][16];
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
 #pragma unroll
@@ -83,6 +87,7 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
             si[ks][b] = h ? cc.inv[k1] : cc.inv[k0];
             const int k = h ? k1 : k0;
             plane[ks][b] = k < cc.n ? k : cc.n - 1;   // padding slots read a valid plane, weight 0
+            poff[ks][b] = OFF32 ? (uint32_t)(plane[ks][b] * y_plane) : 0u;
         }
     // a modulus 256 (always slot 0, the largest) can round to u = 128, whose
     // int8 byte reads as -128: its quotient term must use the byte's value
@@ -90,14 +95,42 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
     const int rk = cc.n;                      // the -r slot
     const int rks = rk >> 5, rh = (rk >> 4) & 1, rb = rk & 15;
 
+    // rows mode (wide rows): a wave takes 32 consecutive columns of one row at
+    // a time, and the row and column group advance by the grid stride without
+    // a division per step.  Otherwise 32 consecutive entries of the flattened
+    // output, the row found by one division (32-bit when the count allows).
     const int64_t total = M * N;
-    const int64_t groups = (total + 31) >> 5;
-    for (int64_t grp = (int64_t)blockIdx.x * 4 + wave; grp < groups; grp += (int64_t)gridDim.x * 4) {
-        const int64_t e = grp * 32 + l32;
-        const bool ok = e < total;
-        const int64_t ee = ok ? e : total - 1;
-        const int64_t i = ee / N, j = ee - i * N;
+    const int64_t cgs = rows_mode ? (N + 31) >> 5 : 1;        // column groups per row
+    const int64_t groups = rows_mode ? M * cgs : (total + 31) >> 5;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    const int64_t g0 = (int64_t)blockIdx.x * 4 + wave;
+    int64_t row = g0 / cgs, cg = g0 - row * cgs;
+    const int64_t drow = stride / cgs, dcg = stride - drow * cgs;
+    const bool small = total < (1ll << 32);
+    for (int64_t grp = g0; grp < groups; grp += stride) {
+        bool ok;
+        int64_t i, j;
+        if (rows_mode) {
+            const int64_t jj = cg * 32 + l32;
+            ok = jj < N;
+            j = ok ? jj : N - 1;
+            i = row;
+            row += drow;
+            cg += dcg;
+            if (cg >= cgs) {
+                cg -= cgs;
+                row++;
+            }
+        } else {
+            const int64_t e0 = grp * 32 + l32;
+            ok = e0 < total;
+            const int64_t ee = ok ? e0 : total - 1;
+            i = small ? (int64_t)((uint32_t)ee / (uint32_t)N) : ee / N;
+            j = ee - i * N;
+        }
+        const int64_t e = i * N + j;
         const int8_t *yp = y + i * y_pitch + j;
+        const uint32_t yo = OFF32 ? (uint32_t)(i * y_pitch + j) : 0u;
 
         float f = 0.0f;
         v4i ua[KS];
@@ -106,7 +139,8 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
             int byte[16];
 #pragma unroll
             for (int b = 0; b < 16; b++) {
-                const int t = (int)yp[plane[ks][b] * y_plane] * sw[ks][b];
+                const int yv = OFF32 ? (int)y[yo + poff[ks][b]] : (int)yp[plane[ks][b] * y_plane];
+                const int t = __mul24(yv, sw[ks][b]);   // |y| <= 128, w < 256
                 int u = reduce_small(t, sq[ks][b], si[ks][b]);
                 if (ks == 0 && b == 0) u = (wrap0 && h == 0) ? (int)(int8_t)u : u;
                 f = __builtin_fmaf((float)u, si[ks][b], f);
@@ -234,19 +268,39 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
     if (total == 0) return RNS_OK;
     if (c.n < 1 || c.n + 1 > 32 * ksteps || ksteps < 1 || ksteps > 2 || nblocks < 1 || nblocks > 2)
         return RNS_E_ARG;
-    const int64_t groups = (total + 31) / 32;
+    // rows mode when whole 32-column groups waste little: N a multiple of 32, or N >= 256
+    const int rows = (N % 32 == 0 || N >= 256) ? 1 : 0;
+    const int64_t groups = rows ? M * ((N + 31) / 32) : (total + 31) / 32;
     int64_t grid = (groups + 3) / 4;
     if (grid > 1536) grid = 1536;             // grid-stride: each wave amortises its set-up
     const dim3 g((unsigned)grid), b(256);
     const int pairs = (reinterpret_cast<uintptr_t>(C) % 16 == 0 && c_limbs % 2 == 0) ? 1 : 0;
+    // the Y planes span y_plane * n bytes from y
+    const bool off32 = (uint64_t)y_plane * (uint64_t)c.n < (1ull << 32);
+#define RNS_CRT_LAUNCH(KS, NB)                                                                              \
+    do {                                                                                                    \
+        if (off32 && rows)                                                                                  \
+            hipLaunchKernelGGL((crt_kernel<KS, NB, true, true>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, \
+                               C, c_limbs, pairs);                                                          \
+        else if (off32)                                                                                     \
+            hipLaunchKernelGGL((crt_kernel<KS, NB, true, false>), g, b, 0, s, c, d, y, y_plane, y_pitch, M,  \
+                               N, C, c_limbs, pairs);                                                       \
+        else if (rows)                                                                                      \
+            hipLaunchKernelGGL((crt_kernel<KS, NB, false, true>), g, b, 0, s, c, d, y, y_plane, y_pitch, M,  \
+                               N, C, c_limbs, pairs);                                                       \
+        else                                                                                                \
+            hipLaunchKernelGGL((crt_kernel<KS, NB, false, false>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, \
+                               N, C, c_limbs, pairs);                                                       \
+    } while (0)
     if (ksteps == 1 && nblocks == 1)
-        hipLaunchKernelGGL((crt_kernel<1, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs);
+        RNS_CRT_LAUNCH(1, 1);
     else if (ksteps == 1)
-        hipLaunchKernelGGL((crt_kernel<1, 2>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs);
+        RNS_CRT_LAUNCH(1, 2);
     else if (nblocks == 1)
-        hipLaunchKernelGGL((crt_kernel<2, 1>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs);
+        RNS_CRT_LAUNCH(2, 1);
     else
-        hipLaunchKernelGGL((crt_kernel<2, 2>), g, b, 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs);
+        RNS_CRT_LAUNCH(2, 2);
+#undef RNS_CRT_LAUNCH
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 
