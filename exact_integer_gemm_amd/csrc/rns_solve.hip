@@ -13,6 +13,7 @@ struct GjConsts {
     int32_t n_primes;
     uint32_t q[kMaxPrimes];
     uint32_t mq[kMaxPrimes];
+    float inv[kMaxPrimes];     // fl(1/q) in binary32
 };
 
 // t mod q for t < 2^32: qh = floor(t * floor(2^32/q) / 2^32) is floor(t/q) or
@@ -20,6 +21,17 @@ struct GjConsts {
 __device__ __forceinline__ uint32_t barrett(uint32_t t, uint32_t q, uint32_t mq) {
     const uint32_t r = t - __umulhi(t, mq) * q;
     return r >= q ? r - q : r;
+}
+
+// t mod q in [0, q) for |t| < 2^22, with full-rate operations only (Barrett's
+// 32-bit high and low products are quarter-rate): the nearest integer k to
+// t/q by one binary32 rounding step (fma with 1.5 * 2^23; |t/q| * 2^-24 <
+// 1/(4q) keeps it exact, t/q being at least 1/(2q) from a half-integer), then
+// t - q k in [-(q-1)/2, (q-1)/2] by a 24-bit multiply-add, then + q if negative.
+__device__ __forceinline__ uint32_t mod_q(int t, int q, float inv) {
+    const int k = __float_as_int(__builtin_fmaf((float)t, inv, kRoundMagic32)) - 0x4b400000;
+    const int r = __mul24(k, -q) + t;
+    return (uint32_t)(r < 0 ? r + q : r);
 }
 
 __global__ __launch_bounds__(64) void zero_i32_kernel(int32_t *__restrict__ p, int64_t count) {
@@ -132,8 +144,8 @@ __global__ __launch_bounds__(64) void gj_update_kernel(GjConsts gc, uint8_t *__r
     const int64_t i = row - (int64_t)e * n;
     if (singular[e]) return;
     const int64_t p = pivrow[e];
-    const uint32_t q = gc.q[e], mq = gc.mq[e];
-    const uint32_t qq = q * q;
+    const uint32_t q = gc.q[e];
+    const float qf = gc.inv[e];
     const uint32_t m = (i == p) ? mcol[(int64_t)e * n + k] : mcol[(int64_t)e * n + i];
     if (i != k && m == 0) return;
     uint8_t *Wr = W + (int64_t)e * n * pitch + i * pitch;
@@ -153,7 +165,7 @@ __global__ __launch_bounds__(64) void gj_update_kernel(GjConsts gc, uint8_t *__r
 #pragma unroll
             for (int b = 0; b < 4; b++) {
                 const uint32_t a = (wv[w] >> (8 * b)) & 0xffu, c = (pv[w] >> (8 * b)) & 0xffu;
-                o |= barrett(a + qq - m * c, q, mq) << (8 * b);
+                o |= mod_q((int)a - (int)(m * c), (int)q, qf) << (8 * b);
             }
             out[w] = o;
         }
@@ -197,7 +209,8 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
     const int e = blockIdx.x;
     if (singular[e]) return;
     const int t = threadIdx.x;
-    const uint32_t q = gc.q[e], mq = gc.mq[e], qq = q * q;
+    const uint32_t q = gc.q[e], mq = gc.mq[e];
+    const float qf = gc.inv[e];
     const uint8_t *We = W + (int64_t)e * n * pitch;
     uint8_t *lb = reinterpret_cast<uint8_t *>(rows);
 
@@ -219,11 +232,17 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
 
     for (int j = 0; j < bw; j++) {
         const int64_t r0 = kb + j;
-        // the first row at or below r0 with a nonzero entry in column j
-        int32_t mine = (int32_t)n;
-        for (int64_t i = r0 + t; i < n; i += 1024)
-            if (lb[i * S + j]) { mine = (int32_t)i; break; }
-        if (mine < n) atomicMin(&piv_sh[j & 1], mine);
+        // the first row at or below r0 with a nonzero entry in column j: each
+        // wave finds its first by a ballot over rows r0 + 1024 it + t, and
+        // one lane per wave meets the others in an LDS minimum
+        for (int64_t base = r0; base < n; base += 1024) {
+            const int64_t i = base + t;
+            const uint64_t m = __ballot(i < n && lb[i * S + j] != 0);
+            if (m) {
+                if ((t & 63) == 0) atomicMin(&piv_sh[j & 1], (int32_t)(base + (t & ~63) + __ffsll((long long)m) - 1));
+                break;
+            }
+        }
         if (t == 0) piv_sh[(j + 1) & 1] = (int32_t)n;      // read last at step j - 1, before the barrier above
         __syncthreads();
         const int64_t p = piv_sh[j & 1];
@@ -245,7 +264,7 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
             if (t == (B + j) / 4) x |= 1u << (8 * ((B + j) % 4));
             uint32_t o = 0;
 #pragma unroll
-            for (int b = 0; b < 4; b++) o |= barrett(((x >> (8 * b)) & 0xffu) * inv, q, mq) << (8 * b);
+            for (int b = 0; b < 4; b++) o |= mod_q((int)(((x >> (8 * b)) & 0xffu) * inv), (int)q, qf) << (8 * b);
             if (p != r0) rows[p * (S / 4) + t] = y;
             rows[r0 * (S / 4) + t] = o;
             if (t == 0 && p != r0) {
@@ -268,7 +287,7 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
 #pragma unroll
             for (int b = 0; b < 4; b++) {
                 const uint32_t a = (wv >> (8 * b)) & 0xffu, c = (pv >> (8 * b)) & 0xffu;
-                o |= barrett(a + qq - f * c, q, mq) << (8 * b);
+                o |= mod_q((int)a - (int)(f * c), (int)q, qf) << (8 * b);
             }
             // bytes of columns <= j stay: column j holds f, which the other threads of this row read
             const int keep = j + 1 - 4 * d;
@@ -338,7 +357,8 @@ __global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8
     const int64_t i0 = (tile / col_tiles) * 64;
     const int64_t c0 = cs + (tile % col_tiles) * 256;
     const int t = threadIdx.x, cg = t & 63, rg = t >> 6;
-    const uint32_t q = gc.q[e], mq = gc.mq[e];
+    const uint32_t q = gc.q[e];
+    const float qf = gc.inv[e];
     const int8_t *Xe = Xb + (int64_t)e * n * B;
     const int8_t *Re = Rb + (int64_t)e * B * pitch;
     const int64_t c = c0 + 4 * cg;
@@ -379,7 +399,6 @@ __global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8
         }
     }
     if (!col_ok) return;
-    const uint32_t off = q * ((1u << 21) / q + 1);   // > |acc| + 255, keeps the sum positive
     uint8_t *We = W + (int64_t)e * n * pitch;
     const uint8_t *Oe = Oc + (int64_t)e * B * pitch;
 #pragma unroll
@@ -401,7 +420,7 @@ __global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8
         for (int k = 0; k < 4; k++) {
             const uint32_t sb = (s >> (8 * k)) & 0xffu;
             const int sv = sgn ? (int)(int8_t)sb : (int)sb;
-            o |= barrett((uint32_t)(acc[r][k] + sv + (int)off), q, mq) << (8 * k);
+            o |= mod_q(acc[r][k] + sv, (int)q, qf) << (8 * k);
         }
         *reinterpret_cast<uint32_t *>(We + i * pitch + c) = o;
     }
@@ -560,6 +579,7 @@ GjConsts gj_consts(const int32_t *primes, int32_t E) {
     for (int e = 0; e < E; e++) {
         gc.q[e] = (uint32_t)primes[e];
         gc.mq[e] = (uint32_t)((1ull << 32) / (uint64_t)primes[e]);
+        gc.inv[e] = 1.0f / (float)primes[e];
     }
     return gc;
 }
