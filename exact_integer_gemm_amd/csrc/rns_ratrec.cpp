@@ -279,7 +279,13 @@ int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, in
         for (auto &z : v) g->clear(&z);
     };
     std::vector<std::thread> pool;
-    for (int i = 1; i < nt; i++) pool.emplace_back(work);
+    for (int i = 1; i < nt; i++) {
+        try {
+            pool.emplace_back(work);
+        } catch (...) {          // no more threads to be had: the ones running share the rest
+            break;
+        }
+    }
     work();
     for (auto &th : pool) th.join();
     for (auto &z : pw) g->clear(&z);

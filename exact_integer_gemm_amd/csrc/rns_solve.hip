@@ -2,6 +2,9 @@
 // batched modular inverse by Gauss-Jordan elimination over every prime at
 // once, and the Dixon lift (the batched residue product of rns_gemm plus the
 // residual update in one limb).
+#include <cstring>
+#include <vector>
+
 #include "rns_device.h"
 #include "../../include/rns_solve.h"
 
@@ -490,6 +493,176 @@ __global__ __launch_bounds__(256) void lift_residual_kernel(const int64_t *__res
     }
 }
 
+// ---- fused lift step (n a multiple of 16, at most kFusedCols right-hand sides) ----
+// One wave per row i of B = A^-1 mod P.  Digit kernel: the wave's lanes split
+// the columns k in 16-byte runs and form, for every prime at once, the dot
+// products of row i of the inverse plane with the residues of r mod that
+// prime (`v_dot4_i32_i8`); the partial sums meet in LDS, lane e reduces prime
+// e's sum mod q_e, and the wave rebuilds the digit by the rounded-quotient CRT
+// (X = sum_e u_e M_e - r P, u_e = y_e (M_e^-1 mod q_e) balanced, r the nearest
+// integer to sum_e u_e / q_e, one exact correction by P), written as the
+// digit's limbs and, apart, its low limb.  Update kernel: r <- (r - A x_low)
+// P^-1 mod 2^64 with the wave's row sum, then the new residues of r mod every
+// prime for the next digit.  Two launches per step in place of the split, the
+// per-prime product, the CRT and the residual update.
+constexpr int kFusedCols = 4;
+constexpr int kLiftChunks = 11;       // 32-bit chunks of P: up to 352 bits
+
+struct LiftConsts {
+    int32_t E;                        // moduli
+    int32_t nch;                      // chunks of P in use
+    int32_t q[kMaxPrimes];
+    int32_t w[kMaxPrimes];            // (P / q)^-1 mod q, balanced
+    uint32_t M[kMaxPrimes][kLiftChunks];   // P / q, little-endian chunks
+    uint32_t P[kLiftChunks];
+};
+
+// the balanced residue of a signed 64-bit value mod q (odd q < 256)
+__device__ __forceinline__ int residue_i64(int64_t v, int q) {
+    const double inv = 1.0 / (double)q;
+    const int hi = (int)(v >> 32);
+    const uint32_t lo = (uint32_t)v;
+    const int rh = hi - q * (int)__builtin_rint((double)hi * inv);
+    const int rl = (int)((double)lo - (double)q * __builtin_rint((double)lo * inv));
+    const int two16 = (1 << 16) % q, two32 = (two16 * two16) % q;
+    const int t = rh * two32 + rl;                       // |t| < 2^16
+    return t - q * (int)__builtin_rintf((float)t / (float)q);
+}
+
+__global__ __launch_bounds__(256) void lift_digit_kernel(LiftConsts lc, const int8_t *__restrict__ Binv, int64_t n,
+                                                         int64_t c, const int8_t *__restrict__ rres, int64_t npad,
+                                                         int64_t *__restrict__ digits, int dl,
+                                                         int64_t *__restrict__ xlow) {
+    __shared__ int32_t part[4][64][kMaxPrimes + 1];
+    __shared__ int32_t uu[4][kMaxPrimes];
+    __shared__ float fs[4][kMaxPrimes];
+    __shared__ int64_t ss[4][kLiftChunks];
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + wv;
+    const bool row_ok = i < n;
+    const int E = lc.E;
+    const int64_t runs = npad / 16;
+    for (int64_t cc = 0; cc < c; cc++) {
+        // eight moduli at a time: 8 partial sums and 16 loads in flight per lane
+        for (int e0 = 0; e0 < E; e0 += 8) {
+            int acc[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) acc[u] = 0;
+            if (row_ok) {
+                for (int64_t run = l; run < runs; run += 64) {
+#pragma unroll
+                    for (int u = 0; u < 8; u++) {
+                        const int e = e0 + u;
+                        if (e < E) {
+                            const v4i a = *(const v4i *)(Binv + ((int64_t)e * n + i) * n + 16 * run);
+                            const v4i x = *(const v4i *)(rres + ((int64_t)e * c + cc) * npad + 16 * run);
+                            int s = acc[u];
+#pragma unroll
+                            for (int w4 = 0; w4 < 4; w4++) s = __builtin_amdgcn_sdot4(a[w4], x[w4], s, false);
+                            acc[u] = s;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                if (e0 + u < E) part[wv][l][e0 + u] = acc[u];
+        }
+        __syncthreads();
+        if (l < E) {
+            int64_t t = 0;                                  // |t| < 2^31 (n <= 2^17, |entries| < 128)
+            for (int j = 0; j < 64; j++) t += part[wv][j][l];
+            const int q = lc.q[l];
+            const int y = (int)(t - (int64_t)q * (int64_t)__builtin_rint((double)t / (double)q));
+            const int yw = y * lc.w[l];                      // |yw| < 2^14
+            const int u = yw - q * (int)__builtin_rintf((float)yw / (float)q);
+            uu[wv][l] = u;
+            fs[wv][l] = (float)u / (float)q;
+        }
+        __syncthreads();
+        if (l < lc.nch) {
+            int64_t s = 0;                                  // |s| < 2^45
+            for (int e = 0; e < E; e++) s += (int64_t)uu[wv][e] * (int64_t)lc.M[e][l];
+            ss[wv][l] = s;
+        }
+        __syncthreads();
+        if (l == 0 && row_ok) {
+            float f = 0.0f;
+            for (int e = 0; e < E; e++) f += fs[wv][e];
+            const int64_t r = (int64_t)__builtin_rintf(f);
+            // X = sum - r P in 32-bit chunks with a sign word
+            uint32_t x[kLiftChunks];
+            int64_t carry = 0;
+            for (int j = 0; j < kLiftChunks; j++) {
+                const int64_t v = (j < lc.nch ? ss[wv][j] - r * (int64_t)lc.P[j] : 0) + carry;
+                x[j] = (uint32_t)v;
+                carry = v >> 32;
+            }
+            // one exact correction: X > P/2 <=> 2X - P > 0; X < -P/2 <=> 2X + P < 0 (P odd)
+            for (int pass = 0; pass < 2; pass++) {
+                int64_t bm = 0, bp = 0;
+                uint32_t nzm = 0;
+                for (int j = 0; j < kLiftChunks; j++) {
+                    const uint32_t two = (x[j] << 1) | (j ? x[j - 1] >> 31 : 0u);
+                    const int64_t dm = (int64_t)two - (int64_t)lc.P[j] + bm;
+                    const int64_t dp = (int64_t)two + (int64_t)lc.P[j] + bp;
+                    nzm |= (uint32_t)dm;
+                    bm = dm >> 32;
+                    bp = dp >> 32;
+                }
+                const int64_t top2 = 2 * carry + (int64_t)(x[kLiftChunks - 1] >> 31);
+                const bool above = top2 + bm > 0 || (top2 + bm == 0 && nzm != 0);
+                const bool below = top2 + bp < 0;
+                if (!above && !below) break;
+                int64_t c2 = 0;
+                for (int j = 0; j < kLiftChunks; j++) {
+                    c2 += (int64_t)x[j] + (above ? -(int64_t)lc.P[j] : (int64_t)lc.P[j]);
+                    x[j] = (uint32_t)c2;
+                    c2 >>= 32;
+                }
+                carry += c2;
+            }
+            int64_t *dst = digits + (i * c + cc) * dl;
+            const uint32_t sgn = (uint32_t)carry;
+            for (int li = 0; li < dl; li++) {
+                const uint32_t lo = 2 * li < kLiftChunks ? x[2 * li] : sgn;
+                const uint32_t hi = 2 * li + 1 < kLiftChunks ? x[2 * li + 1] : sgn;
+                dst[li] = (int64_t)(((uint64_t)hi << 32) | lo);
+            }
+            xlow[cc * n + i] = (int64_t)(((uint64_t)x[1] << 32) | x[0]);
+        }
+        __syncthreads();
+    }
+}
+
+// r <- (r - A x_low) P^-1 mod 2^64 per row (first: r <- b), then the residues of
+// the new r mod every modulus into rres[e][cc][i].
+__global__ __launch_bounds__(256) void lift_update_kernel(LiftConsts lc, const int64_t *__restrict__ A, int64_t n,
+                                                          int64_t c, const int64_t *__restrict__ xlow,
+                                                          int64_t *__restrict__ r, uint64_t p_inv,
+                                                          int8_t *__restrict__ rres, int64_t npad, int first,
+                                                          const int64_t *__restrict__ b) {
+    const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int64_t i = (int64_t)blockIdx.x * 4 + wv;
+    if (i >= n) return;                                   // no barriers below
+    for (int64_t cc = 0; cc < c; cc++) {
+        int64_t v;
+        if (first) {
+            v = b[i * c + cc];
+        } else {
+            uint64_t s = 0;
+            for (int64_t k = l; k < n; k += 64) s += (uint64_t)A[i * n + k] * (uint64_t)xlow[cc * n + k];
+            for (int off = 32; off > 0; off >>= 1) {
+                const uint32_t lo = __shfl_xor((uint32_t)s, off), hi = __shfl_xor((uint32_t)(s >> 32), off);
+                s += ((uint64_t)hi << 32) | lo;
+            }
+            v = (int64_t)(((uint64_t)r[i * c + cc] - s) * p_inv);
+        }
+        if (l == 0) r[i * c + cc] = v;
+        if (l < lc.E) rres[((int64_t)l * c + cc) * npad + i] = (int8_t)residue_i64(v, lc.q[l]);
+    }
+}
+
 }  // namespace rns
 
 using namespace rns;
@@ -582,6 +755,53 @@ GjConsts gj_consts(const int32_t *primes, int32_t E) {
         gc.inv[e] = 1.0f / (float)primes[e];
     }
     return gc;
+}
+
+// The constants of the fused lift step: q, (P/q)^-1 mod q (balanced) and the
+// 32-bit chunks of P/q and P.  False when P needs more than kLiftChunks chunks.
+bool lift_consts(const rns_plan_t &pl, LiftConsts &lc) {
+    std::memset(&lc, 0, sizeof(lc));
+    const int E = pl.n_primes;
+    lc.E = E;
+    auto mul = [](std::vector<uint32_t> &v, uint32_t m) {
+        uint64_t carry = 0;
+        for (auto &x : v) {
+            const uint64_t t = (uint64_t)x * m + carry;
+            x = (uint32_t)t;
+            carry = t >> 32;
+        }
+        if (carry) v.push_back((uint32_t)carry);
+    };
+    std::vector<uint32_t> P{1u};
+    for (int e = 0; e < E; e++) mul(P, (uint32_t)pl.primes[e]);
+    if ((int)P.size() > kLiftChunks) return false;
+    lc.nch = (int)P.size();
+    for (int j = 0; j < lc.nch; j++) lc.P[j] = P[j];
+    for (int e = 0; e < E; e++) {
+        const int q = pl.primes[e];
+        std::vector<uint32_t> M{1u};
+        int64_t m_mod = 1;
+        for (int f = 0; f < E; f++)
+            if (f != e) {
+                mul(M, (uint32_t)pl.primes[f]);
+                m_mod = m_mod * pl.primes[f] % q;
+            }
+        for (int j = 0; j < (int)M.size() && j < kLiftChunks; j++) lc.M[e][j] = M[j];
+        int64_t inv = 1;
+        {
+            // m_mod^-1 mod q by extended Euclid (q need not be prime)
+            int64_t a = m_mod, bq = q, x0 = 1, x1 = 0;
+            while (bq) {
+                const int64_t t = a / bq;
+                int64_t tmp = a - t * bq; a = bq; bq = tmp;
+                tmp = x0 - t * x1; x0 = x1; x1 = tmp;
+            }
+            inv = ((x0 % q) + q) % q;
+        }
+        lc.q[e] = q;
+        lc.w[e] = (int32_t)(inv > q / 2 ? inv - q : inv);
+    }
+    return true;
 }
 
 unsigned grid_for(int64_t count) {
@@ -679,6 +899,30 @@ int rns_dixon_lift(const rns_plan_t *plan, int64_t n, int64_t c, const int8_t *B
     for (int j = 0; j < plan->n_primes; j++) P *= (uint64_t)plan->primes[j];
     uint64_t inv = P;
     for (int it = 0; it < 6; it++) inv *= 2 - P * inv;
+    if (steps > 0 && c <= kFusedCols && n % 16 == 0) {
+        LiftConsts lc;
+        if (lift_consts(*plan, lc)) {
+            const int64_t r_bytes = pad256(n * c * 8), x_bytes = pad256(n * c * 8);
+            const int64_t need_fused = r_bytes + x_bytes + (int64_t)lc.E * c * n;
+            if ((int64_t)ws_bytes >= need_fused) {
+                uint8_t *base = static_cast<uint8_t *>(ws);
+                int64_t *r = reinterpret_cast<int64_t *>(base);
+                int64_t *xlow = reinterpret_cast<int64_t *>(base + r_bytes);
+                int8_t *rres = reinterpret_cast<int8_t *>(base + r_bytes + x_bytes);
+                const unsigned grid = (unsigned)((n + 3) / 4);
+                hipLaunchKernelGGL(lift_update_kernel, dim3(grid), dim3(256), 0, stream, lc, A, n, c, xlow, r, inv,
+                                   rres, n, 1, b);
+                for (int st = 0; st < steps; st++) {
+                    int64_t *xs = digits + (int64_t)st * n * c * d_limbs;
+                    hipLaunchKernelGGL(lift_digit_kernel, dim3(grid), dim3(256), 0, stream, lc, Binv, n, c, rres, n,
+                                       xs, d_limbs, xlow);
+                    hipLaunchKernelGGL(lift_update_kernel, dim3(grid), dim3(256), 0, stream, lc, A, n, c, xlow, r,
+                                       inv, rres, n, 0, b);
+                }
+                return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
+            }
+        }
+    }
     int64_t *r = static_cast<int64_t *>(ws);
     int8_t *gws = static_cast<int8_t *>(ws) + pad256(n * c * 8);
     const size_t gbytes = ws_bytes - (size_t)pad256(n * c * 8);

@@ -274,6 +274,10 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
     n = A.shape[0]
     if A.shape != (n, n) or b.shape[0] != n:
         raise ValueError("A must be [n, n] and b [n, c]")
+    if b.shape[1] == 0:
+        raise ValueError("b needs at least one column")
+    if n == 0:
+        return ([], {"primes": [], "steps": 0, "numerators": [], "denominator": 1}) if return_info else []
     An = A.cpu().numpy()
     bn = b.cpu().numpy()
     amax = int(np.abs(An.astype(object)).max()) if n else 0

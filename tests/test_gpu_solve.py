@@ -59,8 +59,10 @@ def test_batched_inverse_matches_oracle():
         assert np.array_equal(planes[t], np.array(ref_bal, dtype=np.int8)), q
 
 
-def test_lift_digits_match_oracle():
-    n, c = 12, 3
+@pytest.mark.parametrize("n,c", [(12, 3), (32, 1), (48, 4), (32, 5), (16, 2)])
+def test_lift_digits_match_oracle(n, c):
+    """n a multiple of 16 with at most 4 right-hand sides takes the fused step (digit and update
+    kernels); the other shapes the batched residue product."""
     A, b = _system(2, n, c, 10 ** 6, 10 ** 6)
     singular, ws = rg.batched_inverse(dev(A))
     sel = [i for i, s in enumerate(singular.cpu().tolist()) if not s]
@@ -206,3 +208,11 @@ def test_batched_inverse_larger_sizes(n):
     sel = [i for i, s in enumerate(sing) if not s]
     planes = rg.inverse_planes(ws, n, sel).cpu().numpy()
     _check_inverses(A, planes, sel, (0, len(sel) - 1) if n > 4096 else (0, 1, len(sel) // 2, len(sel) - 1))
+
+
+def test_empty_and_degenerate_shapes():
+    assert rg.solve(dev(np.zeros((0, 0))), dev(np.zeros((0, 1)))) == []
+    with pytest.raises(ValueError):
+        rg.solve(dev(np.eye(3)), dev(np.zeros((3, 0))))
+    X = rg.solve(dev([[7]]), dev([[3, -14]]))          # 1 x 1, two right-hand sides
+    assert X == [[Fraction(3, 7), Fraction(-2)]]
