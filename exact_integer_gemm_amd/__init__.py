@@ -53,6 +53,12 @@ class _Plan(ctypes.Structure):
                 ("primes", ctypes.c_int32 * RNS_MAX_PRIMES)]
 
 
+class _SlicedPlan(ctypes.Structure):
+    _fields_ = [("slice", _Plan), ("a_limbs", ctypes.c_int32), ("b_limbs", ctypes.c_int32),
+                ("sa", ctypes.c_int32), ("sb", ctypes.c_int32), ("na", ctypes.c_int32), ("nb", ctypes.c_int32),
+                ("part_limbs", ctypes.c_int32), ("out_limbs_min", ctypes.c_int32)]
+
+
 class _Layout(ctypes.Structure):
     _fields_ = [("m_pad", ctypes.c_int64), ("n_pad", ctypes.c_int64), ("k_pad", ctypes.c_int64),
                 ("k_block", ctypes.c_int64), ("y_pitch", ctypes.c_int64),
@@ -126,6 +132,11 @@ def load() -> ctypes.CDLL:
         "rns_dixon_lift": (ctypes.c_int, [P, I64, I64, VP, VP, VP, I32, VP, I32, VP, SZ, VP]),
         "rns_round_outward": (ctypes.c_int, [VP, I64, I32, I32, I32, VP, VP, VP]),
         "rns_host_bigint_available": (ctypes.c_int, []),
+        "rns_sliced_plan": (ctypes.c_int, [I64, I32, I32, ctypes.POINTER(_SlicedPlan)]),
+        "rns_sliced_workspace_size": (ctypes.c_int, [ctypes.POINTER(_SlicedPlan), I64, I64, I64,
+                                                     ctypes.POINTER(SZ)]),
+        "rns_gemm_sliced": (ctypes.c_int, [ctypes.POINTER(_SlicedPlan), I64, I64, I64, VP, VP, VP, I32, VP,
+                                           SZ, VP]),
         "rns_padic_numerators": (ctypes.c_int, [VP, I32, I64, I32, VP, I64, VP, I32, VP, I32, VP, I32, VP,
                                                 I32, VP, I32]),
         "rns_rational_reconstruct": (ctypes.c_int, [VP, I32, VP, I32, VP, I32, VP, I32, VP, I32, VP, I32]),
@@ -397,3 +408,4 @@ from .enclose import (EnclosePlan, bmm_enclose, digest, enclose_plan, fp64_stats
                       fp64_to_limbs, mm_enclose, mm_enclose_nt, round_outward, width_ulps)
 from .exact_solve import (batched_inverse, dixon_lift, inverse_planes, plan_from_moduli,  # noqa: E402
                     solve)
+from .sliced import SlicedPlan, gemm_sliced, sliced_plan  # noqa: E402

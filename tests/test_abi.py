@@ -306,3 +306,24 @@ def test_enclose_plan_falls_back_to_prime_powers(lib):
     ep = rg.enclose_plan(64, _stats_of(A), _stats_of(B), 64)
     assert ep.c.plan.primes[0] == 256
     assert ep.c.a_bits + ep.c.b_bits + 7 > 335
+
+
+def test_sliced_plan_choices():
+    """Slice widths, counts and output limbs of the sliced product (host only)."""
+    import exact_integer_gemm_amd as rg
+    p = rg.sliced_plan(4096, 4, 4)
+    assert (p.sa, p.sb, p.na, p.nb) == (2, 2, 2, 2)
+    # a slice product spans 2 K 2^256 < P of its primes
+    assert p.slice.log2_P > 1 + 12 + 256
+    assert p.out_limbs_min == 9                 # 510 + 12 bits and a sign: 9 limbs
+    p = rg.sliced_plan(70, 4, 1)
+    assert (p.sa, p.sb, p.na, p.nb) == (3, 1, 2, 1)
+    p = rg.sliced_plan(1 << 17, 8, 8)
+    assert (p.na, p.nb, p.out_limbs_min) == (4, 4, 17)
+    for bad in ((-1, 4, 4), (8, 0, 4), (8, 4, 9)):
+        with pytest.raises(rg.RnsError) as e:
+            rg.sliced_plan(*bad)
+        assert e.value.code == -1
+    with pytest.raises(rg.RnsError) as e:
+        rg.sliced_plan((1 << 17) + 1, 4, 4)
+    assert e.value.code == -2
