@@ -340,7 +340,9 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
 }
 
 // W[i][c] <- W[perm(i)][c] + sum_j X[i][j] R[j][c] (mod q) for columns c >= cs:
-// 64 rows x 256 columns per block of 256 threads, 16 rows x 4 columns each.
+// 64 rows x 256 columns per block of 256 threads, 8 rows x 8 columns each (a
+// wave covers two row groups, 256 contiguous bytes of each row).  The eight
+// source words are fetched first, so that their latency overlaps the product.
 template <int B>
 __global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8_t *__restrict__ W, int64_t n,
                                                               int64_t pitch, int64_t kb, int bw, int64_t cs,
@@ -359,73 +361,85 @@ __global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8
     const int64_t tile = blockIdx.x - (int64_t)e * per;
     const int64_t i0 = (tile / col_tiles) * 64;
     const int64_t c0 = cs + (tile % col_tiles) * 256;
-    const int t = threadIdx.x, cg = t & 63, rg = t >> 6;
+    const int t = threadIdx.x, cg = t & 31, rg = t >> 5;
     const uint32_t q = gc.q[e];
     const float qf = gc.inv[e];
     const int8_t *Xe = Xb + (int64_t)e * n * B;
     const int8_t *Re = Rb + (int64_t)e * B * pitch;
-    const int64_t c = c0 + 4 * cg;
+    uint8_t *We = W + (int64_t)e * n * pitch;
+    const uint8_t *Oe = Oc + (int64_t)e * B * pitch;
+    const int64_t c = c0 + 8 * cg;
     const bool col_ok = c < pitch;
 
+    uint64_t src[8];
+    uint32_t piv = 0;                   // bit r: row r's source is a pivot row (balanced bytes)
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        const int64_t i = i0 + 8 * rg + r;
+        src[r] = 0;
+        if (i < n && col_ok) {
+            if (i >= kb && i < kb + bw) {
+                src[r] = *reinterpret_cast<const uint64_t *>(Re + (i - kb) * pitch + c);
+                piv |= 1u << r;
+            } else {
+                const int64_t pi = perm[(int64_t)e * n + i];
+                src[r] = (pi == i) ? *reinterpret_cast<const uint64_t *>(We + i * pitch + c)
+                                   : *reinterpret_cast<const uint64_t *>(Oe + (pi - kb) * pitch + c);
+            }
+        }
+    }
     for (int it = t; it < 64 * KC; it += 256) {
         const int r = it / KC, d = it - r * KC;
         xs[r][d] = (i0 + r < n) ? reinterpret_cast<const uint32_t *>(Xe + (i0 + r) * B)[d] : 0u;
     }
-    // R^T: four depth rows of this thread's four columns, transposed in registers
-    for (int jc = rg; jc < KC; jc += 4) {
-        uint32_t r4[4];
+    // R^T: four depth rows of this thread's eight columns, transposed in registers
+    for (int jc = rg; jc < KC; jc += 8) {
+        uint64_t r4[4];
 #pragma unroll
         for (int k = 0; k < 4; k++)
-            r4[k] = col_ok ? *reinterpret_cast<const uint32_t *>(Re + (int64_t)(4 * jc + k) * pitch + c) : 0u;
+            r4[k] = col_ok ? *reinterpret_cast<const uint64_t *>(Re + (int64_t)(4 * jc + k) * pitch + c) : 0ull;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {           // column k: byte r is depth row 4 jc + r
+        for (int k = 0; k < 8; k++) {           // column k: byte r is depth row 4 jc + r
             uint32_t v = 0;
 #pragma unroll
-            for (int r = 0; r < 4; r++) v |= ((r4[r] >> (8 * k)) & 0xffu) << (8 * r);
-            rt[jc][4 * cg + k] = v;
+            for (int r = 0; r < 4; r++) v |= (uint32_t)((r4[r] >> (8 * k)) & 0xffu) << (8 * r);
+            rt[jc][8 * cg + k] = v;
         }
     }
     __syncthreads();
-    int acc[16][4];
+    int acc[8][8];
 #pragma unroll
-    for (int r = 0; r < 16; r++)
+    for (int r = 0; r < 8; r++)
 #pragma unroll
-        for (int k = 0; k < 4; k++) acc[r][k] = 0;
+        for (int k = 0; k < 8; k++) acc[r][k] = 0;
 #pragma unroll
     for (int jc = 0; jc < KC; jc++) {
-        const v4u rv = *reinterpret_cast<const v4u *>(&rt[jc][4 * cg]);
+        const v4u r0 = *reinterpret_cast<const v4u *>(&rt[jc][8 * cg]);
+        const v4u r1 = *reinterpret_cast<const v4u *>(&rt[jc][8 * cg + 4]);
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int x = (int)xs[16 * rg + r][jc];
+        for (int r = 0; r < 8; r++) {
+            const int x = (int)xs[8 * rg + r][jc];
 #pragma unroll
-            for (int k = 0; k < 4; k++) acc[r][k] = __builtin_amdgcn_sdot4(x, (int)rv[k], acc[r][k], false);
+            for (int k = 0; k < 4; k++) {
+                acc[r][k] = __builtin_amdgcn_sdot4(x, (int)r0[k], acc[r][k], false);
+                acc[r][k + 4] = __builtin_amdgcn_sdot4(x, (int)r1[k], acc[r][k + 4], false);
+            }
         }
     }
     if (!col_ok) return;
-    uint8_t *We = W + (int64_t)e * n * pitch;
-    const uint8_t *Oe = Oc + (int64_t)e * B * pitch;
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-        const int64_t i = i0 + 16 * rg + r;
+    for (int r = 0; r < 8; r++) {
+        const int64_t i = i0 + 8 * rg + r;
         if (i >= n) break;
-        uint32_t s;
-        bool sgn = false;
-        if (i >= kb && i < kb + bw) {
-            s = *reinterpret_cast<const uint32_t *>(Re + (i - kb) * pitch + c);
-            sgn = true;
-        } else {
-            const int64_t pi = perm[(int64_t)e * n + i];
-            s = (pi == i) ? *reinterpret_cast<const uint32_t *>(We + i * pitch + c)
-                          : *reinterpret_cast<const uint32_t *>(Oe + (pi - kb) * pitch + c);
-        }
-        uint32_t o = 0;
+        const bool sgn = (piv >> r) & 1u;
+        uint64_t o = 0;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-            const uint32_t sb = (s >> (8 * k)) & 0xffu;
+        for (int k = 0; k < 8; k++) {
+            const uint32_t sb = (uint32_t)(src[r] >> (8 * k)) & 0xffu;
             const int sv = sgn ? (int)(int8_t)sb : (int)sb;
-            o |= mod_q(acc[r][k] + sv, (int)q, qf) << (8 * k);
+            o |= (uint64_t)mod_q(acc[r][k] + sv, (int)q, qf) << (8 * k);
         }
-        *reinterpret_cast<uint32_t *>(We + i * pitch + c) = o;
+        *reinterpret_cast<uint64_t *>(We + i * pitch + c) = o;
     }
 }
 
