@@ -11,9 +11,12 @@
  *     Gauss-Jordan elimination of the augmented matrix [A | I], one launch
  *     per elimination step spanning all primes, Barrett reduction in place of
  *     a hardware modulo;
- *   - the lift: per step, x_i = B r_i mod P as one batched INT8 product per
- *     prime with the wide digit assembled by rns_gemm_batched_residue, and the
- *     residual update in one limb as (r_i - A x_i) * P^-1 mod 2^64 (P odd).
+ *   - the lift: per step, x_i = B r_i mod P from one INT8 product per prime
+ *     and the wide digit by the CRT, and the residual update in one limb as
+ *     (r_i - A x_i) * P^-1 mod 2^64 (P odd).  For n a multiple of 16 and at
+ *     most 4 right-hand sides a step is two kernels (every prime's dot
+ *     products and the digit in one, the update and the next residues in the
+ *     other); otherwise it runs through rns_gemm_batched_residue.
  * The rational reconstruction of x mod P^m runs on the host (exact-solve,
  * "Method": a CPU stage), declared at the end of this header.
  *
@@ -86,9 +89,10 @@ int rns_lift_workspace_size(const rns_plan_t *plan, int64_t n, int64_t c, size_t
  * [plan->n_primes][n][n], the balanced residues of A^-1 mod each prime in
  * plan order (rns_inverse_planes).  digits: device int64
  * [steps][n][c][d_limbs], d_limbs >= plan->out_limbs_min: digit i is the
- * balanced representative of B r_i mod P.  Returns RNS_OK, RNS_E_ARG (also
- * for an even modulus), RNS_E_K, RNS_E_OUT_LIMBS, RNS_E_WORKSPACE or
- * RNS_E_HIP.
+ * balanced representative of B r_i mod P.  Both step forms give the same
+ * digits; ws (rns_lift_workspace_size bytes) holds the residual and the
+ * step's scratch.  Returns RNS_OK, RNS_E_ARG (also for an even modulus),
+ * RNS_E_K, RNS_E_OUT_LIMBS, RNS_E_WORKSPACE or RNS_E_HIP.
  */
 int rns_dixon_lift(const rns_plan_t *plan, int64_t n, int64_t c, const int8_t *Binv, const int64_t *A,
                    const int64_t *b, int32_t steps, int64_t *digits, int32_t d_limbs,
