@@ -190,51 +190,118 @@ extern "C" {
 
 int rns_host_bigint_available(void) { return gmp() ? 1 : 0; }
 
+}  // extern "C"
+
+namespace {
+
+// w = D X mod P^m in (-P^m/2, P^m/2) and the common-denominator test |w| <= bound,
+// shared by the two sources of X.  Barrett reduction by P^m for y = D X with
+// |X| <= (P^m - 1)/2 < 2^(L-1): the quotient is below 2^kd (kd = bits of D), and
+// mu = floor(2^(L+kd+1) / P^m) has kd + 2 bits, so the estimate
+// floor(floor(|y| / 2^(L-1)) mu / 2^(kd+2)) is at most the quotient and a few short.
+struct Numerators {
+    const Gmp *g;
+    Z Pz, Dz, Bz, Pm, half, mu;
+    unsigned long L = 0, kd = 0;
+    std::vector<Mpz> pw;     // P^(2^j), j <= levels
+    explicit Numerators(const Gmp *g_) : g(g_), Pz(g_), Dz(g_), Bz(g_), Pm(g_), half(g_), mu(g_) {}
+    ~Numerators() {
+        for (auto &z : pw) g->clear(&z);
+    }
+    void setup(const uint64_t *P, int32_t p_limbs, int32_t steps, const uint64_t *D, int32_t den_limbs,
+               const uint64_t *bound, int32_t b_limbs) {
+        from_mag(g, &Pz, P, p_limbs);
+        from_mag(g, &Dz, D, den_limbs);
+        from_mag(g, &Bz, bound, b_limbs);
+        int levels = 0;
+        while ((1LL << levels) < steps) levels++;
+        pw.resize((size_t)levels + 1);
+        for (auto &z : pw) g->init(&z);
+        g->set(&pw[0], Pz.c());
+        for (int j = 1; j <= levels; j++) g->mul(&pw[j], &pw[j - 1], &pw[j - 1]);
+        g->set_ui(&Pm, 1);
+        for (int j = 0; j <= levels; j++)
+            if ((steps >> j) & 1) g->mul(&Pm, Pm.c(), &pw[j]);
+        g->fdiv_q_2exp(&half, Pm.c(), 1);  // (P^m - 1) / 2, P odd
+        L = (unsigned long)g->sizeinbase(Pm.c(), 2);
+        kd = (unsigned long)g->sizeinbase(Dz.c(), 2);
+        g->set_ui(&mu, 1);
+        g->mul_2exp(&mu, mu.c(), L + kd + 1);
+        g->tdiv_q(&mu, mu.c(), Pm.c());
+    }
+    // X is overwritten
+    void finish(mpz_ptr X, Z &tmp, Z &w, int64_t *out, int32_t w_limbs, int32_t *okp) const {
+        const bool neg = sign(X) < 0;
+        if (neg) g->neg(X, X);
+        g->mul(&w, Dz.c(), X);                   // |y|
+        g->fdiv_q_2exp(&tmp, w.c(), L - 1);
+        g->mul(&tmp, tmp.c(), mu.c());
+        g->fdiv_q_2exp(&tmp, tmp.c(), kd + 2);
+        g->mul(&tmp, tmp.c(), Pm.c());
+        g->sub(&w, w.c(), tmp.c());
+        while (g->cmp(w.c(), Pm.c()) >= 0) g->sub(&w, w.c(), Pm.c());
+        if (neg && sign(w.c()) != 0) g->sub(&w, Pm.c(), w.c());
+        if (g->cmp(w.c(), half.c()) > 0) g->sub(&w, w.c(), Pm.c());
+        if (g->cmpabs(w.c(), Bz.c()) <= 0) {
+            to_twos(g, out, w_limbs, w.c());       // fits: |w| <= bound < 2^(64 w_limbs - 1)
+            *okp = 1;
+        } else {
+            std::memset(out, 0, sizeof(int64_t) * (size_t)w_limbs);
+            *okp = 0;
+        }
+    }
+};
+
+// Up to 16 host threads (or `threads`) take the components from a counter.
+template <class Work>
+void run_threads(int threads, int64_t items, Work work) {
+    int nt = threads ? threads : (int)std::min<unsigned>(std::max(1u, std::thread::hardware_concurrency()), 16u);
+    nt = (int)std::max<int64_t>(1, std::min<int64_t>(nt, items));
+    std::vector<std::thread> pool;
+    for (int i = 1; i < nt; i++) {
+        try {
+            pool.emplace_back(work);
+        } catch (...) {          // no more threads to be had: the ones running share the rest
+            break;
+        }
+    }
+    work();
+    for (auto &th : pool) th.join();
+}
+
+int check_common(int32_t steps, int64_t count, int64_t n_index, int32_t p_limbs, int32_t den_limbs, int32_t b_limbs,
+                 int32_t w_limbs, int32_t threads, const int64_t *index, const uint64_t *P, const uint64_t *D,
+                 const uint64_t *bound, const void *src, int64_t *num, int32_t *ok) {
+    if (steps < 1 || count < 0 || n_index < 0 || p_limbs < 1 || den_limbs < 1 || b_limbs < 1 || w_limbs < 1 ||
+        threads < 0)
+        return RNS_E_ARG;
+    if (!P || !D || !bound || (n_index > 0 && (!src || !index || !num || !ok))) return RNS_E_ARG;
+    for (int64_t t = 0; t < n_index; t++)
+        if (index[t] < 0 || index[t] >= count) return RNS_E_ARG;
+    if (!mag_positive(D, den_limbs) || !(P[0] & 1) || (p_limbs == 1 && P[0] < 3)) return RNS_E_ARG;
+    return RNS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, int32_t d_limbs,
                          const int64_t *index, int64_t n_index, const uint64_t *P, int32_t p_limbs,
                          const uint64_t *D, int32_t den_limbs, const uint64_t *bound, int32_t b_limbs,
                          int64_t *num, int32_t w_limbs, int32_t *ok, int32_t threads) {
-    if (steps < 1 || count < 0 || n_index < 0 || d_limbs < 1 || d_limbs > 64 || p_limbs < 1 || den_limbs < 1 ||
-        b_limbs < 1 || w_limbs < 1 || threads < 0)
-        return RNS_E_ARG;
-    if (!P || !D || !bound || (n_index > 0 && (!digits || !index || !num || !ok))) return RNS_E_ARG;
-    for (int64_t t = 0; t < n_index; t++)
-        if (index[t] < 0 || index[t] >= count) return RNS_E_ARG;
-    if (!mag_positive(D, den_limbs) || !(P[0] & 1) || (p_limbs == 1 && P[0] < 3)) return RNS_E_ARG;
+    if (d_limbs < 1 || d_limbs > 64) return RNS_E_ARG;
+    int rc = check_common(steps, count, n_index, p_limbs, den_limbs, b_limbs, w_limbs, threads, index, P, D, bound,
+                          digits, num, ok);
+    if (rc != RNS_OK) return rc;
     const Gmp *g = gmp();
     if (!g) return RNS_E_HOSTLIB;
-    Z Pz(g), Dz(g), Bz(g), Pm(g), half(g);
-    from_mag(g, &Pz, P, p_limbs);
-    from_mag(g, &Dz, D, den_limbs);
-    from_mag(g, &Bz, bound, b_limbs);
-    if (g->sizeinbase(Bz.c(), 2) >= (size_t)64 * (size_t)w_limbs) return RNS_E_OUT_LIMBS;
+    Numerators nm(g);
+    nm.setup(P, p_limbs, steps, D, den_limbs, bound, b_limbs);
+    if (g->sizeinbase(nm.Bz.c(), 2) >= (size_t)64 * (size_t)w_limbs) return RNS_E_OUT_LIMBS;
     if (n_index == 0) return RNS_OK;
-
-    // P^(2^j) for the pairwise assembly, and P^steps
-    int levels = 0;
-    while ((1LL << levels) < steps) levels++;
-    std::vector<Mpz> pw((size_t)levels + 1);
-    for (auto &z : pw) g->init(&z);
-    g->set(&pw[0], Pz.c());
-    for (int j = 1; j <= levels; j++) g->mul(&pw[j], &pw[j - 1], &pw[j - 1]);
-    g->set_ui(&Pm, 1);
-    for (int j = 0; j <= levels; j++)
-        if ((steps >> j) & 1) g->mul(&Pm, Pm.c(), &pw[j]);
-    g->fdiv_q_2exp(&half, Pm.c(), 1);  // (P^m - 1) / 2, P odd
-    // Barrett reduction by P^m for y = D X with |X| <= (P^m - 1)/2 < 2^(L-1): the quotient is
-    // below 2^kd (kd = bits of D), and mu = floor(2^(L+kd+1) / P^m) has kd + 2 bits, so the
-    // estimate floor(floor(|y| / 2^(L-1)) mu / 2^(kd+2)) is at most the quotient and a few short
-    const unsigned long L = (unsigned long)g->sizeinbase(Pm.c(), 2);
-    const unsigned long kd = (unsigned long)g->sizeinbase(Dz.c(), 2);
-    Z mu(g);
-    g->set_ui(&mu, 1);
-    g->mul_2exp(&mu, mu.c(), L + kd + 1);
-    g->tdiv_q(&mu, mu.c(), Pm.c());
-
-    int nt = threads ? threads : (int)std::min<unsigned>(std::max(1u, std::thread::hardware_concurrency()), 16u);
-    nt = (int)std::max<int64_t>(1, std::min<int64_t>(nt, n_index));
     std::atomic<int64_t> next{0};
-    auto work = [&]() {
+    run_threads(threads, n_index, [&]() {
         std::vector<Mpz> v((size_t)steps);
         for (auto &z : v) g->init(&z);
         Z tmp(g), w(g);
@@ -249,46 +316,50 @@ int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, in
             int64_t n = steps;
             for (int j = 0; n > 1; j++) {
                 for (int64_t i = 0; i < n / 2; i++) {
-                    g->mul(&tmp, &v[2 * i + 1], &pw[j]);
+                    g->mul(&tmp, &v[2 * i + 1], &nm.pw[j]);
                     g->add(&v[i], &v[2 * i], tmp.c());
                 }
                 if (n & 1) g->swap(&v[n / 2], &v[n - 1]);
                 n = (n + 1) / 2;
             }
-            // w = D X mod P^m, balanced
-            const bool neg = sign(&v[0]) < 0;
-            if (neg) g->neg(&v[0], &v[0]);
-            g->mul(&w, Dz.c(), &v[0]);                  // |y|
-            g->fdiv_q_2exp(&tmp, w.c(), L - 1);
-            g->mul(&tmp, tmp.c(), mu.c());
-            g->fdiv_q_2exp(&tmp, tmp.c(), kd + 2);
-            g->mul(&tmp, tmp.c(), Pm.c());
-            g->sub(&w, w.c(), tmp.c());
-            while (g->cmp(w.c(), Pm.c()) >= 0) g->sub(&w, w.c(), Pm.c());
-            if (neg && sign(w.c()) != 0) g->sub(&w, Pm.c(), w.c());
-            if (g->cmp(w.c(), half.c()) > 0) g->sub(&w, w.c(), Pm.c());
-            int64_t *out = num + t * w_limbs;
-            if (g->cmpabs(w.c(), Bz.c()) <= 0) {
-                to_twos(g, out, w_limbs, w.c());  // fits: |w| <= bound < 2^(64 w_limbs - 1)
-                ok[t] = 1;
-            } else {
-                std::memset(out, 0, sizeof(int64_t) * (size_t)w_limbs);
-                ok[t] = 0;
-            }
+            nm.finish(&v[0], tmp, w, num + t * w_limbs, w_limbs, ok + t);
         }
         for (auto &z : v) g->clear(&z);
-    };
-    std::vector<std::thread> pool;
-    for (int i = 1; i < nt; i++) {
-        try {
-            pool.emplace_back(work);
-        } catch (...) {          // no more threads to be had: the ones running share the rest
-            break;
+    });
+    return RNS_OK;
+}
+
+int rns_chunk_numerators(const uint32_t *chunks, int64_t T, int64_t count, const int64_t *index, int64_t n_index,
+                         const uint64_t *P, int32_t p_limbs, int32_t steps, const uint64_t *D, int32_t den_limbs,
+                         const uint64_t *bound, int32_t b_limbs, int64_t *num, int32_t w_limbs, int32_t *ok,
+                         int32_t threads) {
+    if (T < 1) return RNS_E_ARG;
+    int rc = check_common(steps, count, n_index, p_limbs, den_limbs, b_limbs, w_limbs, threads, index, P, D, bound,
+                          chunks, num, ok);
+    if (rc != RNS_OK) return rc;
+    const Gmp *g = gmp();
+    if (!g) return RNS_E_HOSTLIB;
+    Numerators nm(g);
+    nm.setup(P, p_limbs, steps, D, den_limbs, bound, b_limbs);
+    if (g->sizeinbase(nm.Bz.c(), 2) >= (size_t)64 * (size_t)w_limbs) return RNS_E_OUT_LIMBS;
+    if (n_index == 0) return RNS_OK;
+    std::atomic<int64_t> next{0};
+    run_threads(threads, n_index, [&]() {
+        Z X(g), tmp(g), w(g), top(g);
+        for (;;) {
+            const int64_t t = next.fetch_add(1);
+            if (t >= n_index) break;
+            const uint32_t *c = chunks + index[t] * T;
+            // T chunks, two's complement: the unsigned value, less 2^(32 T) when the top bit is set
+            g->import_(&X, (size_t)T, -1, sizeof(uint32_t), 0, 0, c);
+            if (c[T - 1] >> 31) {
+                g->set_ui(&top, 1);
+                g->mul_2exp(&top, top.c(), (unsigned long)(32 * T));
+                g->sub(&X, X.c(), top.c());
+            }
+            nm.finish(&X, tmp, w, num + t * w_limbs, w_limbs, ok + t);
         }
-    }
-    work();
-    for (auto &th : pool) th.join();
-    for (auto &z : pw) g->clear(&z);
+    });
     return RNS_OK;
 }
 
@@ -371,6 +442,25 @@ int rns_rational_reconstruct(const uint64_t *u, int32_t u_limbs, const uint64_t 
         g->neg(&r1, r1.c());
     }
     if (!to_twos(g, num, num_limbs, r1.c()) || !to_mag(g, den, den_limbs, t1.c())) return RNS_E_OUT_LIMBS;
+    return RNS_OK;
+}
+
+int rns_pow_table(const uint64_t *P, int32_t p_limbs, int32_t m, int64_t T, int64_t *out) {
+    if (!P || !out || p_limbs < 1 || m < 1 || T < 1) return RNS_E_ARG;
+    const Gmp *g = gmp();
+    if (!g) return RNS_E_HOSTLIB;
+    Z Pz(g), v(g);
+    from_mag(g, &Pz, P, p_limbs);
+    g->set_ui(&v, 1);
+    std::vector<uint32_t> words((size_t)T);
+    for (int32_t s = 0; s < m; s++) {
+        if (g->sizeinbase(v.c(), 2) > (size_t)32 * (size_t)T) return RNS_E_ARG;
+        std::fill(words.begin(), words.end(), 0u);
+        size_t cnt = 0;
+        g->export_(words.data(), &cnt, -1, sizeof(uint32_t), 0, 0, v.c());
+        for (int64_t t = 0; t < T; t++) out[t * m + s] = (int64_t)words[(size_t)t];
+        g->mul(&v, v.c(), Pz.c());
+    }
     return RNS_OK;
 }
 

@@ -677,6 +677,80 @@ __global__ __launch_bounds__(256) void lift_update_kernel(LiftConsts lc, const i
     }
 }
 
+// ---- p-adic values as binary chunks (the radix conversion of the host stage) ----
+// X = sum_s d_s P^s for every component is the product of the digits with the
+// table pow[t][s] = chunk t of P^s, formed exactly by the residue GEMM: with
+// d = d_lo + 2^192 d_hi (d_lo the low three limbs, unsigned; d_hi the rest,
+// signed), C_lo = pow d_lo and C_hi = pow d_hi give X = sum_t (C_lo[t] +
+// 2^192 C_hi[t]) 2^(32 t), and 2^192 is six chunks.  A carry pass per
+// component then writes X's 32-bit chunks.
+
+// digits [m][count][dl] -> lo [m][count][lo_store], hi [m][count][dl - 3]
+__global__ __launch_bounds__(256) void digit_halves_kernel(const int64_t *__restrict__ digits, int64_t total, int dl,
+                                                           int lo_store, int64_t *__restrict__ lo,
+                                                           int64_t *__restrict__ hi) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+        const int64_t *d = digits + e * dl;
+        if (dl <= 3) {
+            for (int l = 0; l < dl; l++) lo[e * lo_store + l] = d[l];
+        } else {
+            for (int l = 0; l < 3; l++) lo[e * lo_store + l] = d[l];
+            lo[e * lo_store + 3] = 0;
+            for (int l = 3; l < dl; l++) hi[e * (dl - 3) + l - 3] = d[l];
+        }
+    }
+}
+
+constexpr int kCarryLimbs = 5;        // the running sum: below 2^(32 + 192 + 18 + 2) in magnitude
+
+__device__ __forceinline__ void add_signed(uint64_t (&acc)[kCarryLimbs], const int64_t *v, int lv) {
+    const uint64_t ext = v[lv - 1] < 0 ? ~0ull : 0ull;
+    uint64_t carry = 0;
+#pragma unroll
+    for (int i = 0; i < kCarryLimbs; i++) {
+        const uint64_t a = i < lv ? (uint64_t)v[i] : ext;
+        const uint64_t s1 = acc[i] + a;
+        const uint64_t c1 = s1 < a ? 1ull : 0ull;
+        const uint64_t s2 = s1 + carry;
+        carry = c1 | (s2 < s1 ? 1ull : 0ull);
+        acc[i] = s2;
+    }
+}
+
+// One wave per 64 components; chunks gather in LDS and leave 64 at a time per
+// component (256 contiguous bytes).
+__global__ __launch_bounds__(64) void padic_carry_kernel(const int64_t *__restrict__ clo, int lcl,
+                                                         const int64_t *__restrict__ chi, int lch, int has_hi,
+                                                         int64_t T, int64_t count, uint32_t *__restrict__ out) {
+    __shared__ uint32_t tile[64][65];
+    const int lane = threadIdx.x;
+    const int64_t idx0 = (int64_t)blockIdx.x * 64, idx = idx0 + lane;
+    const bool live = idx < count;
+    uint64_t acc[kCarryLimbs];
+#pragma unroll
+    for (int i = 0; i < kCarryLimbs; i++) acc[i] = 0;
+    for (int64_t t0 = 0; t0 < T; t0 += 64) {
+        for (int tt = 0; tt < 64; tt++) {
+            const int64_t t = t0 + tt;
+            uint32_t chunk = 0;
+            if (live && t < T) {
+                add_signed(acc, clo + (t * count + idx) * lcl, lcl);
+                if (has_hi && t >= 6) add_signed(acc, chi + ((t - 6) * count + idx) * lch, lch);
+                chunk = (uint32_t)acc[0];
+#pragma unroll
+                for (int i = 0; i < kCarryLimbs - 1; i++) acc[i] = (acc[i] >> 32) | (acc[i + 1] << 32);
+                acc[kCarryLimbs - 1] = (uint64_t)((int64_t)acc[kCarryLimbs - 1] >> 32);
+            }
+            tile[lane][tt] = chunk;
+        }
+        __syncthreads();
+        const int64_t t = t0 + lane;
+        for (int c = 0; c < 64; c++)
+            if (idx0 + c < count && t < T) out[(idx0 + c) * T + t] = tile[c][lane];
+        __syncthreads();
+    }
+}
+
 }  // namespace rns
 
 using namespace rns;
@@ -880,6 +954,49 @@ int rns_inverse_planes(const int32_t *primes, int32_t n_primes, int64_t n, const
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 
+// plans and buffers of rns_padic_chunks
+struct ChunkLayout {
+    rns_plan_t lo, hi;
+    int has_hi, lo_store, hi_limbs;
+    int64_t lo_off, hi_off, clo_off, chi_off, g_off, total;
+    size_t g_bytes;
+};
+
+static int chunk_layout(int64_t T, int32_t m, int64_t count, int32_t dl, int32_t P_bits, ChunkLayout &L) {
+    if (T < 1 || m < 1 || count < 1 || dl < 1 || dl > RNS_MAX_OUT_LIMBS || P_bits < 2 || P_bits > 64 * dl)
+        return RNS_E_ARG;
+    if (m > RNS_K_MAX) return RNS_E_K;
+    L.has_hi = dl > 3;
+    L.lo_store = L.has_hi ? 4 : dl;
+    L.hi_limbs = L.has_hi ? dl - 3 : 0;
+    // pow chunks < 2^32; the low digit parts < 2^192, the high parts <= 2^(P_bits - 192)
+    int rc = rns_plan(m, 32, L.has_hi ? 192 : P_bits, &L.lo);
+    if (rc != RNS_OK) return rc;
+    size_t glo = 0, ghi = 0;
+    rc = rns_workspace_size(&L.lo, T, count, m, 0, &glo);
+    if (rc != RNS_OK) return rc;
+    if (L.has_hi) {
+        rc = rns_plan(m, 32, P_bits > 192 ? P_bits - 192 : 1, &L.hi);
+        if (rc != RNS_OK) return rc;
+        rc = rns_workspace_size(&L.hi, T, count, m, 0, &ghi);
+        if (rc != RNS_OK) return rc;
+    }
+    if (L.lo.out_limbs_min > kCarryLimbs || (L.has_hi && L.hi.out_limbs_min > kCarryLimbs)) return RNS_E_ARG;
+    int64_t off = 0;
+    L.lo_off = off;
+    off = pad256(off + (int64_t)m * count * L.lo_store * 8);
+    L.hi_off = off;
+    off = pad256(off + (int64_t)m * count * L.hi_limbs * 8);
+    L.clo_off = off;
+    off = pad256(off + T * count * L.lo.out_limbs_min * 8);
+    L.chi_off = off;
+    off = pad256(off + (L.has_hi ? T * count * L.hi.out_limbs_min * 8 : 0));
+    L.g_off = off;
+    L.g_bytes = glo > ghi ? glo : ghi;
+    L.total = off + (int64_t)L.g_bytes;
+    return RNS_OK;
+}
+
 int rns_plan_from_moduli(const int32_t *moduli, int32_t n, int64_t k_max, rns_plan_t *out) {
     if (!moduli || !out || n < 1 || n > kMaxPrimes || k_max < 1 || k_max > RNS_K_MAX) return RNS_E_ARG;
     return plan_from_moduli(moduli, n, k_max, out);
@@ -950,6 +1067,45 @@ int rns_dixon_lift(const rns_plan_t *plan, int64_t n, int64_t c, const int8_t *B
         if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
     }
     return RNS_OK;
+}
+
+int rns_padic_chunks_workspace_size(int64_t T, int32_t m, int64_t count, int32_t d_limbs, int32_t P_bits,
+                                    size_t *bytes) {
+    if (!bytes) return RNS_E_ARG;
+    ChunkLayout L;
+    const int rc = chunk_layout(T, m, count, d_limbs, P_bits, L);
+    if (rc != RNS_OK) return rc;
+    *bytes = (size_t)L.total;
+    return RNS_OK;
+}
+
+int rns_padic_chunks(const int64_t *pow, int64_t T, int32_t m, const int64_t *digits, int64_t count, int32_t d_limbs,
+                     int32_t P_bits, uint32_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!pow || !digits || !out || !ws) return RNS_E_ARG;
+    ChunkLayout L;
+    int rc = chunk_layout(T, m, count, d_limbs, P_bits, L);
+    if (rc != RNS_OK) return rc;
+    if ((int64_t)ws_bytes < L.total) return RNS_E_WORKSPACE;
+    if (T * count > ((int64_t)1 << 40)) return RNS_E_ARG;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int64_t *lo = reinterpret_cast<int64_t *>(base + L.lo_off);
+    int64_t *hi = reinterpret_cast<int64_t *>(base + L.hi_off);
+    int64_t *clo = reinterpret_cast<int64_t *>(base + L.clo_off);
+    int64_t *chi = reinterpret_cast<int64_t *>(base + L.chi_off);
+    void *g = base + L.g_off;
+    hipLaunchKernelGGL(digit_halves_kernel, dim3(grid_for((int64_t)m * count)), dim3(256), 0, stream, digits,
+                       (int64_t)m * count, d_limbs, L.lo_store, lo, hi);
+    if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
+    // C^T = pow [T][m] . digits [m][count]: one exact product per half of the digits
+    rc = rns_gemm(&L.lo, T, count, m, pow, 1, lo, L.lo_store, clo, L.lo.out_limbs_min, g, L.g_bytes, stream);
+    if (rc != RNS_OK) return rc;
+    if (L.has_hi) {
+        rc = rns_gemm(&L.hi, T, count, m, pow, 1, hi, L.hi_limbs, chi, L.hi.out_limbs_min, g, L.g_bytes, stream);
+        if (rc != RNS_OK) return rc;
+    }
+    hipLaunchKernelGGL(padic_carry_kernel, dim3((unsigned)((count + 63) / 64)), dim3(64), 0, stream, clo,
+                       L.lo.out_limbs_min, chi, L.has_hi ? L.hi.out_limbs_min : 1, L.has_hi, T, count, out);
+    return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 
 }  // extern "C"

@@ -242,19 +242,78 @@ def reconstruct_digits(digits: np.ndarray, P: int, m: int, Nb: int, Db: int, thr
     P^m > 2 Nb Db (Db + 1), as in ``reconstruct``).  Components that fail wait for the next
     denominator; each pass at least doubles D, so there are at most log2 Db + 1 passes."""
     digits = np.ascontiguousarray(digits, dtype=np.int64)
-    count = digits.shape[1]
+    return _reconstruct_with(lambda D, bound, idx, th: padic_numerators(digits, P, D, bound, idx, th),
+                             digits.shape[1], P, m, Nb, Db, threads)
+
+
+def pow_table(P: int, m: int, T: int) -> np.ndarray:
+    """int64 [T][m]: entry [t][s] is 32-bit chunk t of P^s (native when GMP is there)."""
+    if host_bigint_available():
+        out = np.zeros((T, m), dtype=np.int64)
+        Pl, pn = _mag(P)
+        _check(load().rns_pow_table(_ptr(Pl), pn, m, T, _ptr(out)), "rns_pow_table")
+        return out
+    tab = np.zeros((m, T), dtype=np.uint32)
+    v = 1
+    for s in range(m):
+        raw = np.frombuffer(v.to_bytes(4 * T, "little"), dtype=np.uint32)
+        tab[s] = raw
+        v *= P
+    return np.ascontiguousarray(tab.T.astype(np.int64))
+
+
+def padic_chunks(digits: torch.Tensor, P: int, m: int) -> torch.Tensor:
+    """The p-adic values sum_s digits[s] P^s of every component as 32-bit two's-complement chunks,
+    int32 [count, T] on the device (rns_padic_chunks: two exact residue products and a carry pass)."""
+    if digits.dim() != 3 or digits.dtype != torch.int64 or digits.device.type != "cuda":
+        raise ValueError("digits must be an int64 [m, count, limbs] tensor on a GPU device")
+    digits = digits.contiguous()
+    _, count, dl = digits.shape
+    T = ((P ** m).bit_length() + 1 + 31) // 32
+    pw = torch.from_numpy(pow_table(P, m, T)).to(digits.device)
+    sz = ctypes.c_size_t()
+    _check(load().rns_padic_chunks_workspace_size(T, m, count, dl, P.bit_length(), ctypes.byref(sz)),
+           "rns_padic_chunks_workspace_size")
+    ws = torch.empty(max(sz.value, 1), dtype=torch.uint8, device=digits.device)
+    out = torch.empty((count, T), dtype=torch.int32, device=digits.device)
+    with torch.cuda.device(digits.device):
+        rc = load().rns_padic_chunks(pw.data_ptr(), T, m, digits.data_ptr(), count, dl, P.bit_length(),
+                                     out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(digits))
+    _check(rc, "rns_padic_chunks")
+    return out
+
+
+def chunk_numerators(chunks: np.ndarray, P: int, m: int, D: int, bound: int, index=None, threads: int = 0):
+    """``padic_numerators`` with the p-adic values given as chunks (uint32 [count][T])."""
+    chunks = np.ascontiguousarray(chunks).view(np.uint32)
+    count, T = chunks.shape
+    idx = np.arange(count, dtype=np.int64) if index is None else np.ascontiguousarray(index, dtype=np.int64)
+    Pl, pn = _mag(P)
+    Dl, dn = _mag(D)
+    Bl, bn = _mag(bound)
+    wl = bound.bit_length() // 64 + 1
+    num = np.zeros((max(len(idx), 1), wl), dtype=np.int64)
+    ok = np.zeros(max(len(idx), 1), dtype=np.int32)
+    rc = load().rns_chunk_numerators(_ptr(chunks), T, count, _ptr(idx), len(idx), _ptr(Pl), pn, m, _ptr(Dl), dn,
+                                     _ptr(Bl), bn, _ptr(num), wl, _ptr(ok), threads)
+    _check(rc, "rns_chunk_numerators")
+    return ok[:len(idx)].astype(bool), _limbs_to_int(num[:len(idx)])
+
+
+def _reconstruct_with(numerators, count: int, P: int, m: int, Nb: int, Db: int, threads: int = 0):
+    """The common-denominator loop of ``reconstruct_digits`` over a numerators source."""
     Pm = P ** m
     D = 1
     nums: List[Optional[int]] = [None] * count
     at: List[int] = [1] * count
     todo = np.arange(count, dtype=np.int64)
     while len(todo):
-        _, (u,) = padic_numerators(digits, P, 1, Pm // 2, todo[:1], threads=1)
+        _, (u,) = numerators(1, Pm // 2, todo[:1], 1)
         f = rational_reconstruct(u, Pm, Nb, Db)
         if f is None:
             raise RnsError(-8, "rational reconstruction failed")
         D *= f.denominator // math.gcd(D, f.denominator)
-        ok, w = padic_numerators(digits, P, D, D * Nb, todo, threads=threads)
+        ok, w = numerators(D, D * Nb, todo, threads)
         if not ok[0]:
             raise RnsError(-8, "a reconstructed component failed the common-denominator test")
         for t in np.flatnonzero(ok):
@@ -262,6 +321,24 @@ def reconstruct_digits(digits: np.ndarray, P: int, m: int, Nb: int, Db: int, thr
             at[todo[t]] = D
         todo = todo[~ok]
     return [v * (D // a) for v, a in zip(nums, at)], D
+
+
+def reconstruct_chunks(chunks: np.ndarray, P: int, m: int, Nb: int, Db: int, threads: int = 0):
+    """(numerators, common denominator) from the p-adic values as chunks (``padic_chunks``)."""
+    chunks = np.ascontiguousarray(chunks).view(np.uint32)
+    return _reconstruct_with(lambda D, bound, idx, th: chunk_numerators(chunks, P, m, D, bound, idx, th),
+                             chunks.shape[0], P, m, Nb, Db, threads)
+
+
+def reconstruct_device(digits: torch.Tensor, P: int, m: int, Nb: int, Db: int):
+    """The reconstruction of device digits [m, count, limbs]: the p-adic values in binary on the GPU,
+    the common denominator and the numerators on the host (native; Python integers without GMP)."""
+    if host_bigint_available():
+        chunks = padic_chunks(digits, P, m).cpu().numpy()          # synchronises
+        return reconstruct_chunks(chunks, P, m, Nb, Db)
+    d = digits.cpu().numpy()
+    per_step = [_limbs_to_int(d[s]) for s in range(m)]
+    return reconstruct(per_step, P, m, Nb, Db)
 
 
 def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
@@ -299,13 +376,9 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
     Nb, Db = _bounds(An, bn)
     P = math.prod(moduli)
     m = lift_steps_for(P, Nb, Db)
-    digits = dixon_lift(p, A, b, planes, m).cpu().numpy()  # synchronises
+    digits = dixon_lift(p, A, b, planes, m)
     c = bn.shape[1]
-    if host_bigint_available():
-        nums, D = reconstruct_digits(digits.reshape(m, n * c, -1), P, m, Nb, Db)
-    else:
-        per_step = [_limbs_to_int(digits[s]) for s in range(m)]
-        nums, D = reconstruct(per_step, P, m, Nb, Db)
+    nums, D = reconstruct_device(digits.reshape(m, n * c, -1), P, m, Nb, Db)
     out = [[Fraction(nums[i * c + k], D) for k in range(c)] for i in range(n)]
     if return_info:
         return out, {"primes": moduli, "steps": m, "log2_P": math.log2(P), "denominator_bits": D.bit_length(),

@@ -99,6 +99,28 @@ int rns_dixon_lift(const rns_plan_t *plan, int64_t n, int64_t c, const int8_t *B
                    void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * rns_padic_chunks_workspace_size -- device bytes of rns_padic_chunks.
+ * Returns RNS_OK, RNS_E_ARG or RNS_E_K.
+ */
+int rns_padic_chunks_workspace_size(int64_t T, int32_t m, int64_t count, int32_t d_limbs, int32_t P_bits,
+                                    size_t *bytes);
+
+/*
+ * rns_padic_chunks -- the p-adic values X_idx = sum_{s < m} digits[s][idx] P^s
+ * of every component, as T little-endian 32-bit two's-complement chunks:
+ * out is device uint32 [count][T].  digits: device int64 [m][count][d_limbs]
+ * (rns_dixon_lift's output, |digit| < 2^(P_bits - 1)); pow: device int64
+ * [T][m], pow[t][s] = chunk t of P^s (in [0, 2^32)), built by the caller.
+ * 32 T must exceed the bit length of P^m (then |X| <= (P^m - 1)/2 fits).
+ * The sum is two exact residue products (the digits' low three limbs and
+ * the rest) and one carry pass: the radix conversion of the host stage on
+ * the GPU.  Returns RNS_OK, RNS_E_ARG, RNS_E_K (m > 2^17), RNS_E_WORKSPACE or
+ * RNS_E_HIP.
+ */
+int rns_padic_chunks(const int64_t *pow, int64_t T, int32_t m, const int64_t *digits, int64_t count, int32_t d_limbs,
+                     int32_t P_bits, uint32_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
  * ---- host stage (exact-solve, "Method": the final rational reconstruction is
  * a CPU stage: a common denominator, then one modular multiply per numerator).
  * Host pointers only; no device memory is touched.  Big integers cross as
@@ -130,6 +152,25 @@ int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, in
                          const int64_t *index, int64_t n_index, const uint64_t *P, int32_t p_limbs,
                          const uint64_t *D, int32_t den_limbs, const uint64_t *bound, int32_t b_limbs,
                          int64_t *num, int32_t w_limbs, int32_t *ok, int32_t threads);
+
+/*
+ * rns_pow_table -- the table of rns_padic_chunks on the host: out[t][s] =
+ * 32-bit chunk t of P^s for s < m, t < T (host int64 [T][m]; P a magnitude of
+ * p_limbs limbs).  Returns RNS_OK, RNS_E_ARG (also when P^(m-1) does not fit
+ * T chunks) or RNS_E_HOSTLIB.
+ */
+int rns_pow_table(const uint64_t *P, int32_t p_limbs, int32_t m, int64_t T, int64_t *out);
+
+/*
+ * rns_chunk_numerators -- rns_padic_numerators with the p-adic values given
+ * as binary chunks (host uint32 [count][T], little-endian two's complement,
+ * rns_padic_chunks's output) and P^steps as the modulus.  Returns RNS_OK,
+ * RNS_E_ARG, RNS_E_OUT_LIMBS or RNS_E_HOSTLIB.
+ */
+int rns_chunk_numerators(const uint32_t *chunks, int64_t T, int64_t count, const int64_t *index, int64_t n_index,
+                         const uint64_t *P, int32_t p_limbs, int32_t steps, const uint64_t *D, int32_t den_limbs,
+                         const uint64_t *bound, int32_t b_limbs, int64_t *num, int32_t w_limbs, int32_t *ok,
+                         int32_t threads);
 
 /*
  * rns_rational_reconstruct -- the fraction N/d with |N| <= Nb, 0 < d <= Db and

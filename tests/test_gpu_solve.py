@@ -216,3 +216,29 @@ def test_empty_and_degenerate_shapes():
         rg.solve(dev(np.eye(3)), dev(np.zeros((3, 0))))
     X = rg.solve(dev([[7]]), dev([[3, -14]]))          # 1 x 1, two right-hand sides
     assert X == [[Fraction(3, 7), Fraction(-2)]]
+
+
+@pytest.mark.parametrize("n_primes,m,count", [(3, 4, 70), (20, 7, 130), (50, 11, 64), (53, 3, 1)])
+def test_padic_chunks_match_the_oracle(n_primes, m, count):
+    """The p-adic values in binary (two exact residue products and a carry pass) against the
+    oracle's sum of digits times powers of P, for one- to six-limb digits."""
+    from oracle import oracle as O
+    rng = np.random.default_rng(20 + n_primes)
+    ps = ODD_PRIMES[:n_primes]
+    P = math.prod(ps)
+    L = (P.bit_length() + 64) // 64
+    vals = [[int(v) for v in rng.integers(-(P // 2), P // 2, size=count, dtype=np.int64)] if P < 2 ** 62 else
+            [int.from_bytes(rng.bytes((P.bit_length() + 7) // 8), "little") % P - P // 2 for _ in range(count)]
+            for _ in range(m)]
+    dig = np.zeros((m, count, L), dtype=np.int64)
+    for s in range(m):
+        for i in range(count):
+            dig[s, i] = O.to_limbs(vals[s][i], L)
+    print(f"padic chunks primes={n_primes} m={m} count={count}", flush=True)
+    chunks = rg.exact_solve.padic_chunks(dev(dig), P, m).cpu().numpy().view(np.uint32)
+    T = chunks.shape[1]
+    ref = D.padic_value([[[v] for v in row] for row in vals], P)
+    for i in range(count):
+        got = int.from_bytes(chunks[i].tobytes(), "little", signed=True)
+        assert got == ref[i][0], i
+    assert 32 * T > (P ** m).bit_length()

@@ -205,3 +205,45 @@ def test_native_rational_reconstruction_long_remainder_sequences():
             v = rng.randrange(M)
             small = 2 ** (nb_bits // 2)
             assert S.rational_reconstruct(v, M, small, small) == D.rational_reconstruct(v, M, small, small)
+
+
+def test_pow_table_chunks():
+    P = O.prod([251, 241, 239, 233])
+    tab = S.pow_table(P, 5, 6)
+    for s in range(5):
+        v = sum(int(tab[t, s]) << (32 * t) for t in range(6))
+        assert v == P ** s and all(0 <= int(x) < 2 ** 32 for x in tab[:, s])
+
+
+def test_pow_table_wide_and_too_narrow():
+    """All 54 primes (P near 2^335): 11 powers over 116 chunks; too few chunks is an error."""
+    P = O.prod(O.primes_largest_first())
+    tab = S.pow_table(P, 11, 116)
+    for s in range(11):
+        assert sum(int(tab[t, s]) << (32 * t) for t in range(116)) == P ** s
+    if S.host_bigint_available():
+        with pytest.raises(Exception):
+            S.pow_table(P, 11, 100)
+
+
+def test_native_numerators_from_chunks_equal_from_digits():
+    """The same numerators whether the p-adic values come as digits or as binary chunks."""
+    _native()
+    rng = random.Random(10)
+    ps = [q for q in O.primes_largest_first() if q % 2][:12]
+    P = O.prod(ps)
+    m, cnt = 9, 13
+    per_step = [[rng.randint(-(P // 2), P // 2) for _ in range(cnt)] for _ in range(m)]
+    L = (P.bit_length() + 64) // 64
+    dig = _digit_array(per_step, L)
+    X = [r[0] for r in D.padic_value([[[v] for v in row] for row in per_step], P)]
+    T = ((P ** m).bit_length() + 1 + 31) // 32
+    chunks = np.array([[(x % (1 << (32 * T))) >> (32 * t) & 0xffffffff for t in range(T)] for x in X],
+                      dtype=np.uint32)
+    Dd = 3 * 7 * 2 ** 40 + 1
+    for Dv, bound in ((1, P ** m // 2), (Dd, Dd * 2 ** 200)):
+        ok1, w1 = S.padic_numerators(dig, P, Dv, bound)
+        ok2, w2 = S.chunk_numerators(chunks, P, m, Dv, bound)
+        assert list(ok1) == list(ok2) and w1 == w2
+    ok, w = S.chunk_numerators(chunks, P, m, 1, P ** m // 2)
+    assert ok.all() and w == X
