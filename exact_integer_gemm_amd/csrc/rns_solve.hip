@@ -682,8 +682,9 @@ __global__ __launch_bounds__(256) void lift_update_kernel(LiftConsts lc, const i
 // table pow[t][s] = chunk t of P^s, formed exactly by the residue GEMM: with
 // d = d_lo + 2^192 d_hi (d_lo the low three limbs, unsigned; d_hi the rest,
 // signed), C_lo = pow d_lo and C_hi = pow d_hi give X = sum_t (C_lo[t] +
-// 2^192 C_hi[t]) 2^(32 t), and 2^192 is six chunks.  A carry pass per
-// component then writes X's 32-bit chunks.
+// 2^192 C_hi[t]) 2^(32 t), and 2^192 is six chunks.  The pieces landing on
+// each chunk are summed in parallel, and a carry pass per component writes X's
+// 32-bit chunks.
 
 // digits [m][count][dl] -> lo [m][count][lo_store], hi [m][count][dl - 3]
 __global__ __launch_bounds__(256) void digit_halves_kernel(const int64_t *__restrict__ digits, int64_t total, int dl,
@@ -701,54 +702,76 @@ __global__ __launch_bounds__(256) void digit_halves_kernel(const int64_t *__rest
     }
 }
 
-constexpr int kCarryLimbs = 5;        // the running sum: below 2^(32 + 192 + 18 + 2) in magnitude
-
-__device__ __forceinline__ void add_signed(uint64_t (&acc)[kCarryLimbs], const int64_t *v, int lv) {
-    const uint64_t ext = v[lv - 1] < 0 ? ~0ull : 0ull;
-    uint64_t carry = 0;
-#pragma unroll
-    for (int i = 0; i < kCarryLimbs; i++) {
-        const uint64_t a = i < lv ? (uint64_t)v[i] : ext;
-        const uint64_t s1 = acc[i] + a;
-        const uint64_t c1 = s1 < a ? 1ull : 0ull;
-        const uint64_t s2 = s1 + carry;
-        carry = c1 | (s2 < s1 ? 1ull : 0ull);
-        acc[i] = s2;
+// W[u][idx] = the sum of the 32-bit pieces that land on chunk u: piece j of
+// C_lo[t] for t + j = u and piece j of C_hi[t] for t + 6 + j = u (the top
+// piece of each signed, the others unsigned), so X = sum_u W[u] 2^(32 u) with
+// |W[u]| below 2^(32 + 6).  One thread per (u, component).  W is [Tp][cp]
+// with Tp >= T and cp >= count; the padding holds zeros.
+__global__ __launch_bounds__(256) void chunk_sums_kernel(const int64_t *__restrict__ clo, int lcl,
+                                                         const int64_t *__restrict__ chi, int lch, int has_hi,
+                                                         int64_t T, int64_t count, int64_t Tp, int64_t cp,
+                                                         int64_t *__restrict__ W) {
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= cp) return;
+    for (int64_t u = blockIdx.y; u < Tp; u += gridDim.y) {
+        int64_t w = 0;
+        if (idx < count && u < T) {
+            for (int j = 0; j < 2 * lcl && j <= u; j++) {
+                const uint32_t *pc = reinterpret_cast<const uint32_t *>(clo + ((u - j) * count + idx) * lcl);
+                w += j == 2 * lcl - 1 ? (int64_t)(int32_t)pc[j] : (int64_t)pc[j];
+            }
+            if (has_hi)
+                for (int j = 0; j < 2 * lch && j + 6 <= u; j++) {
+                    const uint32_t *pc = reinterpret_cast<const uint32_t *>(chi + ((u - 6 - j) * count + idx) * lch);
+                    w += j == 2 * lch - 1 ? (int64_t)(int32_t)pc[j] : (int64_t)pc[j];
+                }
+        }
+        W[u * cp + idx] = w;
     }
 }
 
-// One wave per 64 components; chunks gather in LDS and leave 64 at a time per
-// component (256 contiguous bytes).
-__global__ __launch_bounds__(64) void padic_carry_kernel(const int64_t *__restrict__ clo, int lcl,
-                                                         const int64_t *__restrict__ chi, int lch, int has_hi,
-                                                         int64_t T, int64_t count, uint32_t *__restrict__ out) {
+// The carry pass over W: chunk_u = (W[u] + carry) mod 2^32, carry = the
+// arithmetic shift by 32.  One lane per component walks its chunks in order;
+// its loads run 16 chunks ahead (unconditional: W's zero padding covers
+// every position up to 16 past the last 64-chunk block), and the chunks gather
+// in LDS and leave 64 at a time per component (256 contiguous bytes).  Chunks
+// at u >= T are dropped: X fits T chunks.
+constexpr int kCarryAhead = 16;
+
+__global__ __launch_bounds__(64) void chunk_carry_kernel(const int64_t *__restrict__ W, int64_t T, int64_t count,
+                                                         int64_t cp, uint32_t *__restrict__ out) {
     __shared__ uint32_t tile[64][65];
     const int lane = threadIdx.x;
-    const int64_t idx0 = (int64_t)blockIdx.x * 64, idx = idx0 + lane;
-    const bool live = idx < count;
-    uint64_t acc[kCarryLimbs];
-#pragma unroll
-    for (int i = 0; i < kCarryLimbs; i++) acc[i] = 0;
+    const int64_t idx0 = (int64_t)blockIdx.x * 64;
+    const int64_t *wl = W + idx0 + lane;
+    int64_t carry = 0;
+    int64_t ra[kCarryAhead], rb[kCarryAhead];
+#define CHUNK_LOAD(r, tb)                                                      \
+    _Pragma("unroll") for (int k = 0; k < kCarryAhead; k++) r[k] = wl[((tb) + k) * cp];
+#define CHUNK_CARRY(r, off)                                                    \
+    _Pragma("unroll") for (int k = 0; k < kCarryAhead; k++) {                  \
+        const int64_t s_ = r[k] + carry;                                       \
+        tile[lane][(off) + k] = (uint32_t)s_;                                  \
+        carry = s_ >> 32;                                                      \
+    }
+    CHUNK_LOAD(ra, 0)
     for (int64_t t0 = 0; t0 < T; t0 += 64) {
-        for (int tt = 0; tt < 64; tt++) {
-            const int64_t t = t0 + tt;
-            uint32_t chunk = 0;
-            if (live && t < T) {
-                add_signed(acc, clo + (t * count + idx) * lcl, lcl);
-                if (has_hi && t >= 6) add_signed(acc, chi + ((t - 6) * count + idx) * lch, lch);
-                chunk = (uint32_t)acc[0];
-#pragma unroll
-                for (int i = 0; i < kCarryLimbs - 1; i++) acc[i] = (acc[i] >> 32) | (acc[i + 1] << 32);
-                acc[kCarryLimbs - 1] = (uint64_t)((int64_t)acc[kCarryLimbs - 1] >> 32);
-            }
-            tile[lane][tt] = chunk;
-        }
+        CHUNK_LOAD(rb, t0 + 16)
+        CHUNK_CARRY(ra, 0)
+        CHUNK_LOAD(ra, t0 + 32)
+        CHUNK_CARRY(rb, 16)
+        CHUNK_LOAD(rb, t0 + 48)
+        CHUNK_CARRY(ra, 32)
+        CHUNK_LOAD(ra, t0 + 64)
+        CHUNK_CARRY(rb, 48)
         __syncthreads();
         const int64_t t = t0 + lane;
         for (int c = 0; c < 64; c++)
             if (idx0 + c < count && t < T) out[(idx0 + c) * T + t] = tile[c][lane];
         __syncthreads();
     }
+#undef CHUNK_LOAD
+#undef CHUNK_CARRY
 }
 
 }  // namespace rns
@@ -958,7 +981,8 @@ int rns_inverse_planes(const int32_t *primes, int32_t n_primes, int64_t n, const
 struct ChunkLayout {
     rns_plan_t lo, hi;
     int has_hi, lo_store, hi_limbs;
-    int64_t lo_off, hi_off, clo_off, chi_off, g_off, total;
+    int64_t lo_off, hi_off, clo_off, chi_off, w_off, g_off, total;
+    int64_t wT, wc;                          // rows and columns of W, padded
     size_t g_bytes;
 };
 
@@ -981,7 +1005,6 @@ static int chunk_layout(int64_t T, int32_t m, int64_t count, int32_t dl, int32_t
         rc = rns_workspace_size(&L.hi, T, count, m, 0, &ghi);
         if (rc != RNS_OK) return rc;
     }
-    if (L.lo.out_limbs_min > kCarryLimbs || (L.has_hi && L.hi.out_limbs_min > kCarryLimbs)) return RNS_E_ARG;
     int64_t off = 0;
     L.lo_off = off;
     off = pad256(off + (int64_t)m * count * L.lo_store * 8);
@@ -991,6 +1014,11 @@ static int chunk_layout(int64_t T, int32_t m, int64_t count, int32_t dl, int32_t
     off = pad256(off + T * count * L.lo.out_limbs_min * 8);
     L.chi_off = off;
     off = pad256(off + (L.has_hi ? T * count * L.hi.out_limbs_min * 8 : 0));
+    // W: [Tp][cp] with zero padding for the carry pass's read-ahead
+    L.wT = (T + 63) / 64 * 64 + kCarryAhead;
+    L.wc = (count + 63) / 64 * 64;
+    L.w_off = off;
+    off = pad256(off + L.wT * L.wc * 8);
     L.g_off = off;
     L.g_bytes = glo > ghi ? glo : ghi;
     L.total = off + (int64_t)L.g_bytes;
@@ -1103,8 +1131,14 @@ int rns_padic_chunks(const int64_t *pow, int64_t T, int32_t m, const int64_t *di
         rc = rns_gemm(&L.hi, T, count, m, pow, 1, hi, L.hi_limbs, chi, L.hi.out_limbs_min, g, L.g_bytes, stream);
         if (rc != RNS_OK) return rc;
     }
-    hipLaunchKernelGGL(padic_carry_kernel, dim3((unsigned)((count + 63) / 64)), dim3(64), 0, stream, clo,
-                       L.lo.out_limbs_min, chi, L.has_hi ? L.hi.out_limbs_min : 1, L.has_hi, T, count, out);
+    int64_t *W = reinterpret_cast<int64_t *>(base + L.w_off);
+    const unsigned gy = (unsigned)(L.wT < 65535 ? L.wT : 65535);
+    hipLaunchKernelGGL(chunk_sums_kernel, dim3((unsigned)((L.wc + 255) / 256), gy), dim3(256), 0, stream, clo,
+                       L.lo.out_limbs_min, chi, L.has_hi ? L.hi.out_limbs_min : 1, L.has_hi, T, count, L.wT, L.wc,
+                       W);
+    if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
+    hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)(L.wc / 64)), dim3(64), 0, stream, W, T, count, L.wc,
+                       out);
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 

@@ -160,7 +160,7 @@ def padic_numerators(digits: np.ndarray, P: int, D: int, bound: int, index: Opti
 
 def rational_reconstruct(u: int, M: int, Nb: int, Db: int) -> Optional[Fraction]:
     """N/d with |N| <= Nb, 0 < d <= Db, N = d u (mod M) (native extended Euclid); None if none."""
-    ul, un = _mag(u % M)
+    ul, un = _mag(u if u >= 0 else u % M)       # the native call reduces mod M
     Ml, mn = _mag(M)
     Nl, nn = _mag(Nb)
     Dl, dn = _mag(Db)
@@ -262,15 +262,26 @@ def pow_table(P: int, m: int, T: int) -> np.ndarray:
     return np.ascontiguousarray(tab.T.astype(np.int64))
 
 
-def padic_chunks(digits: torch.Tensor, P: int, m: int) -> torch.Tensor:
+def chunk_count(P: int, m: int) -> int:
+    """32-bit chunks holding every balanced value mod P^m in two's complement."""
+    return ((P ** m).bit_length() + 1 + 31) // 32
+
+
+def padic_chunks(digits: torch.Tensor, P: int, m: int, table: Optional[np.ndarray] = None) -> torch.Tensor:
     """The p-adic values sum_s digits[s] P^s of every component as 32-bit two's-complement chunks,
-    int32 [count, T] on the device (rns_padic_chunks: two exact residue products and a carry pass)."""
+    int32 [count, T] on the device (rns_padic_chunks: two exact residue products and a carry pass).
+    ``table`` is ``pow_table(P, m, chunk_count(P, m))`` when the caller built it already (say while
+    the lift ran)."""
     if digits.dim() != 3 or digits.dtype != torch.int64 or digits.device.type != "cuda":
         raise ValueError("digits must be an int64 [m, count, limbs] tensor on a GPU device")
     digits = digits.contiguous()
     _, count, dl = digits.shape
-    T = ((P ** m).bit_length() + 1 + 31) // 32
-    pw = torch.from_numpy(pow_table(P, m, T)).to(digits.device)
+    T = chunk_count(P, m)
+    if table is None:
+        table = pow_table(P, m, T)
+    if table.shape != (T, m):
+        raise ValueError("table must be pow_table(P, m, chunk_count(P, m))")
+    pw = torch.from_numpy(np.ascontiguousarray(table, dtype=np.int64)).to(digits.device)
     sz = ctypes.c_size_t()
     _check(load().rns_padic_chunks_workspace_size(T, m, count, dl, P.bit_length(), ctypes.byref(sz)),
            "rns_padic_chunks_workspace_size")
@@ -301,15 +312,23 @@ def chunk_numerators(chunks: np.ndarray, P: int, m: int, D: int, bound: int, ind
 
 
 def _reconstruct_with(numerators, count: int, P: int, m: int, Nb: int, Db: int, threads: int = 0):
-    """The common-denominator loop of ``reconstruct_digits`` over a numerators source."""
+    """The common-denominator loop of ``reconstruct_digits`` over a numerators source.  A component
+    reconstructed alone needs only P^k > 2 Nb Db (its fraction is unique there), so its Euclidean
+    remainder sequence runs on u mod P^k; the one-multiply test of the others keeps P^m."""
     Pm = P ** m
+    target = 2 * Nb * Db
+    Pk = P
+    while Pk <= target:
+        Pk *= P
     D = 1
     nums: List[Optional[int]] = [None] * count
     at: List[int] = [1] * count
     todo = np.arange(count, dtype=np.int64)
     while len(todo):
         _, (u,) = numerators(1, Pm // 2, todo[:1], 1)
-        f = rational_reconstruct(u, Pm, Nb, Db)
+        # u + P^m is non-negative and congruent to u mod P^k (P^k divides P^m); the native call
+        # reduces it
+        f = rational_reconstruct(u + Pm if u < 0 else u, Pk, Nb, Db)
         if f is None:
             raise RnsError(-8, "rational reconstruction failed")
         D *= f.denominator // math.gcd(D, f.denominator)
@@ -320,7 +339,8 @@ def _reconstruct_with(numerators, count: int, P: int, m: int, Nb: int, Db: int, 
             nums[todo[t]] = w[t]
             at[todo[t]] = D
         todo = todo[~ok]
-    return [v * (D // a) for v, a in zip(nums, at)], D
+    scale = {a: D // a for a in set(at)}
+    return [v * scale[a] for v, a in zip(nums, at)], D
 
 
 def reconstruct_chunks(chunks: np.ndarray, P: int, m: int, Nb: int, Db: int, threads: int = 0):
@@ -330,11 +350,13 @@ def reconstruct_chunks(chunks: np.ndarray, P: int, m: int, Nb: int, Db: int, thr
                              chunks.shape[0], P, m, Nb, Db, threads)
 
 
-def reconstruct_device(digits: torch.Tensor, P: int, m: int, Nb: int, Db: int):
+def reconstruct_device(digits: torch.Tensor, P: int, m: int, Nb: int, Db: int,
+                       table: Optional[np.ndarray] = None):
     """The reconstruction of device digits [m, count, limbs]: the p-adic values in binary on the GPU,
-    the common denominator and the numerators on the host (native; Python integers without GMP)."""
+    the common denominator and the numerators on the host (native; Python integers without GMP).
+    ``table``: the power table of ``padic_chunks``, if already built."""
     if host_bigint_available():
-        chunks = padic_chunks(digits, P, m).cpu().numpy()          # synchronises
+        chunks = padic_chunks(digits, P, m, table).cpu().numpy()   # synchronises
         return reconstruct_chunks(chunks, P, m, Nb, Db)
     d = digits.cpu().numpy()
     per_step = [_limbs_to_int(d[s]) for s in range(m)]
@@ -377,8 +399,10 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
     P = math.prod(moduli)
     m = lift_steps_for(P, Nb, Db)
     digits = dixon_lift(p, A, b, planes, m)
+    # the lift runs asynchronously: build the radix-conversion table on the host meanwhile
+    table = pow_table(P, m, chunk_count(P, m)) if host_bigint_available() else None
     c = bn.shape[1]
-    nums, D = reconstruct_device(digits.reshape(m, n * c, -1), P, m, Nb, Db)
+    nums, D = reconstruct_device(digits.reshape(m, n * c, -1), P, m, Nb, Db, table)
     out = [[Fraction(nums[i * c + k], D) for k in range(c)] for i in range(n)]
     if return_info:
         return out, {"primes": moduli, "steps": m, "log2_P": math.log2(P), "denominator_bits": D.bit_length(),
