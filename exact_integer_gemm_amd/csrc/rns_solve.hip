@@ -2,6 +2,7 @@
 // batched modular inverse by Gauss-Jordan elimination over every prime at
 // once, and the Dixon lift (the batched residue product of rns_gemm plus the
 // residual update in one limb).
+#include <algorithm>
 #include <cstring>
 #include <vector>
 
@@ -702,48 +703,70 @@ __global__ __launch_bounds__(256) void digit_halves_kernel(const int64_t *__rest
     }
 }
 
-// W[u][idx] = the sum of the 32-bit pieces that land on chunk u: piece j of
-// C_lo[t] for t + j = u and piece j of C_hi[t] for t + 6 + j = u (the top
-// piece of each signed, the others unsigned), so X = sum_u W[u] 2^(32 u) with
-// |W[u]| below 2^(32 + 6).  One thread per (u, component).  W is [Tp][cp]
-// with Tp >= T and cp >= count; the padding holds zeros.
-__global__ __launch_bounds__(256) void chunk_sums_kernel(const int64_t *__restrict__ clo, int lcl,
-                                                         const int64_t *__restrict__ chi, int lch, int has_hi,
-                                                         int64_t T, int64_t count, int64_t Tp, int64_t cp,
-                                                         int64_t *__restrict__ W) {
+// ---- chunk arithmetic: big integers per component as 32-bit chunks ----
+// A source of pieces: entries src[t][idx] of `limbs` int64 limbs (two's
+// complement), each worth 2^(32 (t + shift)) times its value, added with `sign`.
+struct PieceSrc {
+    const int64_t *p;
+    int limbs, shift, sign;
+    int64_t rows;
+};
+
+struct SumArgs {
+    PieceSrc src[2];
+    int nsrc;
+    const int64_t *base;       // optional chunk values base[u][idx] (rows base_rows), added as they are
+    int64_t base_rows;
+    int64_t bias_u;            // 2^31 is added at chunk bias_u (-1: none)
+    int64_t T, count, Tp, cp;  // chunks and components; W is [Tp][cp], zero beyond [T][count]
+};
+
+// W[u][idx] = base[u] + the sum of the 32-bit pieces landing on chunk u:
+// piece j of an entry at row t lands on t + shift + j (the top piece signed,
+// the others unsigned).  The value is sum_u W[u] 2^(32 u), with no carries yet.
+// One thread per (u, component).
+__global__ __launch_bounds__(256) void chunk_sums_kernel(SumArgs a, int64_t *__restrict__ W) {
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= cp) return;
-    for (int64_t u = blockIdx.y; u < Tp; u += gridDim.y) {
+    if (idx >= a.cp) return;
+    for (int64_t u = blockIdx.y; u < a.Tp; u += gridDim.y) {
         int64_t w = 0;
-        if (idx < count && u < T) {
-            for (int j = 0; j < 2 * lcl && j <= u; j++) {
-                const uint32_t *pc = reinterpret_cast<const uint32_t *>(clo + ((u - j) * count + idx) * lcl);
-                w += j == 2 * lcl - 1 ? (int64_t)(int32_t)pc[j] : (int64_t)pc[j];
-            }
-            if (has_hi)
-                for (int j = 0; j < 2 * lch && j + 6 <= u; j++) {
-                    const uint32_t *pc = reinterpret_cast<const uint32_t *>(chi + ((u - 6 - j) * count + idx) * lch);
-                    w += j == 2 * lch - 1 ? (int64_t)(int32_t)pc[j] : (int64_t)pc[j];
+        if (idx < a.count && u < a.T) {
+            if (a.base && u < a.base_rows) w = a.base[u * a.count + idx];
+            if (u == a.bias_u) w += (int64_t)1 << 31;
+            for (int si = 0; si < a.nsrc; si++) {
+                const PieceSrc &ps = a.src[si];
+                int64_t v = 0;
+                for (int j = 0; j < 2 * ps.limbs; j++) {
+                    const int64_t t = u - ps.shift - j;
+                    if (t < 0) break;
+                    if (t >= ps.rows) continue;
+                    const uint32_t *pc = reinterpret_cast<const uint32_t *>(ps.p + (t * a.count + idx) * ps.limbs);
+                    v += j == 2 * ps.limbs - 1 ? (int64_t)(int32_t)pc[j] : (int64_t)pc[j];
                 }
+                w += ps.sign < 0 ? -v : v;
+            }
         }
-        W[u * cp + idx] = w;
+        W[u * a.cp + idx] = w;
     }
 }
 
 // The carry pass over W: chunk_u = (W[u] + carry) mod 2^32, carry = the
 // arithmetic shift by 32.  One lane per component walks its chunks in order;
 // its loads run 16 chunks ahead (unconditional: W's zero padding covers
-// every position up to 16 past the last 64-chunk block), and the chunks gather
-// in LDS and leave 64 at a time per component (256 contiguous bytes).  Chunks
-// at u >= T are dropped: X fits T chunks.
+// every position up to 16 past the last 64-chunk block).  Chunks at u >= T
+// are dropped: the value fits T chunks.  Output either as uint32 [count][T]
+// (the chunks gather in LDS and leave 64 at a time per component, 256
+// contiguous bytes) or, with out64, as int64 [T][count] chunk values, the top
+// one signed (the operand layout of a following product).
 constexpr int kCarryAhead = 16;
 
 __global__ __launch_bounds__(64) void chunk_carry_kernel(const int64_t *__restrict__ W, int64_t T, int64_t count,
-                                                         int64_t cp, uint32_t *__restrict__ out) {
+                                                         int64_t cp, uint32_t *__restrict__ out,
+                                                         int64_t *__restrict__ out64) {
     __shared__ uint32_t tile[64][65];
     const int lane = threadIdx.x;
-    const int64_t idx0 = (int64_t)blockIdx.x * 64;
-    const int64_t *wl = W + idx0 + lane;
+    const int64_t idx0 = (int64_t)blockIdx.x * 64, idx = idx0 + lane;
+    const int64_t *wl = W + idx;
     int64_t carry = 0;
     int64_t ra[kCarryAhead], rb[kCarryAhead];
 #define CHUNK_LOAD(r, tb)                                                      \
@@ -764,14 +787,71 @@ __global__ __launch_bounds__(64) void chunk_carry_kernel(const int64_t *__restri
         CHUNK_CARRY(ra, 32)
         CHUNK_LOAD(ra, t0 + 64)
         CHUNK_CARRY(rb, 48)
-        __syncthreads();
-        const int64_t t = t0 + lane;
-        for (int c = 0; c < 64; c++)
-            if (idx0 + c < count && t < T) out[(idx0 + c) * T + t] = tile[c][lane];
-        __syncthreads();
+        if (out64) {
+            if (idx < count)
+                for (int k = 0; k < 64 && t0 + k < T; k++) {
+                    const uint32_t ch = tile[lane][k];
+                    out64[(t0 + k) * count + idx] = t0 + k == T - 1 ? (int64_t)(int32_t)ch : (int64_t)ch;
+                }
+        } else {
+            __syncthreads();
+            const int64_t t = t0 + lane;
+            for (int c = 0; c < 64; c++)
+                if (idx0 + c < count && t < T) out[(idx0 + c) * T + t] = tile[c][lane];
+            __syncthreads();
+        }
     }
 #undef CHUNK_LOAD
 #undef CHUNK_CARRY
+}
+
+// Toeplitz matrix of a chunk vector: out[r][t] = c[r + r0 - t] inside 0..Tc-1,
+// else 0 ([rows][cols] int64), so out . x is the product c x restricted to
+// the chunk positions r0 .. r0 + rows - 1.
+__global__ __launch_bounds__(256) void toeplitz_kernel(const int64_t *__restrict__ c, int64_t Tc, int64_t rows,
+                                                       int64_t cols, int64_t r0, int64_t *__restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= cols) return;
+    for (int64_t r = blockIdx.y; r < rows; r += gridDim.y) {
+        const int64_t d = r + r0 - t;
+        out[r * cols + t] = d >= 0 && d < Tc ? c[d] : 0;
+    }
+}
+
+// The bound test of the numerators: ok = |w| <= B for w in Tw two's-complement
+// chunks and B >= 0 in TB chunks, without carries: with v = w (w >= 0) or the
+// bitwise complement of w (w < 0, then |w| <= B <=> v < B), the highest chunk
+// where v and B differ decides.  One wave per component; w leaves as w_limbs
+// int64 limbs when ok, zeros otherwise.
+__global__ __launch_bounds__(256) void chunk_bound_kernel(const uint32_t *__restrict__ w, int64_t Tw, int64_t count,
+                                                          const uint32_t *__restrict__ B, int64_t TB,
+                                                          int64_t *__restrict__ num, int w_limbs,
+                                                          int32_t *__restrict__ ok) {
+    const int l = threadIdx.x & 63;
+    const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (idx >= count) return;                             // no barriers below
+    const uint32_t *wi = w + idx * Tw;
+    const bool neg = (int32_t)wi[Tw - 1] < 0;
+    const uint32_t fill = neg ? ~0u : 0u;
+    const int64_t len = Tw > TB ? Tw : TB;
+    int64_t key = -1;                                     // 2 * (highest differing chunk) + (v < B there)
+    for (int64_t i = l; i < len; i += 64) {
+        const uint32_t wv = i < Tw ? wi[i] : fill;
+        const uint32_t v = neg ? ~wv : wv;
+        const uint32_t b = i < TB ? B[i] : 0u;
+        if (v != b) key = 2 * i + (v < b ? 1 : 0);
+    }
+    for (int off = 32; off > 0; off >>= 1) {
+        const int64_t o = __shfl_xor(key, off);
+        key = o > key ? o : key;
+    }
+    const bool good = key < 0 ? !neg : (key & 1) != 0;
+    if (l == 0) ok[idx] = good ? 1 : 0;
+    for (int li = l; li < w_limbs; li += 64) {
+        const int64_t c0 = 2 * (int64_t)li, c1 = c0 + 1;
+        const uint32_t lo = c0 < Tw ? wi[c0] : fill, hi = c1 < Tw ? wi[c1] : fill;
+        num[idx * w_limbs + li] = good ? (int64_t)(((uint64_t)hi << 32) | lo) : 0;
+    }
 }
 
 }  // namespace rns
@@ -986,6 +1066,21 @@ struct ChunkLayout {
     size_t g_bytes;
 };
 
+// W rows and columns for a carry pass over T chunks of count components:
+// zero padding for the read-ahead
+static int64_t carry_rows(int64_t T) { return (T + 63) / 64 * 64 + kCarryAhead; }
+static int64_t carry_cols(int64_t count) { return (count + 63) / 64 * 64; }
+
+// chunk sums into W, then the carry pass into out (uint32 [count][T]) or out64 (int64 [T][count])
+static int carry_chunks(const SumArgs &sa, int64_t *W, uint32_t *out, int64_t *out64, hipStream_t stream) {
+    const unsigned gy = (unsigned)(sa.Tp < 65535 ? sa.Tp : 65535);
+    hipLaunchKernelGGL(chunk_sums_kernel, dim3((unsigned)((sa.cp + 255) / 256), gy), dim3(256), 0, stream, sa, W);
+    if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
+    hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)(sa.cp / 64)), dim3(64), 0, stream, W, sa.T, sa.count,
+                       sa.cp, out, out64);
+    return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
+}
+
 static int chunk_layout(int64_t T, int32_t m, int64_t count, int32_t dl, int32_t P_bits, ChunkLayout &L) {
     if (T < 1 || m < 1 || count < 1 || dl < 1 || dl > RNS_MAX_OUT_LIMBS || P_bits < 2 || P_bits > 64 * dl)
         return RNS_E_ARG;
@@ -1015,14 +1110,76 @@ static int chunk_layout(int64_t T, int32_t m, int64_t count, int32_t dl, int32_t
     L.chi_off = off;
     off = pad256(off + (L.has_hi ? T * count * L.hi.out_limbs_min * 8 : 0));
     // W: [Tp][cp] with zero padding for the carry pass's read-ahead
-    L.wT = (T + 63) / 64 * 64 + kCarryAhead;
-    L.wc = (count + 63) / 64 * 64;
+    L.wT = carry_rows(T);
+    L.wc = carry_cols(count);
     L.w_off = off;
     off = pad256(off + L.wT * L.wc * 8);
     L.g_off = off;
     L.g_bytes = glo > ghi ? glo : ghi;
     L.total = off + (int64_t)L.g_bytes;
     return RNS_OK;
+}
+
+// The Barrett step on chunks: Y = D X ([TY][count], TY = T + TD), a = the
+// rows of Y from s1c, P1 = a mu + 2^(32 k2c - 1) ([TP1][count], TP1 = Ta +
+// Tmu), q = the rows of P1 from k2c, and (Y - q Pm) mod 2^(32 Tw).  Three
+// exact residue products with Toeplitz matrices of the constants' chunks.
+struct ModmulLayout {
+    int64_t TY, Ta, TP1, Tq;
+    rns_plan_t py, p1, pz;
+    int64_t toep_off, c_off, y_off, p1_off, w_off, g_off, total;
+    int64_t wT, wc;
+    size_t g_bytes;
+};
+
+static int modmul_layout(int64_t T, int64_t count, int64_t TD, int64_t Tmu, int64_t TP, int64_t s1c, int64_t k2c,
+                         int64_t Tw, ModmulLayout &L) {
+    if (T < 1 || count < 1 || TD < 1 || Tmu < 1 || TP < 1 || Tw < 1 || s1c < 0 || k2c < 1) return RNS_E_ARG;
+    L.TY = T + TD;
+    if (s1c >= L.TY || Tw > L.TY) return RNS_E_ARG;
+    L.Ta = L.TY - s1c;
+    L.TP1 = L.Ta + Tmu;
+    if (k2c >= L.TP1) return RNS_E_ARG;
+    L.Tq = L.TP1 - k2c;
+    if (L.TY * count > ((int64_t)1 << 40) || L.TP1 * count > ((int64_t)1 << 40)) return RNS_E_ARG;
+    // chunk entries: constants in [0, 2^32), operands' chunks of magnitude at most 2^32
+    int rc = rns_plan(T, 32, 32, &L.py);
+    if (rc == RNS_OK) rc = rns_plan(L.Ta, 32, 32, &L.p1);
+    if (rc == RNS_OK) rc = rns_plan(L.Tq, 32, 32, &L.pz);
+    if (rc != RNS_OK) return rc;
+    size_t g0 = 0, g1 = 0, g2 = 0;
+    rc = rns_workspace_size(&L.py, L.TY, count, T, 0, &g0);
+    if (rc == RNS_OK) rc = rns_workspace_size(&L.p1, L.TP1, count, L.Ta, 0, &g1);
+    if (rc == RNS_OK) rc = rns_workspace_size(&L.pz, Tw, count, L.Tq, 0, &g2);
+    if (rc != RNS_OK) return rc;
+    const int64_t toep = std::max(L.TY * T, std::max(L.TP1 * L.Ta, Tw * L.Tq));
+    const int64_t cbytes = std::max(L.TY * L.py.out_limbs_min, std::max(L.TP1 * L.p1.out_limbs_min,
+                                                                          Tw * L.pz.out_limbs_min)) * count * 8;
+    L.wT = carry_rows(std::max(L.TY, L.TP1));
+    L.wc = carry_cols(count);
+    int64_t off = 0;
+    L.toep_off = off;
+    off = pad256(off + toep * 8);
+    L.c_off = off;
+    off = pad256(off + cbytes);
+    L.y_off = off;
+    off = pad256(off + L.TY * count * 8);
+    L.p1_off = off;
+    off = pad256(off + L.TP1 * count * 8);
+    L.w_off = off;
+    off = pad256(off + L.wT * L.wc * 8);
+    L.g_off = off;
+    L.g_bytes = std::max(g0, std::max(g1, g2));
+    L.total = off + (int64_t)L.g_bytes;
+    return RNS_OK;
+}
+
+static int launch_toeplitz(const int64_t *c, int64_t Tc, int64_t rows, int64_t cols, int64_t *out,
+                           hipStream_t stream) {
+    const unsigned gy = (unsigned)(rows < 65535 ? rows : 65535);
+    hipLaunchKernelGGL(toeplitz_kernel, dim3((unsigned)((cols + 255) / 256), gy), dim3(256), 0, stream, c, Tc, rows,
+                       cols, (int64_t)0, out);
+    return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 
 int rns_plan_from_moduli(const int32_t *moduli, int32_t n, int64_t k_max, rns_plan_t *out) {
@@ -1108,8 +1265,8 @@ int rns_padic_chunks_workspace_size(int64_t T, int32_t m, int64_t count, int32_t
 }
 
 int rns_padic_chunks(const int64_t *pow, int64_t T, int32_t m, const int64_t *digits, int64_t count, int32_t d_limbs,
-                     int32_t P_bits, uint32_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
-    if (!pow || !digits || !out || !ws) return RNS_E_ARG;
+                     int32_t P_bits, int32_t layout, void *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!pow || !digits || !out || !ws || (layout != 0 && layout != 1)) return RNS_E_ARG;
     ChunkLayout L;
     int rc = chunk_layout(T, m, count, d_limbs, P_bits, L);
     if (rc != RNS_OK) return rc;
@@ -1132,13 +1289,93 @@ int rns_padic_chunks(const int64_t *pow, int64_t T, int32_t m, const int64_t *di
         if (rc != RNS_OK) return rc;
     }
     int64_t *W = reinterpret_cast<int64_t *>(base + L.w_off);
-    const unsigned gy = (unsigned)(L.wT < 65535 ? L.wT : 65535);
-    hipLaunchKernelGGL(chunk_sums_kernel, dim3((unsigned)((L.wc + 255) / 256), gy), dim3(256), 0, stream, clo,
-                       L.lo.out_limbs_min, chi, L.has_hi ? L.hi.out_limbs_min : 1, L.has_hi, T, count, L.wT, L.wc,
-                       W);
-    if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
-    hipLaunchKernelGGL(chunk_carry_kernel, dim3((unsigned)(L.wc / 64)), dim3(64), 0, stream, W, T, count, L.wc,
-                       out);
+    SumArgs sa{};
+    sa.src[0] = PieceSrc{clo, L.lo.out_limbs_min, 0, 1, T};
+    if (L.has_hi) sa.src[1] = PieceSrc{chi, L.hi.out_limbs_min, 6, 1, T};
+    sa.nsrc = L.has_hi ? 2 : 1;
+    sa.bias_u = -1;
+    sa.T = T;
+    sa.count = count;
+    sa.Tp = L.wT;
+    sa.cp = L.wc;
+    return carry_chunks(sa, W, layout ? nullptr : static_cast<uint32_t *>(out),
+                        layout ? static_cast<int64_t *>(out) : nullptr, stream);
+}
+
+
+int rns_chunk_modmul_workspace_size(int64_t T, int64_t count, int64_t TD, int64_t Tmu, int64_t TP, int64_t s1c,
+                                    int64_t k2c, int64_t Tw, size_t *bytes) {
+    if (!bytes) return RNS_E_ARG;
+    ModmulLayout L;
+    const int rc = modmul_layout(T, count, TD, Tmu, TP, s1c, k2c, Tw, L);
+    if (rc != RNS_OK) return rc;
+    *bytes = (size_t)L.total;
+    return RNS_OK;
+}
+
+int rns_chunk_modmul(const int64_t *X, int64_t T, int64_t count, const int64_t *Dc, int64_t TD, const int64_t *muc,
+                     int64_t Tmu, const int64_t *Pmc, int64_t TP, int64_t s1c, int64_t k2c, int64_t Tw,
+                     uint32_t *out, void *ws, size_t ws_bytes, hipStream_t stream) {
+    if (!X || !Dc || !muc || !Pmc || !out || !ws) return RNS_E_ARG;
+    ModmulLayout L;
+    int rc = modmul_layout(T, count, TD, Tmu, TP, s1c, k2c, Tw, L);
+    if (rc != RNS_OK) return rc;
+    if ((int64_t)ws_bytes < L.total) return RNS_E_WORKSPACE;
+    uint8_t *base = static_cast<uint8_t *>(ws);
+    int64_t *toep = reinterpret_cast<int64_t *>(base + L.toep_off);
+    int64_t *C = reinterpret_cast<int64_t *>(base + L.c_off);
+    int64_t *Y = reinterpret_cast<int64_t *>(base + L.y_off);
+    int64_t *P1 = reinterpret_cast<int64_t *>(base + L.p1_off);
+    int64_t *W = reinterpret_cast<int64_t *>(base + L.w_off);
+    void *g = base + L.g_off;
+    SumArgs sa{};
+    sa.nsrc = 1;
+    sa.bias_u = -1;
+    sa.count = count;
+    sa.cp = L.wc;
+    // Y = D X
+    rc = launch_toeplitz(Dc, TD, L.TY, T, toep, stream);
+    if (rc == RNS_OK) rc = rns_gemm(&L.py, L.TY, count, T, toep, 1, X, 1, C, L.py.out_limbs_min, g, L.g_bytes, stream);
+    if (rc != RNS_OK) return rc;
+    sa.src[0] = PieceSrc{C, L.py.out_limbs_min, 0, 1, L.TY};
+    sa.T = L.TY;
+    sa.Tp = carry_rows(L.TY);
+    rc = carry_chunks(sa, W, nullptr, Y, stream);
+    if (rc != RNS_OK) return rc;
+    // P1 = a mu + 2^(32 k2c - 1), a = floor(Y / 2^(32 s1c))
+    rc = launch_toeplitz(muc, Tmu, L.TP1, L.Ta, toep, stream);
+    if (rc == RNS_OK)
+        rc = rns_gemm(&L.p1, L.TP1, count, L.Ta, toep, 1, Y + s1c * count, 1, C, L.p1.out_limbs_min, g, L.g_bytes,
+                      stream);
+    if (rc != RNS_OK) return rc;
+    sa.src[0] = PieceSrc{C, L.p1.out_limbs_min, 0, 1, L.TP1};
+    sa.T = L.TP1;
+    sa.Tp = carry_rows(L.TP1);
+    sa.bias_u = k2c - 1;
+    rc = carry_chunks(sa, W, nullptr, P1, stream);
+    if (rc != RNS_OK) return rc;
+    // (Y - q Pm) mod 2^(32 Tw), q = floor(P1 / 2^(32 k2c))
+    rc = launch_toeplitz(Pmc, TP, Tw, L.Tq, toep, stream);
+    if (rc == RNS_OK)
+        rc = rns_gemm(&L.pz, Tw, count, L.Tq, toep, 1, P1 + k2c * count, 1, C, L.pz.out_limbs_min, g, L.g_bytes,
+                      stream);
+    if (rc != RNS_OK) return rc;
+    sa.src[0] = PieceSrc{C, L.pz.out_limbs_min, 0, -1, Tw};
+    sa.base = Y;
+    sa.base_rows = L.TY;
+    sa.bias_u = -1;
+    sa.T = Tw;
+    sa.Tp = carry_rows(Tw);
+    return carry_chunks(sa, W, out, nullptr, stream);
+}
+
+
+int rns_chunk_bound(const uint32_t *w, int64_t Tw, int64_t count, const uint32_t *B, int64_t TB, int64_t *num,
+                    int32_t w_limbs, int32_t *ok, hipStream_t stream) {
+    if (!w || !B || !num || !ok || Tw < 1 || count < 0 || TB < 1 || w_limbs < 1) return RNS_E_ARG;
+    if (count == 0) return RNS_OK;
+    hipLaunchKernelGGL(chunk_bound_kernel, dim3((unsigned)((count + 3) / 4)), dim3(256), 0, stream, w, Tw, count, B,
+                       TB, num, w_limbs, ok);
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 

@@ -267,9 +267,11 @@ def chunk_count(P: int, m: int) -> int:
     return ((P ** m).bit_length() + 1 + 31) // 32
 
 
-def padic_chunks(digits: torch.Tensor, P: int, m: int, table: Optional[np.ndarray] = None) -> torch.Tensor:
+def padic_chunks(digits: torch.Tensor, P: int, m: int, table: Optional[np.ndarray] = None,
+                 transposed: bool = False) -> torch.Tensor:
     """The p-adic values sum_s digits[s] P^s of every component as 32-bit two's-complement chunks,
-    int32 [count, T] on the device (rns_padic_chunks: two exact residue products and a carry pass).
+    int32 [count, T] on the device (rns_padic_chunks: two exact residue products and a carry pass),
+    or with ``transposed`` int64 [T, count] chunk values (the top one signed).
     ``table`` is ``pow_table(P, m, chunk_count(P, m))`` when the caller built it already (say while
     the lift ran)."""
     if digits.dim() != 3 or digits.dtype != torch.int64 or digits.device.type != "cuda":
@@ -286,12 +288,82 @@ def padic_chunks(digits: torch.Tensor, P: int, m: int, table: Optional[np.ndarra
     _check(load().rns_padic_chunks_workspace_size(T, m, count, dl, P.bit_length(), ctypes.byref(sz)),
            "rns_padic_chunks_workspace_size")
     ws = torch.empty(max(sz.value, 1), dtype=torch.uint8, device=digits.device)
-    out = torch.empty((count, T), dtype=torch.int32, device=digits.device)
+    if transposed:
+        out = torch.empty((T, count), dtype=torch.int64, device=digits.device)
+    else:
+        out = torch.empty((count, T), dtype=torch.int32, device=digits.device)
     with torch.cuda.device(digits.device):
         rc = load().rns_padic_chunks(pw.data_ptr(), T, m, digits.data_ptr(), count, dl, P.bit_length(),
-                                     out.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(digits))
+                                     int(transposed), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream_ptr(digits))
     _check(rc, "rns_padic_chunks")
     return out
+
+
+def _chunks_of(v: int, n: Optional[int] = None) -> np.ndarray:
+    """int64 vector of the 32-bit chunks of a non-negative integer (n of them, or as many as needed)."""
+    n = max(1, (v.bit_length() + 31) // 32) if n is None else n
+    return np.frombuffer(v.to_bytes(4 * n, "little"), dtype=np.uint32).astype(np.int64)
+
+
+class ModmulConstants:
+    """The fixed part of the GPU's one modular multiply per numerator (``chunk_modmul``) for P^m and
+    a denominator bound Db, computable before the digits exist (say while the lift runs).
+
+    With L = bits(P^m) and G = 64 guard bits: s1 = 32 floor((L - 1 - G) / 32), so 2^s1 <= P^m 2^-G;
+    |a| = |floor(D X / 2^s1)| <= Db P^m / 2^(s1 + 1) + 1 < 2^abits for any D <= Db and
+    |X| <= P^m / 2; k2 = 32 ceil((abits + G) / 32); mu = floor(2^(s1 + k2) / P^m).  Then the
+    rounded quotient is within 1/2 + 2^(1 - G) of D X / P^m, and Tw chunks hold |w| < P^m."""
+
+    G = 64
+
+    def __init__(self, P: int, m: int, Db: int, device):
+        Pm = P ** m
+        L = Pm.bit_length()
+        self.s1c = (L - 1 - self.G) // 32
+        abits = Db.bit_length() + L - 32 * self.s1c + 1
+        self.k2c = (abits + self.G + 31) // 32
+        mu = (1 << (32 * (self.s1c + self.k2c))) // Pm
+        self.Tw = L // 32 + 2
+        self.mu = torch.from_numpy(_chunks_of(mu)).to(device)
+        self.Pm = torch.from_numpy(_chunks_of(Pm)).to(device)
+
+
+def chunk_modmul(Xt: torch.Tensor, D: int, consts: ModmulConstants) -> torch.Tensor:
+    """w0 = D X - q P^m mod 2^(32 Tw) for every component (uint32 chunks as int32 [count, Tw] on the
+    device; rns_chunk_modmul): D X mod P^m up to one correction by +-P^m."""
+    if Xt.dim() != 2 or Xt.dtype != torch.int64 or Xt.device.type != "cuda":
+        raise ValueError("Xt must be an int64 [T, count] tensor on a GPU device")
+    Xt = Xt.contiguous()
+    T, count = Xt.shape
+    Dc = torch.from_numpy(_chunks_of(D)).to(Xt.device)
+    args = (T, count, Dc.numel(), consts.mu.numel(), consts.Pm.numel(), consts.s1c, consts.k2c, consts.Tw)
+    sz = ctypes.c_size_t()
+    _check(load().rns_chunk_modmul_workspace_size(*args, ctypes.byref(sz)), "rns_chunk_modmul_workspace_size")
+    ws = torch.empty(max(sz.value, 1), dtype=torch.uint8, device=Xt.device)
+    out = torch.empty((count, consts.Tw), dtype=torch.int32, device=Xt.device)
+    with torch.cuda.device(Xt.device):
+        rc = load().rns_chunk_modmul(Xt.data_ptr(), T, count, Dc.data_ptr(), Dc.numel(), consts.mu.data_ptr(),
+                                     consts.mu.numel(), consts.Pm.data_ptr(), consts.Pm.numel(), consts.s1c,
+                                     consts.k2c, consts.Tw, out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                     _stream_ptr(Xt))
+    _check(rc, "rns_chunk_modmul")
+    return out
+
+
+def chunk_bound(w: torch.Tensor, bound: int):
+    """(ok, numerators) on the device for chunk values w (int32 [count, Tw]): ok = |w| <= bound, the
+    numerator w as int64 limbs [count, limbs] when ok (rns_chunk_bound)."""
+    count, Tw = w.shape
+    B = torch.from_numpy(_chunks_of(bound).astype(np.uint32).view(np.int32)).to(w.device)
+    wl = bound.bit_length() // 64 + 1
+    num = torch.empty((max(count, 1), wl), dtype=torch.int64, device=w.device)
+    ok = torch.empty(max(count, 1), dtype=torch.int32, device=w.device)
+    with torch.cuda.device(w.device):
+        rc = load().rns_chunk_bound(w.data_ptr(), Tw, count, B.data_ptr(), B.numel(), num.data_ptr(), wl,
+                                    ok.data_ptr(), _stream_ptr(w))
+    _check(rc, "rns_chunk_bound")
+    return ok[:count], num[:count]
 
 
 def chunk_numerators(chunks: np.ndarray, P: int, m: int, D: int, bound: int, index=None, threads: int = 0):
@@ -350,14 +422,51 @@ def reconstruct_chunks(chunks: np.ndarray, P: int, m: int, Nb: int, Db: int, thr
                              chunks.shape[0], P, m, Nb, Db, threads)
 
 
+class ReconstructionPrep:
+    """What the reconstruction needs before the digits exist: the power table of ``padic_chunks``
+    and the constants of ``chunk_modmul`` (built on the host while the lift runs)."""
+
+    def __init__(self, P: int, m: int, Db: int, device):
+        self.table = pow_table(P, m, chunk_count(P, m))
+        self.consts = ModmulConstants(P, m, Db, device)
+
+
 def reconstruct_device(digits: torch.Tensor, P: int, m: int, Nb: int, Db: int,
-                       table: Optional[np.ndarray] = None):
-    """The reconstruction of device digits [m, count, limbs]: the p-adic values in binary on the GPU,
-    the common denominator and the numerators on the host (native; Python integers without GMP).
-    ``table``: the power table of ``padic_chunks``, if already built."""
+                       prep: Optional[ReconstructionPrep] = None):
+    """The reconstruction of device digits [m, count, limbs]: the p-adic values in binary and the
+    one modular multiply per numerator on the GPU; the sample's rational reconstruction, the
+    +-P^m correction and the bound test on the host (native; Python integers without GMP)."""
     if host_bigint_available():
-        chunks = padic_chunks(digits, P, m, table).cpu().numpy()   # synchronises
-        return reconstruct_chunks(chunks, P, m, Nb, Db)
+        if prep is None:
+            prep = ReconstructionPrep(P, m, Db, digits.device)
+        Xt = padic_chunks(digits, P, m, prep.table, transposed=True)
+        count = Xt.shape[1]
+        cache = {}
+
+        half = P ** m // 2
+
+        def numerators(D, bound, idx, threads):
+            if D == 1 and bound >= half:
+                # the balanced p-adic values themselves, from their chunk values
+                cols = Xt[:, torch.as_tensor(idx, device=Xt.device)].t().cpu().numpy()
+                raw = np.ascontiguousarray(cols.astype(np.uint32)).tobytes()
+                w = 4 * cols.shape[1]
+                return (np.ones(len(idx), dtype=bool),
+                        [int.from_bytes(raw[i * w:(i + 1) * w], "little", signed=True) for i in range(len(idx))])
+            if D > Db:
+                raise RnsError(-8, "a common denominator above the determinant bound")
+            key = (D, bound)
+            if key not in cache:
+                # D x mod P^m and the bound test on the GPU for every component (P^m > 2 D Nb (Db + 1))
+                cache.clear()
+                ok_d, num_d = chunk_bound(chunk_modmul(Xt, D, prep.consts), bound)
+                cache[key] = (ok_d.cpu().numpy().astype(bool), num_d.cpu().numpy())   # synchronises
+            ok_all, num_all = cache[key]
+            sel = np.asarray(idx, dtype=np.int64)
+            ok = ok_all[sel]
+            return ok, _limbs_to_int(num_all[sel])
+
+        return _reconstruct_with(numerators, count, P, m, Nb, Db)
     d = digits.cpu().numpy()
     per_step = [_limbs_to_int(d[s]) for s in range(m)]
     return reconstruct(per_step, P, m, Nb, Db)
@@ -399,10 +508,10 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
     P = math.prod(moduli)
     m = lift_steps_for(P, Nb, Db)
     digits = dixon_lift(p, A, b, planes, m)
-    # the lift runs asynchronously: build the radix-conversion table on the host meanwhile
-    table = pow_table(P, m, chunk_count(P, m)) if host_bigint_available() else None
+    # the lift runs asynchronously: build the reconstruction's tables on the host meanwhile
+    prep = ReconstructionPrep(P, m, Db, A.device) if host_bigint_available() else None
     c = bn.shape[1]
-    nums, D = reconstruct_device(digits.reshape(m, n * c, -1), P, m, Nb, Db, table)
+    nums, D = reconstruct_device(digits.reshape(m, n * c, -1), P, m, Nb, Db, prep)
     out = [[Fraction(nums[i * c + k], D) for k in range(c)] for i in range(n)]
     if return_info:
         return out, {"primes": moduli, "steps": m, "log2_P": math.log2(P), "denominator_bits": D.bit_length(),

@@ -108,7 +108,9 @@ int rns_padic_chunks_workspace_size(int64_t T, int32_t m, int64_t count, int32_t
 /*
  * rns_padic_chunks -- the p-adic values X_idx = sum_{s < m} digits[s][idx] P^s
  * of every component, as T little-endian 32-bit two's-complement chunks:
- * out is device uint32 [count][T].  digits: device int64 [m][count][d_limbs]
+ * layout 0: out is device uint32 [count][T]; layout 1: out is device int64
+ * [T][count], each chunk's value (the top chunk signed, the others in
+ * [0, 2^32)), the operand layout of rns_chunk_modmul.  digits: device int64 [m][count][d_limbs]
  * (rns_dixon_lift's output, |digit| < 2^(P_bits - 1)); pow: device int64
  * [T][m], pow[t][s] = chunk t of P^s (in [0, 2^32)), built by the caller.
  * 32 T must exceed the bit length of P^m (then |X| <= (P^m - 1)/2 fits).
@@ -118,7 +120,54 @@ int rns_padic_chunks_workspace_size(int64_t T, int32_t m, int64_t count, int32_t
  * RNS_E_HIP.
  */
 int rns_padic_chunks(const int64_t *pow, int64_t T, int32_t m, const int64_t *digits, int64_t count, int32_t d_limbs,
-                     int32_t P_bits, uint32_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
+                     int32_t P_bits, int32_t layout, void *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rns_chunk_modmul_workspace_size -- device bytes of rns_chunk_modmul.
+ * Returns RNS_OK, RNS_E_ARG or RNS_E_K.
+ */
+int rns_chunk_modmul_workspace_size(int64_t T, int64_t count, int64_t TD, int64_t Tmu, int64_t TP, int64_t s1c,
+                                    int64_t k2c, int64_t Tw, size_t *bytes);
+
+/*
+ * rns_chunk_modmul -- the one modular multiply per numerator (exact-solve,
+ * "Method": the numerators are D x mod P^m for the common denominator D) as a
+ * Barrett step on the GPU, for every component at once.  With the
+ * non-negative integers D, mu and Pm given by their 32-bit chunks (device
+ * int64 vectors Dc[TD], muc[Tmu], Pmc[TP], values in [0, 2^32)) and X_idx the
+ * signed integer of the chunks X[0..T)[idx] (device int64 [T][count], layout
+ * 1 of rns_padic_chunks), it writes
+ *   Y = D X,  a = floor(Y / 2^(32 s1c)),
+ *   q = floor((a mu + 2^(32 k2c - 1)) / 2^(32 k2c)),
+ *   out[idx] = (Y - q Pm) mod 2^(32 Tw)   (device uint32 [count][Tw], two's complement).
+ * With mu = floor(2^(32 (s1c + k2c)) / Pm), 2^(32 s1c) <= Pm 2^-G and
+ * |a| <= 2^(32 k2c - G) for G >= 2, |Y / Pm - q| < 1/2 + 2^(1 - G): the result
+ * is D X mod Pm up to one correction by +-Pm, which the caller makes (and Tw
+ * chunks must hold Pm in two's complement).  Three exact residue products
+ * with Toeplitz matrices of the constants' chunks and three carry passes.
+ * Requires Tw <= T + TD, s1c < T + TD, k2c < T + TD - s1c + Tmu, and the
+ * contraction lengths T, T + TD - s1c and T + TD - s1c + Tmu - k2c at most
+ * 2^17.  Returns RNS_OK, RNS_E_ARG, RNS_E_K, RNS_E_WORKSPACE or RNS_E_HIP.
+ */
+int rns_chunk_modmul(const int64_t *X, int64_t T, int64_t count, const int64_t *Dc, int64_t TD, const int64_t *muc,
+                     int64_t Tmu, const int64_t *Pmc, int64_t TP, int64_t s1c, int64_t k2c, int64_t Tw,
+                     uint32_t *out, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rns_chunk_bound -- the bound test of the numerators (exact-solve, "Method":
+ * a numerator over the common denominator is accepted when it lies within
+ * the bound): ok[idx] = 1 and num[idx] = w_idx as w_limbs int64 two's-complement
+ * limbs when |w_idx| <= B, else ok[idx] = 0 and num[idx] = 0.  w: device
+ * uint32 [count][Tw] two's complement (rns_chunk_modmul's output); B: device
+ * uint32 [TB], a non-negative integer; num: device int64 [count][w_limbs]
+ * (w_limbs must hold B plus a sign); ok: device int32 [count].  For
+ * rns_chunk_modmul's output with G >= 63 (|w| < (1/2 + 2^-62) Pm, w congruent
+ * to D X) and Pm > 2 B (1 + 2^-60), |w| <= B holds exactly when it holds for
+ * the balanced residue of D X mod Pm, and then the two are equal: no
+ * correction by +-Pm is needed.  Returns RNS_OK, RNS_E_ARG or RNS_E_HIP.
+ */
+int rns_chunk_bound(const uint32_t *w, int64_t Tw, int64_t count, const uint32_t *B, int64_t TB, int64_t *num,
+                    int32_t w_limbs, int32_t *ok, hipStream_t stream);
 
 /*
  * ---- host stage (exact-solve, "Method": the final rational reconstruction is

@@ -242,3 +242,72 @@ def test_padic_chunks_match_the_oracle(n_primes, m, count):
         got = int.from_bytes(chunks[i].tobytes(), "little", signed=True)
         assert got == ref[i][0], i
     assert 32 * T > (P ** m).bit_length()
+    # the operand layout: int64 [T][count] chunk values, the top one signed
+    cols = rg.exact_solve.padic_chunks(dev(dig), P, m, transposed=True).cpu().numpy()
+    assert cols.shape == (T, count)
+    assert np.array_equal(cols[:-1].T.astype(np.uint32), chunks[:, :-1])
+    assert np.array_equal(cols[-1], chunks[:, -1].view(np.int32).astype(np.int64))
+
+
+@pytest.mark.parametrize("n_primes,m,count,dbits", [(3, 6, 70, 50), (20, 9, 130, 700), (50, 12, 65, 2500),
+                                                    (53, 4, 1, 10)])
+def test_chunk_modmul_is_d_times_x_mod_pm(n_primes, m, count, dbits):
+    """The GPU's one modular multiply per numerator: (D X - q P^m) mod 2^(32 Tw) equal to the Barrett
+    step written out in Python integers, congruent to D X mod P^m and below P^m in magnitude, for
+    balanced p-adic values (extremes included) and denominators up to the bound."""
+    from oracle import oracle as O
+    rng = random.Random(n_primes + m)
+    P = math.prod(ODD_PRIMES[:n_primes])
+    Pm = P ** m
+    half = (Pm - 1) // 2
+    Db = (1 << dbits) - 1
+    L = (P.bit_length() + 64) // 64
+    vals = [[rng.randrange(-(P // 2), P // 2 + 1) for _ in range(count)] for _ in range(m)]
+    vals[m - 1][0] = P // 2                             # the largest value, then its negative
+    if count > 1:
+        vals[m - 1][1] = -(P // 2)
+    dig = np.zeros((m, count, L), dtype=np.int64)
+    for s_ in range(m):
+        for i in range(count):
+            dig[s_, i] = O.to_limbs(vals[s_][i], L)
+    X = D.padic_value([[[v] for v in row] for row in vals], P)
+    consts = rg.exact_solve.ModmulConstants(P, m, Db, torch.device("cuda", 0))
+    mu = sum(int(v) << (32 * i) for i, v in enumerate(consts.mu.cpu().tolist()))
+    Xt = rg.exact_solve.padic_chunks(dev(dig), P, m, transposed=True)
+    for Dv in (Db, rng.randrange(1, Db), 1):
+        print(f"chunk modmul primes={n_primes} m={m} count={count} D bits={Dv.bit_length()}", flush=True)
+        w0 = rg.exact_solve.chunk_modmul(Xt, Dv, consts).cpu().numpy().view(np.uint32)
+        assert w0.shape == (count, consts.Tw)
+        for i in range(count):
+            got = int.from_bytes(w0[i].tobytes(), "little", signed=True)
+            x = X[i][0]
+            assert abs(x) <= half
+            Y = Dv * x
+            q = ((Y >> (32 * consts.s1c)) * mu + (1 << (32 * consts.k2c - 1))) >> (32 * consts.k2c)
+            assert got == Y - q * Pm, (Dv.bit_length(), i)
+            assert (got - Y) % Pm == 0 and abs(got) < Pm
+
+
+@pytest.mark.parametrize("Tw,bbits", [(5, 70), (40, 1000), (300, 5000), (3, 94)])
+def test_chunk_bound_edges(Tw, bbits):
+    """The numerators' bound test: ok exactly when |w| <= B, at B, B + 1, -B, -B - 1, 0, -1, the
+    extremes of Tw chunks and random values; the numerator's limbs when ok, zeros otherwise."""
+    rng = random.Random(Tw)
+    B = rng.getrandbits(bbits) | (1 << (bbits - 1))
+    top = 2 ** (32 * Tw - 1)
+    vals = [B, B + 1, -B, -B - 1, 0, -1, 1, top - 1, -top, B - 1, -(B - 1)]
+    vals += [rng.randrange(-B, B + 1) for _ in range(40)] + [rng.randrange(-top, top) for _ in range(20)]
+    vals += [rng.choice([-1, 1]) * (B + rng.randrange(1, 2 ** 40)) for _ in range(10)]
+    w = np.zeros((len(vals), Tw), dtype=np.uint32)
+    for i, v in enumerate(vals):
+        w[i] = np.frombuffer((v % (1 << (32 * Tw))).to_bytes(4 * Tw, "little"), dtype=np.uint32)
+    print(f"chunk bound Tw={Tw} B bits={bbits}", flush=True)
+    ok, num = rg.exact_solve.chunk_bound(torch.from_numpy(w.view(np.int32)).cuda(), B)
+    ok = ok.cpu().numpy()
+    num = num.cpu().numpy()
+    wl = num.shape[1]
+    assert wl * 64 > bbits
+    for i, v in enumerate(vals):
+        assert bool(ok[i]) == (abs(v) <= B), (i, v)
+        got = int.from_bytes(num[i].tobytes(), "little", signed=True)
+        assert got == (v if abs(v) <= B else 0), i

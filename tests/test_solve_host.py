@@ -247,3 +247,33 @@ def test_native_numerators_from_chunks_equal_from_digits():
         assert list(ok1) == list(ok2) and w1 == w2
     ok, w = S.chunk_numerators(chunks, P, m, 1, P ** m // 2)
     assert ok.all() and w == X
+
+
+def _barrett_step(X, D, c, Pm):
+    """The integer function rns_chunk_modmul computes, in Python integers."""
+    Y = D * X
+    a = Y >> (32 * c.s1c)
+    mu = sum(int(v) << (32 * i) for i, v in enumerate(c.mu.tolist()))
+    q = (a * mu + (1 << (32 * c.k2c - 1))) >> (32 * c.k2c)
+    return Y - q * Pm
+
+
+@pytest.mark.parametrize("n_primes,m,dbits", [(3, 5, 40), (12, 40, 900), (50, 30, 3000)])
+def test_modmul_constants_leave_one_correction(n_primes, m, dbits):
+    """The Barrett constants: for every D <= Db and |X| <= P^m / 2, D X - q P^m is congruent to
+    D X mod P^m and below P^m in magnitude (one +-P^m correction gives the balanced residue), and
+    fits the Tw output chunks; extremes of D and X included."""
+    P = O.prod(O.primes_largest_first()[1:1 + n_primes])
+    Pm = P ** m
+    Db = (1 << dbits) - 1
+    c = S.ModmulConstants(P, m, Db, "cpu")
+    assert sum(int(v) << (32 * i) for i, v in enumerate(c.Pm.tolist())) == Pm
+    rng = random.Random(n_primes)
+    half = (Pm - 1) // 2
+    cases = [(Db, half), (Db, -half), (1, half), (Db, 0), (Db - 1, -1)]
+    cases += [(rng.randrange(1, Db + 1), rng.randrange(-half, half + 1)) for _ in range(200)]
+    for D, X in cases:
+        w0 = _barrett_step(X, D, c, Pm)
+        assert (w0 - D * X) % Pm == 0
+        assert abs(w0) < Pm and abs(w0) < 2 ** (32 * c.Tw - 1)
+        assert abs(w0) <= Pm // 2 + Pm // 2 ** 60
