@@ -544,22 +544,27 @@ __device__ __forceinline__ int residue_i64(int64_t v, int q) {
     return t - q * (int)__builtin_rintf((float)t / (float)q);
 }
 
+template <int W>
 __global__ __launch_bounds__(256) void lift_digit_kernel(LiftConsts lc, const int8_t *__restrict__ Binv, int64_t n,
                                                          int64_t c, const int8_t *__restrict__ rres, int64_t npad,
                                                          int64_t *__restrict__ digits, int dl,
                                                          int64_t *__restrict__ xlow) {
-    __shared__ int32_t part[4][64][kMaxPrimes + 1];
-    __shared__ int32_t uu[4][kMaxPrimes];
-    __shared__ float fs[4][kMaxPrimes];
-    __shared__ int64_t ss[4][kLiftChunks];
+    constexpr int R = 4 / W;                               // rows per block
+    __shared__ int32_t part[R][64][kMaxPrimes + 1];
+    __shared__ int32_t uu[R][kMaxPrimes];
+    __shared__ float fs[R][kMaxPrimes];
+    __shared__ int64_t ss[R][kLiftChunks];
     const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * 4 + wv;
+    const int rw = wv / W, ww = wv % W;                    // the wave's row in the block, its place in the row
+    const int64_t i = (int64_t)blockIdx.x * R + rw;
     const bool row_ok = i < n;
+    const bool lead = ww == 0;                             // the row's first wave finishes the digit
     const int E = lc.E;
     const int64_t runs = npad / 16;
     for (int64_t cc = 0; cc < c; cc++) {
-        // eight moduli at a time: 8 partial sums and 16 loads in flight per lane
-        for (int e0 = 0; e0 < E; e0 += 8) {
+        // the row's W waves take alternate batches of eight moduli: 8 partial sums and 16 loads in
+        // flight per lane
+        for (int e0 = 8 * ww; e0 < E; e0 += 8 * W) {
             int acc[8];
 #pragma unroll
             for (int u = 0; u < 8; u++) acc[u] = 0;
@@ -581,35 +586,35 @@ __global__ __launch_bounds__(256) void lift_digit_kernel(LiftConsts lc, const in
             }
 #pragma unroll
             for (int u = 0; u < 8; u++)
-                if (e0 + u < E) part[wv][l][e0 + u] = acc[u];
+                if (e0 + u < E) part[rw][l][e0 + u] = acc[u];
         }
         __syncthreads();
-        if (l < E) {
+        if (lead && l < E) {
             int64_t t = 0;                                  // |t| < 2^31 (n <= 2^17, |entries| < 128)
-            for (int j = 0; j < 64; j++) t += part[wv][j][l];
+            for (int j = 0; j < 64; j++) t += part[rw][j][l];
             const int q = lc.q[l];
             const int y = (int)(t - (int64_t)q * (int64_t)__builtin_rint((double)t / (double)q));
             const int yw = y * lc.w[l];                      // |yw| < 2^14
             const int u = yw - q * (int)__builtin_rintf((float)yw / (float)q);
-            uu[wv][l] = u;
-            fs[wv][l] = (float)u / (float)q;
+            uu[rw][l] = u;
+            fs[rw][l] = (float)u / (float)q;
         }
         __syncthreads();
-        if (l < lc.nch) {
+        if (lead && l < lc.nch) {
             int64_t s = 0;                                  // |s| < 2^45
-            for (int e = 0; e < E; e++) s += (int64_t)uu[wv][e] * (int64_t)lc.M[e][l];
-            ss[wv][l] = s;
+            for (int e = 0; e < E; e++) s += (int64_t)uu[rw][e] * (int64_t)lc.M[e][l];
+            ss[rw][l] = s;
         }
         __syncthreads();
-        if (l == 0 && row_ok) {
+        if (lead && l == 0 && row_ok) {
             float f = 0.0f;
-            for (int e = 0; e < E; e++) f += fs[wv][e];
+            for (int e = 0; e < E; e++) f += fs[rw][e];
             const int64_t r = (int64_t)__builtin_rintf(f);
             // X = sum - r P in 32-bit chunks with a sign word
             uint32_t x[kLiftChunks];
             int64_t carry = 0;
             for (int j = 0; j < kLiftChunks; j++) {
-                const int64_t v = (j < lc.nch ? ss[wv][j] - r * (int64_t)lc.P[j] : 0) + carry;
+                const int64_t v = (j < lc.nch ? ss[rw][j] - r * (int64_t)lc.P[j] : 0) + carry;
                 x[j] = (uint32_t)v;
                 carry = v >> 32;
             }
@@ -652,29 +657,50 @@ __global__ __launch_bounds__(256) void lift_digit_kernel(LiftConsts lc, const in
 
 // r <- (r - A x_low) P^-1 mod 2^64 per row (first: r <- b), then the residues of
 // the new r mod every modulus into rres[e][cc][i].
+template <int W>
 __global__ __launch_bounds__(256) void lift_update_kernel(LiftConsts lc, const int64_t *__restrict__ A, int64_t n,
                                                           int64_t c, const int64_t *__restrict__ xlow,
                                                           int64_t *__restrict__ r, uint64_t p_inv,
                                                           int8_t *__restrict__ rres, int64_t npad, int first,
                                                           const int64_t *__restrict__ b) {
+    constexpr int R = 4 / W;                              // rows per block; W waves share a row's k range
+    __shared__ uint64_t part[4];
     const int wv = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int64_t i = (int64_t)blockIdx.x * 4 + wv;
-    if (i >= n) return;                                   // no barriers below
+    const int rw = wv / W, ww = wv % W;
+    const int64_t i = (int64_t)blockIdx.x * R + rw;
+    const bool row_ok = i < n;
     for (int64_t cc = 0; cc < c; cc++) {
-        int64_t v;
-        if (first) {
-            v = b[i * c + cc];
-        } else {
-            uint64_t s = 0;
-            for (int64_t k = l; k < n; k += 64) s += (uint64_t)A[i * n + k] * (uint64_t)xlow[cc * n + k];
+        uint64_t s = 0;
+        if (!first && row_ok) {
+            const int64_t *Ai = A + i * n;
+            const int64_t *xc = xlow + cc * n;
+            int64_t k = (int64_t)ww * 64 + l;
+            // four products in flight per lane
+            for (; k + 3 * 64 * W < n; k += 4 * 64 * W) {
+                const uint64_t a0 = (uint64_t)Ai[k], a1 = (uint64_t)Ai[k + 64 * W];
+                const uint64_t a2 = (uint64_t)Ai[k + 128 * W], a3 = (uint64_t)Ai[k + 192 * W];
+                const uint64_t x0 = (uint64_t)xc[k], x1 = (uint64_t)xc[k + 64 * W];
+                const uint64_t x2 = (uint64_t)xc[k + 128 * W], x3 = (uint64_t)xc[k + 192 * W];
+                s += a0 * x0 + a1 * x1 + a2 * x2 + a3 * x3;
+            }
+            for (; k < n; k += 64 * W) s += (uint64_t)Ai[k] * (uint64_t)xc[k];
             for (int off = 32; off > 0; off >>= 1) {
                 const uint32_t lo = __shfl_xor((uint32_t)s, off), hi = __shfl_xor((uint32_t)(s >> 32), off);
                 s += ((uint64_t)hi << 32) | lo;
             }
-            v = (int64_t)(((uint64_t)r[i * c + cc] - s) * p_inv);
         }
-        if (l == 0) r[i * c + cc] = v;
-        if (l < lc.E) rres[((int64_t)l * c + cc) * npad + i] = (int8_t)residue_i64(v, lc.q[l]);
+        if (W > 1) {
+            if (l == 0) part[wv] = s;
+            __syncthreads();
+            if (ww == 0)
+                for (int w2 = 1; w2 < W; w2++) s += part[wv + w2];
+            __syncthreads();
+        }
+        if (ww == 0 && row_ok) {
+            const int64_t v = first ? b[i * c + cc] : (int64_t)(((uint64_t)r[i * c + cc] - s) * p_inv);
+            if (l == 0) r[i * c + cc] = v;
+            if (l < lc.E) rres[((int64_t)l * c + cc) * npad + i] = (int8_t)residue_i64(v, lc.q[l]);
+        }
     }
 }
 
@@ -1225,15 +1251,34 @@ int rns_dixon_lift(const rns_plan_t *plan, int64_t n, int64_t c, const int8_t *B
                 int64_t *r = reinterpret_cast<int64_t *>(base);
                 int64_t *xlow = reinterpret_cast<int64_t *>(base + r_bytes);
                 int8_t *rres = reinterpret_cast<int8_t *>(base + r_bytes + x_bytes);
-                const unsigned grid = (unsigned)((n + 3) / 4);
-                hipLaunchKernelGGL(lift_update_kernel, dim3(grid), dim3(256), 0, stream, lc, A, n, c, xlow, r, inv,
-                                   rres, n, 1, b);
+                // each row's work spread over W waves: W = 4 up to 1024 rows and 2 up to 2048 (4n waves,
+                // all resident at once); above, one wave per row
+                const int W = n <= 1024 ? 4 : (n <= 2048 ? 2 : 1);
+                const unsigned grid = (unsigned)((n * W + 3) / 4);
+                auto update = [&](int first) {
+                    if (W == 4)
+                        hipLaunchKernelGGL(lift_update_kernel<4>, dim3(grid), dim3(256), 0, stream, lc, A, n, c, xlow,
+                                           r, inv, rres, n, first, b);
+                    else if (W == 2)
+                        hipLaunchKernelGGL(lift_update_kernel<2>, dim3(grid), dim3(256), 0, stream, lc, A, n, c, xlow,
+                                           r, inv, rres, n, first, b);
+                    else
+                        hipLaunchKernelGGL(lift_update_kernel<1>, dim3(grid), dim3(256), 0, stream, lc, A, n, c, xlow,
+                                           r, inv, rres, n, first, b);
+                };
+                update(1);
                 for (int st = 0; st < steps; st++) {
                     int64_t *xs = digits + (int64_t)st * n * c * d_limbs;
-                    hipLaunchKernelGGL(lift_digit_kernel, dim3(grid), dim3(256), 0, stream, lc, Binv, n, c, rres, n,
-                                       xs, d_limbs, xlow);
-                    hipLaunchKernelGGL(lift_update_kernel, dim3(grid), dim3(256), 0, stream, lc, A, n, c, xlow, r,
-                                       inv, rres, n, 0, b);
+                    if (W == 4)
+                        hipLaunchKernelGGL(lift_digit_kernel<4>, dim3(grid), dim3(256), 0, stream, lc, Binv, n, c,
+                                           rres, n, xs, d_limbs, xlow);
+                    else if (W == 2)
+                        hipLaunchKernelGGL(lift_digit_kernel<2>, dim3(grid), dim3(256), 0, stream, lc, Binv, n, c,
+                                           rres, n, xs, d_limbs, xlow);
+                    else
+                        hipLaunchKernelGGL(lift_digit_kernel<1>, dim3(grid), dim3(256), 0, stream, lc, Binv, n, c,
+                                           rres, n, xs, d_limbs, xlow);
+                    update(0);
                 }
                 return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
             }

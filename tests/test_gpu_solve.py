@@ -77,6 +77,40 @@ def test_lift_digits_match_oracle(n, c):
         assert [[int(v) for v in row] for row in got] == ref[s], s
 
 
+@pytest.mark.parametrize("n,c", [(1040, 1), (2064, 2)])
+def test_lift_digits_large_p_adic_identity(n, c):
+    """The fused lift where a row's work is spread over two waves (up to 2048 rows) or one: its first
+    three digits x_s (balanced, |x_s| < P/2) satisfy A (x_0 + x_1 P + x_2 P^2) = b mod P^3, checked
+    mod q^3 for every prime q of P (P^3 divides v exactly when every q^3 does), which fixes the
+    balanced digits uniquely."""
+    from oracle import oracle as O
+    rng = np.random.default_rng(n)
+    A = rng.integers(-2 ** 15, 2 ** 15, size=(n, n))
+    b = rng.integers(-2 ** 15, 2 ** 15, size=(n, c))
+    print(f"lift digits n={n} c={c}", flush=True)
+    singular, ws = rg.batched_inverse(dev(A))
+    sel = [i for i, s_ in enumerate(singular.cpu().tolist()) if not s_]
+    moduli = [ODD_PRIMES[i] for i in sel]
+    P = math.prod(moduli)
+    p = rg.plan_from_moduli(moduli, n)
+    planes = rg.inverse_planes(ws, n, sel)
+    del ws
+    digits = rg.dixon_lift(p, dev(A), dev(b), planes, 3).cpu().numpy()
+    xs = [O.decode_array(digits[s_]) for s_ in range(3)]          # [n][c] Python ints per step
+    for s_ in range(3):
+        assert all(abs(int(v)) < P // 2 + 1 for row in xs[s_] for v in row)
+    for q in moduli:
+        qk = q ** 3
+        X = np.array([[(int(xs[0][i][k]) + int(xs[1][i][k]) * P + int(xs[2][i][k]) * P * P) % qk
+                       for k in range(c)] for i in range(n)], dtype=np.int64)
+        # A X mod q^3 from two float64 products of 12-bit halves of X (sums below 2^47: exact)
+        Af = (A % qk).astype(np.float64)
+        lo = (Af @ (X & 4095).astype(np.float64)).astype(np.int64)
+        hi = (Af @ (X >> 12).astype(np.float64)).astype(np.int64)
+        res = ((hi % qk) * 4096 + lo - b) % qk
+        assert not res.any(), q
+
+
 @pytest.mark.parametrize("seed,n,c", [(3, 5, 1), (4, 16, 3), (5, 40, 2), (6, 1, 1)])
 def test_solve_matches_fraction_elimination(seed, n, c):
     print(f"solve n={n} c={c}", flush=True)
