@@ -254,7 +254,7 @@ def solve_bench(args):
         e3.record(stream)
         # the reconstruction's tables are built on the host while the lift runs, as solve() does
         t_tab = time.perf_counter()
-        prep = XS.ReconstructionPrep(P, m, Db, dev) if native else None
+        prep = XS.ReconstructionPrep(P, m, Db, dev, Nb, n * c) if native else None
         t_tab = time.perf_counter() - t_tab
         e3.synchronize()
         t_host = time.perf_counter()

@@ -139,7 +139,7 @@ def load() -> ctypes.CDLL:
                                                            ctypes.POINTER(SZ)]),
         "rns_chunk_modmul": (ctypes.c_int, [VP, I64, I64, VP, I64, VP, I64, VP, I64, I64, I64, I64, VP, VP, SZ,
                                             VP]),
-        "rns_chunk_bound": (ctypes.c_int, [VP, I64, I64, VP, I64, VP, I32, VP, VP]),
+        "rns_chunk_bound": (ctypes.c_int, [VP, I64, I64, VP, I64, VP, I32, VP, VP, VP]),
         "rns_chunk_numerators": (ctypes.c_int, [VP, I64, I64, VP, I64, VP, I32, I32, VP, I32, VP, I32, VP,
                                                 I32, VP, I32]),
         "rns_sliced_plan": (ctypes.c_int, [I64, I32, I32, ctypes.POINTER(_SlicedPlan)]),

@@ -852,7 +852,7 @@ __global__ __launch_bounds__(256) void toeplitz_kernel(const int64_t *__restrict
 __global__ __launch_bounds__(256) void chunk_bound_kernel(const uint32_t *__restrict__ w, int64_t Tw, int64_t count,
                                                           const uint32_t *__restrict__ B, int64_t TB,
                                                           int64_t *__restrict__ num, int w_limbs,
-                                                          int32_t *__restrict__ ok) {
+                                                          int32_t *__restrict__ ok, int32_t *__restrict__ used) {
     const int l = threadIdx.x & 63;
     const int64_t idx = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (idx >= count) return;                             // no barriers below
@@ -861,18 +861,26 @@ __global__ __launch_bounds__(256) void chunk_bound_kernel(const uint32_t *__rest
     const uint32_t fill = neg ? ~0u : 0u;
     const int64_t len = Tw > TB ? Tw : TB;
     int64_t key = -1;                                     // 2 * (highest differing chunk) + (v < B there)
+    int64_t top = -1;                                     // the highest chunk of w that is not sign fill
     for (int64_t i = l; i < len; i += 64) {
         const uint32_t wv = i < Tw ? wi[i] : fill;
         const uint32_t v = neg ? ~wv : wv;
         const uint32_t b = i < TB ? B[i] : 0u;
         if (v != b) key = 2 * i + (v < b ? 1 : 0);
+        if (v != 0) top = i;
     }
     for (int off = 32; off > 0; off >>= 1) {
-        const int64_t o = __shfl_xor(key, off);
+        const int64_t o = __shfl_xor(key, off), ot = __shfl_xor(top, off);
         key = o > key ? o : key;
+        top = ot > top ? ot : top;
     }
     const bool good = key < 0 ? !neg : (key & 1) != 0;
-    if (l == 0) ok[idx] = good ? 1 : 0;
+    if (l == 0) {
+        ok[idx] = good ? 1 : 0;
+        // limbs that hold w with its sign: the chunks up to top, and one more for the sign bit
+        const int64_t lim = (top + 2) / 2 + 1;
+        used[idx] = good ? (int32_t)(lim < w_limbs ? lim : w_limbs) : 0;
+    }
     for (int li = l; li < w_limbs; li += 64) {
         const int64_t c0 = 2 * (int64_t)li, c1 = c0 + 1;
         const uint32_t lo = c0 < Tw ? wi[c0] : fill, hi = c1 < Tw ? wi[c1] : fill;
@@ -1416,11 +1424,11 @@ int rns_chunk_modmul(const int64_t *X, int64_t T, int64_t count, const int64_t *
 
 
 int rns_chunk_bound(const uint32_t *w, int64_t Tw, int64_t count, const uint32_t *B, int64_t TB, int64_t *num,
-                    int32_t w_limbs, int32_t *ok, hipStream_t stream) {
-    if (!w || !B || !num || !ok || Tw < 1 || count < 0 || TB < 1 || w_limbs < 1) return RNS_E_ARG;
+                    int32_t w_limbs, int32_t *ok, int32_t *used, hipStream_t stream) {
+    if (!w || !B || !num || !ok || !used || Tw < 1 || count < 0 || TB < 1 || w_limbs < 1) return RNS_E_ARG;
     if (count == 0) return RNS_OK;
     hipLaunchKernelGGL(chunk_bound_kernel, dim3((unsigned)((count + 3) / 4)), dim3(256), 0, stream, w, Tw, count, B,
-                       TB, num, w_limbs, ok);
+                       TB, num, w_limbs, ok, used);
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 

@@ -119,7 +119,7 @@ def _limbs_to_int(limbs: np.ndarray) -> List[int]:
     """int64 [..., L] two's-complement limbs -> Python ints (flattened)."""
     L = limbs.shape[-1]
     flat = np.ascontiguousarray(limbs.reshape(-1, L), dtype=np.int64)
-    raw = flat.tobytes()
+    raw = memoryview(flat).cast("B")          # no copy
     w = 8 * L
     return [int.from_bytes(raw[i * w:(i + 1) * w], "little", signed=True) for i in range(flat.shape[0])]
 
@@ -352,18 +352,20 @@ def chunk_modmul(Xt: torch.Tensor, D: int, consts: ModmulConstants) -> torch.Ten
 
 
 def chunk_bound(w: torch.Tensor, bound: int):
-    """(ok, numerators) on the device for chunk values w (int32 [count, Tw]): ok = |w| <= bound, the
-    numerator w as int64 limbs [count, limbs] when ok (rns_chunk_bound)."""
+    """(ok, numerators, used) on the device for chunk values w (int32 [count, Tw]): ok = |w| <=
+    bound, the numerator w as int64 limbs [count, limbs] when ok, and the limbs each accepted
+    numerator needs with its sign (rns_chunk_bound)."""
     count, Tw = w.shape
     B = torch.from_numpy(_chunks_of(bound).astype(np.uint32).view(np.int32)).to(w.device)
     wl = bound.bit_length() // 64 + 1
     num = torch.empty((max(count, 1), wl), dtype=torch.int64, device=w.device)
     ok = torch.empty(max(count, 1), dtype=torch.int32, device=w.device)
+    used = torch.empty(max(count, 1), dtype=torch.int32, device=w.device)
     with torch.cuda.device(w.device):
         rc = load().rns_chunk_bound(w.data_ptr(), Tw, count, B.data_ptr(), B.numel(), num.data_ptr(), wl,
-                                    ok.data_ptr(), _stream_ptr(w))
+                                    ok.data_ptr(), used.data_ptr(), _stream_ptr(w))
     _check(rc, "rns_chunk_bound")
-    return ok[:count], num[:count]
+    return ok[:count], num[:count], used[:count]
 
 
 def chunk_numerators(chunks: np.ndarray, P: int, m: int, D: int, bound: int, index=None, threads: int = 0):
@@ -383,15 +385,22 @@ def chunk_numerators(chunks: np.ndarray, P: int, m: int, D: int, bound: int, ind
     return ok[:len(idx)].astype(bool), _limbs_to_int(num[:len(idx)])
 
 
-def _reconstruct_with(numerators, count: int, P: int, m: int, Nb: int, Db: int, threads: int = 0):
-    """The common-denominator loop of ``reconstruct_digits`` over a numerators source.  A component
-    reconstructed alone needs only P^k > 2 Nb Db (its fraction is unique there), so its Euclidean
-    remainder sequence runs on u mod P^k; the one-multiply test of the others keeps P^m."""
-    Pm = P ** m
+def _sample_modulus(P: int, Nb: int, Db: int) -> int:
+    """The least power P^k > 2 Nb Db: a component reconstructed alone has a unique fraction there."""
     target = 2 * Nb * Db
     Pk = P
     while Pk <= target:
         Pk *= P
+    return Pk
+
+
+def _reconstruct_with(numerators, count: int, P: int, m: int, Nb: int, Db: int, threads: int = 0,
+                      Pm: Optional[int] = None, Pk: Optional[int] = None):
+    """The common-denominator loop of ``reconstruct_digits`` over a numerators source.  A component
+    reconstructed alone needs only P^k > 2 Nb Db (its fraction is unique there), so its Euclidean
+    remainder sequence runs on u mod P^k; the one-multiply test of the others keeps P^m."""
+    Pm = P ** m if Pm is None else Pm
+    Pk = _sample_modulus(P, Nb, Db) if Pk is None else Pk
     D = 1
     nums: List[Optional[int]] = [None] * count
     at: List[int] = [1] * count
@@ -411,6 +420,8 @@ def _reconstruct_with(numerators, count: int, P: int, m: int, Nb: int, Db: int, 
             nums[todo[t]] = w[t]
             at[todo[t]] = D
         todo = todo[~ok]
+    if all(a is D for a in at):        # one denominator for every component: the common case
+        return nums, D
     scale = {a: D // a for a in set(at)}
     return [v * scale[a] for v, a in zip(nums, at)], D
 
@@ -426,9 +437,16 @@ class ReconstructionPrep:
     """What the reconstruction needs before the digits exist: the power table of ``padic_chunks``
     and the constants of ``chunk_modmul`` (built on the host while the lift runs)."""
 
-    def __init__(self, P: int, m: int, Db: int, device):
+    def __init__(self, P: int, m: int, Db: int, device, Nb: Optional[int] = None, count: int = 0):
         self.table = pow_table(P, m, chunk_count(P, m))
         self.consts = ModmulConstants(P, m, Db, device)
+        self.Pm = P ** m
+        self.Pk = _sample_modulus(P, Nb, Db) if Nb is not None else None
+        # pinned host memory for the numerators (every bound D Nb with D <= Db fits)
+        self.pinned = None
+        if Nb is not None and count > 0:
+            wl = (Db * Nb).bit_length() // 64 + 1
+            self.pinned = torch.empty(count * wl, dtype=torch.int64, pin_memory=True)
 
 
 def reconstruct_device(digits: torch.Tensor, P: int, m: int, Nb: int, Db: int,
@@ -438,7 +456,7 @@ def reconstruct_device(digits: torch.Tensor, P: int, m: int, Nb: int, Db: int,
     +-P^m correction and the bound test on the host (native; Python integers without GMP)."""
     if host_bigint_available():
         if prep is None:
-            prep = ReconstructionPrep(P, m, Db, digits.device)
+            prep = ReconstructionPrep(P, m, Db, digits.device, Nb, digits.shape[1])
         Xt = padic_chunks(digits, P, m, prep.table, transposed=True)
         count = Xt.shape[1]
         cache = {}
@@ -459,14 +477,22 @@ def reconstruct_device(digits: torch.Tensor, P: int, m: int, Nb: int, Db: int,
             if key not in cache:
                 # D x mod P^m and the bound test on the GPU for every component (P^m > 2 D Nb (Db + 1))
                 cache.clear()
-                ok_d, num_d = chunk_bound(chunk_modmul(Xt, D, prep.consts), bound)
-                cache[key] = (ok_d.cpu().numpy().astype(bool), num_d.cpu().numpy())   # synchronises
+                ok_d, num_d, used_d = chunk_bound(chunk_modmul(Xt, D, prep.consts), bound)
+                # copy only the limbs the widest accepted numerator needs
+                u = max(1, int(used_d.max()))                                      # synchronises
+                num_d = num_d[:, :u].contiguous()
+                if prep.pinned is not None and prep.pinned.numel() >= num_d.numel():
+                    num_h = prep.pinned[:num_d.numel()].view(num_d.shape)
+                    num_h.copy_(num_d)                                             # synchronises
+                else:
+                    num_h = num_d.cpu()
+                cache[key] = (ok_d.cpu().numpy().astype(bool), num_h.numpy())
             ok_all, num_all = cache[key]
             sel = np.asarray(idx, dtype=np.int64)
             ok = ok_all[sel]
             return ok, _limbs_to_int(num_all[sel])
 
-        return _reconstruct_with(numerators, count, P, m, Nb, Db)
+        return _reconstruct_with(numerators, count, P, m, Nb, Db, Pm=prep.Pm, Pk=prep.Pk)
     d = digits.cpu().numpy()
     per_step = [_limbs_to_int(d[s]) for s in range(m)]
     return reconstruct(per_step, P, m, Nb, Db)
@@ -509,7 +535,7 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
     m = lift_steps_for(P, Nb, Db)
     digits = dixon_lift(p, A, b, planes, m)
     # the lift runs asynchronously: build the reconstruction's tables on the host meanwhile
-    prep = ReconstructionPrep(P, m, Db, A.device) if host_bigint_available() else None
+    prep = ReconstructionPrep(P, m, Db, A.device, Nb, n * bn.shape[1]) if host_bigint_available() else None
     c = bn.shape[1]
     nums, D = reconstruct_device(digits.reshape(m, n * c, -1), P, m, Nb, Db, prep)
     out = [[Fraction(nums[i * c + k], D) for k in range(c)] for i in range(n)]

@@ -160,14 +160,16 @@ int rns_chunk_modmul(const int64_t *X, int64_t T, int64_t count, const int64_t *
  * limbs when |w_idx| <= B, else ok[idx] = 0 and num[idx] = 0.  w: device
  * uint32 [count][Tw] two's complement (rns_chunk_modmul's output); B: device
  * uint32 [TB], a non-negative integer; num: device int64 [count][w_limbs]
- * (w_limbs must hold B plus a sign); ok: device int32 [count].  For
+ * (w_limbs must hold B plus a sign); ok: device int32 [count]; used: device
+ * int32 [count], the limbs that hold an accepted w with its sign (at most
+ * w_limbs; 0 when not accepted), so a caller may copy fewer.  For
  * rns_chunk_modmul's output with G >= 63 (|w| < (1/2 + 2^-62) Pm, w congruent
  * to D X) and Pm > 2 B (1 + 2^-60), |w| <= B holds exactly when it holds for
  * the balanced residue of D X mod Pm, and then the two are equal: no
  * correction by +-Pm is needed.  Returns RNS_OK, RNS_E_ARG or RNS_E_HIP.
  */
 int rns_chunk_bound(const uint32_t *w, int64_t Tw, int64_t count, const uint32_t *B, int64_t TB, int64_t *num,
-                    int32_t w_limbs, int32_t *ok, hipStream_t stream);
+                    int32_t w_limbs, int32_t *ok, int32_t *used, hipStream_t stream);
 
 /*
  * ---- host stage (exact-solve, "Method": the final rational reconstruction is

@@ -336,12 +336,19 @@ def test_chunk_bound_edges(Tw, bbits):
     for i, v in enumerate(vals):
         w[i] = np.frombuffer((v % (1 << (32 * Tw))).to_bytes(4 * Tw, "little"), dtype=np.uint32)
     print(f"chunk bound Tw={Tw} B bits={bbits}", flush=True)
-    ok, num = rg.exact_solve.chunk_bound(torch.from_numpy(w.view(np.int32)).cuda(), B)
+    ok, num, used = rg.exact_solve.chunk_bound(torch.from_numpy(w.view(np.int32)).cuda(), B)
     ok = ok.cpu().numpy()
     num = num.cpu().numpy()
+    used = used.cpu().numpy()
     wl = num.shape[1]
     assert wl * 64 > bbits
     for i, v in enumerate(vals):
         assert bool(ok[i]) == (abs(v) <= B), (i, v)
         got = int.from_bytes(num[i].tobytes(), "little", signed=True)
         assert got == (v if abs(v) <= B else 0), i
+        if ok[i]:
+            # the reported limbs hold the value with its sign, and no more than w_limbs
+            assert 1 <= used[i] <= wl and v.bit_length() < 64 * used[i], (i, used[i])
+            assert int.from_bytes(num[i, :used[i]].tobytes(), "little", signed=True) == v
+        else:
+            assert used[i] == 0
