@@ -210,6 +210,8 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
     __shared__ uint32_t rows[NMAX * S / 4];
     __shared__ int16_t pl[NMAX];
     __shared__ int32_t piv_sh[2];
+    __shared__ uint32_t ftab[256][WD];  // the pivot row's window times every multiplier f, mod q
+    __shared__ uint8_t inv_tab[256];     // inverses mod q (Fermat), once per launch
     const int e = blockIdx.x;
     if (singular[e]) return;
     const int t = threadIdx.x;
@@ -232,6 +234,15 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
     }
     for (int64_t i = t; i < n; i += 1024) pl[i] = (int16_t)i;
     if (t < 2) piv_sh[t] = (int32_t)n;
+    if (t > 0 && t < (int)q) {
+        uint32_t inv = 1, base = (uint32_t)t, ex = q - 2;
+        while (ex) {
+            if (ex & 1) inv = barrett(inv * base, q, mq);
+            base = barrett(base * base, q, mq);
+            ex >>= 1;
+        }
+        inv_tab[t] = (uint8_t)inv;
+    }
     __syncthreads();
 
     for (int j = 0; j < bw; j++) {
@@ -256,13 +267,7 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
         }
         // interchange rows r0 and p, put Y's unit in column j, scale by the pivot's inverse
         if (t < S / 4) {
-            const uint32_t a = lb[p * S + j];
-            uint32_t inv = 1, base = a, ex = q - 2;
-            while (ex) {
-                if (ex & 1) inv = barrett(inv * base, q, mq);
-                base = barrett(base * base, q, mq);
-                ex >>= 1;
-            }
+            const uint32_t inv = inv_tab[lb[p * S + j]];
             uint32_t x = rows[p * (S / 4) + t];
             const uint32_t y = rows[r0 * (S / 4) + t];
             if (t == (B + j) / 4) x |= 1u << (8 * ((B + j) % 4));
@@ -278,21 +283,35 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
             }
         }
         __syncthreads();
-        // eliminate column j from every other row over the window j+1 .. B+j
+        // f times the pivot row's window, for every f < q: the elimination then subtracts bytes
         const int d0 = (j + 1) / 4;
-        for (int64_t it = t; it < n * WD; it += 1024) {
-            const int64_t i = it / WD;
-            const int d = d0 + (int)(it - i * WD);
+        for (int it = t; it < (int)q * WD; it += 1024) {
+            const int f = it / WD, dd = it - f * WD;
+            const uint32_t pv = d0 + dd < S / 4 ? rows[r0 * (S / 4) + d0 + dd] : 0u;
+            uint32_t o = 0;
+#pragma unroll
+            for (int b = 0; b < 4; b++)
+                o |= mod_q(f * (int)((pv >> (8 * b)) & 0xffu), (int)q, qf) << (8 * b);
+            ftab[f][dd] = o;
+        }
+        __syncthreads();
+        // eliminate column j from every other row over the window j+1 .. B+j: per byte a - f c mod q
+        // with a and f c in [0, q), two bytes at a time in 16-bit lanes (256 + a - f c, then + q
+        // where bit 8 is clear, i.e. where a < f c)
+        const uint32_t qq = q | (q << 16);
+        for (int it = t; it < (int)n * WD; it += 1024) {   // n <= NMAX: 32-bit indices
+            const int i = it / WD;
+            const int dd = it - i * WD, d = d0 + dd;
             if (i == r0 || d >= S / 4) continue;
             const uint32_t f = lb[i * S + j];
             if (!f) continue;
-            const uint32_t pv = rows[r0 * (S / 4) + d], wv = rows[i * (S / 4) + d];
-            uint32_t o = 0;
-#pragma unroll
-            for (int b = 0; b < 4; b++) {
-                const uint32_t a = (wv >> (8 * b)) & 0xffu, c = (pv >> (8 * b)) & 0xffu;
-                o |= mod_q((int)a - (int)(f * c), (int)q, qf) << (8 * b);
-            }
+            const uint32_t fc = ftab[f][dd], wv = rows[i * (S / 4) + d];
+            uint32_t x = ((wv & 0x00ff00ffu) | 0x01000100u) - (fc & 0x00ff00ffu);
+            uint32_t y = (((wv >> 8) & 0x00ff00ffu) | 0x01000100u) - ((fc >> 8) & 0x00ff00ffu);
+            const uint32_t mx = (~x >> 8) & 0x00010001u, my = (~y >> 8) & 0x00010001u;
+            x = (x + (((mx << 8) - mx) & qq)) & 0x00ff00ffu;
+            y = (y + (((my << 8) - my) & qq)) & 0x00ff00ffu;
+            uint32_t o = x | (y << 8);
             // bytes of columns <= j stay: column j holds f, which the other threads of this row read
             const int keep = j + 1 - 4 * d;
             if (keep > 0) {
