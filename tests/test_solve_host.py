@@ -277,3 +277,30 @@ def test_modmul_constants_leave_one_correction(n_primes, m, dbits):
         assert (w0 - D * X) % Pm == 0
         assert abs(w0) < Pm and abs(w0) < 2 ** (32 * c.Tw - 1)
         assert abs(w0) <= Pm // 2 + Pm // 2 ** 60
+
+
+def _lane_sub_mod(wv, fc, q):
+    """Four bytes a - c mod q (a, c in [0, q)) two at a time in 16-bit lanes, as the panel
+    elimination forms them: 256 + a - c per lane, then + q where bit 8 is clear."""
+    M = 0xFFFFFFFF
+    qq = q | (q << 16)
+    x = (((wv & 0x00FF00FF) | 0x01000100) - (fc & 0x00FF00FF)) & M
+    y = ((((wv >> 8) & 0x00FF00FF) | 0x01000100) - ((fc >> 8) & 0x00FF00FF)) & M
+    mx, my = ((~x & M) >> 8) & 0x00010001, ((~y & M) >> 8) & 0x00010001
+    x = (x + ((((mx << 8) - mx) & M) & qq)) & 0x00FF00FF
+    y = (y + ((((my << 8) - my) & M) & qq)) & 0x00FF00FF
+    return (x | (y << 8)) & M
+
+
+def test_panel_lane_subtraction_every_prime():
+    """The byte arithmetic of the panel elimination equals (a - c) mod q bytewise for every odd
+    prime below 256, at the extremes 0 and q - 1 and on random bytes."""
+    rng = random.Random(3)
+    for q in [p for p in O.primes_largest_first() if p % 2]:
+        cases = [[rng.choice([0, q - 1]) for _ in range(8)] for _ in range(200)]
+        cases += [[rng.randrange(q) for _ in range(8)] for _ in range(500)]
+        for v in cases:
+            a, c = v[:4], v[4:]
+            wv = sum(x << (8 * b) for b, x in enumerate(a))
+            fc = sum(x << (8 * b) for b, x in enumerate(c))
+            assert _lane_sub_mod(wv, fc, q) == sum(((a[b] - c[b]) % q) << (8 * b) for b in range(4)), q
