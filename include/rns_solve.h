@@ -6,19 +6,25 @@
  * product P of primes below 256, r_0 = b, x_i = B r_i mod P and
  * r_{i+1} = (r_i - A x_i) / P, the digits x_i give x mod P^m, from which the
  * rational solution is reconstructed once P^m exceeds twice the Hadamard
- * bound on numerator and denominator.  Two parts run here:
+ * bound on numerator and denominator.  The parts:
  *   - the batched modular inverse: A^-1 mod q_j for every prime by
- *     Gauss-Jordan elimination of the augmented matrix [A | I], one launch
- *     per elimination step spanning all primes, Barrett reduction in place of
- *     a hardware modulo;
+ *     Gauss-Jordan elimination of the augmented matrix [A | I], in panels of
+ *     columns (a panel kernel per prime, then a rank-update of the rest;
+ *     up to 4096 rows) or one step per launch pair above, reductions by
+ *     exact floating-point rounding steps or Barrett;
  *   - the lift: per step, x_i = B r_i mod P from one INT8 product per prime
  *     and the wide digit by the CRT, and the residual update in one limb as
  *     (r_i - A x_i) * P^-1 mod 2^64 (P odd).  For n a multiple of 16 and at
  *     most 4 right-hand sides a step is two kernels (every prime's dot
  *     products and the digit in one, the update and the next residues in the
- *     other); otherwise it runs through rns_gemm_batched_residue.
- * The rational reconstruction of x mod P^m runs on the host (exact-solve,
- * "Method": a CPU stage), declared at the end of this header.
+ *     other); otherwise it runs through rns_gemm_batched_residue;
+ *   - the reconstruction's bulk work (exact-solve, "Method", where it is a CPU
+ *     stage): the p-adic values in binary (rns_padic_chunks), the one
+ *     modular multiply per numerator (rns_chunk_modmul) and the bound test
+ *     (rns_chunk_bound), as exact residue products and chunk passes.
+ * The host stage (a component's rational reconstruction by the extended
+ * Euclidean algorithm, tables, and the same multiply on host threads) is
+ * declared at the end of this header.
  *
  * Conventions of rns_gemm.h: device pointers owned by the caller,
  * asynchronous launches on the caller's stream, 0 on success and a negative
