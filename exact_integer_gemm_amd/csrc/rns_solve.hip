@@ -393,6 +393,19 @@ __global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8
 
     uint64_t src[8];
     uint32_t piv = 0;                   // bit r: row r's source is a pivot row (balanced bytes)
+    // a row's own words are fetched together with its permutation entry, not after it: only the
+    // few rows that traded places with a pivot row (at most B per panel) then read their copy
+    // (in-bounds addresses for every lane, so the loads need no branch)
+    int32_t pis[8];
+    uint64_t own[8];
+    const int64_t cl = col_ok ? c : 0;
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+        const int64_t i = i0 + 8 * rg + r;
+        const int64_t ic = i < n ? i : n - 1;
+        pis[r] = perm[(int64_t)e * n + ic];
+        own[r] = *reinterpret_cast<const uint64_t *>(We + ic * pitch + cl);
+    }
 #pragma unroll
     for (int r = 0; r < 8; r++) {
         const int64_t i = i0 + 8 * rg + r;
@@ -402,12 +415,12 @@ __global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8
                 src[r] = *reinterpret_cast<const uint64_t *>(Re + (i - kb) * pitch + c);
                 piv |= 1u << r;
             } else {
-                const int64_t pi = perm[(int64_t)e * n + i];
-                src[r] = (pi == i) ? *reinterpret_cast<const uint64_t *>(We + i * pitch + c)
-                                   : *reinterpret_cast<const uint64_t *>(Oe + (pi - kb) * pitch + c);
+                src[r] = pis[r] == i ? own[r] : *reinterpret_cast<const uint64_t *>(Oe + (pis[r] - kb) * pitch + c);
             }
         }
     }
+#pragma unroll
+    for (int r = 0; r < 8; r++) asm volatile("" ::"v"(own[r]));   // the own loads stay unconditional
     for (int it = t; it < 64 * KC; it += 256) {
         const int r = it / KC, d = it - r * KC;
         xs[r][d] = (i0 + r < n) ? reinterpret_cast<const uint32_t *>(Xe + (i0 + r) * B)[d] : 0u;
