@@ -239,13 +239,13 @@ def solve_bench(args):
         e0.record(stream)
         singular, ws = XS.batched_inverse(A)
         e1.record(stream)
+        Nb, Db = XS._bounds(A_h, b_h)                  # on the host while the inverse runs, as solve() does
         sing = singular.cpu().tolist()
         sel = [i for i, v in enumerate(sing) if not v]
         moduli = [XS.ODD_PRIMES[i] for i in sel]
         p = XS.plan_from_moduli(moduli, n)
         planes = XS.inverse_planes(ws, n, sel)
         del ws
-        Nb, Db = XS._bounds(A_h, b_h)
         P = math.prod(moduli)
         m = XS.lift_steps_for(P, Nb, Db)
         e2, e3 = ev(), ev()

@@ -452,15 +452,39 @@ int rns_pow_table(const uint64_t *P, int32_t p_limbs, int32_t m, int64_t T, int6
     Z Pz(g), v(g);
     from_mag(g, &Pz, P, p_limbs);
     g->set_ui(&v, 1);
-    std::vector<uint32_t> words((size_t)T);
+    // the powers' chunks power by power, then written out transposed in 64 x 64 blocks (a column
+    // of out is m * 8 bytes apart, so writing it power by power touches a new line per chunk)
+    // (exported as native 64-bit words, GMP's fast path, and split into chunks here)
+    const size_t T64 = ((size_t)T + 1) / 2;
+    std::vector<uint64_t> words((size_t)m * T64, 0u);
     for (int32_t s = 0; s < m; s++) {
         if (g->sizeinbase(v.c(), 2) > (size_t)32 * (size_t)T) return RNS_E_ARG;
-        std::fill(words.begin(), words.end(), 0u);
         size_t cnt = 0;
-        g->export_(words.data(), &cnt, -1, sizeof(uint32_t), 0, 0, v.c());
-        for (int64_t t = 0; t < T; t++) out[t * m + s] = (int64_t)words[(size_t)t];
+        g->export_(words.data() + (size_t)s * T64, &cnt, -1, sizeof(uint64_t), 0, 0, v.c());
         g->mul(&v, v.c(), Pz.c());
     }
+    for (int64_t t0 = 0; t0 < T; t0 += 64)
+        for (int32_t s0 = 0; s0 < m; s0 += 64)
+            for (int64_t t = t0; t < std::min<int64_t>(t0 + 64, T); t++)
+                for (int32_t s = s0; s < std::min<int32_t>(s0 + 64, m); s++)
+                    out[t * m + s] = (int64_t)((words[(size_t)s * T64 + (size_t)(t >> 1)] >> (32 * (t & 1))) &
+                                               0xffffffffull);
+    return RNS_OK;
+}
+
+int rns_pow2_quotient(int64_t e, const uint64_t *d, int32_t d_limbs, uint64_t *q, int32_t q_limbs) {
+    if (!d || !q || e < 0 || d_limbs < 1 || q_limbs < 1 || !mag_positive(d, d_limbs)) return RNS_E_ARG;
+    const Gmp *g = gmp();
+    if (!g) return RNS_E_HOSTLIB;
+    Z dz(g), qz(g);
+    from_mag(g, &dz, d, d_limbs);
+    g->set_ui(&qz, 1);
+    g->mul_2exp(&qz, qz.c(), (unsigned long)e);
+    g->tdiv_q(&qz, qz.c(), dz.c());
+    if (g->sizeinbase(qz.c(), 2) > (size_t)64 * (size_t)q_limbs) return RNS_E_OUT_LIMBS;
+    std::memset(q, 0, sizeof(uint64_t) * (size_t)q_limbs);
+    size_t cnt = 0;
+    g->export_(q, &cnt, -1, sizeof(uint64_t), 0, 0, qz.c());
     return RNS_OK;
 }
 

@@ -108,11 +108,22 @@ def _bounds(A: np.ndarray, b: np.ndarray):
     else:
         rows2 = [sum(int(v) * int(v) for v in row) for row in A.tolist()]
         b2 = [[int(v) * int(v) for v in row] for row in b.tolist()]
-    D = math.prod(_ceil_sqrt(r2) for r2 in rows2)
+    D = _prod_tree([_ceil_sqrt(r2) for r2 in rows2])
     N = 1
     for k in range(b.shape[1]):
-        N = max(N, math.prod(_ceil_sqrt(r2 + b2[i][k]) for i, r2 in enumerate(rows2)))
+        N = max(N, _prod_tree([_ceil_sqrt(r2 + b2[i][k]) for i, r2 in enumerate(rows2)]))
     return N, max(D, 1)
+
+
+def _prod_tree(vals: List[int]) -> int:
+    """The product of many integers by pairwise rounds (balanced operand sizes)."""
+    vals = list(vals) or [1]
+    while len(vals) > 1:
+        nxt = [vals[i] * vals[i + 1] for i in range(0, len(vals) - 1, 2)]
+        if len(vals) % 2:
+            nxt.append(vals[-1])
+        vals = nxt
+    return vals[0]
 
 
 def _limbs_to_int(limbs: np.ndarray) -> List[int]:
@@ -191,7 +202,12 @@ def lift_steps_for(P: int, Nb: int, Db: int) -> int:
     reconstruction per denominator and a rigorous one-multiply test for every
     other component."""
     target = 2 * Nb * Db * (Db + 1)
-    m, Pm = 1, P
+    # start just below the answer from the bit lengths, then step
+    m = max(1, int(target.bit_length() / math.log2(P)) - 1)
+    Pm = P ** m
+    while Pm > target and m > 1:
+        m -= 1
+        Pm //= P
     while Pm <= target:
         m += 1
         Pm *= P
@@ -323,7 +339,15 @@ class ModmulConstants:
         self.s1c = (L - 1 - self.G) // 32
         abits = Db.bit_length() + L - 32 * self.s1c + 1
         self.k2c = (abits + self.G + 31) // 32
-        mu = (1 << (32 * (self.s1c + self.k2c))) // Pm
+        e = 32 * (self.s1c + self.k2c)
+        if host_bigint_available():
+            Pl, pn = _mag(Pm)
+            ql = (e - L + 1) // 64 + 2
+            q = np.zeros(ql, dtype=np.uint64)
+            _check(load().rns_pow2_quotient(e, _ptr(Pl), pn, _ptr(q), ql), "rns_pow2_quotient")
+            mu = int.from_bytes(q.tobytes(), "little")
+        else:
+            mu = (1 << e) // Pm
         self.Tw = L // 32 + 2
         self.mu = torch.from_numpy(_chunks_of(mu)).to(device)
         self.Pm = torch.from_numpy(_chunks_of(Pm)).to(device)
@@ -388,7 +412,11 @@ def chunk_numerators(chunks: np.ndarray, P: int, m: int, D: int, bound: int, ind
 def _sample_modulus(P: int, Nb: int, Db: int) -> int:
     """The least power P^k > 2 Nb Db: a component reconstructed alone has a unique fraction there."""
     target = 2 * Nb * Db
-    Pk = P
+    k = max(1, int(target.bit_length() / math.log2(P)) - 1)     # just below, from the bit lengths
+    Pk = P ** k
+    while Pk > target and k > 1:
+        k -= 1
+        Pk //= P
     while Pk <= target:
         Pk *= P
     return Pk
@@ -518,19 +546,19 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
     if n * amax >= 1 << 63:
         raise ValueError("n * max|A| must stay below 2^63 (the residual is one signed limb)")
     singular, ws = batched_inverse(A)
+    Nb, Db = _bounds(An, bn)                           # on the host while the inverse runs
     sing = singular.cpu().tolist()                     # synchronises
     sel = [i for i, s in enumerate(sing) if not s]
     if not sel:
         # det A vanishes mod every odd prime below 256, hence mod their product; below that product
         # (Hadamard) it is zero, so A is singular over the rationals.
-        if _bounds(An, bn)[1] < math.prod(ODD_PRIMES):
+        if Db < math.prod(ODD_PRIMES):
             return None
         raise RnsError(-3, "A is singular modulo every odd prime below 256, but det A may be nonzero")
     moduli = [ODD_PRIMES[i] for i in sel]
     p = plan_from_moduli(moduli, max(n, 1))
     planes = inverse_planes(ws, n, sel)
     del ws
-    Nb, Db = _bounds(An, bn)
     P = math.prod(moduli)
     m = lift_steps_for(P, Nb, Db)
     digits = dixon_lift(p, A, b, planes, m)

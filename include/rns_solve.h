@@ -219,6 +219,14 @@ int rns_padic_numerators(const int64_t *digits, int32_t steps, int64_t count, in
 int rns_pow_table(const uint64_t *P, int32_t p_limbs, int32_t m, int64_t T, int64_t *out);
 
 /*
+ * rns_pow2_quotient -- q = floor(2^e / d) for a magnitude d > 0 (d_limbs
+ * limbs), written as q_limbs limbs: the reciprocal of rns_chunk_modmul's
+ * Barrett step.  Returns RNS_OK, RNS_E_ARG, RNS_E_OUT_LIMBS (q does not fit)
+ * or RNS_E_HOSTLIB.
+ */
+int rns_pow2_quotient(int64_t e, const uint64_t *d, int32_t d_limbs, uint64_t *q, int32_t q_limbs);
+
+/*
  * rns_chunk_numerators -- rns_padic_numerators with the p-adic values given
  * as binary chunks (host uint32 [count][T], little-endian two's complement,
  * rns_padic_chunks's output) and P^steps as the modulus.  Returns RNS_OK,
