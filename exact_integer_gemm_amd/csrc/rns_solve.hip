@@ -298,27 +298,31 @@ __global__ __launch_bounds__(1024) void gj_panel_kernel(GjConsts gc, const uint8
         // eliminate column j from every other row over the window j+1 .. B+j: per byte a - f c mod q
         // with a and f c in [0, q), two bytes at a time in 16-bit lanes (256 + a - f c, then + q
         // where bit 8 is clear, i.e. where a < f c)
+        // One thread per row (n <= NMAX: 32-bit indices): the row's multiplier f is read once and a
+        // row with f = 0 is skipped whole.  The window's WD dwords all lie inside the row (d0 + WD <=
+        // S / 4, the last one the zero padding at j >= B - 4).
         const uint32_t qq = q | (q << 16);
-        for (int it = t; it < (int)n * WD; it += 1024) {   // n <= NMAX: 32-bit indices
-            const int i = it / WD;
-            const int dd = it - i * WD, d = d0 + dd;
-            if (i == r0 || d >= S / 4) continue;
+        const int keep = j + 1 - 4 * d0;                     // bytes of dword d0 left of column j + 1
+        const uint32_t km = keep > 0 ? (1u << (8 * keep)) - 1u : 0u;   // keep <= 3
+        for (int i = t; i < (int)n; i += 1024) {
+            if (i == r0) continue;
             const uint32_t f = lb[i * S + j];
             if (!f) continue;
-            const uint32_t fc = ftab[f][dd], wv = rows[i * (S / 4) + d];
-            uint32_t x = ((wv & 0x00ff00ffu) | 0x01000100u) - (fc & 0x00ff00ffu);
-            uint32_t y = (((wv >> 8) & 0x00ff00ffu) | 0x01000100u) - ((fc >> 8) & 0x00ff00ffu);
-            const uint32_t mx = (~x >> 8) & 0x00010001u, my = (~y >> 8) & 0x00010001u;
-            x = (x + (((mx << 8) - mx) & qq)) & 0x00ff00ffu;
-            y = (y + (((my << 8) - my) & qq)) & 0x00ff00ffu;
-            uint32_t o = x | (y << 8);
-            // bytes of columns <= j stay: column j holds f, which the other threads of this row read
-            const int keep = j + 1 - 4 * d;
-            if (keep > 0) {
-                const uint32_t m = (1u << (8 * keep)) - 1u;
-                o = (o & ~m) | (wv & m);
+            uint32_t *row = rows + i * (S / 4) + d0;
+            const uint32_t *ft = ftab[f];
+#pragma unroll
+            for (int dd = 0; dd < WD; dd++) {
+                const uint32_t fc = ft[dd], wv = row[dd];
+                uint32_t x = ((wv & 0x00ff00ffu) | 0x01000100u) - (fc & 0x00ff00ffu);
+                uint32_t y = (((wv >> 8) & 0x00ff00ffu) | 0x01000100u) - ((fc >> 8) & 0x00ff00ffu);
+                const uint32_t mx = (~x >> 8) & 0x00010001u, my = (~y >> 8) & 0x00010001u;
+                x = (x + (((mx << 8) - mx) & qq)) & 0x00ff00ffu;
+                y = (y + (((my << 8) - my) & qq)) & 0x00ff00ffu;
+                uint32_t o = x | (y << 8);
+                // bytes of columns <= j are left as they were (the window starts in their dword)
+                if (dd == 0) o = (o & ~km) | (wv & km);
+                row[dd] = o;
             }
-            rows[i * (S / 4) + d] = o;
         }
         __syncthreads();
     }
