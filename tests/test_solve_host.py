@@ -304,3 +304,33 @@ def test_panel_lane_subtraction_every_prime():
             wv = sum(x << (8 * b) for b, x in enumerate(a))
             fc = sum(x << (8 * b) for b, x in enumerate(c))
             assert _lane_sub_mod(wv, fc, q) == sum(((a[b] - c[b]) % q) << (8 * b) for b in range(4)), q
+
+
+def test_pow2_quotient_native():
+    """floor(2^e / d) from GMP equals Python's integer division (the Barrett reciprocal)."""
+    _native()
+    rng = random.Random(4)
+    for _ in range(40):
+        d = rng.getrandbits(rng.randrange(1, 3000)) | 1
+        e = rng.randrange(0, 6000)
+        ql = max(1, (e - d.bit_length() + 1) // 64 + 2)
+        q = np.zeros(ql, dtype=np.uint64)
+        dl, dn = S._mag(d)
+        assert S.load().rns_pow2_quotient(e, S._ptr(dl), dn, S._ptr(q), ql) == 0
+        assert int.from_bytes(q.tobytes(), "little") == (1 << e) // d
+
+
+def test_step_count_and_sample_modulus_are_least():
+    """The lift's step count is the least m with P^m > 2 Nb Db (Db + 1), and the sample's modulus
+    the least power P^k > 2 Nb Db, across sizes (computed from bit lengths, then corrected)."""
+    rng = random.Random(5)
+    odd = [p for p in O.primes_largest_first() if p % 2]
+    for _ in range(300):
+        P = O.prod(rng.sample(odd, rng.randrange(1, 8)))
+        Nb, Db = rng.getrandbits(rng.randrange(1, 900)) + 1, rng.getrandbits(rng.randrange(1, 900)) + 1
+        m = S.lift_steps_for(P, Nb, Db)
+        target = 2 * Nb * Db * (Db + 1)
+        assert P ** m > target and (m == 1 or P ** (m - 1) <= target)
+        Pk = S._sample_modulus(P, Nb, Db)
+        assert Pk > 2 * Nb * Db and (Pk == P or Pk // P <= 2 * Nb * Db)
+        assert Pk % P == 0 and round(math.log(Pk, P)) >= 1
