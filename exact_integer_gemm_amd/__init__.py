@@ -134,6 +134,7 @@ def load() -> ctypes.CDLL:
         "rns_host_bigint_available": (ctypes.c_int, []),
         "rns_pow_table": (ctypes.c_int, [VP, I32, I32, I64, VP]),
         "rns_pow2_quotient": (ctypes.c_int, [I64, VP, I32, VP, I32]),
+        "rns_reduce_fractions": (ctypes.c_int, [VP, I64, I32, VP, I32, VP, VP, I32]),
         "rns_padic_chunks_workspace_size": (ctypes.c_int, [I64, I32, I64, I32, I32, ctypes.POINTER(SZ)]),
         "rns_padic_chunks": (ctypes.c_int, [VP, I64, I32, VP, I64, I32, I32, I32, VP, VP, SZ, VP]),
         "rns_chunk_modmul_workspace_size": (ctypes.c_int, [I64, I64, I64, I64, I64, I64, I64, I64,

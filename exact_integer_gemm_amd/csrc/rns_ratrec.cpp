@@ -55,6 +55,8 @@ struct Gmp {
     void (*submul_ui)(mpz_ptr, mpz_srcptr, unsigned long);
     void (*mul_2exp)(mpz_ptr, mpz_srcptr, unsigned long);
     void (*tdiv_q)(mpz_ptr, mpz_srcptr, mpz_srcptr);
+    void (*gcd)(mpz_ptr, mpz_srcptr, mpz_srcptr);
+    void (*divexact)(mpz_ptr, mpz_srcptr, mpz_srcptr);
     bool ok = false;
 };
 
@@ -92,6 +94,8 @@ const Gmp *gmp() {
         get(g.submul_ui, "__gmpz_submul_ui");
         get(g.mul_2exp, "__gmpz_mul_2exp");
         get(g.tdiv_q, "__gmpz_tdiv_q");
+        get(g.gcd, "__gmpz_gcd");
+        get(g.divexact, "__gmpz_divexact");
         g.ok = all;
     });
     return g.ok ? &g : nullptr;
@@ -486,6 +490,38 @@ int rns_pow2_quotient(int64_t e, const uint64_t *d, int32_t d_limbs, uint64_t *q
     size_t cnt = 0;
     g->export_(q, &cnt, -1, sizeof(uint64_t), 0, 0, qz.c());
     return RNS_OK;
+}
+
+
+int rns_reduce_fractions(const int64_t *num, int64_t count, int32_t limbs, const uint64_t *D, int32_t d_limbs,
+                         int64_t *num_out, uint64_t *den_out, int32_t threads) {
+    if (count < 0 || limbs < 1 || d_limbs < 1 || threads < 0 || !D || !mag_positive(D, d_limbs) ||
+        (count > 0 && (!num || !num_out || !den_out)))
+        return RNS_E_ARG;
+    const Gmp *g = gmp();
+    if (!g) return RNS_E_HOSTLIB;
+    std::atomic<int64_t> next{0};
+    std::atomic<int> fail{0};
+    run_threads(threads, count, [&] {
+        Z Dz(g), x(g), gz(g), t(g);
+        std::vector<uint64_t> tmp((size_t)limbs);
+        from_mag(g, &Dz, D, d_limbs);
+        for (int64_t i = next++; i < count; i = next++) {
+            from_twos(g, &x, num + i * limbs, limbs, tmp.data());
+            g->gcd(&gz, x.c(), Dz.c());                  // gcd(|N|, D) > 0 since D > 0
+            g->divexact(&t, x.c(), gz.c());
+            to_twos(g, num_out + i * limbs, limbs, t.c());
+            g->divexact(&t, Dz.c(), gz.c());
+            if (g->sizeinbase(t.c(), 2) > (size_t)64 * (size_t)d_limbs) {
+                fail = 1;
+                continue;
+            }
+            std::memset(den_out + i * d_limbs, 0, sizeof(uint64_t) * (size_t)d_limbs);
+            size_t cnt = 0;
+            g->export_(den_out + i * d_limbs, &cnt, -1, sizeof(uint64_t), 0, 0, t.c());
+        }
+    });
+    return fail ? RNS_E_OUT_LIMBS : RNS_OK;
 }
 
 }  // extern "C"

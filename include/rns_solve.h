@@ -227,6 +227,16 @@ int rns_pow_table(const uint64_t *P, int32_t p_limbs, int32_t m, int64_t T, int6
 int rns_pow2_quotient(int64_t e, const uint64_t *d, int32_t d_limbs, uint64_t *q, int32_t q_limbs);
 
 /*
+ * rns_reduce_fractions -- N_i / D in lowest terms for every i: with
+ * g = gcd(|N_i|, D), num_out[i] = N_i / g (int64 [count][limbs], two's
+ * complement, the layout of num) and den_out[i] = D / g (uint64
+ * [count][d_limbs] magnitudes); up to 16 host threads (or `threads`).
+ * Returns RNS_OK, RNS_E_ARG, RNS_E_OUT_LIMBS or RNS_E_HOSTLIB.
+ */
+int rns_reduce_fractions(const int64_t *num, int64_t count, int32_t limbs, const uint64_t *D, int32_t d_limbs,
+                         int64_t *num_out, uint64_t *den_out, int32_t threads);
+
+/*
  * rns_chunk_numerators -- rns_padic_numerators with the p-adic values given
  * as binary chunks (host uint32 [count][T], little-endian two's complement,
  * rns_padic_chunks's output) and P^steps as the modulus.  Returns RNS_OK,

@@ -2,6 +2,7 @@
 reconstruction of the lift digits) against the oracle, on the CPU: the digits
 come from the oracle's own recurrence."""
 import math
+from fractions import Fraction
 import random
 
 import numpy as np
@@ -334,3 +335,16 @@ def test_step_count_and_sample_modulus_are_least():
         Pk = S._sample_modulus(P, Nb, Db)
         assert Pk > 2 * Nb * Db and (Pk == P or Pk // P <= 2 * Nb * Db)
         assert Pk % P == 0 and round(math.log(Pk, P)) >= 1
+
+
+def test_fractions_in_lowest_terms_native():
+    """Batched reduction N_i / D: equal to Fraction's own normalisation, signs, zero and shared
+    factors included."""
+    _native()
+    rng = random.Random(6)
+    D = 2 ** 5 * 3 ** 7 * 251 * (rng.getrandbits(3000) | 1)
+    nums = [0, 1, -1, D, -D, 2 * D, 3 ** 5, -(2 ** 70) * 251] + [rng.randrange(-D * 4, D * 4) for _ in range(60)]
+    nums += [rng.getrandbits(2000) * 3 ** 4 * 2 ** 3 for _ in range(20)]
+    got = S.to_fractions(nums, D)
+    assert got == [Fraction(v, D) for v in nums]
+    assert all(math.gcd(f.numerator, f.denominator) == 1 and f.denominator > 0 for f in got)
