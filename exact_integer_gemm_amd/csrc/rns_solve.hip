@@ -383,8 +383,10 @@ __global__ __launch_bounds__(256) void gj_block_update_kernel(GjConsts gc, uint8
     const int e = (int)(blockIdx.x / per);
     if (singular[e]) return;
     const int64_t tile = blockIdx.x - (int64_t)e * per;
-    const int64_t i0 = (tile / col_tiles) * 64;
-    const int64_t c0 = cs + (tile % col_tiles) * 256;
+    // row tiles fastest: the blocks an XCD runs together share a column tile, so its R^T comes
+    // from that XCD's L2
+    const int64_t i0 = (tile % row_tiles) * 64;
+    const int64_t c0 = cs + (tile / row_tiles) * 256;
     const int t = threadIdx.x, cg = t & 31, rg = t >> 5;
     const uint32_t q = gc.q[e];
     const float qf = gc.inv[e];
