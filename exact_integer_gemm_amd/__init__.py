@@ -2,9 +2,10 @@
 
 A thin Python binding over ``librns_gemm.so`` (C ABI: ``include/rns_gemm.h``).
 The binding only marshals arguments: every step of the product (residue split,
-prime-batched INT8 MFMA products with the mod-q epilogue, Garner
-reconstruction) runs in the library's HIP kernels.  PyTorch provides device
-memory and the current stream.
+prime-batched INT8 MFMA products with the mod-q epilogue, and the
+reconstruction: the centered CRT by rounded quotient of Ozaki Scheme II
+§3.5.2 by default, balanced Garner as ``method="garner"``) runs in the
+library's HIP kernels.  PyTorch provides device memory and the current stream.
 
     import exact_integer_gemm_amd as rg
     plan = rg.plan(K, a_bits, b_bits)          # primes for |A|<=2^a, |B|<=2^b

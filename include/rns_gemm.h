@@ -4,10 +4,12 @@
  * The product C = A @ B of signed multi-limb integer matrices is computed
  * exactly: every operand entry is reduced to balanced residues modulo primes
  * below 256, one INT8 matrix product per prime is accumulated in int32 and
- * reduced mod that prime, and balanced Garner mixed-radix reconstruction
- * rebuilds the exact signed result (exact-solve, "Method"; enclosure-gemm,
- * "Method"; Ozaki Scheme II paper, §3.1: the integer products are exact and
- * the result is reconstructed once).
+ * reduced mod that prime, and the exact signed result is rebuilt from its
+ * residues by the centered CRT with a rounded quotient (Ozaki Scheme II
+ * paper, §3.5.2), with balanced Garner mixed-radix reconstruction
+ * (exact-solve, "Method"; enclosure-gemm, "Method") available as
+ * rns_reconstruct_garner for the same result (Ozaki Scheme II paper, §3.1:
+ * the integer products are exact and the result is reconstructed once).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -158,7 +160,10 @@ int rns_workspace_size(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
  *
  * Three kernels run on `stream`: the residue split of A and B into int8
  * planes, the prime-batched INT8 MFMA product with a fused mod-q epilogue,
- * and Garner reconstruction.  The result equals the integer product whenever
+ * and the reconstruction: the centered CRT by rounded quotient (Ozaki Scheme
+ * II paper, §3.5.2; described under rns_reconstruct below), whose output is
+ * bit for bit the one balanced Garner gives (rns_reconstruct_garner).  The
+ * result equals the integer product whenever
  * the operands respect the plan's declared bounds; if an entry exceeds its
  * bound, a flag is recorded for rns_status and C is unspecified.
  * Returns RNS_OK, RNS_E_ARG, RNS_E_K (K > plan->k_max), RNS_E_OUT_LIMBS,

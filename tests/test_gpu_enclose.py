@@ -16,6 +16,7 @@ import torch
 
 import exact_integer_gemm_amd as rg
 from oracle import enclose as E
+import workloads as W
 
 pytestmark = pytest.mark.gpu
 
@@ -206,21 +207,33 @@ def test_scaling_and_rounding_kernels_alone():
         assert same_bits(lo32.cpu().numpy(), rlo32) and same_bits(hi32.cpu().numpy(), rhi32), q
 
 
-def test_enclosure_shape_full_size_sampled():
-    """A[1024,4096] @ B[4096,1024] of N(0,1) binary64 entries: sampled
-    entries against the oracle, and the bracket width everywhere."""
+def test_enclosure_shape_full_size():
+    """A[1024,4096] @ B[4096,1024] of N(0,1) binary64 entries: the whole (lo,
+    hi) against the SHA-256 of the oracle's enclosure of every entry
+    (tests/golden/enclosure_digest.json, written from oracle/ only), sampled
+    entries against the live oracle, and the bracket width everywhere."""
+    import hashlib
+    import json
+    import os
     print("enclose full size 1024x4096x1024", flush=True)
-    rng = np.random.default_rng(10)
-    A = rng.standard_normal((1024, 4096))
-    B = rng.standard_normal((4096, 1024))
+    dg = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                     "enclosure_digest.json")))
+    A, B = W.fp64_normal_pair(dg["seed"], dg["M"], dg["K"], dg["N"])
+    assert hashlib.sha256(A.tobytes()).hexdigest() == dg["inputs_sha256"]["A"]
+    assert hashlib.sha256(B.tobytes()).hexdigest() == dg["inputs_sha256"]["B"]
     lo, hi, ep = rg.mm_enclose(dev(A), dev(B), return_plan=True)
     torch.cuda.synchronize()
     print(f"plan: fa={ep.fa} fb={ep.fb} primes={ep.n_primes} limbs={ep.limbs}", flush=True)
+    assert (ep.fa, ep.fb) == (dg["Fa"], dg["Fb"])
+    glo_all, ghi_all = lo.cpu().numpy(), hi.cpu().numpy()
+    slo = hashlib.sha256(np.ascontiguousarray(glo_all).tobytes()).hexdigest()
+    shi = hashlib.sha256(np.ascontiguousarray(ghi_all).tobytes()).hexdigest()
+    print(f"lo sha256 {slo} (oracle {dg['lo_sha256']}); hi sha256 {shi} (oracle {dg['hi_sha256']})", flush=True)
     w = rg.width_ulps(lo, hi)
     assert int(w.min()) >= 0 and int(w.max()) <= 1
+    rng = np.random.default_rng(10)
     rows = np.sort(rng.choice(1024, size=6, replace=False))
     cols = np.sort(rng.choice(1024, size=48, replace=False))
     rlo, rhi = E.enclose(A[rows], B[:, cols])
-    glo = lo.cpu().numpy()[np.ix_(rows, cols)]
-    ghi = hi.cpu().numpy()[np.ix_(rows, cols)]
-    assert same_bits(glo, rlo) and same_bits(ghi, rhi)
+    assert same_bits(glo_all[np.ix_(rows, cols)], rlo) and same_bits(ghi_all[np.ix_(rows, cols)], rhi)
+    assert slo == dg["lo_sha256"] and shi == dg["hi_sha256"]

@@ -4,9 +4,16 @@ Every comparison is bit-exact: the path computes integers.  Small and medium
 shapes (several tiles plus a ragged tail in M, N and K) are compared in full
 against the C oracle; stage-level checks compare the residue planes the split
 kernel wrote, and the per-prime products the MFMA kernel wrote, with the
-oracle's stage definitions.  The full-size workloads are checked on sampled
-rows against the oracle and on the whole output by the Freivalds identity.
+oracle's stage definitions.  The five full-size workloads are compared in
+full with the oracle, element by element, and by the SHA-256 of the output
+bytes against the digest the oracle alone wrote into
+tests/golden/workload_digests.json (enclosure-gemm, "Correctness": SHA-256
+over the raw bits).
 """
+import hashlib
+import json
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -451,6 +458,25 @@ def test_freivalds_helper_catches_one_wrong_entry():
     assert not freivalds_mod(mod_p_limbs(A), mod_p_limbs(B), mod_p_limbs(O.encode_array(Cv, 4)), 1)
 
 
+DIGESTS = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                                    "workload_digests.json")))
+
+
+def sha256(a):
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def check_digest(name, C, inputs):
+    """The output's SHA-256 equals the oracle's stored digest (inputs too)."""
+    d = DIGESTS[name]
+    for k, arr in inputs.items():
+        assert sha256(arr) == d["inputs_sha256"][k], f"{name}: input {k} differs from the digest's"
+    got = sha256(C)
+    print(f"{name}: output sha256 {got} (oracle digest {d['C_sha256']})", flush=True)
+    assert C.shape == (d["M"], d["N"], d["out_limbs"])
+    assert got == d["C_sha256"]
+
+
 def test_workload_tiny():
     wl = W.make("tiny")
     p, ws, C = run_gemm(wl.A, wl.B, wl.a_bits, wl.b_bits)
@@ -458,6 +484,7 @@ def test_workload_tiny():
     Av, Bv = O.decode_array(wl.A), O.decode_array(wl.B)
     ref = np.array(O.int_matmul(Av.tolist(), Bv.tolist()), dtype=object)
     assert np.array_equal(O.decode_array(C), ref)
+    check_digest("tiny", C, {"A": wl.A, "B": wl.B})
 
 
 def test_workload_square():
@@ -466,19 +493,21 @@ def test_workload_square():
     assert p.n_primes == 10 and C.shape[-1] == 2
     ref = oracle_c(wl.A, wl.B, 2)
     assert np.array_equal(C, ref)
+    check_digest("square", C, {"A": wl.A, "B": wl.B})
 
 
 @pytest.mark.parametrize("name,nprimes", [("enclosure", 16), ("wide", 29)])
-def test_workload_large_sampled(name, nprimes):
+def test_workload_large_full(name, nprimes):
+    """Every entry of the full-size product against the C oracle (OpenMP over
+    rows), and the output's SHA-256 against the oracle's digest."""
     print(f"workload {name}", flush=True)
     wl = W.make(name)
     p, ws, C = run_gemm(wl.A, wl.B, wl.a_bits, wl.b_bits)
     assert p.n_primes == nprimes
     assert rg.status(ws) == 0
-    rng = np.random.default_rng(7)
-    rows = np.sort(rng.choice(wl.M, size=8, replace=False))
-    ref = oracle_c(wl.A[rows], wl.B, C.shape[-1])
-    assert np.array_equal(C[rows], ref)
+    check_digest(name, C, {"A": wl.A, "B": wl.B})
+    ref = oracle_c(wl.A, wl.B, C.shape[-1])
+    assert np.array_equal(C, ref)
     assert freivalds_mod(mod_p_limbs(wl.A), mod_p_limbs(wl.B), mod_p_limbs(C), 3)
 
 
@@ -489,3 +518,4 @@ def test_workload_dixon():
     assert X.shape == (1024, 16, 6)
     ref = O.residue_gemm_via_crt(wl.A_res, wl.B[..., 0], O.primes_largest_first())
     assert np.array_equal(O.decode_array(X), ref)
+    check_digest("dixon", X, {"A_res": wl.A_res, "B": wl.B})

@@ -442,3 +442,51 @@ def test_crt_with_prime_power_moduli():
         r0, _ = sympy_crt(ms, [r % q for r, q in zip(res, ms)])
         assert (int(r0) - X) % P == 0
         assert O.mixed_radix_value(O.garner_digits(res, ms), ms) == X
+
+
+# --------------------------------------------------------------------------
+# stored digests of the five workloads (tests/golden/workload_digests.json)
+# --------------------------------------------------------------------------
+def _digests():
+    return json.load(open(os.path.join(os.path.dirname(__file__), "golden", "workload_digests.json")))
+
+
+def _sha(a):
+    import hashlib
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+def test_workload_digest_inputs():
+    """The seeded generators still draw the inputs the digests were made from."""
+    import workloads as W
+    d = _digests()
+    for name in W.NAMES:
+        wl = W.make(name, primes=O.primes_largest_first()) if name == "dixon" else W.make(name)
+        arrays = {"A_res": wl.A_res, "B": wl.B} if name == "dixon" else {"A": wl.A, "B": wl.B}
+        for k, a in arrays.items():
+            assert _sha(a) == d[name]["inputs_sha256"][k], (name, k)
+
+
+@pytest.mark.parametrize("name", ["tiny", "dixon"])
+def test_workload_digest_outputs_small(name):
+    """The small digests recomputed by independent oracle routes: the tiny
+    product by the Python triple loop, the batched step by Garner digits
+    instead of the textbook CRT the digest script used."""
+    import workloads as W
+    d = _digests()[name]
+    if name == "tiny":
+        wl = W.make("tiny")
+        C = O.int_matmul(O.decode_array(wl.A).tolist(), O.decode_array(wl.B).tolist())
+        arr = O.encode_array(np.array(C, dtype=object), d["out_limbs"])
+    else:
+        primes = O.primes_largest_first()
+        wl = W.make("dixon", primes=primes)
+        # per-prime products mod q, then Garner with 2 first (range (-P/2, P/2])
+        Y = [O.residue_product(wl.A_res[j].astype(np.int64), O.balanced_array(wl.B[..., 0], q), q)
+             for j, q in enumerate(primes)]
+        order = sorted(range(len(primes)), key=lambda j: primes[j] != 2)
+        qs = [primes[j] for j in order]
+        flat = [Y[j].ravel() for j in order]
+        vals = [O.mixed_radix_value(O.garner_digits([int(f[e]) for f in flat], qs), qs) for e in range(flat[0].size)]
+        arr = O.encode_array(np.array(vals, dtype=object).reshape(Y[0].shape), d["out_limbs"])
+    assert _sha(arr) == d["C_sha256"]

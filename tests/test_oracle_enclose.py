@@ -138,3 +138,16 @@ def test_bracket_is_one_step_and_contains():
     for idx, v in np.ndenumerate(V):
         assert E.exact(lo[idx]) <= v <= E.exact(hi[idx])
         assert hi[idx] == lo[idx] or hi[idx] == math.nextafter(lo[idx], math.inf)
+
+
+def test_enclosure_digest_inputs():
+    """The stored enclosure digest was made from the inputs the generator draws."""
+    import hashlib
+    import json
+    import os
+    import workloads as W
+    dg = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "enclosure_digest.json")))
+    A, B = W.fp64_normal_pair(dg["seed"], dg["M"], dg["K"], dg["N"])
+    assert hashlib.sha256(A.tobytes()).hexdigest() == dg["inputs_sha256"]["A"]
+    assert hashlib.sha256(B.tobytes()).hexdigest() == dg["inputs_sha256"]["B"]
+    assert (E.coarsest_lossless_scale(A), E.coarsest_lossless_scale(B)) == (dg["Fa"], dg["Fb"])

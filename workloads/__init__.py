@@ -144,6 +144,15 @@ def make(name: str, primes: Optional[Sequence[int]] = None, scale: float = 1.0) 
     raise KeyError(name)
 
 
+def fp64_normal_pair(seed: int, M: int, K: int, N: int):
+    """Binary64 operands A[M,K], B[K,N] with N(0,1) entries (the enclosure
+    product's inputs), drawn A first, then B."""
+    rng = np.random.default_rng(seed)
+    A = rng.standard_normal((M, K))
+    B = rng.standard_normal((K, N))
+    return A, B
+
+
 def random_operands(seed: int, M: int, N: int, K: int, la: int, lb: int,
                     a_bits: int, b_bits: int):
     """Generic seeded operands: entries uniform in [-2^bits, 2^bits] as limbs.
