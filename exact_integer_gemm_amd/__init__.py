@@ -108,6 +108,7 @@ def load() -> ctypes.CDLL:
         "rns_workspace_layout": (ctypes.c_int, [P, I64, I64, I64, I32, ctypes.POINTER(_Layout)]),
         "rns_gemm": (ctypes.c_int, [P, I64, I64, I64, VP, I32, VP, I32, VP, I32, VP, SZ, VP]),
         "rns_gemm_batched_residue": (ctypes.c_int, [P, I64, I64, I64, VP, VP, I32, VP, I32, VP, SZ, VP]),
+        "rns_gemm_noalloc": (ctypes.c_int, [P, I64, I64, I64, VP, I32, VP, I32, VP, I32, VP]),
         "rns_split": (ctypes.c_int, [P, I64, I64, I64, VP, I32, VP, I32, VP, SZ, VP]),
         "rns_residue_products": (ctypes.c_int, [P, I64, I64, I64, VP, VP, SZ, VP]),
         "rns_reconstruct": (ctypes.c_int, [P, I64, I64, I64, I32, VP, I32, VP, SZ, VP]),
@@ -282,6 +283,29 @@ def gemm(p: Plan, A: torch.Tensor, B: torch.Tensor, out_limbs: Optional[int] = N
                              out.data_ptr(), lc, workspace.data_ptr(), workspace.numel(),
                              _stream_ptr(A))
     _check(rc, "rns_gemm")
+    return out
+
+
+def gemm_noalloc(p: Plan, A: torch.Tensor, B: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+    """C = A @ B exactly, like ``gemm``, with the library's fixed device
+    scratch array as the workspace (``rns_gemm_noalloc``): no device memory is
+    allocated, so ``out`` must be given.  Calls on one GPU share the array."""
+    _need(A, torch.int64, 3, "A")
+    _need(B, torch.int64, 3, "B")
+    _need(out, torch.int64, 3, "out")
+    M, K, la = A.shape
+    K2, N, lb = B.shape
+    if K2 != K:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if B.device != A.device or out.device != A.device:
+        raise ValueError("A, B and out on different devices")
+    if tuple(out.shape[:2]) != (M, N):
+        raise ValueError("out has the wrong shape")
+    c = p._c()
+    with torch.cuda.device(A.device):
+        rc = load().rns_gemm_noalloc(ctypes.byref(c), M, N, K, A.data_ptr(), la, B.data_ptr(), lb,
+                                     out.data_ptr(), out.shape[2], _stream_ptr(A))
+    _check(rc, "rns_gemm_noalloc")
     return out
 
 

@@ -661,6 +661,7 @@ const char *rns_error_string(int code) {
         case -7: return "non-finite operand";
         case -8: return "no fraction within the bounds matches the residue";
         case -9: return "the host big-integer library (libgmp.so.10) is not available";
+        case RNS_E_SCRATCH: return "workspace exceeds the fixed scratch array of rns_gemm_noalloc";
         default: return "unknown error code";
     }
 }

@@ -60,7 +60,8 @@ enum rns_status_code {
     RNS_E_CAPACITY = -3,   /* the bound 2*K*2^(a_bits+b_bits) is not below P of all 54 primes */
     RNS_E_OUT_LIMBS = -4,  /* c_limbs < plan->out_limbs_min or > RNS_MAX_OUT_LIMBS */
     RNS_E_WORKSPACE = -5,  /* ws_bytes smaller than rns_workspace_size reports */
-    RNS_E_HIP = -6         /* a HIP launch or copy failed */
+    RNS_E_HIP = -6,        /* a HIP launch or copy failed */
+    RNS_E_SCRATCH = -10    /* rns_gemm_noalloc: the workspace exceeds RNS_NOALLOC_SCRATCH_BYTES */
 };
 
 /* Bits of the status word read by rns_status. */
@@ -238,6 +239,24 @@ int rns_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
 int rns_reconstruct_garner(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
                            int32_t batched_residue, int64_t *C, int32_t c_limbs,
                            void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * rns_gemm_noalloc -- rns_gemm for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments, checks, result and errors as rns_gemm, minus
+ * the workspace: the library uses a fixed array of RNS_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) that every GPU it runs on holds until the process ends.  The call
+ * allocates nothing.  Shapes whose rns_workspace_size exceeds the array are
+ * rejected with RNS_E_SCRATCH before anything is launched.  All calls on one
+ * GPU share that GPU's array and leave their data in it: calls that overlap
+ * on one GPU (other streams, other host threads) race and must be ordered by
+ * the caller.  rns_status does not apply to these calls.
+ */
+#define RNS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int rns_gemm_noalloc(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
+                     const int64_t *A, int32_t a_limbs,
+                     const int64_t *B, int32_t b_limbs,
+                     int64_t *C, int32_t c_limbs, hipStream_t stream);
 
 /*
  * rns_status -- synchronises `stream`, then reports in *flags the

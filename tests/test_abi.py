@@ -327,3 +327,14 @@ def test_sliced_plan_choices():
     with pytest.raises(rg.RnsError) as e:
         rg.sliced_plan((1 << 17) + 1, 4, 4)
     assert e.value.code == -2
+
+
+def test_noalloc_rejects_before_any_device_work(lib):
+    """rns_gemm_noalloc validates the plan and the sizes and refuses shapes
+    whose workspace exceeds its fixed array, all on the host."""
+    p = rg.plan(4096, 100, 100)
+    c = p._c()
+    assert lib.rns_gemm_noalloc(ctypes.byref(c), 2048, 2048, 4096, None, 2, None, 2, None, 4, None) == -10
+    assert lib.rns_gemm_noalloc(None, 8, 8, 8, None, 1, None, 1, None, 1, None) == -1
+    assert lib.rns_gemm_noalloc(ctypes.byref(c), 8, 8, 2 ** 17 + 1, None, 1, None, 1, None, 4, None) == -2
+    assert "scratch" in lib.rns_error_string(-10).decode()
