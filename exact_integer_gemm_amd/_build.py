@@ -7,7 +7,8 @@ device kernels, with shared device helpers in
 ``csrc/rns_device.h``; ``csrc/rns_ratrec.cpp`` the host stage of the exact solve
 (big integers through the system's libgmp.so.10, opened at run time);
 ``csrc/rns_sliced.hip`` products beyond the residue capacity by operand slices;
-``csrc/rns_noalloc.hip`` the product with the workspace in a fixed device array.
+``csrc/rns_noalloc.hip`` the product with the workspace in a fixed device array;
+``csrc/rns_skinny.hip`` the batched-residue product for skinny right-hand sides.
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librns_gemm.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("rns_host.cpp", "rns_split.hip", "rns_gemm.hip", "rns_crt.hip", "rns_garner.hip",
                                                     "rns_enclose.hip", "rns_solve.hip", "rns_ratrec.cpp",
-                                                    "rns_sliced.hip", "rns_noalloc.hip")]
+                                                    "rns_sliced.hip", "rns_noalloc.hip", "rns_skinny.hip")]
 HEADERS = [os.path.join(CSRC, "rns_internal.h"), os.path.join(CSRC, "rns_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "rns_gemm.h"),
            os.path.join(os.path.dirname(HERE), "include", "rns_enclose.h"),

@@ -53,24 +53,25 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
     const int h = lane >> 5, l32 = lane & 31;
 
     // first-operand fragments of the digits: block (ks, nb), lane (c32, h),
-    // byte b = digit 32*nb + c32 of the constant of slot 32*ks + 16*h + b
+    // byte b = digit 32*nb + c32 of the constant of slot 32*ks + 16*h + b.
+    // The block first transposes the digit table (a kernel argument) into
+    // LDS, digit-major, so that each fragment is one 16-byte LDS read.
+    __shared__ v4i dT[kCrtDigits][kCrtSlots / 16];
+    {
+        int8_t *t = (int8_t *)&dT[0][0];
+        for (int i = threadIdx.x; i < kCrtDigits * kCrtSlots; i += blockDim.x) {
+            const int c = i / kCrtSlots, k = i - c * kCrtSlots;
+            t[i] = k < kCrtSlots - 8 ? cd.d[k][c] : (int8_t)0;
+        }
+    }
+    __syncthreads();
     v4i dig[KS][NB];
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
 #pragma unroll
         for (int nb = 0; nb < NB; nb++) {
             const int c = 32 * nb + l32;
-#pragma unroll
-            for (int x = 0; x < 4; x++) {
-                uint32_t v = 0;
-#pragma unroll
-                for (int b = 0; b < 4; b++) {
-                    const int k = 32 * ks + 16 * h + 4 * x + b;
-                    const int8_t dd = (k < kCrtSlots - 8 && c < kCrtDigits) ? cd.d[k][c] : (int8_t)0;
-                    v |= (uint32_t)(uint8_t)dd << (8 * b);
-                }
-                dig[ks][nb][x] = (int)v;
-            }
+            dig[ks][nb] = c < kCrtDigits ? dT[c][2 * ks + h] : v4i{0, 0, 0, 0};
         }
 
     // this lane's slot constants

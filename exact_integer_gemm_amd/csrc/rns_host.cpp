@@ -284,6 +284,67 @@ void build_crt(const rns_plan_t &pl, CrtConsts &c, CrtDigits &d, int *ksteps, in
     *nblocks = (used + 31) / 32;
 }
 
+// ---- table cache ---------------------------------------------------------------
+// The constant tables depend only on the plan's moduli (and, for the split,
+// on the operand limb counts).  Building them costs tens of microseconds of
+// host time (big-integer products for the CRT, modular powers for the
+// split), as much as a whole small product on the GPU, so each host thread
+// keeps the tables of its last few plans.
+struct TableKey {
+    int32_t n = 0, x0 = 0, x1 = 0;
+    int32_t q[kMaxPrimes] = {};
+    bool operator==(const TableKey &o) const {
+        return n == o.n && x0 == o.x0 && x1 == o.x1 && std::memcmp(q, o.q, sizeof(int32_t) * n) == 0;
+    }
+};
+TableKey table_key(const rns_plan_t &pl, int x0 = 0, int x1 = 0) {
+    TableKey k;
+    k.n = pl.n_primes;
+    k.x0 = x0;
+    k.x1 = x1;
+    for (int i = 0; i < pl.n_primes; i++) k.q[i] = pl.primes[i];
+    return k;
+}
+template <class V, int N = 8>
+struct TableCache {
+    TableKey key[N];
+    V val[N];
+    bool used[N] = {};
+    int next = 0;
+    template <class Build>
+    const V &get(const TableKey &k, Build build) {
+        for (int i = 0; i < N; i++)
+            if (used[i] && key[i] == k) return val[i];
+        const int i = next;
+        next = (next + 1) % N;
+        build(val[i]);
+        key[i] = k;
+        used[i] = true;
+        return val[i];
+    }
+};
+struct CrtTables {
+    CrtConsts c;
+    CrtDigits d;
+    int ksteps, nblocks;
+};
+const SplitConsts &split_tables(const rns_plan_t &pl, int la, int lb) {
+    static thread_local TableCache<SplitConsts> cache;
+    return cache.get(table_key(pl, la, lb), [&](SplitConsts &v) { build_split(pl, la, lb, v); });
+}
+const EpiConsts &epi_tables(const rns_plan_t &pl) {
+    static thread_local TableCache<EpiConsts> cache;
+    return cache.get(table_key(pl), [&](EpiConsts &v) { build_epi(pl, v); });
+}
+const CrtTables &crt_tables(const rns_plan_t &pl) {
+    static thread_local TableCache<CrtTables> cache;
+    return cache.get(table_key(pl), [&](CrtTables &v) { build_crt(pl, v.c, v.d, &v.ksteps, &v.nblocks); });
+}
+const GarnerConsts &garner_tables(const rns_plan_t &pl) {
+    static thread_local TableCache<GarnerConsts, 4> cache;
+    return cache.get(table_key(pl), [&](GarnerConsts &v) { build_garner(pl, v); });
+}
+
 // ---- layout ------------------------------------------------------------------
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
@@ -378,8 +439,7 @@ int stage_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
     if (rc || !work) return rc;
     if (!B) return RNS_E_ARG;
     int8_t *base = (int8_t *)ws;
-    SplitConsts sc;
-    build_split(*plan, batched ? 1 : a_limbs, b_limbs, sc);
+    const SplitConsts &sc = split_tables(*plan, batched ? 1 : a_limbs, b_limbs);
     SplitOperand sa{}, sb{};
     if (!batched) {
         sa.x = A; sa.planes = base + L.pub.a_off; sa.rows = M; sa.k = K;
@@ -423,8 +483,7 @@ int stage_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, cons
             if (rc) return rc;
         }
     }
-    EpiConsts ec;
-    build_epi(*plan, ec);
+    const EpiConsts &ec = epi_tables(*plan);
     return launch_gemm(L.pub.tile_config, n, apl, base + L.pub.b_off, base + L.pub.y_off,
                        L.pub.m_pad, L.pub.n_pad, L.pub.k_pad, L.pub.m_pad * L.pub.k_pad,
                        L.pub.n_pad * L.pub.k_pad, L.pub.m_pad * L.pub.y_pitch,
@@ -448,16 +507,12 @@ int stage_reconstruct(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, b
     rc = prepare(plan, M, N, K, batched, ws, ws_bytes, &L, &work);
     if (rc || !work) return rc;
     if (method == kReconGarner) {
-        GarnerConsts gc;
-        build_garner(*plan, gc);
+        const GarnerConsts &gc = garner_tables(*plan);
         return launch_garner(gc, (const int8_t *)ws + L.pub.y_off, L.pub.m_pad * L.pub.y_pitch,
                              L.pub.y_pitch, M, N, C, c_limbs, stream);
     }
-    CrtConsts cc;
-    CrtDigits cd;
-    int ks = 0, nb = 0;
-    build_crt(*plan, cc, cd, &ks, &nb);
-    return launch_crt(cc, cd, ks, nb, (const int8_t *)ws + L.pub.y_off,
+    const CrtTables &ct = crt_tables(*plan);
+    return launch_crt(ct.c, ct.d, ct.ksteps, ct.nblocks, (const int8_t *)ws + L.pub.y_off,
                       L.pub.m_pad * L.pub.y_pitch, L.pub.y_pitch, M, N, C, c_limbs, stream);
 }
 
@@ -479,6 +534,16 @@ int run(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
     if (!B || (!batched && !A) || !ws) return RNS_E_ARG;
     const Layout L = make_layout(*plan, M, N, K, batched);
     if (ws_bytes < (size_t)L.pub.total_bytes) return RNS_E_WORKSPACE;
+    if (batched && b_limbs == 1 && N <= 16 && K >= 16 && K % 16 == 0 && K <= RNS_SKINNY_K_MAX &&
+        reinterpret_cast<uintptr_t>(A_res) % 16 == 0 &&
+        skinny_rr_bytes(plan->n_primes, K) <= (int64_t)plan->n_primes * L.pub.n_pad * L.pub.k_pad) {
+        // skinny right-hand side: its residue planes, in the products' operand
+        // layout, go where the split's B planes would
+        rc = launch_skinny(plan->n_primes, A_res, B, M, N, K, (int8_t *)ws + L.pub.b_off, (int8_t *)ws + L.pub.y_off,
+                           L.pub.m_pad * L.pub.y_pitch, L.pub.y_pitch, epi_tables(*plan), stream);
+        if (rc) return rc;
+        return stage_reconstruct(plan, M, N, K, batched, C, c_limbs, ws, ws_bytes, stream);
+    }
     rc = stage_split(plan, M, N, K, batched ? nullptr : A, a_limbs, B, b_limbs, ws, ws_bytes, stream, fp);
     if (rc) return rc;
     rc = stage_products(plan, M, N, K, A_res, ws, ws_bytes, stream);

@@ -420,6 +420,46 @@ def test_batched_residue_any_int8_and_extremes():
     assert np.array_equal(O.decode_array(X), ref)
 
 
+# The skinny right-hand side (N <= 16, one limb, K a multiple of 16 up to
+# 4096) takes the fused split-and-products kernel: ragged rows (not a
+# multiple of the 256-row blocks), every column count, K not a multiple of
+# the 64-wide chunks, all 54 primes or a few, the prime-power moduli (256
+# included), any int8 plane values and right-hand sides at the int64 ends.
+SKINNY = [
+    # M, N, K, n, prime_powers, seed
+    (1, 1, 16, 1, False, 91),
+    (100, 16, 1024, 54, False, 92),
+    (300, 7, 48, 20, False, 93),
+    (513, 16, 1040, 54, False, 94),
+    (256, 3, 4096, 54, False, 95),
+    (777, 16, 208, 54, True, 96),
+    (64, 1, 4096, 6, True, 97),
+]
+
+
+@pytest.mark.parametrize("M,N,K,n,pp,seed", SKINNY)
+def test_batched_residue_skinny_fused(M, N, K, n, pp, seed):
+    print(f"skinny fused M={M} N={N} K={K} n={n} prime_powers={pp}", flush=True)
+    rng = np.random.default_rng(seed)
+    p = rg.plan_n(n, prime_powers=pp)
+    A_res = rng.integers(-128, 128, size=(n, M, K), dtype=np.int64).astype(np.int8)
+    r = rng.integers(-(1 << 62), 1 << 62, size=(K, N), dtype=np.int64)
+    r[0, :] = -(2 ** 63)
+    r[-1, :] = 2 ** 63 - 1
+    r[1::5, :] = rng.integers(-(1 << 34), 1 << 34, size=r[1::5, :].shape, endpoint=True)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None])).cpu().numpy()
+    ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
+    assert np.array_equal(O.decode_array(X), ref)
+    # the stage calls (split, general product kernel, reconstruction) agree bit for bit
+    ws = rg.new_workspace(p, M, N, K, True)
+    Ad, rd = dev(A_res), dev(r[..., None])
+    out = torch.empty((M, N, p.out_limbs_min), dtype=torch.int64, device="cuda")
+    rg.split(p, None, rd, ws, M=M)
+    rg.residue_products(p, M, N, K, ws, A_res=Ad)
+    rg.reconstruct(p, M, N, K, ws, out, batched=True)
+    assert np.array_equal(out.cpu().numpy(), X)
+
+
 # ---------------------------------------------------------------------------
 # the five workloads at full size
 # ---------------------------------------------------------------------------
