@@ -3,31 +3,27 @@
 // reconstruction takes the centered representative by rounding to nearest),
 // with the sum over primes on the matrix cores.
 //
-// For an entry with residues y_k (balanced, one per plane):
-//   u_k = y_k * (M_k^-1 mod q_k) mod q_k, balanced      (M_k = P / q_k)
-//   r   = nearest integer to sum_k u_k / q_k            (binary32)
-//   X'  = sum_k u_k M_k - r P
+// For an entry with residues y_k (the int8 bytes of the product planes):
+//   e_k = w_k M_k, w_k = M_k^-1 mod q_k balanced    (M_k = P / q_k, |e_k| <= P/2)
+//   r   = nearest integer to sum_k y_k w_k / q_k     (fixed point, error < 2^-19)
+//   X'  = sum_k y_k e_k - r P
 // X' is congruent to the product entry X mod P and, when r is the true
-// nearest integer, equal to it.  X' is formed in balanced base-256 chunks
-// by one int8 MFMA: the entry's slots (u_0 .. u_{n-1}, -r) against the
-// digits of (M_0 .. M_{n-1}, P); |chunk sum| <= 55 * 128 * 128 < 2^20.
+// nearest integer, equal to it.  No residue is reduced per entry: the
+// multiplier w_k is folded into the constant e_k.  X' is formed in balanced
+// base-256 chunks by one int8 MFMA: the entry's slots (y_0 .. y_{n-1},
+// -r_lo, -r_hi; r = r_lo + 256 r_hi, r_lo in [-127, 128]) against the digits
+// of (e_0 .. e_{n-1}, P, 256 P);
+// |chunk sum| <= 56 * 128 * 128 < 2^20.
 //
 // A wave takes 32 entries.  Lane (l32, h) holds entry l32 and slots
 // 16h .. 16h + 15 of each 32-slot K step: exactly the second-operand
 // fragment of v_mfma_i32_32x32x32_i8, whose result gives lane (l32, h) the
-// chunk sums 8*gq + 4h + e (gq, e < 4) of its entry.  The two halves swap
-// their 4-chunk groups and each carries the whole value into 32-bit words;
-// each then stores half of the entry's limbs.
+// chunk sums 8*gq + 4h + e (gq, e < 4) of its entry.  The two halves trade
+// their 16-bit pairs of chunks and each carries the whole value into 32-bit
+// words; each then stores half of the entry's limbs.
 #include "rns_device.h"
 
 namespace rns {
-
-// u = t - q * round(t / q) for |t| < 2^22 (binary32 rounding step, ties to
-// even, so q = 2 gives u = t for t in {0, 1}).
-__device__ __forceinline__ int reduce_small(int t, int q, float inv) {
-    const int k = __float_as_int(__builtin_fmaf((float)t, inv, kRoundMagic32)) - 0x4b400000;
-    return __mul24(k, -q) + t;                // |k| < 2^15, q <= 256: 24-bit operands
-}
 
 // The value x of the lane in the other half-wave (lane l xor 32), by
 // v_permlane32_swap: swapping x with itself gives the lower half-wave the
@@ -74,27 +70,20 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
             dig[ks][nb] = c < kCrtDigits ? dT[c][2 * ks + h] : v4i{0, 0, 0, 0};
         }
 
-    // this lane's slot constants
-    int sq[KS][16], sw[KS][16], plane[KS][16];
-    float si[KS][16];
+    // this lane's slot constants: the fixed-point weights and plane offsets
+    int shi[KS][16], slo[KS][16], plane[KS][16];
     uint32_t poff[KS][16];
 #pragma unroll
     for (int ks = 0; ks < KS; ks++)
 #pragma unroll
         for (int b = 0; b < 16; b++) {
             const int k0 = 32 * ks + b, k1 = k0 + 16;
-            sq[ks][b] = h ? cc.q[k1] : cc.q[k0];
-            sw[ks][b] = h ? cc.w[k1] : cc.w[k0];
-            si[ks][b] = h ? cc.inv[k1] : cc.inv[k0];
+            shi[ks][b] = h ? cc.chi[k1] : cc.chi[k0];
+            slo[ks][b] = h ? cc.clo[k1] : cc.clo[k0];
             const int k = h ? k1 : k0;
-            plane[ks][b] = k < cc.n ? k : cc.n - 1;   // padding slots read a valid plane, weight 0
+            plane[ks][b] = k < cc.n ? k : cc.n - 1;   // other slots read a valid plane, weight 0
             poff[ks][b] = OFF32 ? (uint32_t)(plane[ks][b] * y_plane) : 0u;
         }
-    // a modulus 256 (always slot 0, the largest) can round to u = 128, whose
-    // int8 byte reads as -128: its quotient term must use the byte's value
-    const bool wrap0 = cc.q[0] == 256;
-    const int rk = cc.n;                      // the -r slot
-    const int rks = rk >> 5, rh = (rk >> 4) & 1, rb = rk & 15;
 
     // rows mode (wide rows): a wave takes 32 consecutive columns of one row at
     // a time, and the row and column group advance by the grid stride without
@@ -133,7 +122,9 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
         const int8_t *yp = y + i * y_pitch + j;
         const uint32_t yo = OFF32 ? (uint32_t)(i * y_pitch + j) : 0u;
 
-        float f = 0.0f;
+        // the slots' bytes, and the fixed-point sum of y_k c_k in two 16-bit halves
+        // of c_k (|sum y chi| < 2^27, |sum y clo| < 2^29 per half-wave)
+        int ahi = 0, alo = 0;
         v4i ua[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ks++) {
@@ -141,32 +132,37 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
 #pragma unroll
             for (int b = 0; b < 16; b++) {
                 const int yv = OFF32 ? (int)y[yo + poff[ks][b]] : (int)yp[plane[ks][b] * y_plane];
-                const int t = __mul24(yv, sw[ks][b]);   // |y| <= 128, w < 256
-                int u = reduce_small(t, sq[ks][b], si[ks][b]);
-                if (ks == 0 && b == 0) u = (wrap0 && h == 0) ? (int)(int8_t)u : u;
-                f = __builtin_fmaf((float)u, si[ks][b], f);
-                byte[b] = u;
+                ahi = __mul24(yv, shi[ks][b]) + ahi;
+                alo = __mul24(yv, slo[ks][b]) + alo;
+                byte[b] = yv;
             }
 #pragma unroll
             for (int wd = 0; wd < 4; wd++)
                 ua[ks][wd] = (int)pack4(byte[4 * wd], byte[4 * wd + 1], byte[4 * wd + 2], byte[4 * wd + 3]);
         }
-        const float ft = f + __uint_as_float(partner_u32(__float_as_uint(f), h));
-        const float rf = __builtin_rintf(ft);
-        const bool near_half = __builtin_fabsf(ft - rf) > 0.5f - 0x1p-10f;
-        const int r = (int)rf;
-        if (h == rh) {
-            // slot n carries -r (|r| <= 28); its byte was zero (weight 0)
+        ahi += (int)partner_u32((uint32_t)ahi, h);
+        alo += (int)partner_u32((uint32_t)alo, h);
+        // F / 2^31 is within 2^-19 of S / P; r = floor(F / 2^31 + 1/2)
+        const int64_t F = ((int64_t)ahi << 16) + alo;
+        const int64_t r64 = (F + (1ll << 30)) >> 31;
+        const int64_t fr = F - (r64 << 31);        // in [-2^30, 2^30)
+        const bool near_half = fr < -(1ll << 30) + (1ll << 21) || fr >= (1ll << 30) - (1ll << 21);
+        const int r = (int)r64;
+        const int rlo = ((r + 127) & 255) - 127;  // r = rlo + 256 rhi, rlo in [-127, 128]:
+        const int rhi = (r - rlo) >> 8;           // -rlo and -rhi fit int8
+        // slots n and n + 1 carry -rlo and -rhi (their bytes were read from a
+        // valid plane with weight zero); a slot's K step, half-wave, word and
+        // byte are uniform
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const int k = cc.n + t, val = t ? -rhi : -rlo;
+            const int ks_k = k >> 5, h_k = (k >> 4) & 1, x_k = (k >> 2) & 3, sh = 8 * (k & 3);
 #pragma unroll
             for (int ks = 0; ks < KS; ks++)
-                if (ks == rks) {
-                    const int wd = rb >> 2, sh = 8 * (rb & 3);
 #pragma unroll
-                    for (int x = 0; x < 4; x++)
-                        if (x == wd)
-                            ua[ks][x] = (int)(((uint32_t)ua[ks][x] & ~(0xffu << sh)) |
-                                              ((uint32_t)(-r & 0xff) << sh));
-                }
+                for (int x = 0; x < 4; x++)
+                    if (ks == ks_k && x == x_k && h == h_k)
+                        ua[ks][x] = (int)(((uint32_t)ua[ks][x] & ~(0xffu << sh)) | ((uint32_t)(val & 0xff) << sh));
         }
 
         v16i acc[NB];
@@ -178,31 +174,40 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
                 acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[ks][nb], ua[ks], acc[nb], 0, 0, 0);
         }
 
-        // 4-chunk groups: this lane's group (nb, gq) sits at word 8*nb + 2*gq + h
-        int64_t g[NB][4], gp[NB][4];
+        // Lane (l32, h) holds the chunk sums a[4 gq + e] of digits
+        // 32 nb + 8 gq + 4 h + e (|a| < 2^20).  Their pairs lo = a0 + 2^8 a1
+        // and hi = a2 + 2^8 a3 (|.| < 2^29) are the 16-bit places 2 w and
+        // 2 w + 1 of X' for word w = 8 nb + 2 gq + h.  v_permlane32_swap of a
+        // value with itself hands every lane both half-waves' values: the
+        // first result is the lower half's (word 8 nb + 2 gq), the second the
+        // upper half's (word 8 nb + 2 gq + 1).  Every lane then carries the
+        // whole value through 2 W places of 16 bits in 32-bit arithmetic.
+        int part[2 * W];
 #pragma unroll
         for (int nb = 0; nb < NB; nb++)
 #pragma unroll
             for (int gq = 0; gq < 4; gq++) {
                 const v16i &a = acc[nb];
-                g[nb][gq] = (int64_t)a[4 * gq] + ((int64_t)a[4 * gq + 1] << 8) +
-                            ((int64_t)a[4 * gq + 2] << 16) + ((int64_t)a[4 * gq + 3] << 24);
-                const uint32_t lo = partner_u32((uint32_t)g[nb][gq], h);
-                const uint32_t hi = partner_u32((uint32_t)((uint64_t)g[nb][gq] >> 32), h);
-                gp[nb][gq] = (int64_t)(((uint64_t)hi << 32) | lo);
+                const int lo = a[4 * gq] + (a[4 * gq + 1] << 8);
+                const int hi = a[4 * gq + 2] + (a[4 * gq + 3] << 8);
+                const auto sl = __builtin_amdgcn_permlane32_swap((uint32_t)lo, (uint32_t)lo, false, false);
+                const auto sh = __builtin_amdgcn_permlane32_swap((uint32_t)hi, (uint32_t)hi, false, false);
+                const int w0 = 8 * nb + 2 * gq;
+                part[2 * w0] = (int)sl[0];
+                part[2 * w0 + 1] = (int)sh[0];
+                part[2 * w0 + 2] = (int)sl[1];
+                part[2 * w0 + 3] = (int)sh[1];
             }
         uint32_t wv[W];
-        int64_t carry = 0;
+        int c16 = 0;
 #pragma unroll
-        for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-            for (int gq = 0; gq < 4; gq++)
-#pragma unroll
-                for (int hh = 0; hh < 2; hh++) {
-                    carry += (hh == h) ? g[nb][gq] : gp[nb][gq];
-                    wv[8 * nb + 2 * gq + hh] = (uint32_t)carry;
-                    carry >>= 32;
-                }
+        for (int w = 0; w < W; w++) {
+            const int t0 = part[2 * w] + c16;
+            const int t1 = part[2 * w + 1] + (t0 >> 16);
+            c16 = t1 >> 16;
+            wv[w] = __builtin_amdgcn_perm((uint32_t)t1, (uint32_t)t0, 0x05040100u);   // low halves of t0, t1
+        }
+        int64_t carry = c16;
         // carry is now the sign word (0 or -1): X' = wv + carry * 2^(32 W)
 
         if (near_half) {
@@ -267,7 +272,7 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
                int32_t c_limbs, hipStream_t s) {
     const int64_t total = M * N;
     if (total == 0) return RNS_OK;
-    if (c.n < 1 || c.n + 1 > 32 * ksteps || ksteps < 1 || ksteps > 2 || nblocks < 1 || nblocks > 2)
+    if (c.n < 1 || c.n + 2 > 32 * ksteps || ksteps < 1 || ksteps > 2 || nblocks < 1 || nblocks > 2)
         return RNS_E_ARG;
     // rows mode when whole 32-column groups waste little: N a multiple of 32, or N >= 256
     const int rows = (N % 32 == 0 || N >= 256) ? 1 : 0;

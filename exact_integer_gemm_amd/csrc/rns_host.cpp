@@ -238,29 +238,35 @@ void build_garner(const rns_plan_t &pl, GarnerConsts &g) {
     }
 }
 
-// CRT by rounded quotient: per-slot q, (P/q)^-1 mod q and fl(1/q); P's words;
-// the balanced base-256 digits of every M_k = P / q_k and of P.  Returns the
-// MFMA K steps and N blocks through *ksteps, *nblocks.
+// CRT by rounded quotient: per slot the fixed-point weight c_k = round(w_k
+// 2^31 / q_k), P's words, and the balanced base-256 digits of every basis
+// element e_k = w_k M_k (signed), of P and of 256 P.  Returns the MFMA K
+// steps and N blocks through *ksteps, *nblocks.
+// balanced base-256 digits of +-v (out[i] in [-128, 127], sum out[i] 256^i);
+// returns the digits in use
+int signed_digits(const Big &v, bool neg, int8_t *out) {
+    int carry = 0, last = 0;
+    const int nbytes = 4 * (int)v.w.size();
+    for (int ci = 0; ci < kCrtDigits; ci++) {
+        int byte = ci < nbytes ? (int)((v.w[ci / 4] >> (8 * (ci % 4))) & 0xffu) : 0;
+        if (neg) byte = -byte;
+        byte += carry;                       // in [-256, 256]
+        carry = 0;
+        while (byte >= 128) { byte -= 256; carry++; }
+        while (byte < -128) { byte += 256; carry--; }
+        out[ci] = (int8_t)byte;
+        if (byte) last = ci + 1;
+    }
+    return last;
+}
+int64_t floor_div(int64_t a, int64_t b) {   // b > 0
+    return a >= 0 ? a / b : -((-a + b - 1) / b);
+}
 void build_crt(const rns_plan_t &pl, CrtConsts &c, CrtDigits &d, int *ksteps, int *nblocks) {
     const int n = pl.n_primes;
     std::memset(&c, 0, sizeof(c));
     std::memset(&d, 0, sizeof(d));
     c.n = n;
-    for (int k = 0; k < kCrtSlots; k++) { c.q[k] = 1; c.w[k] = 0; c.inv[k] = 0.0f; }
-    auto digits = [&](const Big &v, int8_t *out) {
-        // balanced base-256 digits: v = sum_c out[c] 256^c, out[c] in [-128, 127]
-        int carry = 0, last = 0;
-        const int nbytes = 4 * (int)v.w.size();
-        for (int ci = 0; ci < kCrtDigits; ci++) {
-            int byte = carry;
-            if (ci < nbytes) byte += (int)((v.w[ci / 4] >> (8 * (ci % 4))) & 0xffu);
-            carry = 0;
-            if (byte >= 128) { byte -= 256; carry = 1; }
-            out[ci] = (int8_t)byte;
-            if (byte) last = ci + 1;
-        }
-        return last;                          // digits in use
-    };
     Big P(1);
     for (int k = 0; k < n; k++) P.mul_small((uint32_t)pl.primes[k]);
     int used = 0;
@@ -273,14 +279,20 @@ void build_crt(const rns_plan_t &pl, CrtConsts &c, CrtDigits &d, int *ksteps, in
                 Mk.mul_small((uint32_t)pl.primes[j]);
                 Mk_mod = Mk_mod * pl.primes[j] % q;
             }
-        c.q[k] = q;
-        c.w[k] = balanced(inv_mod(Mk_mod, q), q);
-        c.inv[k] = 1.0f / (float)q;
-        used = std::max(used, digits(Mk, d.d[k]));
+        const int w = balanced(inv_mod(Mk_mod, q), q);
+        const int64_t cfix = floor_div((((int64_t)w << 31) * 2) + q, 2 * (int64_t)q);   // round(w 2^31 / q)
+        c.chi[k] = (int32_t)(cfix >> 16);
+        c.clo[k] = (int32_t)(cfix & 0xffff);
+        Big E = Mk;
+        E.mul_small((uint32_t)(w < 0 ? -w : w));
+        used = std::max(used, signed_digits(E, w < 0, d.d[k]));
     }
-    used = std::max(used, digits(P, d.d[n]));
+    used = std::max(used, signed_digits(P, false, d.d[n]));
+    Big P256 = P;
+    P256.mul_small(256u);
+    used = std::max(used, signed_digits(P256, false, d.d[n + 1]));
     for (int i = 0; i < 16; i++) c.P[i] = i < (int)P.w.size() ? P.w[i] : 0u;
-    *ksteps = (n + 1 + 31) / 32;
+    *ksteps = (n + 2 + 31) / 32;
     *nblocks = (used + 31) / 32;
 }
 

@@ -76,28 +76,34 @@ __host__ __device__ constexpr int tri_index(int j, int k) {
 
 // ---- CRT by rounded quotient (kernel 3, default) -----------------------------
 // Ozaki Scheme II paper, §3.5.2: the centered representative is taken by
-// rounding to nearest.  With M_k = P / q_k and u_k = y_k * (M_k^-1 mod q_k)
-// mod q_k (balanced), S = sum_k u_k M_k = X (mod P) and S / P = sum_k u_k /
-// q_k, so X = S - r P with r the nearest integer to sum_k u_k / q_k.  One
-// INT8 MFMA per 32 entries forms S - r P in balanced base-256 chunks: the
-// entries' slots (u_0 .. u_{n-1}, -r) times the balanced base-256 digits of
-// (M_0 .. M_{n-1}, P).  r comes from a binary32 sum (error < 2^-12); where
-// that sum is within 2^-10 of a half-integer the result is compared with
-// P/2 exactly and moved by one period if needed.
-constexpr int kCrtSlots = 64;        // n primes + the -r slot, padded to two K steps of 32
-constexpr int kCrtDigits = 48;       // balanced base-256 digits kept per constant (P < 2^336)
+// rounding to nearest.  With M_k = P / q_k and w_k = M_k^-1 mod q_k
+// (balanced, |w_k| <= q_k / 2), the CRT basis element e_k = w_k M_k is 1 mod
+// q_k and 0 mod the other moduli, and |e_k| <= P / 2.  So for any
+// representatives y_k of the residues (the int8 bytes as stored),
+// S = sum_k y_k e_k = X (mod P) and S / P = sum_k y_k w_k / q_k exactly;
+// X = S - r P with r the nearest integer to that sum.  No residue is reduced
+// per entry: the multiplier w_k lives in the constant e_k.  r comes from a
+// fixed-point sum: c_k = round(w_k 2^31 / q_k), so sum_k y_k c_k / 2^31 is
+// within n * 128 / 2^32 < 2^-19 of S / P; where it lies within 2^-10 of a
+// half-integer the result is compared with P/2 exactly and moved by one
+// period if needed.  One INT8 MFMA per 32 entries forms S - r P in balanced
+// base-256 chunks: the entries' slots (y_0 .. y_{n-1}, -r_lo, -r_hi) times
+// the balanced base-256 digits of (e_0 .. e_{n-1}, P, 256 P), where
+// r = r_lo + 256 r_hi with r_lo in [-127, 128] (so -r_lo fits a byte).
+constexpr int kCrtSlots = 64;        // n moduli + the two -r slots, padded to two K steps of 32
+constexpr int kCrtDigits = 48;       // balanced base-256 digits kept per constant (256 P < 2^384)
 
 struct CrtConsts {
-    int32_t n;                       // primes; slot n holds -r
-    int32_t q[kCrtSlots];            // per slot; padding slots q = 1, w = 0, inv = 0
-    int32_t w[kCrtSlots];            // M_k^-1 mod q_k, balanced
-    float inv[kCrtSlots];            // fl(1/q_k)
+    int32_t n;                       // moduli; slots n and n + 1 hold -r_lo and -r_hi
+    int32_t chi[kCrtSlots];          // c_k = chi 2^16 + clo, clo in [0, 2^16); zero past slot n - 1
+    int32_t clo[kCrtSlots];
     uint32_t P[16];                  // P, little-endian 32-bit words
 };
-// Balanced base-256 digits of M_0 .. M_{n-1} and P (slot n); the kernel
-// takes them as an argument and lays out its MFMA fragments itself.
+// Balanced base-256 digits of e_0 .. e_{n-1}, P (slot n) and 256 P (slot
+// n + 1); the kernel takes them as an argument and lays out its MFMA
+// fragments itself.
 struct CrtDigits {
-    int8_t d[kCrtSlots - 8][kCrtDigits];   // slots 0 .. 55 (n + 1 <= 55)
+    int8_t d[kCrtSlots - 8][kCrtDigits];   // slots 0 .. 55 (n + 2 <= 56)
 };
 
 // ---- residue plane layout ----------------------------------------------------
