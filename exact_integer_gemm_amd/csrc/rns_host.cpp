@@ -166,20 +166,24 @@ bool plan_ok(const rns_plan_t *p) {
 void build_split(const rns_plan_t &pl, int la, int lb, SplitConsts &c) {
     std::memset(&c, 0, sizeof(c));
     c.n = pl.n_primes;
+    const int limbs[2] = {la > 0 ? la : 1, lb};
     for (int j = 0; j < pl.n_primes; j++) {
         const int q = pl.primes[j];
         c.q[j] = q;
-        c.inv[j] = 1.0f / (float)q;
-        for (int w = 0; w < 2 * RNS_MAX_IN_LIMBS; w++) {
-            uint32_t packed = 0;
-            for (int b = 0; b < 4; b++) {
-                const int64_t v = powmod(256, 4 * w + b, q);   // 256^(4w+b) mod q, in [0, q)
-                packed |= (uint32_t)v << (8 * b);
-            }
-            c.w[j][w] = packed;
+        float inv = 1.0f / (float)q;
+        if (q % 2 == 0) inv = std::nextafterf(inv, 0.0f);   // q is a power of two
+        c.inv[j] = inv;
+        for (int b = 0; b < kSplitBytes; b++) {
+            const int64_t v = powmod(256, b, q);              // in [0, q)
+            const int64_t t = v > q / 2 ? v - q : v;          // balanced, |t| <= 127
+            c.t[j][b / 4] |= (uint32_t)(uint8_t)(int8_t)t << (8 * (b % 4));
         }
-        c.h_a[j] = (int32_t)powmod(2, 64 * (int64_t)(la > 0 ? la : 1) - 1, q);
-        c.h_b[j] = (int32_t)powmod(2, 64 * (int64_t)lb - 1, q);
+        for (int o = 0; o < 2; o++) {
+            int64_t sum = 0;                                  // 1 + 256 + ... + 256^(8L-2) mod q
+            for (int b = 0; b < 8 * limbs[o] - 1; b++) sum = (sum + powmod(256, b, q)) % q;
+            const int64_t cl = 128 * sum % q;
+            c.start[o][j] = (int32_t)(cl + (int64_t)q * ((kSplitSumBias + q - 1) / q));
+        }
     }
 }
 

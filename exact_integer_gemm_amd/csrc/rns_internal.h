@@ -24,19 +24,22 @@ constexpr double kRoundMagic = 6755399441055744.0;
 constexpr float kRoundMagic32 = 12582912.0f;
 
 // ---- residue split (kernel 1) ---------------------------------------------
-// An operand entry x of L limbs is read as U = x + 2^(64L-1) (its top bit
-// flipped), an unsigned 64L-bit number, so x = U - 2^(64L-1).  With U's bytes
-// u_b,  x mod q = sum_b u_b * (256^b mod q) - (2^(64L-1) mod q)  (mod q),
-// which four-byte dot products evaluate: each 32-bit word of U against a
-// word of four packed constants 256^(4w+i) mod q.
+// An L-limb entry x is sum_b a_b 256^b + c_L over its bytes, with a_b the
+// byte minus 128 (the top byte: its signed value) and c_L = 128 (1 + 256 +
+// ... + 256^(8L-2)).  So x mod q = sum_b a_b t_b + c_L mod q with
+// t_b = 256^b mod q: an INT8 dot product on the matrix cores.
+constexpr int kSplitBytes = 8 * RNS_MAX_IN_LIMBS;   // 32 byte positions
 struct SplitConsts {
-    int32_t n;
+    alignas(16) uint32_t t[kMaxPrimes][kSplitBytes / 4];   // balanced t_b as packed int8, b = 0 .. 31
+    int32_t start[2][kMaxPrimes];   // accumulator start for A (0) and B (1): c_L mod q plus a
+                                    // multiple of q that keeps every sum positive
     int32_t q[kMaxPrimes];
-    float inv[kMaxPrimes];                 // fl(1/q) in binary32
-    uint32_t w[kMaxPrimes][2 * RNS_MAX_IN_LIMBS];  // packed bytes 256^(4w+i) mod q
-    int32_t h_a[kMaxPrimes];               // 2^(64*la - 1) mod q
-    int32_t h_b[kMaxPrimes];               // 2^(64*lb - 1) mod q
+    float inv[kMaxPrimes];          // binary32 1/q; for q a power of two the float just below
+                                    // it, so that a sum = q/2 (mod q) gives +q/2
+    int32_t n;
 };
+// |sum_b a_b t_b| <= 32 * 128 * 127 < 2^19: the start adds at least this much.
+constexpr int32_t kSplitSumBias = 1 << 19;
 
 // ---- mod-q epilogue of the residue product (kernel 2) ----------------------
 // The int32 accumulator s itself goes through the binary64 rounding step.

@@ -1,6 +1,30 @@
 // K1 of the exact residue GEMM on gfx950: int64-limb operands -> balanced
 // int8 residue planes, one per prime (enclosure-gemm, "Method": the residue
 // split), and the repack of caller-given residue planes.
+//
+// The split runs on the matrix cores.  Write an L-limb entry x in bytes x_b
+// (little-endian two's complement) and let a_b = x_b - 128 for every byte but
+// the top one, whose signed value is a_b itself; then
+//     x = sum_b a_b 256^b + c_L,   c_L = 128 (1 + 256 + ... + 256^(8L-2)),
+// so  x = sum_b a_b t_b + c_L (mod q)  with t_b = 256^b mod q (balanced):
+// a dot product of signed bytes.  The bytes a_b are the entry's bytes with
+// bit 7 flipped (all but the top one), so the first operand of
+// v_mfma_i32_32x32x32_i8 is the loaded entry XOR a constant, and its
+// second operand holds the t_b of 32 moduli.  The accumulator starts at
+// c_L mod q plus a multiple of q above 32 * 128 * 127, which keeps every sum
+// t in (0, 2^21); one binary32 rounding step then reduces t mod q.
+//
+// Two packings of the 32 byte positions of one product (lane (row, h) of the
+// first operand holds 16 of them; the same 16 positions are lane (col, h) of
+// the second operand, whatever their order inside the instruction):
+//   pair   (L <= 2): lane (row, h) holds entry 32 h + row of a 64-entry group;
+//          column c holds the t_b of modulus c % 16 in half c / 16 and zeros
+//          in the other half.  Column c then gives entry 32 (c / 16) + row mod
+//          modulus c % 16: 64 entries x 16 moduli per product.
+//   single (L = 3, 4): lane (row, h) holds bytes 16 h .. 16 h + 15 of entry
+//          row; column c holds t_{16 h + j} of modulus c: 32 entries x 32
+//          moduli per product.
+// Result lane (c, hh) holds rows 8 g + 4 hh + e (g, e < 4) of column c.
 #include "rns_device.h"
 
 namespace rns {
@@ -8,26 +32,20 @@ namespace rns {
 // ============================================================================
 // K1: residue split
 // ============================================================================
-// One thread handles a run of 16 consecutive k of one plane row (a row of A,
-// or a column of B), so each prime's 16 residues leave as one 16-byte store
-// into the K-blocked plane.
-constexpr int kSplitThreads = 256;
-constexpr int kRun = 16;
+constexpr int kSplitThreads = 256;                 // four waves
+constexpr int kSplitWaves = kSplitThreads / 64;
+constexpr int kRowsPair = 8;                       // plane rows per wave, pair packing
+constexpr int kRowsSingle = 4;                     // plane rows per wave, single packing
 
-// Small problems (a few hundred blocks or fewer) would leave most compute
-// units idle while each thread loops over every prime; their grid repeats
-// the task blocks for groups of primes instead (the entries are loaded once
-// per group).
-constexpr int64_t kSplitTargetBlocks = 1024;
+typedef uint64_t u64;
 
-struct SplitArgs {
-    SplitOperand op[2];
-    int64_t tasks[2];      // r_pad * (k_pad / 16) per operand
-    int32_t blocks0;       // task blocks that serve operand 0
-    int32_t task_blocks;   // task blocks of both operands
-    int32_t prime_groups;  // the grid is prime_groups x task_blocks
-    uint32_t flag_bit[2];  // RNS_FLAG_* recorded for an out-of-bound entry of each operand
-    uint32_t *status;      // [2 + gridDim.x] words
+struct SplitStatus {
+    uint32_t *status;      // [kStatusHeader + total] words
+    int64_t work;          // row path: wave units; column path: workgroup tiles
+    int32_t first;         // this launch's first status word (after the header)
+    int32_t total;         // status words of every launch of the split
+    uint32_t flag_bit;     // RNS_FLAG_* recorded for an out-of-bound entry
+    int32_t b_start;       // 1: the operand takes start_b (the B offsets)
 };
 
 // |x| <= 2^bits for an L-limb value, bits >= 0.  For x < 0 use ~x = -x-1:
@@ -50,172 +68,573 @@ __device__ __forceinline__ bool within_bound(const uint64_t (&x)[L], int bits) {
     return below || is_pow;
 }
 
-template <int L, bool FP>
-__device__ void split_run(const SplitOperand &op, const SplitConsts &c, const int32_t *h,
-                          int64_t task, int p_begin, int p_end, uint32_t &flag) {
-    // 64 consecutive tasks (one wave) cover one K block (64 k) of 16 plane
-    // rows: lane / 4 picks the row, lane % 4 the run of 16 k.  The wave's
-    // stores then fill 1 KB of the K-blocked plane contiguously.
-    const int64_t lane = task & 63, wv = task >> 6;
-    const int64_t groups = op.r_pad / 16;
-    const int64_t kb = wv / groups, rg = wv - kb * groups;
-    const int64_t r = rg * 16 + (lane >> 2);
-    const int64_t k0 = kb * kKBlock + (lane & 3) * kRun;
-    const bool row_ok = r < op.rows;
+// The first-operand bytes of limb l of an L-limb entry: bit 7 of every byte
+// flipped but for the entry's top byte; limbs past the entry are zero.
+template <int L>
+__device__ __forceinline__ u64 operand_limb(u64 x, int l) {
+    return l < L - 1 ? x ^ 0x8080808080808080ull : l == L - 1 ? x ^ 0x0080808080808080ull : 0ull;
+}
 
-    // All 16 L limbs are requested before any is used: a padding entry reads
-    // entry 0 (the operand is not empty when there are tasks) and is then
-    // replaced by zero, so no load sits behind a branch and a wait.
-    // (binary64 operands: one word per entry, scaled into L limbs here)
-    constexpr int W = FP ? 1 : L;
-    uint64_t xs[kRun][W];
-#pragma unroll
-    for (int e = 0; e < kRun; e++) {
-        const int64_t k = k0 + e;
-        const bool ok = row_ok && k < op.k;
-        const int64_t idx = !ok ? 0 : op.transposed ? (k * op.rows + r) : (r * op.k + k);
-#pragma unroll
-        for (int l = 0; l < W; l++) xs[e][l] = (uint64_t)op.x[idx * W + l];
-    }
-    // U = x + 2^(64L-1) as 2L little-endian 32-bit words, per element
-    uint32_t u[kRun][2 * L];
-    uint32_t lowbit = 0;   // bit e: x_e is odd (residue mod 2)
-#pragma unroll
-    for (int e = 0; e < kRun; e++) {
-        const int64_t k = k0 + e;
-        const bool ok = row_ok && k < op.k;
-        uint64_t x[L];
-        if constexpr (FP) {
-            fp64_floor_scaled<L>(ok ? xs[e][0] : 0ull, op.scale, x);
-        } else {
-#pragma unroll
-            for (int l = 0; l < L; l++) x[l] = ok ? xs[e][l] : 0ull;
-        }
-        if (op.bits >= 0 && !within_bound<L>(x, op.bits)) flag = 1;
-        lowbit |= (uint32_t)(x[0] & 1u) << e;
-#pragma unroll
-        for (int l = 0; l < L; l++) {
-            uint64_t v = x[l] ^ (l == L - 1 ? (1ull << 63) : 0ull);
-            u[e][2 * l] = (uint32_t)v;
-            u[e][2 * l + 1] = (uint32_t)(v >> 32);
-        }
-    }
+__device__ __forceinline__ v4i as_v4i(u64 lo, u64 hi) {
+    return v4i{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
+}
 
-    int8_t *dst = op.planes + kb * (op.r_pad * kKBlock) + r * kKBlock + (lane & 3) * kRun;
-    const int64_t plane = op.r_pad * op.k_pad;
-    for (int p = p_begin; p < p_end; p++) {
-        const int q = c.q[p];
-        uint32_t word[4];
-        if (q == 2) {
+// W consecutive words from an 8-byte aligned address (one wide load)
+template <int W>
+__device__ __forceinline__ void load_words(const int64_t *p, u64 (&w)[W]) {
+    __builtin_memcpy(w, p, sizeof(w));
+}
+
+// The limbs of an entry from its loaded words (binary64: floor(x * 2^scale));
+// an entry outside the operand (ok false) is zero.
+template <int L, bool FP, int W>
+__device__ __forceinline__ void entry_limbs(const u64 (&xs)[W], bool ok, int scale, u64 (&x)[L]) {
+    if constexpr (FP) {
+        fp64_floor_scaled<L>(ok ? xs[0] : 0ull, scale, x);
+    } else {
 #pragma unroll
-            for (int w = 0; w < 4; w++) {
-                uint32_t b = (lowbit >> (4 * w)) & 0xFu;
-                // spread 4 bits into the low bit of 4 bytes
-                word[w] = (b & 1u) | ((b & 2u) << 7) | ((b & 4u) << 14) | ((b & 8u) << 21);
-            }
-        } else {
-            const float inv = c.inv[p];
-            const int hp = h[p];
-            int res[kRun];
-#pragma unroll
-            for (int e = 0; e < kRun; e++) {
-                uint32_t t = (uint32_t)(-hp);
-#pragma unroll
-                for (int w = 0; w < 2 * L; w++)
-                    t = __builtin_amdgcn_udot4(u[e][w], c.w[p][w], t, false);
-                res[e] = reduce_low_byte_f32((int)t, q, inv);
-            }
-#pragma unroll
-            for (int w = 0; w < 4; w++)
-                word[w] = pack4(res[4 * w], res[4 * w + 1], res[4 * w + 2], res[4 * w + 3]);
-        }
-        v4u out = {word[0], word[1], word[2], word[3]};
-        *(v4u *)(dst + p * plane) = out;
+        for (int l = 0; l < L; l++) x[l] = ok ? xs[l] : 0ull;
     }
 }
 
-// FP: both operands are binary64 (one kernel per operand kind keeps the
-// register allocation of each path separate)
-template <bool FP>
-__global__ __launch_bounds__(kSplitThreads) void split_kernel(SplitArgs args, SplitConsts c) {
-    const int tb = (int)blockIdx.x % args.task_blocks, pg = (int)blockIdx.x / args.task_blocks;
-    const int p_begin = pg * c.n / args.prime_groups, p_end = (pg + 1) * c.n / args.prime_groups;
-    const int which = tb < args.blocks0 ? 0 : 1;
-    const int64_t block = which == 0 ? tb : tb - args.blocks0;
-    const int64_t task = block * kSplitThreads + threadIdx.x;
-    const SplitOperand &op = args.op[which];
-    const int32_t *h = which == 0 ? c.h_a : c.h_b;
-    uint32_t flag = 0;
-    if (task < args.tasks[which]) {
-        switch (op.limbs) {
-            case 1: split_run<1, FP>(op, c, h, task, p_begin, p_end, flag); break;
-            case 2: split_run<2, FP>(op, c, h, task, p_begin, p_end, flag); break;
-            case 3: split_run<3, FP>(op, c, h, task, p_begin, p_end, flag); break;
-            default: split_run<4, FP>(op, c, h, task, p_begin, p_end, flag); break;
+// The per-modulus constants of one operand, staged in LDS once per
+// workgroup: the columns of every block of moduli read them from there.
+struct SplitLds {
+    v4i t[kMaxPrimes][2];      // t_b, b = 0 .. 31
+    int32_t start[kMaxPrimes];
+    int32_t q[kMaxPrimes];
+    float inv[kMaxPrimes];
+};
+constexpr int kTWords = kMaxPrimes * kSplitBytes / 4;
+constexpr int kLdsWords = kTWords + 3 * kMaxPrimes;     // the image without its tail padding
+constexpr int kLdsLoads = (kLdsWords + kSplitThreads - 1) / kSplitThreads;
+static_assert(sizeof(SplitLds) >= 4 * kLdsWords && offsetof(SplitLds, inv) == 4 * (kTWords + 2 * kMaxPrimes),
+              "LDS image layout");
+
+// Each thread reads its share of the constants (word w of the LDS image)
+// from the kernel arguments; issued before the entry loads, written to LDS
+// after them.
+struct TableWords {
+    uint32_t v[kLdsLoads];
+};
+
+__device__ __forceinline__ TableWords table_load(const SplitConsts &c, int sidx) {
+    TableWords tw;
+#pragma unroll
+    for (int j = 0; j < kLdsLoads; j++) {
+        int w = (int)threadIdx.x + kSplitThreads * j;
+        w = w < kLdsWords ? w : kLdsWords - 1;
+        const uint32_t *src = w < kTWords ? &c.t[0][0] + w
+                            : w < kTWords + kMaxPrimes ? (const uint32_t *)&c.start[sidx][w - kTWords]
+                            : w < kTWords + 2 * kMaxPrimes ? (const uint32_t *)&c.q[w - kTWords - kMaxPrimes]
+                            : (const uint32_t *)&c.inv[w - kTWords - 2 * kMaxPrimes];
+        tw.v[j] = *src;
+    }
+    return tw;
+}
+
+__device__ __forceinline__ void table_commit(const TableWords &tw, SplitLds &lds) {
+#pragma unroll
+    for (int j = 0; j < kLdsLoads; j++) {
+        const int w = (int)threadIdx.x + kSplitThreads * j;
+        if (w < kLdsWords) reinterpret_cast<uint32_t *>(&lds)[w] = tw.v[j];
+    }
+    __syncthreads();
+}
+
+// The second operand and the per-column constants of one block of moduli.
+// A column past the last modulus repeats the last one.
+struct Column {
+    v4i t;         // t_b bytes of this lane's half (zero where the lane holds none)
+    v16i start;    // accumulator start
+    int q;
+    float inv;
+    int p;         // modulus index
+};
+
+template <bool PAIR>
+__device__ __forceinline__ Column column(const SplitLds &lds, int n, int blk, int lane) {
+    Column col;
+    const int h = lane >> 5, c32 = lane & 31;
+    int p, half;
+    bool sel;
+    if constexpr (PAIR) {
+        p = 16 * blk + (c32 & 15);
+        half = 0;
+        sel = (c32 >> 4) == h;
+    } else {
+        p = 32 * blk + c32;
+        half = h;
+        sel = true;
+    }
+    col.p = p < n ? p : n - 1;
+    const v4i t = lds.t[col.p][half];
+    col.t = sel ? t : v4i{0, 0, 0, 0};
+    const int s0 = lds.start[col.p];
+#pragma unroll
+    for (int e = 0; e < 16; e++) col.start[e] = s0;
+    col.q = lds.q[col.p];
+    col.inv = lds.inv[col.p];
+    return col;
+}
+
+// The 16 sums of a lane reduced mod q and packed: word g holds rows 8 g + 4 hh .. + 3.
+__device__ __forceinline__ void reduce_pack(const v16i &acc, int q, float inv, uint32_t (&w)[4]) {
+#pragma unroll
+    for (int g = 0; g < 4; g++)
+        w[g] = pack4(reduce_low_byte_f32(acc[4 * g], q, inv), reduce_low_byte_f32(acc[4 * g + 1], q, inv),
+                     reduce_low_byte_f32(acc[4 * g + 2], q, inv), reduce_low_byte_f32(acc[4 * g + 3], q, inv));
+}
+
+// The half-waves trade words so that every lane holds 16 consecutive rows:
+// the lower lane rows 0 .. 15 (its own 0-3 and 8-11, its partner's 4-7 and
+// 12-15), the upper lane rows 16 .. 31.
+__device__ __forceinline__ v4u rows16(const uint32_t (&w)[4]) {
+    const auto a = __builtin_amdgcn_permlane32_swap(w[0], w[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(w[1], w[3], false, false);
+    return v4u{a[0], a[1], b[0], b[1]};
+}
+
+// The lane's half (limbs 2 h, 2 h + 1) of an entry of L = 3 or 4 limbs, and
+// the whole entry by trading halves with the partner lane (for the bound check).
+template <int L>
+__device__ __forceinline__ void whole_entry(u64 p0, u64 p1, u64 (&x)[L]) {
+    uint32_t v[4] = {(uint32_t)p0, (uint32_t)(p0 >> 32), (uint32_t)p1, (uint32_t)(p1 >> 32)};
+    uint32_t lo[4], hi[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const auto s = __builtin_amdgcn_permlane32_swap(v[i], v[i], false, false);
+        lo[i] = s[0];
+        hi[i] = s[1];
+    }
+    u64 all[4] = {lo[0] | (u64)lo[1] << 32, lo[2] | (u64)lo[3] << 32, hi[0] | (u64)hi[1] << 32,
+                  hi[2] | (u64)hi[3] << 32};
+#pragma unroll
+    for (int l = 0; l < L; l++) x[l] = all[l];
+}
+
+// The words one thread loads for an entry: binary64, one word; integer
+// entries on the row path with the pair packing and on the column path, the
+// L limbs; on the row path with the single packing, the lane's limbs 2 h and
+// 2 h + 1 (the second read again from limb 2 h where it lies past the entry,
+// and dropped later).
+template <int L, bool FP, bool PART>
+struct EntryWords {
+    static constexpr int W = FP ? 1 : (PART ? 2 : L);
+};
+
+template <int L, bool FP, bool PART>
+__device__ __forceinline__ void load_entry(const int64_t *x, int64_t e, int h,
+                                           u64 (&w)[EntryWords<L, FP, PART>::W]) {
+    if constexpr (FP) {
+        w[0] = (u64)x[e];
+    } else if constexpr (!PART) {
+        load_words<L>(x + e * L, w);
+    } else {
+        w[0] = (u64)x[e * L + 2 * h];
+        w[1] = (u64)x[e * L + (2 * h + 1 < L ? 2 * h + 1 : 2 * h)];
+    }
+}
+
+// The lane's first-operand fragment of an entry on the row path; sets flag
+// when the entry lies outside the declared bound.
+template <int L, bool FP, bool PAIR>
+__device__ __forceinline__ v4i fragment(const u64 (&w)[EntryWords<L, FP, !PAIR>::W], bool ok,
+                                        const SplitOperand &op, int h, uint32_t &flag) {
+    if constexpr (PAIR) {
+        u64 x[L];
+        entry_limbs<L, FP>(w, ok, op.scale, x);
+        if (op.bits >= 0 && !within_bound<L>(x, op.bits)) flag = 1;
+        return as_v4i(operand_limb<L>(x[0], 0), L > 1 ? operand_limb<L>(x[L > 1 ? 1 : 0], 1) : 0ull);
+    } else if constexpr (FP) {
+        u64 x[L];
+        entry_limbs<L, true>(w, ok, op.scale, x);
+        if (op.bits >= 0 && !within_bound<L>(x, op.bits)) flag = 1;
+        const u64 p0 = h ? x[2] : x[0];
+        const u64 p1 = h ? (L > 3 ? x[L - 1] : 0ull) : x[1];
+        return as_v4i(operand_limb<L>(p0, 2 * h), operand_limb<L>(p1, 2 * h + 1));
+    } else {
+        const u64 p0 = ok ? w[0] : 0ull;
+        const u64 p1 = (ok && 2 * h + 1 < L) ? w[1] : 0ull;
+        if (op.bits >= 0) {
+            u64 x[L];
+            whole_entry<L>(p0, p1, x);
+            if (!within_bound<L>(x, op.bits)) flag = 1;
         }
+        return as_v4i(operand_limb<L>(p0, 2 * h), operand_limb<L>(p1, 2 * h + 1));
+    }
+}
+
+// Workgroup barrier ordering LDS only: pending global stores keep flowing.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Output staging: the results of one block of moduli for one wave unit
+// (R plane rows of one K block: PB contiguous bytes of each plane) pass
+// through LDS, so that each store writes 256 or 512 contiguous bytes of
+// one or a few planes rather than 64 bytes of each of 16 planes.  Rows of a
+// modulus sit PB + 16 bytes apart: the 16-byte pieces that lanes of one
+// modulus column write land in distinct banks.
+template <bool PAIR>
+struct OutStage {
+    static constexpr int P = PAIR ? 16 : 32;                        // moduli per block
+    static constexpr int PB = (PAIR ? kRowsPair : kRowsSingle) * kKBlock;   // bytes per modulus
+    static constexpr int PITCH = PB + 16;
+    static constexpr int BYTES = P * PITCH;
+};
+constexpr int kOutStageBytes = OutStage<true>::BYTES > OutStage<false>::BYTES ? OutStage<true>::BYTES
+                                                                               : OutStage<false>::BYTES;
+
+// The products of F first-operand fragments against NB blocks of moduli.
+// Fragment f's 16-byte result of lane (c, hh) lies off[f] + 32 s + 16 hh
+// bytes into the unit's PB bytes of its modulus (s = c / 16 in the pair
+// packing, else 0); the product of the next fragment is issued before the
+// current one is reduced.  Every lane stores: a column past the last modulus
+// repeats the last one, writing the same bytes to the same place as the
+// column that owns it.
+template <bool PAIR, int NB, int F>
+__device__ __forceinline__ void products(const v4i (&a)[F], const SplitLds &lds, int n, int lane, int8_t *unit_dst,
+                                         int64_t plane, const int (&off)[F], uint8_t *ostage) {
+    using O = OutStage<PAIR>;
+    const int cs = PAIR ? 32 * ((lane >> 4) & 1) + 16 * (lane >> 5) : 16 * (lane >> 5);
+#pragma unroll
+    for (int blk = 0; blk < NB; blk++) {
+        const Column col = column<PAIR>(lds, n, blk, lane);
+        uint8_t *mine = ostage + (PAIR ? (lane & 15) : (lane & 31)) * O::PITCH + cs;
+        v16i acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[0], col.t, col.start, 0, 0, 0);
+#pragma unroll
+        for (int f = 0; f < F; f++) {
+            const v16i cur = acc;
+            if (f + 1 < F)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[f + 1 < F ? f + 1 : f], col.t, col.start, 0, 0, 0);
+            uint32_t w[4];
+            reduce_pack(cur, col.q, col.inv, w);
+            *(v4u *)(mine + off[f]) = rows16(w);
+        }
+        // LDS operations of a wave complete in order; this keeps the
+        // compiler from moving the reads above the writes
+        asm volatile("" ::: "memory");
+        // store j: 16-byte piece ch = 64 j + lane, modulus ch / (PB / 16) of the block
+#pragma unroll
+        for (int j = 0; j < O::P * O::PB / 1024; j++) {
+            const int ch = 64 * j + lane;
+            const int pl = ch / (O::PB / 16), piece = ch % (O::PB / 16);
+            int p = O::P * blk + pl;
+            p = p < n ? p : n - 1;
+            const v4u v = *(const v4u *)(ostage + pl * O::PITCH + piece * 16);
+            *(v4u *)(unit_dst + (int64_t)p * plane + piece * 16) = v;
+        }
+        asm volatile("" ::: "memory");
+    }
+}
+
+// Row path (the operand is [rows][K]: A, or B given as B^T).  A wave unit
+// is R plane rows of one K block, 64 consecutive entries of a row per load;
+// waves run through the units with the grid's stride and load the next unit
+// while the current one is in the matrix cores.
+//   fragment f: pair, row r0 + f, entry k = 64 kb + lane;
+//               single, row r0 + f / 2, entry k = 64 kb + 32 (f % 2) + lane % 32.
+template <int L, bool FP, int NB>
+__device__ void split_rows(const SplitOperand &op, const SplitConsts &c, int sidx, SplitLds &lds,
+                           uint8_t *ostage, int64_t units, uint32_t &flag) {
+    constexpr bool PAIR = L <= 2;
+    constexpr int R = PAIR ? kRowsPair : kRowsSingle;
+    constexpr int F = PAIR ? R : 2 * R;
+    constexpr int W = EntryWords<L, FP, !PAIR>::W;
+    const int lane = threadIdx.x & 63, h = lane >> 5;
+    const int64_t groups = op.r_pad / R;
+    const int64_t stride = (int64_t)gridDim.x * kSplitWaves;
+    int64_t unit = (int64_t)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
+
+    // all loads are unconditional: an entry outside the operand (or of a
+    // unit past the end) reads entry 0 and is then taken as zero
+    u64 xs[F][W];
+    bool ok[F];
+    auto load_unit = [&](int64_t u, bool valid) {
+        const int64_t kb = u / groups, r0 = (u - kb * groups) * R;
+#pragma unroll
+        for (int f = 0; f < F; f++) {
+            const int64_t r = r0 + (PAIR ? f : f >> 1);
+            const int64_t k = kb * kKBlock + (PAIR ? lane : 32 * (f & 1) + (lane & 31));
+            ok[f] = valid && r < op.rows && k < op.k;
+            load_entry<L, FP, !PAIR>(op.x, ok[f] ? r * op.k + k : 0, h, xs[f]);
+        }
+    };
+    const TableWords tw = table_load(c, sidx);
+    load_unit(unit < units ? unit : 0, unit < units);
+    table_commit(tw, lds);
+
+    const int64_t plane = op.r_pad * op.k_pad;
+    int off[F];
+#pragma unroll
+    for (int f = 0; f < F; f++) off[f] = PAIR ? f * kKBlock : (f >> 1) * kKBlock + 32 * (f & 1);
+    auto body = [&](int64_t u) {
+        v4i a[F];
+#pragma unroll
+        for (int f = 0; f < F; f++) a[f] = fragment<L, FP, PAIR>(xs[f], ok[f], op, h, flag);
+        const int64_t kb = u / groups, r0 = (u - kb * groups) * R;
+        const int64_t next = u + stride;
+        load_unit(next < units ? next : u, next < units);
+        int8_t *dst = op.planes + kb * (op.r_pad * kKBlock) + r0 * kKBlock;
+        products<PAIR, NB, F>(a, lds, c.n, lane, dst, plane, off, ostage);
+    };
+    // The first unit runs outside the loop, so that every wait for a unit's
+    // loads follows the previous unit's stores alike and counts them exactly.
+    if (unit < units) {
+        body(unit);
+        for (unit += stride; unit < units; unit += stride) body(unit);
+    }
+}
+
+// Column path (the operand is [K][rows]: B).  A workgroup tile is NT plane
+// rows of one K block; its 64 NT entries are loaded NT consecutive plane
+// rows at a time, turned into operand bytes and staged in LDS by plane row,
+// and each wave then reads the fragments of its NT / 4 rows as on the row
+// path.  Workgroups run through the tiles with the grid's stride and load
+// the next tile while the current one is in the matrix cores.
+template <bool PAIR>
+struct ColsTile {
+    static constexpr int NT = PAIR ? 32 : 16;          // plane rows per tile
+    static constexpr int ES = PAIR ? 16 : 32;          // staged bytes per entry
+    static constexpr int PITCH = 64 * ES + 16;         // LDS bytes per plane row
+    static constexpr int EPT = 64 * NT / kSplitThreads;   // entries per thread
+    static constexpr int BYTES = NT * PITCH;
+};
+constexpr int kColsLdsBytes = ColsTile<true>::BYTES > ColsTile<false>::BYTES ? ColsTile<true>::BYTES
+                                                                               : ColsTile<false>::BYTES;
+
+template <int L, bool FP, int NB>
+__device__ void split_cols(const SplitOperand &op, const SplitConsts &c, int sidx, SplitLds &lds,
+                           uint8_t *stage, uint8_t *ostage, int64_t tiles, uint32_t &flag) {
+    constexpr bool PAIR = L <= 2;
+    using T = ColsTile<PAIR>;
+    constexpr int F = 8;                               // fragments per wave and tile
+    constexpr int W = EntryWords<L, FP, false>::W;
+    const int lane = threadIdx.x & 63, h = lane >> 5, wave = threadIdx.x >> 6;
+    const int64_t nts = (op.r_pad + T::NT - 1) / T::NT;
+
+    // thread entry j of a tile: i = thread + 256 j, plane row n0 + i % NT, k = 64 kb + i / NT
+    u64 xs[T::EPT][W];
+    bool ok[T::EPT];
+    auto load_tile = [&](int64_t t, bool valid) {
+        const int64_t kb = t / nts, n0 = (t - kb * nts) * T::NT;
+#pragma unroll
+        for (int j = 0; j < T::EPT; j++) {
+            const int i = (int)threadIdx.x + kSplitThreads * j;
+            const int64_t n = n0 + i % T::NT, k = kb * kKBlock + i / T::NT;
+            ok[j] = valid && n < op.rows && k < op.k;
+            load_entry<L, FP, false>(op.x, ok[j] ? k * op.rows + n : 0, h, xs[j]);
+        }
+    };
+    int64_t tile = blockIdx.x;
+    const TableWords tw = table_load(c, sidx);
+    load_tile(tile < tiles ? tile : 0, tile < tiles);
+    table_commit(tw, lds);
+
+    const int64_t plane = op.r_pad * op.k_pad;
+    auto body = [&](int64_t t, bool first) {
+        // operand bytes of the loaded entries into LDS, [plane row][k]
+        if (!first) lds_barrier();      // every wave has read the previous tile
+#pragma unroll
+        for (int j = 0; j < T::EPT; j++) {
+            u64 x[L];
+            entry_limbs<L, FP>(xs[j], ok[j], op.scale, x);
+            if (op.bits >= 0 && !within_bound<L>(x, op.bits)) flag = 1;
+            const int i = (int)threadIdx.x + kSplitThreads * j;
+            uint8_t *p = stage + (i % T::NT) * T::PITCH + (i / T::NT) * T::ES;
+            *(v4i *)p = as_v4i(operand_limb<L>(x[0], 0), L > 1 ? operand_limb<L>(x[L > 1 ? 1 : 0], 1) : 0ull);
+            if constexpr (!PAIR)
+                *(v4i *)(p + 16) = as_v4i(operand_limb<L>(x[2 < L ? 2 : 0], 2),
+                                          L > 3 ? operand_limb<L>(x[L - 1], 3) : 0ull);
+        }
+        lds_barrier();
+
+        // Wave w takes plane rows n0 + RW w' .. + RW - 1 (RW = NT / 4): fragment
+        // f is, pair, row n0 + RW w' + f, entry k = lane; single, row
+        // n0 + RW w' + f / 2, bytes 16 h of entry 32 (f % 2) + lane % 32.  A
+        // tile reaches past the plane only by whole waves (plane rows come in
+        // 16s): such a wave repeats one that lies inside (w' = w - a for the
+        // a waves inside), writing the same bytes to the same place.
+        constexpr int RW = T::NT / kSplitWaves;
+        const int64_t kb = t / nts, n0 = (t - kb * nts) * T::NT;
+        const int inside = (int)((op.r_pad - n0) / RW);
+        const int wv = wave < inside ? wave : wave - inside;
+        v4i a[F];
+        int off[F];
+#pragma unroll
+        for (int f = 0; f < F; f++) {
+            const int rl = RW * wv + (PAIR ? f : f >> 1);
+            const int eo = PAIR ? lane * 16 : (32 * (f & 1) + (lane & 31)) * 32 + 16 * h;
+            a[f] = *(const v4i *)(stage + rl * T::PITCH + eo);
+            off[f] = (PAIR ? f : f >> 1) * kKBlock + (PAIR ? 0 : 32 * (f & 1));
+        }
+        const int64_t next = t + gridDim.x;
+        load_tile(next < tiles ? next : t, next < tiles);
+        int8_t *dst = op.planes + kb * (op.r_pad * kKBlock) + (n0 + RW * wv) * kKBlock;
+        products<PAIR, NB, F>(a, lds, c.n, lane, dst, plane, off, ostage);
+    };
+    // the first tile runs outside the loop (exact waits, as on the row path)
+    if (tile < tiles) {
+        body(tile, true);
+        for (tile += gridDim.x; tile < tiles; tile += gridDim.x) body(tile, false);
+    }
+}
+
+template <int L, bool FP, bool COLS, int NB>
+__global__ __launch_bounds__(kSplitThreads, 2) void split_kernel(SplitOperand op, SplitConsts c, SplitStatus st) {
+    __shared__ SplitLds lds;
+    __shared__ __align__(16) uint8_t ostage[kSplitWaves][kOutStageBytes];
+    uint8_t *mine = ostage[threadIdx.x >> 6];
+    uint32_t flag = 0;
+    if constexpr (COLS) {
+        __shared__ __align__(16) uint8_t stage[kColsLdsBytes];
+        split_cols<L, FP, NB>(op, c, st.b_start, lds, stage, mine, st.work, flag);
+    } else {
+        split_rows<L, FP, NB>(op, c, st.b_start, lds, mine, st.work, flag);
     }
     // one status word per block, written unconditionally (no clearing pass);
-    // block 0 also writes the header: the block count and its check word
+    // the first block of the first launch also writes the header: the block
+    // count of the whole split and its check word
     const bool any = __syncthreads_or(flag != 0);
     if (threadIdx.x == 0) {
-        args.status[kStatusHeader + blockIdx.x] =
-            any ? args.flag_bit[which] : 0u;
-        if (blockIdx.x == 0) {
-            args.status[0] = gridDim.x;
-            args.status[1] = gridDim.x ^ kStatusCheck;
+        st.status[kStatusHeader + st.first + blockIdx.x] = any ? st.flag_bit : 0u;
+        if (st.first == 0 && blockIdx.x == 0) {
+            st.status[0] = (uint32_t)st.total;
+            st.status[1] = (uint32_t)st.total ^ kStatusCheck;
         }
     }
 }
 
-static int split_prime_groups(int64_t task_blocks, int n) {
-    if (task_blocks <= 0 || task_blocks >= kSplitTargetBlocks / 2) return 1;
-    const int64_t g = (kSplitTargetBlocks + task_blocks - 1) / task_blocks;
-    return (int)(g < n ? g : n);
+// Work of one operand: row path, wave units; column path, workgroup tiles.
+static int64_t split_work(const SplitOperand &op, bool pair, bool cols) {
+    const int64_t kblocks = op.k_pad / kKBlock;
+    if (cols) {
+        const int64_t nt = pair ? ColsTile<true>::NT : ColsTile<false>::NT;
+        return (op.r_pad + nt - 1) / nt * kblocks;
+    }
+    return op.r_pad / (pair ? kRowsPair : kRowsSingle) * kblocks;
 }
 
-int64_t split_status_slots(const SplitOperand *a, const SplitOperand *b, int n) {
-    int64_t ta = a ? a->r_pad * (a->k_pad / kRun) : 0;
-    int64_t tb = b->r_pad * (b->k_pad / kRun);
-    const int64_t blocks = (ta + kSplitThreads - 1) / kSplitThreads + (tb + kSplitThreads - 1) / kSplitThreads;
-    return kStatusHeader + blocks * split_prime_groups(blocks, n);
+// blocks the work asks for (before the cap at what the device holds at once)
+static int64_t split_blocks(const SplitOperand &op, bool pair, bool cols) {
+    const int64_t w = split_work(op, pair, cols);
+    return cols ? w : (w + kSplitWaves - 1) / kSplitWaves;
+}
+
+// blocks of one operand for any limb count and either path
+static int64_t split_blocks_max(const SplitOperand &op) {
+    int64_t m = 0;
+    for (int pair = 0; pair < 2; pair++)
+        for (int cols = 0; cols < 2; cols++) {
+            const int64_t b = split_blocks(op, pair != 0, cols != 0);
+            m = b > m ? b : m;
+        }
+    return m;
+}
+
+int64_t split_status_slots(const SplitOperand *a, const SplitOperand *b, int) {
+    return kStatusHeader + (a ? split_blocks_max(*a) : 0) + split_blocks_max(*b);
+}
+
+// Resident blocks of a kernel on the current device (compute units times
+// blocks per unit), found once per kernel.
+template <typename Kern>
+static int64_t resident_blocks(Kern kernel) {
+    static const int64_t cached = [&] {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, kSplitThreads, 0) != hipSuccess || per < 1)
+            per = 1;
+        return (int64_t)cus * per;
+    }();
+    return cached;
+}
+
+template <int L, bool FP, bool COLS, int NB>
+static int64_t launch_one(const SplitOperand &op, const SplitConsts &c, SplitStatus st, int64_t blocks,
+                          bool dry, hipStream_t s) {
+    auto kernel = split_kernel<L, FP, COLS, NB>;
+    const int64_t cap = resident_blocks(kernel);
+    const int64_t grid = blocks < cap ? blocks : cap;
+    if (!dry) hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kSplitThreads), 0, s, op, c, st);
+    return grid;
+}
+
+template <int L, bool FP, bool COLS>
+static int64_t launch_nb(int nb, const SplitOperand &op, const SplitConsts &c, const SplitStatus &st,
+                         int64_t blocks, bool dry, hipStream_t s) {
+    switch (nb) {
+        case 1: return launch_one<L, FP, COLS, 1>(op, c, st, blocks, dry, s);
+        case 2: return launch_one<L, FP, COLS, 2>(op, c, st, blocks, dry, s);
+        case 3: if constexpr (L <= 2) return launch_one<L, FP, COLS, 3>(op, c, st, blocks, dry, s); else return -1;
+        case 4: if constexpr (L <= 2) return launch_one<L, FP, COLS, 4>(op, c, st, blocks, dry, s); else return -1;
+        default: return -1;
+    }
+}
+
+template <bool FP, bool COLS>
+static int64_t launch_kind(int nb, const SplitOperand &op, const SplitConsts &c, const SplitStatus &st,
+                           int64_t blocks, bool dry, hipStream_t s) {
+    switch (op.limbs) {
+        case 1: return launch_nb<1, FP, COLS>(nb, op, c, st, blocks, dry, s);
+        case 2: return launch_nb<2, FP, COLS>(nb, op, c, st, blocks, dry, s);
+        case 3: return launch_nb<3, FP, COLS>(nb, op, c, st, blocks, dry, s);
+        default: return launch_nb<4, FP, COLS>(nb, op, c, st, blocks, dry, s);
+    }
+}
+
+// The grid of one operand's launch (dry) or the launch itself.
+static int64_t launch_operand(const SplitOperand &op, const SplitConsts &c, const SplitStatus &st, bool dry,
+                              hipStream_t s) {
+    const bool pair = op.limbs <= 2, cols = op.transposed != 0;
+    const int per = pair ? 16 : 32;
+    const int nb = (c.n + per - 1) / per;
+    const int64_t blocks = split_blocks(op, pair, cols);
+    if (op.fp64)
+        return cols ? launch_kind<true, true>(nb, op, c, st, blocks, dry, s)
+                    : launch_kind<true, false>(nb, op, c, st, blocks, dry, s);
+    return cols ? launch_kind<false, true>(nb, op, c, st, blocks, dry, s)
+                : launch_kind<false, false>(nb, op, c, st, blocks, dry, s);
 }
 
 int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts &c,
                  uint32_t *status, int64_t status_slots, hipStream_t s) {
-    SplitArgs args{};
-    // operand 0 is A when present, else B alone
-    const SplitOperand *ops[2] = {a ? a : b, a ? b : nullptr};
-    int64_t blocks[2] = {0, 0};
+    if (c.n < 1 || c.n > kMaxPrimes) return RNS_E_ARG;
+    const SplitOperand *ops[2] = {a, b};
+    int64_t grid[2] = {0, 0};
+    SplitStatus st[2] = {};
     for (int i = 0; i < 2; i++) {
         if (!ops[i]) continue;
-        args.op[i] = *ops[i];
-        args.tasks[i] = ops[i]->r_pad * (ops[i]->k_pad / kRun);
-        blocks[i] = (args.tasks[i] + kSplitThreads - 1) / kSplitThreads;
+        const SplitOperand &op = *ops[i];
+        // the paths assume whole 16-row groups and whole K blocks
+        if (op.limbs < 1 || op.limbs > RNS_MAX_IN_LIMBS || op.r_pad % 16 || op.k_pad % kKBlock ||
+            op.rows > op.r_pad || op.k > op.k_pad || op.rows < 0 || op.k < 0)
+            return RNS_E_ARG;
+        st[i].status = status;
+        st[i].work = split_work(op, op.limbs <= 2, op.transposed != 0);
+        st[i].flag_bit = i == 0 ? RNS_FLAG_A_RANGE : RNS_FLAG_B_RANGE;
+        st[i].b_start = i;
+        if (st[i].work > 0) grid[i] = launch_operand(op, c, st[i], true, s);
+        if (grid[i] < 0) return RNS_E_ARG;
     }
-    const int64_t task_blocks = blocks[0] + blocks[1];
-    if (task_blocks <= 0) return RNS_OK;
-    if (c.n < 1 || c.n > kMaxPrimes) return RNS_E_ARG;
-    const int groups = split_prime_groups(task_blocks, c.n);
-    const int64_t grid = task_blocks * groups;
-    if (grid + kStatusHeader > status_slots || grid > 0x7fffffff) return RNS_E_ARG;
-    args.blocks0 = (int32_t)blocks[0];
-    args.task_blocks = (int32_t)task_blocks;
-    args.prime_groups = groups;
-    args.flag_bit[0] = a ? RNS_FLAG_A_RANGE : RNS_FLAG_B_RANGE;
-    args.flag_bit[1] = RNS_FLAG_B_RANGE;
-    args.status = status;
-    SplitConsts cc = c;
-    if (!a) {
-        // operand 0 is B: its offset constant lives in h_a's place
-        for (int p = 0; p < kMaxPrimes; p++) cc.h_a[p] = c.h_b[p];
+    const int64_t total = grid[0] + grid[1];
+    if (total <= 0) return RNS_OK;
+    if (total + kStatusHeader > status_slots || total > 0x7fffffff) return RNS_E_ARG;
+    int64_t first = 0;
+    for (int i = 0; i < 2; i++) {
+        if (grid[i] == 0) continue;
+        st[i].first = (int32_t)first;
+        st[i].total = (int32_t)total;
+        launch_operand(*ops[i], c, st[i], false, s);
+        if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
+        first += grid[i];
     }
-    const bool fp = ops[0]->fp64 != 0;
-    if (ops[1] && (ops[1]->fp64 != 0) != fp) return RNS_E_ARG;
-    if (fp)
-        hipLaunchKernelGGL(split_kernel<true>, dim3((unsigned)grid), dim3(kSplitThreads), 0, s, args, cc);
-    else
-        hipLaunchKernelGGL(split_kernel<false>, dim3((unsigned)grid), dim3(kSplitThreads), 0, s, args, cc);
-    return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
+    return RNS_OK;
 }
 
 // ============================================================================
