@@ -65,7 +65,7 @@ class _Layout(ctypes.Structure):
                 ("k_block", ctypes.c_int64), ("y_pitch", ctypes.c_int64),
                 ("a_off", ctypes.c_int64), ("b_off", ctypes.c_int64), ("y_off", ctypes.c_int64),
                 ("status_off", ctypes.c_int64), ("total_bytes", ctypes.c_int64),
-                ("tile_config", ctypes.c_int32)]
+                ("tile_config", ctypes.c_int32), ("a_plane", ctypes.c_int64), ("b_plane", ctypes.c_int64)]
 
 
 class _FpStats(ctypes.Structure):
@@ -428,14 +428,14 @@ def workspace_planes(p: Plan, workspace: torch.Tensor, M: int, N: int, K: int,
     out = {"layout": L}
     kb = L["k_block"]
 
-    def blocked(off, rows):
+    def blocked(off, rows, pitch):
         kpad = L["k_pad"]
-        v = ws8[off:off + n * rows * kpad].view(n, kpad // kb, rows, kb)
+        v = ws8.as_strided((n, kpad // kb, rows, kb), (pitch, rows * kb, kb, 1), off)
         return v.permute(0, 2, 1, 3).reshape(n, rows, kpad)
 
     if L["a_off"] >= 0:
-        out["A"] = blocked(L["a_off"], L["m_pad"])
-    out["B"] = blocked(L["b_off"], L["n_pad"])
+        out["A"] = blocked(L["a_off"], L["m_pad"], L["a_plane"])
+    out["B"] = blocked(L["b_off"], L["n_pad"], L["b_plane"])
     out["Y"] = ws8.as_strided((n, L["m_pad"], L["n_pad"]),
                               (L["m_pad"] * L["y_pitch"], L["y_pitch"], 1), L["y_off"])
     return out

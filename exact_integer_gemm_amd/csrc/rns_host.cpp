@@ -381,6 +381,13 @@ int64_t plane_pitch(int64_t bytes) {
     return p;
 }
 
+// Pitch of the operand residue planes: their bytes, plus 4 KiB when those
+// are a multiple of 64 KiB, so that the same offset of consecutive planes
+// does not fall into the same cache sets and memory channels.
+int64_t operand_plane_pitch(int64_t bytes) {
+    return bytes % 65536 == 0 ? bytes + 4096 : bytes;
+}
+
 struct Layout {
     rns_layout_t pub;
     int64_t status_slots;
@@ -411,8 +418,10 @@ Layout make_layout(const rns_plan_t &pl, int64_t M, int64_t N, int64_t K, bool b
     int64_t off = 0;
     auto take = [&](int64_t bytes) { int64_t o = off; off = round_up(off + bytes, 256); return o; };
     L.pub.status_off = take(L.status_slots * 4);
-    L.pub.a_off = L.a_in_place ? -1 : take((int64_t)n * L.pub.m_pad * L.pub.k_pad);
-    L.pub.b_off = take((int64_t)n * L.pub.n_pad * L.pub.k_pad);
+    L.pub.a_plane = L.a_in_place ? L.pub.m_pad * L.pub.k_pad : operand_plane_pitch(L.pub.m_pad * L.pub.k_pad);
+    L.pub.b_plane = operand_plane_pitch(L.pub.n_pad * L.pub.k_pad);
+    L.pub.a_off = L.a_in_place ? -1 : take((int64_t)n * L.pub.a_plane);
+    L.pub.b_off = take((int64_t)n * L.pub.b_plane);
     L.pub.y_off = take((int64_t)n * L.pub.m_pad * L.pub.y_pitch);
     L.partial_off = cfg == kTileBig ? take(kTailUnitsMax * kTailUnitBytes) : -1;
     L.pub.total_bytes = off;
@@ -458,13 +467,13 @@ int stage_split(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
     const SplitConsts &sc = split_tables(*plan, batched ? 1 : a_limbs, b_limbs);
     SplitOperand sa{}, sb{};
     if (!batched) {
-        sa.x = A; sa.planes = base + L.pub.a_off; sa.rows = M; sa.k = K;
+        sa.x = A; sa.planes = base + L.pub.a_off; sa.plane = L.pub.a_plane; sa.rows = M; sa.k = K;
         sa.r_pad = L.pub.m_pad; sa.k_pad = L.pub.k_pad; sa.limbs = a_limbs;
         sa.bits = (plan->a_bits >= 0 && plan->a_bits < 64 * a_limbs - 1) ? plan->a_bits : -1;
         sa.transposed = 0;
         if (fp) { sa.fp64 = 1; sa.scale = fp->fa; }
     }
-    sb.x = B; sb.planes = base + L.pub.b_off; sb.rows = N; sb.k = K;
+    sb.x = B; sb.planes = base + L.pub.b_off; sb.plane = L.pub.b_plane; sb.rows = N; sb.k = K;
     sb.r_pad = L.pub.n_pad; sb.k_pad = L.pub.k_pad; sb.limbs = b_limbs;
     sb.bits = (plan->b_bits >= 0 && plan->b_bits < 64 * b_limbs - 1) ? plan->b_bits : -1;
     sb.transposed = 1;
@@ -495,14 +504,14 @@ int stage_products(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K, cons
             a_kstep = kKBlock;
         } else {
             rc = launch_repack_residues(A_res, n, M, K, base + L.pub.a_off, L.pub.m_pad,
-                                        L.pub.k_pad, stream);
+                                        L.pub.k_pad, L.pub.a_plane, stream);
             if (rc) return rc;
         }
     }
     const EpiConsts &ec = epi_tables(*plan);
     return launch_gemm(L.pub.tile_config, n, apl, base + L.pub.b_off, base + L.pub.y_off,
-                       L.pub.m_pad, L.pub.n_pad, L.pub.k_pad, L.pub.m_pad * L.pub.k_pad,
-                       L.pub.n_pad * L.pub.k_pad, L.pub.m_pad * L.pub.y_pitch,
+                       L.pub.m_pad, L.pub.n_pad, L.pub.k_pad, L.pub.a_plane,
+                       L.pub.b_plane, L.pub.m_pad * L.pub.y_pitch,
                        a_row, a_kstep, kKBlock, L.pub.n_pad * kKBlock, L.pub.y_pitch,
                        L.partial_off >= 0 ? base + L.partial_off : nullptr, ec, stream);
 }

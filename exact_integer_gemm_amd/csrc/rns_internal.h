@@ -138,7 +138,8 @@ __host__ __device__ constexpr TileShape tile_shape(int cfg) {
 // ---- launchers (rns_split.hip, rns_gemm.hip, rns_garner.hip) ------------------
 struct SplitOperand {
     const int64_t *x;      // [rows][cols][limbs] for A, [K][N][limbs] for B
-    int8_t *planes;        // [n][r_pad][k_pad]
+    int8_t *planes;        // n planes of [k_pad / 64][r_pad][64], `plane` bytes apart
+    int64_t plane;
     int64_t rows;          // A: M        B: N  (plane rows)
     int64_t k;             // K
     int64_t r_pad, k_pad;  // padded plane rows (multiple of 16); K padded to whole K blocks
@@ -168,7 +169,7 @@ int gemm_fp64_scaled(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
                      const Fp64Scales &scales, int64_t *C, int32_t c_limbs,
                      void *ws, size_t ws_bytes, hipStream_t stream);
 int launch_repack_residues(const int8_t *src, int64_t n, int64_t M, int64_t K,
-                           int8_t *dst, int64_t m_pad, int64_t k_pad, hipStream_t s);
+                           int8_t *dst, int64_t m_pad, int64_t k_pad, int64_t plane, hipStream_t s);
 int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
                 int64_t m_pad, int64_t n_pad, int64_t k_pad,
                 int64_t a_plane, int64_t b_plane, int64_t y_plane,

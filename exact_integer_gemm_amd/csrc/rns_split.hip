@@ -367,7 +367,7 @@ __device__ void split_rows(const SplitOperand &op, const SplitConsts &c, int sid
     load_unit(unit < units ? unit : 0, unit < units);
     table_commit(tw, lds);
 
-    const int64_t plane = op.r_pad * op.k_pad;
+    const int64_t plane = op.plane;
     int off[F];
 #pragma unroll
     for (int f = 0; f < F; f++) off[f] = PAIR ? f * kKBlock : (f >> 1) * kKBlock + 32 * (f & 1);
@@ -434,7 +434,7 @@ __device__ void split_cols(const SplitOperand &op, const SplitConsts &c, int sid
     load_tile(tile < tiles ? tile : 0, tile < tiles);
     table_commit(tw, lds);
 
-    const int64_t plane = op.r_pad * op.k_pad;
+    const int64_t plane = op.plane;
     auto body = [&](int64_t t, bool first) {
         // operand bytes of the loaded entries into LDS, [plane row][k]
         if (!first) lds_barrier();      // every wave has read the previous tile
@@ -613,7 +613,8 @@ int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts
         const SplitOperand &op = *ops[i];
         // the paths assume whole 16-row groups and whole K blocks
         if (op.limbs < 1 || op.limbs > RNS_MAX_IN_LIMBS || op.r_pad % 16 || op.k_pad % kKBlock ||
-            op.rows > op.r_pad || op.k > op.k_pad || op.rows < 0 || op.k < 0)
+            op.rows > op.r_pad || op.k > op.k_pad || op.rows < 0 || op.k < 0 ||
+            op.plane < op.r_pad * op.k_pad)
             return RNS_E_ARG;
         st[i].status = status;
         st[i].work = split_work(op, op.limbs <= 2, op.transposed != 0);
@@ -641,26 +642,26 @@ int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts
 // repack of caller-given residue planes into the padded tile layout
 // ============================================================================
 __global__ void repack_kernel(const int8_t *src, int64_t n, int64_t M, int64_t K,
-                              int8_t *dst, int64_t m_pad, int64_t k_pad) {
+                              int8_t *dst, int64_t m_pad, int64_t k_pad, int64_t plane) {
     const int64_t total = n * m_pad * k_pad;
     for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
          i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t p = i / (m_pad * k_pad);
         const int64_t rem = i - p * m_pad * k_pad;
         const int64_t m = rem / k_pad, k = rem - m * k_pad;
-        dst[p * m_pad * k_pad + (k / kKBlock) * (m_pad * kKBlock) + m * kKBlock + k % kKBlock] =
+        dst[p * plane + (k / kKBlock) * (m_pad * kKBlock) + m * kKBlock + k % kKBlock] =
             (m < M && k < K) ? src[(p * M + m) * K + k] : (int8_t)0;
     }
 }
 
 int launch_repack_residues(const int8_t *src, int64_t n, int64_t M, int64_t K,
-                           int8_t *dst, int64_t m_pad, int64_t k_pad, hipStream_t s) {
+                           int8_t *dst, int64_t m_pad, int64_t k_pad, int64_t plane, hipStream_t s) {
     const int64_t total = n * m_pad * k_pad;
     if (total == 0) return RNS_OK;
     int64_t grid = (total + 255) / 256;
     if (grid > 65536) grid = 65536;
     hipLaunchKernelGGL(repack_kernel, dim3((unsigned)grid), dim3(256), 0, s, src, n, M, K, dst, m_pad,
-                       k_pad);
+                       k_pad, plane);
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 

@@ -273,8 +273,11 @@ int rns_status(const void *ws, hipStream_t stream, uint32_t *flags);
  * plan->primes[j], stored as int8.  Operand planes are K-blocked in blocks
  * of k_block (64) entries, so that a 64-wide K step of a row tile is one
  * contiguous run of whole cache lines:
- *   A planes at a_off: [n][k_pad / k_block][m_pad][k_block]  (row m, column k of A)
- *   B planes at b_off: [n][k_pad / k_block][n_pad][k_block]  (column n, row k of B)
+ *   A planes at a_off, a_plane bytes apart:  [k_pad / k_block][m_pad][k_block]  (row m, column k of A)
+ *   B planes at b_off, b_plane bytes apart:  [k_pad / k_block][n_pad][k_block]  (column n, row k of B)
+ * A plane pitch is its m_pad * k_pad (n_pad * k_pad) bytes, plus 4 KiB when
+ * that is a multiple of 64 KiB: with equal power-of-two strides the same
+ * offset of every plane would share cache sets and memory channels.
  * Product planes are row-major with a row pitch of y_pitch bytes (an odd
  * multiple of 128, which spreads a tile's rows over the L2 channels):
  *   Y planes at y_off: [n][m_pad][y_pitch], entries 0..n_pad-1 of each row
@@ -290,6 +293,7 @@ typedef struct rns_layout {
     int64_t status_off;
     int64_t total_bytes;
     int32_t tile_config;     /* which GEMM tiling was chosen */
+    int64_t a_plane, b_plane;   /* bytes from one residue plane to the next */
 } rns_layout_t;
 
 int rns_workspace_layout(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
