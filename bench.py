@@ -78,19 +78,81 @@ def measured_traffic(workload):
         return None
 
 
-def gemm_kernel_name(n, M, N):
-    """The product kernels the library launches for this shape (its tile choice)."""
+def gemm_kernel_name(tile_config, n, M, N):
+    """The product kernels of the tiling the library chose (the layout's tile_config)."""
     import torch
-    if N <= 32:
+    if tile_config == 2:
         return "gemm_kernel<128,32,64,4,1> (skinny tiles)"
-    tiles = n * ((M + 255) // 256) * ((N + 255) // 256)
-    if M < 256 or N < 256 or tiles < 256:
+    if tile_config == 1:
         return "gemm_kernel<64,64,64,2,2> (small tiles)"
+    tiles = n * ((M + 255) // 256) * ((N + 255) // 256)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if tiles > cus and cus % 8 == 0:
         return ("gemm_ps_kernel<4> (persistent, one workgroup per CU) + gemm_tail_kernel<8> "
                 "when tiles past the last whole round are split over K")
     return "gemm_pp_kernel<4> (one 256x256 tile per workgroup)"
+
+
+def spread(samples_ms):
+    """Median, min and max of per-step stage times, in microseconds."""
+    a = np.asarray(samples_ms, dtype=np.float64) * 1e3
+    return {"median": float(np.median(a)), "min": float(a.min()), "max": float(a.max())}
+
+
+def output_digest(workload, C):
+    """SHA-256 of the output bytes next to the oracle's digest of the same workload."""
+    import hashlib
+    got = hashlib.sha256(np.ascontiguousarray(C.cpu().numpy()).tobytes()).hexdigest()
+    ref = None
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tests", "golden", "workload_digests.json")
+    if os.path.exists(path):
+        entry = json.load(open(path)).get(workload)
+        if entry and entry.get("out_limbs") == C.shape[-1]:
+            ref = entry.get("C_sha256")
+    return {"output_sha256": got, "oracle_sha256": ref,
+            "matches_oracle": (got == ref) if ref is not None else None}
+
+
+def gfx_clock_during(run, seconds=1.5):
+    """Median shader clock (MHz, mean over the XCDs) and socket power (W) that
+    amd-smi reports while run() is called back to back for about `seconds`;
+    (None, None) where amd-smi is not available."""
+    import subprocess
+    import threading
+    import torch
+    samples = []
+    stop = threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-c", "-p", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                g = json.loads(r.stdout)["gpu_data"][0]
+                clk = [v["clk"]["value"] for k, v in g["clock"].items() if k.startswith("gfx_")]
+                pw = g["power"]["socket_power"]["value"]
+                samples.append((float(np.mean(clk)), float(pw)))
+            except Exception:
+                return
+            stop.wait(0.2)
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler)
+    th.start()
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(8):
+            run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    # drop the first sample (taken while the loop ramped up)
+    samples = samples[1:] if len(samples) > 2 else samples
+    if not samples:
+        return None, None
+    return float(np.median([c for c, _ in samples])), float(np.median([p for _, p in samples]))
 
 
 def copy_probe():
@@ -188,7 +250,7 @@ def enclosure_fp64(args):
                    "parallelism": "single-gpu"},
         "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
                      "frac": gemm_tops / PEAK_INT8_TOPS, "traffic": None,
-                     "kernel": gemm_kernel_name(ep.n_primes, M, N)},
+                     "kernel": gemm_kernel_name(rg.layout(plan, M, N, K)["tile_config"], ep.n_primes, M, N)},
         "stages": out_st,
         "width_ulps_max": int(width.max()), "width_ulps_zero_frac": float((width == 0).float().mean()),
     }
@@ -230,7 +292,8 @@ def solve_bench(args):
     def ev():
         return torch.cuda.Event(enable_timing=True)
 
-    times = {"inverse_ms": [], "lift_ms": [], "prep_during_lift_s": [], "reconstruct_s": [], "total_s": []}
+    times = {"inverse_ms": [], "lift_ms": [], "prep_during_lift_s": [], "reconstruct_s": [],
+             "lowest_terms_s": [], "stages_total_s": []}
     native = XS.host_bigint_available()
     info = None
     for it in range(max(args.steps, 1) + 1):
@@ -259,6 +322,8 @@ def solve_bench(args):
         e3.synchronize()
         t_host = time.perf_counter()
         nums, den = XS.reconstruct_device(digits.reshape(m, n * c, -1), P, m, Nb, Db, prep)
+        t_rec = time.perf_counter()
+        XS.to_fractions(nums, den)
         t_end = time.perf_counter()
         if it == 0:
             info = {"primes": len(moduli), "steps": m, "log2_P": math.log2(P),
@@ -273,13 +338,24 @@ def solve_bench(args):
         times["inverse_ms"].append(e0.elapsed_time(e1))
         times["lift_ms"].append(e2.elapsed_time(e3))
         times["prep_during_lift_s"].append(t_tab)
-        times["reconstruct_s"].append(t_end - t_host)
-        times["total_s"].append(t_end - t_start)
+        times["reconstruct_s"].append(t_rec - t_host)
+        times["lowest_terms_s"].append(t_end - t_rec)
+        times["stages_total_s"].append(t_end - t_start)
     med = {k: float(np.median(v)) for k, v in times.items()}
+    # the step itself: rg.solve(A, b) end to end, lowest-terms Fractions returned
+    totals = []
+    for _ in range(max(args.steps, 1)):
+        t = time.perf_counter()
+        x = rg.solve(A, b)
+        totals.append(time.perf_counter() - t)
+    med["total_s"] = float(np.median(totals))
+    med["total_s_min"], med["total_s_max"] = float(min(totals)), float(max(totals))
+    info["solution_is_fractions"] = bool(x is not None and isinstance(x[0][0], XS.Fraction))
     # the lift's products: 2 n n c per prime per step
     lift_ops = 2.0 * n * n * c * info["primes"] * info["steps"]
     out = {
-        "metric": "exact rational solve wall time (Dixon lift on the residue engine)",
+        "metric": "exact rational solve wall time (rg.solve end to end: Dixon lift on the residue engine, "
+                  "lowest-terms Fractions returned)",
         "value": med["total_s"], "unit": "s", "n_gpus": 1, "steps": args.steps, "warmup": 1,
         "ms_per_step": med["total_s"] * 1e3, "higher_is_better": False, "scaling": "weak",
         "vs_baseline": None, "dtype": "int8", "data": "synthetic",
@@ -410,6 +486,10 @@ def main():
     lc = plan.out_limbs_min
     C = torch.empty((M, N, lc), dtype=torch.int64, device=dev)
     ws = rg.new_workspace(plan, M, N, K, batched, dev)
+    tile_config = rg.layout(plan, M, N, K, batched)["tile_config"]
+    if batched:
+        dixon_bench(args, rg, wl, plan, A_res, B, C, ws, stream)
+        return
 
     def step(evs=None):
         if evs is not None:
@@ -440,8 +520,14 @@ def main():
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
     st = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(3)] for e in evs])  # ms
+    # means (the roofline divides by the average launch) and per-stage spread
     split_ms, gemm_ms, recon_ms = (float(x) for x in st.mean(axis=0))
     flags = rg.status(ws)
+    digest = output_digest(args.workload, C)
+
+    # the shader clock while the products run back to back (they run power
+    # limited): the same peak scaled to that clock
+    clk_mhz, power_w = gfx_clock_during(lambda: rg.residue_products(plan, M, N, K, ws, A_res=A_res))
 
     # Garner reconstruction (same output) timed outside the step, for its
     # O(p^2) share next to the CRT that the step uses
@@ -488,9 +574,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": gemm_tops, "peak": PEAK_INT8_TOPS,
                      "unit": "TOP/s", "frac": gemm_tops / PEAK_INT8_TOPS,
                      "traffic": measured_traffic(args.workload),
-                     "kernel": gemm_kernel_name(n, M, N),
-                     "algorithmic_ops_per_launch": gemm_ops},
+                     "kernel": gemm_kernel_name(tile_config, n, M, N),
+                     "algorithmic_ops_per_launch": gemm_ops,
+                     "clock_MHz_during_products": clk_mhz, "socket_power_W_during_products": power_w,
+                     "frac_at_measured_clock": (gemm_tops / (PEAK_INT8_TOPS * clk_mhz / 2400.0)
+                                                if clk_mhz else None)},
+        "output": digest,
         "stages": {
+            "split_us_spread": spread(st[:, 0]), "products_us_spread": spread(st[:, 1]),
+            "reconstruct_us_spread": spread(st[:, 2]),
             "split_us": split_ms * 1e3, "split_GBps": split_bytes / (split_ms * 1e-3) / 1e9,
             "gemm_us": gemm_ms * 1e3, "gemm_TOPs": gemm_tops,
             "gemm_min_GBps": gemm_min_bytes / (gemm_ms * 1e-3) / 1e9,
@@ -507,6 +599,71 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, plan, C, batched, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def dixon_bench(args, rg, wl, plan, A_res, B, C, ws, stream):
+    """The Dixon-lift step as one rns_gemm_batched_residue call (the residue
+    split of r, the 54 residue products, the reconstruction), captured once
+    in a HIP graph and replayed, so that host dispatch does not pace a step
+    of a few tens of microseconds."""
+    import torch
+    M, N, K, n = wl.M, wl.N, wl.K, plan.n_primes
+    lc = C.shape[-1]
+
+    def call():
+        rg.gemm_batched_residue(plan, A_res, B, out=C, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1) / args.steps
+    eager_out = C.clone()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for _ in range(args.warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for s in range(args.steps):
+        g.replay()
+        evs[s + 1].record(stream)
+    torch.cuda.synchronize()
+    per = [evs[s].elapsed_time(evs[s + 1]) for s in range(args.steps)]
+    ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
+    same_as_eager = bool(torch.equal(C, eager_out))
+    digest = output_digest(args.workload, C)
+
+    logical = 2.0 * M * N * K * n
+    step_bytes = n * M * K + K * N * 8 * B.shape[-1] + M * N * 8 * lc
+    out = {
+        "metric": METRIC, "value": logical / (ms_step * 1e-3), "unit": "ops/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "n_primes": n, "limbs_out": lc,
+                   "parallelism": "single-gpu", "note": wl.note,
+                   "launch": "one rns_gemm_batched_residue call per step, replayed from a HIP graph"},
+        "roofline": {"bound": "hbm", "achieved": step_bytes / (ms_step * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                     "traffic": None, "scope": "whole step (its three kernels run inside one call)",
+                     "algorithmic_bytes_per_step": step_bytes},
+        "output": digest,
+        "stages": {"step_us_spread": spread(per), "eager_call_us": eager_ms * 1e3,
+                   "graph_output_equals_eager": same_as_eager},
+        "status_flags": rg.status(ws),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, plan, C, True, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

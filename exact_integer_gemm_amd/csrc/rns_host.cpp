@@ -560,12 +560,13 @@ int run(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
     const Layout L = make_layout(*plan, M, N, K, batched);
     if (ws_bytes < (size_t)L.pub.total_bytes) return RNS_E_WORKSPACE;
     if (batched && b_limbs == 1 && N <= 16 && K >= 16 && K % 16 == 0 && K <= RNS_SKINNY_K_MAX &&
-        reinterpret_cast<uintptr_t>(A_res) % 16 == 0 &&
-        skinny_rr_bytes(plan->n_primes, K) <= (int64_t)plan->n_primes * L.pub.n_pad * L.pub.k_pad) {
-        // skinny right-hand side: its residue planes, in the products' operand
-        // layout, go where the split's B planes would
+        (plan->b_bits < 0 || plan->b_bits >= 63) && reinterpret_cast<uintptr_t>(A_res) % 16 == 0 &&
+        skinny_rr_bytes(plan->n_primes, K) <= (int64_t)plan->n_primes * L.pub.b_plane) {
+        // skinny right-hand side without a bound to check: its residue planes,
+        // in the products' operand layout, go where the split's B planes would
         rc = launch_skinny(plan->n_primes, A_res, B, M, N, K, (int8_t *)ws + L.pub.b_off, (int8_t *)ws + L.pub.y_off,
-                           L.pub.m_pad * L.pub.y_pitch, L.pub.y_pitch, epi_tables(*plan), stream);
+                           L.pub.m_pad * L.pub.y_pitch, L.pub.y_pitch,
+                           reinterpret_cast<uint32_t *>((int8_t *)ws + L.pub.status_off), epi_tables(*plan), stream);
         if (rc) return rc;
         return stage_reconstruct(plan, M, N, K, batched, C, c_limbs, ws, ws_bytes, stream);
     }

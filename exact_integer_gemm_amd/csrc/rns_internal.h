@@ -181,12 +181,14 @@ int launch_zero(int64_t *C, int64_t count, hipStream_t s);
 // The batched-residue product for N <= 16 one-limb right-hand sides (K a
 // multiple of 16, up to RNS_SKINNY_K_MAX; a 16-byte aligned): the residue
 // split of r into MFMA-ready planes, then the products; writes the product
-// planes like launch_gemm does.
+// planes like launch_gemm does.  It checks no bound on r (plans without one
+// for r take it) and writes a status header of zero blocks.
 #define RNS_SKINNY_K_MAX 4096
 // rr: scratch of skinny_rr_bytes(n, K) bytes (16-byte aligned) for r's residue planes.
 int64_t skinny_rr_bytes(int n, int64_t K);
 int launch_skinny(int n, const int8_t *a, const int64_t *r, int64_t M, int64_t N, int64_t K, int8_t *rr,
-                  int8_t *y, int64_t y_plane, int64_t y_pitch, const EpiConsts &c, hipStream_t s);
+                  int8_t *y, int64_t y_plane, int64_t y_pitch, uint32_t *status, const EpiConsts &c,
+                  hipStream_t s);
 // ksteps / nblocks: MFMA K steps (slots n + 1 in 32s) and N blocks (digits in 32s)
 int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
                const int8_t *y, int64_t y_plane, int64_t y_pitch, int64_t M, int64_t N, int64_t *C,

@@ -63,6 +63,7 @@ struct SkinnyArgs {
     const int64_t *r;                 // right-hand side [K][N]
     int8_t *rr;                       // residue planes of r [n][KC][4][16][16]
     int8_t *y;                        // product planes [n][.][y_pitch]
+    uint32_t *status;                 // the workspace's status header
     int64_t y_plane, y_pitch;
     int32_t n, M, N, K, KC;
     int32_t row_blocks;
@@ -77,6 +78,11 @@ __global__ __launch_bounds__(256) void skinny_split_kernel(SkinnyArgs g, EpiCons
     const int j = (int)(id / per_prime);
     const int rem = (int)(id - (int64_t)j * per_prime);
     const int quad = rem >> 4, c = rem & 15;
+    if (id == 0) {
+        // no bound is checked on this path: a header of zero blocks (no flags)
+        g.status[0] = 0u;
+        g.status[1] = kStatusCheck;
+    }
     if (j >= g.n) return;
     const int q = ec.q[j];
     const ResidueConsts rc = rt.c[j];
@@ -173,7 +179,8 @@ __global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(SkinnyArgs g, Epi
 int64_t skinny_rr_bytes(int n, int64_t K) { return (int64_t)n * ((K + 63) / 64) * 1024; }
 
 int launch_skinny(int n, const int8_t *a, const int64_t *r, int64_t M, int64_t N, int64_t K, int8_t *rr,
-                  int8_t *y, int64_t y_plane, int64_t y_pitch, const EpiConsts &c, hipStream_t s) {
+                  int8_t *y, int64_t y_plane, int64_t y_pitch, uint32_t *status, const EpiConsts &c,
+                  hipStream_t s) {
     if (n < 1 || n > kMaxPrimes || M < 1 || N < 1 || N > 16 || K < 16 || K % 16 || K > RNS_SKINNY_K_MAX ||
         M > (1 << 24) || (reinterpret_cast<uintptr_t>(a) & 15) || (reinterpret_cast<uintptr_t>(rr) & 15))
         return RNS_E_ARG;
@@ -181,7 +188,7 @@ int launch_skinny(int n, const int8_t *a, const int64_t *r, int64_t M, int64_t N
     const int64_t grid = row_blocks * n;
     if (grid > 0x7fffffff || (int64_t)n * M * K > ((int64_t)1 << 40)) return RNS_E_ARG;
     const int64_t kc = (K + 63) / 64;
-    SkinnyArgs g{a, r, rr, y, y_plane, y_pitch, (int32_t)n, (int32_t)M, (int32_t)N, (int32_t)K, (int32_t)kc,
+    SkinnyArgs g{a, r, rr, y, status, y_plane, y_pitch, (int32_t)n, (int32_t)M, (int32_t)N, (int32_t)K, (int32_t)kc,
                  (int32_t)row_blocks};
     // per prime: the packed byte weights 256^b mod q, 2^63 mod q and fl(1/q)
     ResidueTables rt;

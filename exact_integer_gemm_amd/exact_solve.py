@@ -526,6 +526,20 @@ def reconstruct_device(digits: torch.Tensor, P: int, m: int, Nb: int, Db: int,
     return reconstruct(per_step, P, m, Nb, Db)
 
 
+def _make_reduced(frac=Fraction):
+    """A constructor of N/D already in lowest terms: Fraction's private
+    ``_normalize=False`` skips the gcd where the running Python has it (3.10 and
+    3.11); elsewhere the plain constructor (which repeats the gcd, same value)."""
+    try:
+        frac(1, 1, _normalize=False)
+    except TypeError:
+        return frac
+    return lambda n, d: frac(n, d, _normalize=False)
+
+
+_reduced_fraction = _make_reduced()
+
+
 def to_fractions(nums: Sequence[int], D: int, threads: int = 0) -> List[Fraction]:
     """[N_i / D] in lowest terms; the gcds on host threads by GMP when it is there (Python's gcd of
     two 27,000-bit numbers takes about a millisecond, and an n = 1024 solve has 1024 of them)."""
@@ -544,8 +558,7 @@ def to_fractions(nums: Sequence[int], D: int, threads: int = 0) -> List[Fraction
     red = _limbs_to_int(num_out)
     raw = memoryview(den_out).cast("B")
     w = 8 * dn
-    return [Fraction(v, int.from_bytes(raw[i * w:(i + 1) * w], "little"), _normalize=False)
-            for i, v in enumerate(red)]
+    return [_reduced_fraction(v, int.from_bytes(raw[i * w:(i + 1) * w], "little")) for i, v in enumerate(red)]
 
 
 def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
@@ -564,7 +577,7 @@ def solve(A: torch.Tensor, b: torch.Tensor, return_info: bool = False):
         return ([], {"primes": [], "steps": 0, "numerators": [], "denominator": 1}) if return_info else []
     An = A.cpu().numpy()
     bn = b.cpu().numpy()
-    amax = int(np.abs(An.astype(object)).max()) if n else 0
+    amax = max(int(An.max()), -int(An.min())) if n else 0     # exact: Python ints, no int64 overflow
     if n * amax >= 1 << 63:
         raise ValueError("n * max|A| must stay below 2^63 (the residual is one signed limb)")
     singular, ws = batched_inverse(A)

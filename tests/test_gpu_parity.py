@@ -271,9 +271,11 @@ def test_batched_residue_small(M, N, K, n, seed):
     p = rg.plan_n(n)
     A_res = W.balanced_residue_planes(rng, p.primes, M, K)
     r = rng.integers(-(1 << 34), 1 << 34, size=(K, N), endpoint=True)
-    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None])).cpu().numpy()
+    ws0 = rg.new_workspace(p, M, N, K, True)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
     ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
     assert np.array_equal(O.decode_array(X), ref)
+    assert rg.status(ws0) == 0          # the fused path leaves a readable status (no bound on r)
 
 
 def _planted(n, values, prime_powers=False):
@@ -385,9 +387,11 @@ def test_prime_power_int32_edge():
     A_res = np.full((3, M, K), -128, dtype=np.int8)
     A_res[1:] = 5
     r = np.full((K, N), -128, dtype=np.int64)
-    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None])).cpu().numpy()
+    ws0 = rg.new_workspace(p, M, N, K, True)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
     ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
     assert np.array_equal(O.decode_array(X), ref)
+    assert rg.status(ws0) == 0          # the fused path leaves a readable status (no bound on r)
 
 
 @pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", [SMALL[1], SMALL[3], SMALL[7],
@@ -415,9 +419,11 @@ def test_batched_residue_any_int8_and_extremes():
     r[:, 3] = -(2 ** 63)
     r[:, 4] = 2 ** 63 - 1
     r[::3, 5] = rng.integers(-(2 ** 62), 2 ** 62, size=r[::3, 5].shape)
-    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None])).cpu().numpy()
+    ws0 = rg.new_workspace(p, M, N, K, True)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
     ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
     assert np.array_equal(O.decode_array(X), ref)
+    assert rg.status(ws0) == 0          # the fused path leaves a readable status (no bound on r)
 
 
 # The skinny right-hand side (N <= 16, one limb, K a multiple of 16 up to
@@ -447,9 +453,11 @@ def test_batched_residue_skinny_fused(M, N, K, n, pp, seed):
     r[0, :] = -(2 ** 63)
     r[-1, :] = 2 ** 63 - 1
     r[1::5, :] = rng.integers(-(1 << 34), 1 << 34, size=r[1::5, :].shape, endpoint=True)
-    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None])).cpu().numpy()
+    ws0 = rg.new_workspace(p, M, N, K, True)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
     ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
     assert np.array_equal(O.decode_array(X), ref)
+    assert rg.status(ws0) == 0          # the fused path leaves a readable status (no bound on r)
     # the stage calls (split, general product kernel, reconstruction) agree bit for bit
     ws = rg.new_workspace(p, M, N, K, True)
     Ad, rd = dev(A_res), dev(r[..., None])

@@ -348,3 +348,41 @@ def test_fractions_in_lowest_terms_native():
     got = S.to_fractions(nums, D)
     assert got == [Fraction(v, D) for v in nums]
     assert all(math.gcd(f.numerator, f.denominator) == 1 and f.denominator > 0 for f in got)
+
+
+def test_reduced_fraction_constructor_fallback():
+    """Where Fraction has no ``_normalize`` argument the plain constructor
+    serves (same value for inputs in lowest terms); where it has one, the
+    unnormalised construction gives the same Fraction."""
+    class NoNormalize(Fraction):
+        def __new__(cls, numerator=0, denominator=None):
+            return super().__new__(cls, numerator, denominator)
+
+    assert S._make_reduced(NoNormalize) is NoNormalize
+    make = S._make_reduced()
+    for n, d in [(3, 7), (-5, 12), (0, 1), (2 ** 200 + 1, 3 ** 90)]:
+        assert make(n, d) == Fraction(n, d)
+
+
+def test_to_fractions_without_the_native_stage(monkeypatch):
+    """The pure-Python branch of to_fractions (no GMP on the host) normalises
+    like Fraction itself."""
+    monkeypatch.setattr(S, "host_bigint_available", lambda: False)
+    D = 2 ** 5 * 3 ** 3 * 251
+    nums = [0, 1, -1, D, -2 * D, 6, -(2 ** 70) * 251, 12345]
+    assert S.to_fractions(nums, D) == [Fraction(v, D) for v in nums]
+
+
+def test_python_rational_reconstruction_against_the_oracle():
+    """The pure-Python extended Euclid (used when GMP is missing) against the
+    oracle's rational reconstruction, found and not-found cases alike."""
+    rng = random.Random(12)
+    M = O.prod([q for q in O.primes_largest_first() if q % 2][:8]) ** 3
+    for _ in range(200):
+        a, d = rng.randrange(-2 ** 40, 2 ** 40), rng.randrange(1, 2 ** 40)
+        if math.gcd(a, d) != 1 or math.gcd(d, M) != 1:
+            continue
+        u = a * pow(d, -1, M) % M
+        assert S._ratrec(u, M, 2 ** 40, 2 ** 40) == D.rational_reconstruct(u, M, 2 ** 40, 2 ** 40) == Fraction(a, d)
+        v = rng.randrange(M)
+        assert S._ratrec(v, M, 2 ** 20, 2 ** 20) == D.rational_reconstruct(v, M, 2 ** 20, 2 ** 20)
