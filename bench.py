@@ -44,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target wall time of the CPU oracle sample")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip sampling the shader clock with amd-smi (profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -527,7 +529,8 @@ def main():
 
     # the shader clock while the products run back to back (they run power
     # limited): the same peak scaled to that clock
-    clk_mhz, power_w = gfx_clock_during(lambda: rg.residue_products(plan, M, N, K, ws, A_res=A_res))
+    clk_mhz, power_w = (None, None) if args.no_clock else gfx_clock_during(
+        lambda: rg.residue_products(plan, M, N, K, ws, A_res=A_res))
 
     # Garner reconstruction (same output) timed outside the step, for its
     # O(p^2) share next to the CRT that the step uses
