@@ -284,7 +284,7 @@ void build_crt(const rns_plan_t &pl, CrtConsts &c, CrtDigits &d, int *ksteps, in
                 Mk_mod = Mk_mod * pl.primes[j] % q;
             }
         const int w = balanced(inv_mod(Mk_mod, q), q);
-        const int64_t cfix = floor_div((((int64_t)w << 31) * 2) + q, 2 * (int64_t)q);   // round(w 2^31 / q)
+        const int64_t cfix = floor_div((int64_t)w * (INT64_C(1) << 32) + q, 2 * (int64_t)q);   // round(w 2^31 / q)
         c.chi[k] = (int32_t)(cfix >> 16);
         c.clo[k] = (int32_t)(cfix & 0xffff);
         Big E = Mk;

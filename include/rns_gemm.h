@@ -212,10 +212,12 @@ int rns_gemm_batched_residue(const rns_plan_t *plan, int64_t M, int64_t N, int64
  * rns_reconstruct      -- kernel 3: C from the Y planes, the centered CRT
  *                         value by rounded quotient (Ozaki Scheme II paper,
  *                         §3.5.2: the centered representative by rounding to
- *                         nearest): u_j = y_j * (M_j^-1 mod q_j) balanced,
- *                         M_j = P / q_j, X = sum_j u_j M_j - r P with r the
- *                         nearest integer to sum_j u_j / q_j, the sum over
- *                         primes formed on the matrix cores; where the
+ *                         nearest): with M_j = P / q_j, w_j = M_j^-1 mod q_j
+ *                         (balanced) and the basis e_j = w_j M_j,
+ *                         X = sum_j y_j e_j - r P with r the nearest integer
+ *                         to sum_j y_j w_j / q_j (the y_j as stored, no
+ *                         per-entry reduction), the sum over primes formed
+ *                         on the matrix cores; where the
  *                         binary32 estimate of r is near a half-integer the
  *                         result is compared with P/2 exactly and moved by one
  *                         period, so C is the same exact value as Garner's.
