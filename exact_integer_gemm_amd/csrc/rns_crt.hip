@@ -267,6 +267,239 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
     }
 }
 
+// Quad form (rows mode, or N a multiple of 4): a wave takes 128 entries,
+// four consecutive ones per lane pair.  Lane (l32, h) reads, for each of its
+// 16 slots per K step, the 4-byte word of entries 4 l32 .. 4 l32 + 3 of one
+// plane; a 4 x 4 byte transpose of four such words gives four slots of each
+// of the four entries, so one load serves four entries.  The fixed-point sum
+// of y_k c_k runs on the matrix cores as well: a first product against the
+// balanced base-256 digits of c_k (rows 0-3, repeated in rows 4-7 so that
+// both half-waves receive them) leaves F in four partial sums
+// (|partial| <= 64 * 128 * 128 < 2^20).
+template <int KS, int NB, bool OFF32, bool ROWS>
+__global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd,
+                                                   const int8_t *__restrict__ y, int64_t y_plane,
+                                                   int64_t y_pitch, int64_t M, int64_t N,
+                                                   int64_t *__restrict__ C, int c_limbs, int pair_stores) {
+    constexpr int W = 8 * NB;                 // 32-bit words of X'
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = lane >> 5, l32 = lane & 31;
+
+    __shared__ v4i dT[kCrtDigits][kCrtSlots / 16];
+    {
+        int8_t *t = (int8_t *)&dT[0][0];
+        for (int i = threadIdx.x; i < kCrtDigits * kCrtSlots; i += blockDim.x) {
+            const int c = i / kCrtSlots, k = i - c * kCrtSlots;
+            t[i] = k < kCrtSlots - 8 ? cd.d[k][c] : (int8_t)0;
+        }
+    }
+    __syncthreads();
+    v4i dig[KS][NB];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            const int c = 32 * nb + l32;
+            dig[ks][nb] = c < kCrtDigits ? dT[c][2 * ks + h] : v4i{0, 0, 0, 0};
+        }
+    // fixed-point fragments: row l32 < 8 holds digit l32 % 4 of c_k for the lane's slots
+    v4i fx[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+        uint32_t wd[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int b = 0; b < 16; b++) {
+            const int k = 32 * ks + 16 * h + b;
+            const uint32_t byte = l32 < 8 ? (cc.cb[k] >> (8 * (l32 & 3))) & 0xffu : 0u;
+            wd[b >> 2] |= byte << (8 * (b & 3));
+        }
+        fx[ks] = v4i{(int)wd[0], (int)wd[1], (int)wd[2], (int)wd[3]};
+    }
+    // the lane's slot planes (slots past the moduli read the last plane; their weights are zero)
+    int plane[KS][16];
+    uint32_t poff[KS][16];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+        for (int b = 0; b < 16; b++) {
+            const int k = 32 * ks + 16 * h + b;
+            plane[ks][b] = k < cc.n ? k : cc.n - 1;
+            poff[ks][b] = OFF32 ? (uint32_t)(plane[ks][b] * y_plane) : 0u;
+        }
+
+    const int64_t total = M * N;
+    const int64_t cgs = ROWS ? (N + 127) >> 7 : 1;            // 128-column groups per row
+    const int64_t groups = ROWS ? M * cgs : (total + 127) >> 7;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    const int64_t g0 = (int64_t)blockIdx.x * 4 + wave;
+    int64_t row = g0 / cgs, cg = g0 - row * cgs;
+    const int64_t drow = stride / cgs, dcg = stride - drow * cgs;
+    for (int64_t grp = g0; grp < groups; grp += stride) {
+        int64_t i, j0, lim;                   // entries j0 + m < lim (columns, or flat indices) are real
+        if (ROWS) {
+            i = row;
+            j0 = cg * 128 + 4 * l32;          // within the plane's row pitch (a multiple of 128)
+            lim = N;
+            row += drow;
+            cg += dcg;
+            if (cg >= cgs) {
+                cg -= cgs;
+                row++;
+            }
+        } else {
+            // N is a multiple of 4: a quad of flat indices lies in one row
+            const int64_t f0 = grp * 128 + 4 * l32;
+            const int64_t ff = f0 < total ? f0 : total - 4;
+            i = ff / N;
+            j0 = ff - i * N;
+            lim = f0 < total ? j0 + (total - f0) : 0;
+        }
+        uint32_t q[KS][16];
+        const uint32_t yo = OFF32 ? (uint32_t)(i * y_pitch + j0) : 0u;
+        const int8_t *yp = y + i * y_pitch + j0;
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int b = 0; b < 16; b++)
+                q[ks][b] = OFF32 ? *(const uint32_t *)(y + (yo + poff[ks][b]))
+                                 : *(const uint32_t *)(yp + (int64_t)plane[ks][b] * y_plane);
+        // 4 x 4 byte transposes: ua[m][ks] word wd = slots 4 wd .. 4 wd + 3 of entry m
+        v4i ua[4][KS];
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int wd = 0; wd < 4; wd++) {
+                const uint32_t *qq = &q[ks][4 * wd];
+                const uint32_t a = __builtin_amdgcn_perm(qq[1], qq[0], 0x05010400u);
+                const uint32_t b = __builtin_amdgcn_perm(qq[3], qq[2], 0x05010400u);
+                const uint32_t c = __builtin_amdgcn_perm(qq[1], qq[0], 0x07030602u);
+                const uint32_t d = __builtin_amdgcn_perm(qq[3], qq[2], 0x07030602u);
+                ua[0][ks][wd] = (int)__builtin_amdgcn_perm(b, a, 0x05040100u);
+                ua[1][ks][wd] = (int)__builtin_amdgcn_perm(b, a, 0x07060302u);
+                ua[2][ks][wd] = (int)__builtin_amdgcn_perm(d, c, 0x05040100u);
+                ua[3][ks][wd] = (int)__builtin_amdgcn_perm(d, c, 0x07060302u);
+            }
+
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            // F = sum_k y_k c_k from the four digit sums
+            v16i fs = v16i{0};
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++)
+                fs = __builtin_amdgcn_mfma_i32_32x32x32_i8(fx[ks], ua[m][ks], fs, 0, 0, 0);
+            const int64_t F = (int64_t)fs[0] + (int64_t)fs[1] * 256 + (int64_t)fs[2] * 65536 +
+                              (int64_t)fs[3] * 16777216;
+            // F / 2^31 is within 2^-19 of S / P; r = floor(F / 2^31 + 1/2)
+            const int64_t r64 = (F + (1ll << 30)) >> 31;
+            const int64_t fr = F - r64 * (1ll << 31);
+            const bool near_half = fr < -(1ll << 30) + (1ll << 21) || fr >= (1ll << 30) - (1ll << 21);
+            const int r = (int)r64;
+            const int rlo = ((r + 127) & 255) - 127;
+            const int rhi = (r - rlo) >> 8;
+            v4i u[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ks++) u[ks] = ua[m][ks];
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const int k = cc.n + t, val = t ? -rhi : -rlo;
+                const int ks_k = k >> 5, h_k = (k >> 4) & 1, x_k = (k >> 2) & 3, sh = 8 * (k & 3);
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+                    for (int x = 0; x < 4; x++)
+                        if (ks == ks_k && x == x_k && h == h_k)
+                            u[ks][x] = (int)(((uint32_t)u[ks][x] & ~(0xffu << sh)) | ((uint32_t)(val & 0xff) << sh));
+            }
+            v16i acc[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++) {
+                acc[nb] = v16i{0};
+#pragma unroll
+                for (int ks = 0; ks < KS; ks++)
+                    acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[ks][nb], u[ks], acc[nb], 0, 0, 0);
+            }
+            int part[2 * W];
+#pragma unroll
+            for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                for (int gq = 0; gq < 4; gq++) {
+                    const v16i &a = acc[nb];
+                    const int lo = a[4 * gq] + (a[4 * gq + 1] << 8);
+                    const int hi = a[4 * gq + 2] + (a[4 * gq + 3] << 8);
+                    const auto sl = __builtin_amdgcn_permlane32_swap((uint32_t)lo, (uint32_t)lo, false, false);
+                    const auto sh = __builtin_amdgcn_permlane32_swap((uint32_t)hi, (uint32_t)hi, false, false);
+                    const int w0 = 8 * nb + 2 * gq;
+                    part[2 * w0] = (int)sl[0];
+                    part[2 * w0 + 1] = (int)sh[0];
+                    part[2 * w0 + 2] = (int)sl[1];
+                    part[2 * w0 + 3] = (int)sh[1];
+                }
+            uint32_t wv[W];
+            int c16 = 0;
+#pragma unroll
+            for (int w = 0; w < W; w++) {
+                const int t0 = part[2 * w] + c16;
+                const int t1 = part[2 * w + 1] + (t0 >> 16);
+                c16 = t1 >> 16;
+                wv[w] = __builtin_amdgcn_perm((uint32_t)t1, (uint32_t)t0, 0x05040100u);
+            }
+            int64_t carry = c16;
+            if (near_half) {
+                int64_t bm = 0, bp = 0;
+                uint32_t nzm = 0, nzp = 0;
+#pragma unroll
+                for (int w = 0; w < W; w++) {
+                    const uint32_t two = (wv[w] << 1) | (w ? (wv[w - 1] >> 31) : 0u);
+                    const uint32_t pw = w < 16 ? cc.P[w] : 0u;
+                    const int64_t dm = (int64_t)two - pw + bm;
+                    const int64_t dp = (int64_t)two + pw + bp;
+                    nzm |= (uint32_t)dm;
+                    nzp |= (uint32_t)dp;
+                    bm = dm >> 32;
+                    bp = dp >> 32;
+                }
+                const int64_t top2 = 2 * carry + (int64_t)(wv[W - 1] >> 31);
+                const int64_t tm = top2 + bm, tp = top2 + bp;
+                const bool above = tm > 0 || (tm == 0 && nzm != 0);
+                const bool below = tp < 0 || (tp == 0 && nzp == 0);
+                if (above || below) {
+                    int64_t c2 = 0;
+#pragma unroll
+                    for (int w = 0; w < W; w++) {
+                        const int64_t pw = w < 16 ? (int64_t)cc.P[w] : 0;
+                        c2 += (int64_t)wv[w] + (above ? -pw : pw);
+                        wv[w] = (uint32_t)c2;
+                        c2 >>= 32;
+                    }
+                    carry += c2;
+                }
+            }
+            if (j0 + m < lim) {
+                int64_t *ce = C + (i * N + j0 + m) * c_limbs;
+                const uint32_t sign = (uint32_t)carry;
+#pragma unroll
+                for (int t = 0; t < RNS_MAX_OUT_LIMBS / 4; t++) {
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int ii = 0; ii < 4; ii++) {
+                        const int i0 = 8 * t + ii, i1 = 8 * t + 4 + ii;
+                        const uint32_t a0 = i0 < W ? wv[i0] : sign, a1 = i1 < W ? wv[i1] : sign;
+                        wd[ii] = h ? a1 : a0;
+                    }
+                    const int l = 4 * t + 2 * h;
+                    if (pair_stores) {
+                        if (l < c_limbs) *(v4u *)(ce + l) = v4u{wd[0], wd[1], wd[2], wd[3]};
+                    } else {
+                        if (l < c_limbs) ce[l] = (int64_t)(((uint64_t)wd[1] << 32) | wd[0]);
+                        if (l + 1 < c_limbs) ce[l + 1] = (int64_t)(((uint64_t)wd[3] << 32) | wd[2]);
+                    }
+                }
+            }
+        }
+    }
+}
+
 int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
                const int8_t *y, int64_t y_plane, int64_t y_pitch, int64_t M, int64_t N, int64_t *C,
                int32_t c_limbs, hipStream_t s) {
@@ -274,15 +507,52 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
     if (total == 0) return RNS_OK;
     if (c.n < 1 || c.n + 2 > 32 * ksteps || ksteps < 1 || ksteps > 2 || nblocks < 1 || nblocks > 2)
         return RNS_E_ARG;
+    const int pairs = (reinterpret_cast<uintptr_t>(C) % 16 == 0 && c_limbs % 2 == 0) ? 1 : 0;
+    // the Y planes span y_plane * n bytes from y
+    const bool off32 = (uint64_t)y_plane * (uint64_t)c.n < (1ull << 32);
+    // quad form: rows mode when whole 128-column groups waste little (N a
+    // multiple of 128, or N >= 1024), else flat when N is a multiple of 4
+    // (the row pitch of the planes is a multiple of 128, so a quad never
+    // leaves its row)
+    if (N % 128 == 0 || N >= 1024 || N % 4 == 0) {
+        const int rows4 = (N % 128 == 0 || N >= 1024) ? 1 : 0;
+        if (!rows4 && N % 4) return RNS_E_ARG;
+        const int64_t groups4 = rows4 ? M * ((N + 127) / 128) : (total + 127) / 128;
+        int64_t grid4 = (groups4 + 3) / 4;
+        if (grid4 > 1536) grid4 = 1536;
+        const dim3 g4((unsigned)grid4), b4(256);
+#define RNS_CRT4_LAUNCH(KS, NB)                                                                             \
+    do {                                                                                                    \
+        if (off32 && rows4)                                                                                 \
+            hipLaunchKernelGGL((crt4_kernel<KS, NB, true, true>), g4, b4, 0, s, c, d, y, y_plane, y_pitch, M, \
+                               N, C, c_limbs, pairs);                                                       \
+        else if (off32)                                                                                     \
+            hipLaunchKernelGGL((crt4_kernel<KS, NB, true, false>), g4, b4, 0, s, c, d, y, y_plane, y_pitch,  \
+                               M, N, C, c_limbs, pairs);                                                    \
+        else if (rows4)                                                                                     \
+            hipLaunchKernelGGL((crt4_kernel<KS, NB, false, true>), g4, b4, 0, s, c, d, y, y_plane, y_pitch,  \
+                               M, N, C, c_limbs, pairs);                                                    \
+        else                                                                                                \
+            hipLaunchKernelGGL((crt4_kernel<KS, NB, false, false>), g4, b4, 0, s, c, d, y, y_plane, y_pitch, \
+                               M, N, C, c_limbs, pairs);                                                    \
+    } while (0)
+        if (ksteps == 1 && nblocks == 1)
+            RNS_CRT4_LAUNCH(1, 1);
+        else if (ksteps == 1)
+            RNS_CRT4_LAUNCH(1, 2);
+        else if (nblocks == 1)
+            RNS_CRT4_LAUNCH(2, 1);
+        else
+            RNS_CRT4_LAUNCH(2, 2);
+#undef RNS_CRT4_LAUNCH
+        return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
+    }
     // rows mode when whole 32-column groups waste little: N a multiple of 32, or N >= 256
     const int rows = (N % 32 == 0 || N >= 256) ? 1 : 0;
     const int64_t groups = rows ? M * ((N + 31) / 32) : (total + 31) / 32;
     int64_t grid = (groups + 3) / 4;
     if (grid > 1536) grid = 1536;             // grid-stride: each wave amortises its set-up
     const dim3 g((unsigned)grid), b(256);
-    const int pairs = (reinterpret_cast<uintptr_t>(C) % 16 == 0 && c_limbs % 2 == 0) ? 1 : 0;
-    // the Y planes span y_plane * n bytes from y
-    const bool off32 = (uint64_t)y_plane * (uint64_t)c.n < (1ull << 32);
 #define RNS_CRT_LAUNCH(KS, NB)                                                                              \
     do {                                                                                                    \
         if (off32 && rows)                                                                                  \

@@ -287,6 +287,12 @@ void build_crt(const rns_plan_t &pl, CrtConsts &c, CrtDigits &d, int *ksteps, in
         const int64_t cfix = floor_div((int64_t)w * (INT64_C(1) << 32) + q, 2 * (int64_t)q);   // round(w 2^31 / q)
         c.chi[k] = (int32_t)(cfix >> 16);
         c.clo[k] = (int32_t)(cfix & 0xffff);
+        int64_t rest = cfix;                          // |c_k| <= 2^30: four balanced digits
+        for (int i = 0; i < 4; i++) {
+            const int64_t dgt = ((rest % 256) + 256 + 128) % 256 - 128;
+            c.cb[k] |= (uint32_t)(uint8_t)(int8_t)dgt << (8 * i);
+            rest = (rest - dgt) / 256;
+        }
         Big E = Mk;
         E.mul_small((uint32_t)(w < 0 ? -w : w));
         used = std::max(used, signed_digits(E, w < 0, d.d[k]));

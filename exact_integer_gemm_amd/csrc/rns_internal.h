@@ -100,6 +100,7 @@ struct CrtConsts {
     int32_t n;                       // moduli; slots n and n + 1 hold -r_lo and -r_hi
     int32_t chi[kCrtSlots];          // c_k = chi 2^16 + clo, clo in [0, 2^16); zero past slot n - 1
     int32_t clo[kCrtSlots];
+    uint32_t cb[kCrtSlots];          // c_k as four balanced base-256 digits (packed int8, low first)
     uint32_t P[16];                  // P, little-endian 32-bit words
 };
 // Balanced base-256 digits of e_0 .. e_{n-1}, P (slot n) and 256 P (slot
