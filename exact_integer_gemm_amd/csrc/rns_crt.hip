@@ -513,8 +513,9 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
     // quad form: rows mode when whole 128-column groups waste little (N a
     // multiple of 128, or N >= 1024), else flat when N is a multiple of 4
     // (the row pitch of the planes is a multiple of 128, so a quad never
-    // leaves its row)
-    if (N % 128 == 0 || N >= 1024 || N % 4 == 0) {
+    // leaves its row).  Below 1024 groups of 128 entries (4 per compute
+    // unit) the byte form's four times as many waves hide latency better.
+    if ((N % 128 == 0 || N >= 1024 || N % 4 == 0) && total >= 1024 * 128) {
         const int rows4 = (N % 128 == 0 || N >= 1024) ? 1 : 0;
         if (!rows4 && N % 4) return RNS_E_ARG;
         const int64_t groups4 = rows4 ? M * ((N + 127) / 128) : (total + 127) / 128;

@@ -76,6 +76,28 @@ def test_product_exact_small(M, N, K, la, lb, ab, bb, seed):
     assert rg.status(ws) == 0
 
 
+# The reconstruction's quad form (four entries per lane pair) runs from
+# 1024 groups of 128 entries: flat groups when N is a multiple of 4 below
+# 1024 columns, 128-column row groups from 1024 columns (a ragged last group
+# here); smaller outputs take the byte form.
+QUAD = [
+    (520, 276, 70, 1, 2, 50, 90, 41),     # flat quads, N % 128 != 0
+    (150, 1100, 33, 2, 1, 100, 40, 42),   # row groups of 128 columns, ragged last group
+    (260, 512, 64, 1, 1, 62, 62, 43),     # row groups, N a multiple of 128
+]
+
+
+@pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", QUAD)
+def test_reconstruction_quad_form(M, N, K, la, lb, ab, bb, seed):
+    print(f"quad CRT M={M} N={N} K={K}", flush=True)
+    A, B = W.random_operands(seed, M, N, K, la, lb, ab, bb)
+    p, ws, C = run_gemm(A, B, ab, bb)
+    assert np.array_equal(C, oracle_c(A, B, p.out_limbs_min))
+    out = torch.empty((M, N, p.out_limbs_min), dtype=torch.int64, device="cuda")
+    rg.reconstruct(p, M, N, K, ws, out, method="garner")
+    assert np.array_equal(out.cpu().numpy(), C)
+
+
 @pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", [SMALL[1], SMALL[3], SMALL[4], SMALL[7]])
 def test_stage_planes(M, N, K, la, lb, ab, bb, seed):
     """Split planes and per-prime products against the oracle's stage definitions."""
