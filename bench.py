@@ -606,10 +606,11 @@ def main():
 
 
 def dixon_bench(args, rg, wl, plan, A_res, B, C, ws, stream):
-    """The Dixon-lift step as one rns_gemm_batched_residue call (the residue
-    split of r, the 54 residue products, the reconstruction), captured once
-    in a HIP graph and replayed, so that host dispatch does not pace a step
-    of a few tens of microseconds."""
+    """The Dixon-lift step as one rns_gemm_batched_residue call (one kernel:
+    the products on r's bytes and the reconstruction).  Steps run back to
+    back on one stream; they are captured G at a time in a HIP graph and
+    replayed, so that host dispatch does not pace a step of some tens of
+    microseconds (G divides the step count; every step is a full call)."""
     import torch
     M, N, K, n = wl.M, wl.N, wl.K, plan.n_primes
     lc = C.shape[-1]
@@ -629,20 +630,23 @@ def dixon_bench(args, rg, wl, plan, A_res, B, C, ws, stream):
     eager_ms = e0.elapsed_time(e1) / args.steps
     eager_out = C.clone()
 
+    G = max(d for d in range(1, 26) if args.steps % d == 0)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        call()
-    for _ in range(args.warmup):
+        for _ in range(G):
+            call()
+    for _ in range(max(1, args.warmup // G)):
         g.replay()
     torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    reps = args.steps // G
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
     evs[0].record(stream)
-    for s in range(args.steps):
+    for s in range(reps):
         g.replay()
         evs[s + 1].record(stream)
     torch.cuda.synchronize()
-    per = [evs[s].elapsed_time(evs[s + 1]) for s in range(args.steps)]
+    per = [evs[s].elapsed_time(evs[s + 1]) / G for s in range(reps)]
     ms_step = evs[0].elapsed_time(evs[-1]) / args.steps
     same_as_eager = bool(torch.equal(C, eager_out))
     digest = output_digest(args.workload, C)
@@ -655,13 +659,18 @@ def dixon_bench(args, rg, wl, plan, A_res, B, C, ws, stream):
         "scaling": "weak", "vs_baseline": None, "dtype": "int8", "data": "synthetic",
         "config": {"workload": args.workload, "M": M, "N": N, "K": K, "n_primes": n, "limbs_out": lc,
                    "parallelism": "single-gpu", "note": wl.note,
-                   "launch": "one rns_gemm_batched_residue call per step, replayed from a HIP graph"},
+                   "launch": "one rns_gemm_batched_residue call per step, G steps per HIP graph replay",
+                   "steps_per_graph": G},
         "roofline": {"bound": "hbm", "achieved": step_bytes / (ms_step * 1e-3) / 1e9, "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": step_bytes / (ms_step * 1e-3) / 1e9 / PEAK_HBM_GBPS,
-                     "traffic": None, "scope": "whole step (its three kernels run inside one call)",
-                     "algorithmic_bytes_per_step": step_bytes},
+                     "traffic": None, "scope": "whole step (one kernel)",
+                     "algorithmic_bytes_per_step": step_bytes,
+                     # the kernel's int8 products: nine 16-column blocks (the eight bytes of r
+                     # and the row sums) per product row, for every prime
+                     "int8_mfma_ops_per_step": 2.0 * n * M * 9 * 16 * K,
+                     "int8_mfma_frac": 2.0 * n * M * 9 * 16 * K / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS},
         "output": digest,
-        "stages": {"step_us_spread": spread(per), "eager_call_us": eager_ms * 1e3,
+        "stages": {"step_us_spread_per_replay": spread(per), "eager_call_us": eager_ms * 1e3,
                    "graph_output_equals_eager": same_as_eager},
         "status_flags": rg.status(ws),
     }

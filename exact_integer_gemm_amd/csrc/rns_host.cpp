@@ -362,6 +362,45 @@ const CrtTables &crt_tables(const rns_plan_t &pl) {
     static thread_local TableCache<CrtTables> cache;
     return cache.get(table_key(pl), [&](CrtTables &v) { build_crt(pl, v.c, v.d, &v.ksteps, &v.nblocks); });
 }
+// The fused lift step's constants: 256^b mod q (b < 8) balanced, c_1 mod q,
+// and the reconstruction's fixed-point weights and P.
+void build_step(const rns_plan_t &pl, const CrtConsts &c, StepConsts &v) {
+    std::memset(&v, 0, sizeof v);
+    v.n = pl.n_primes;
+    for (int j = 0; j < pl.n_primes; j++) {
+        const int q = pl.primes[j];
+        int p = 1 % q, sum = 0;
+        for (int b = 0; b < 8; b++) {
+            const int bal = p > q / 2 ? p - q : p;
+            v.tb[j][b >> 2] |= (uint32_t)(uint8_t)(int8_t)bal << (8 * (b & 3));
+            if (b < 7) sum = (sum + p) % q;
+            p = p * 256 % q;
+        }
+        v.q[j] = (uint16_t)q;
+        v.c1[j] = (uint8_t)(128 * sum % q);
+    }
+    for (int k = 0; k < kCrtSlots; k++)
+        for (int d = 0; d < 4; d++) {
+            const int b = k & 15;
+            v.fx[k >> 5][(k >> 4) & 1][d][b >> 2] |= ((c.cb[k] >> (8 * d)) & 0xffu) << (8 * (b & 3));
+        }
+    std::memcpy(v.P, c.P, sizeof v.P);
+}
+struct StepTables {
+    StepConsts c;
+    CrtDigits d;
+    int ksteps, nblocks;
+};
+const StepTables &step_tables(const rns_plan_t &pl) {
+    static thread_local TableCache<StepTables> cache;
+    return cache.get(table_key(pl), [&](StepTables &v) {
+        const CrtTables &ct = crt_tables(pl);
+        build_step(pl, ct.c, v.c);
+        v.d = ct.d;
+        v.ksteps = ct.ksteps;
+        v.nblocks = ct.nblocks;
+    });
+}
 const GarnerConsts &garner_tables(const rns_plan_t &pl) {
     static thread_local TableCache<GarnerConsts, 4> cache;
     return cache.get(table_key(pl), [&](GarnerConsts &v) { build_garner(pl, v); });
@@ -565,16 +604,12 @@ int run(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
     if (!B || (!batched && !A) || !ws) return RNS_E_ARG;
     const Layout L = make_layout(*plan, M, N, K, batched);
     if (ws_bytes < (size_t)L.pub.total_bytes) return RNS_E_WORKSPACE;
-    if (batched && b_limbs == 1 && N <= 16 && K >= 16 && K % 16 == 0 && K <= RNS_SKINNY_K_MAX &&
-        (plan->b_bits < 0 || plan->b_bits >= 63) && reinterpret_cast<uintptr_t>(A_res) % 16 == 0 &&
-        skinny_rr_bytes(plan->n_primes, K) <= (int64_t)plan->n_primes * L.pub.b_plane) {
-        // skinny right-hand side without a bound to check: its residue planes,
-        // in the products' operand layout, go where the split's B planes would
-        rc = launch_skinny(plan->n_primes, A_res, B, M, N, K, (int8_t *)ws + L.pub.b_off, (int8_t *)ws + L.pub.y_off,
-                           L.pub.m_pad * L.pub.y_pitch, L.pub.y_pitch,
-                           reinterpret_cast<uint32_t *>((int8_t *)ws + L.pub.status_off), epi_tables(*plan), stream);
-        if (rc) return rc;
-        return stage_reconstruct(plan, M, N, K, batched, C, c_limbs, ws, ws_bytes, stream);
+    if (batched && b_limbs == 1 && N <= 16 && K >= 16 && K % 16 == 0 && K <= RNS_LIFT_K_MAX &&
+        (plan->b_bits < 0 || plan->b_bits >= 63) && reinterpret_cast<uintptr_t>(A_res) % 16 == 0) {
+        // skinny right-hand side without a bound to check: one kernel
+        const StepTables &lt = step_tables(*plan);
+        return launch_lift_step(lt.c, lt.d, lt.ksteps, lt.nblocks, A_res, B, M, N, K, C, c_limbs,
+                                reinterpret_cast<uint32_t *>((int8_t *)ws + L.pub.status_off), stream);
     }
     rc = stage_split(plan, M, N, K, batched ? nullptr : A, a_limbs, B, b_limbs, ws, ws_bytes, stream, fp);
     if (rc) return rc;

@@ -179,17 +179,28 @@ int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
 int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t y_pitch,
                   int64_t M, int64_t N, int64_t *C, int32_t c_limbs, hipStream_t s);
 int launch_zero(int64_t *C, int64_t count, hipStream_t s);
-// The batched-residue product for N <= 16 one-limb right-hand sides (K a
-// multiple of 16, up to RNS_SKINNY_K_MAX; a 16-byte aligned): the residue
-// split of r into MFMA-ready planes, then the products; writes the product
-// planes like launch_gemm does.  It checks no bound on r (plans without one
-// for r take it) and writes a status header of zero blocks.
-#define RNS_SKINNY_K_MAX 4096
-// rr: scratch of skinny_rr_bytes(n, K) bytes (16-byte aligned) for r's residue planes.
-int64_t skinny_rr_bytes(int n, int64_t K);
-int launch_skinny(int n, const int8_t *a, const int64_t *r, int64_t M, int64_t N, int64_t K, int8_t *rr,
-                  int8_t *y, int64_t y_plane, int64_t y_pitch, uint32_t *status, const EpiConsts &c,
-                  hipStream_t s);
+// The whole batched step for N <= 16 one-limb right-hand sides without a
+// bound to check (K a multiple of 16, up to RNS_LIFT_K_MAX; a 16-byte aligned):
+// the products on r's bytes and the reconstruction in one kernel, C written
+// directly (no residue planes in the workspace) and a status header of zero
+// blocks.  K <= 2^16 keeps every int32 byte product within 2^30.
+#define RNS_LIFT_K_MAX 65536
+// Its per-plan constants: the moduli, 256^b mod q_j (b < 8, balanced int8,
+// packed four to a word), c_1 mod q_j (c_1 = 128 (1 + 256 + ... + 256^6)),
+// P, and the reconstruction's fixed-point weights c_k (CrtConsts::cb) as
+// MFMA fragments: fx[ks][h][d] holds digit d of c_k for slots
+// k = 32 ks + 16 h .. 32 ks + 16 h + 15, one byte each.
+struct StepConsts {
+    uint32_t tb[kMaxPrimes][2];
+    uint32_t fx[2][2][4][4];
+    uint32_t P[16];
+    uint16_t q[kMaxPrimes];
+    uint8_t c1[kMaxPrimes];
+    int32_t n;
+};
+int launch_lift_step(const StepConsts &lc, const CrtDigits &cd, int ksteps, int nblocks, const int8_t *a,
+                     const int64_t *r, int64_t M, int64_t N, int64_t K, int64_t *C, int32_t c_limbs,
+                     uint32_t *status, hipStream_t s);
 // ksteps / nblocks: MFMA K steps (slots n + 1 in 32s) and N blocks (digits in 32s)
 int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
                const int8_t *y, int64_t y_plane, int64_t y_pitch, int64_t M, int64_t N, int64_t *C,

@@ -1,223 +1,442 @@
-// The batched-residue product for skinny right-hand sides, fused with the
-// residue split of that right-hand side (exact-solve, "Method": each lift
-// step applies every prime's inverse plane to the residual as one batched
-// INT8 product; the CRT of the wide digit follows).
+// The batched-residue lift step for skinny right-hand sides in one kernel
+// (exact-solve, "Method": each lift step applies every prime's inverse plane
+// to the residual as one batched INT8 product, and the CRT assembles the
+// wide digit).
 //
-// Y_j = (A_j @ (r mod q_j)) mod q_j, balanced, for every prime j, where A_j
-// is the caller's int8 plane j ([n][M][K], row-major, read as an integer
-// matrix mod q_j) and r is the int64 right-hand side [K][N] with N <= 16.
-// The product is memory-bound (K bytes of A per 2*16*K operations), so each
-// plane is streamed from HBM exactly once, straight into the operand
-// registers of v_mfma_i32_16x16x64_i8, while the small right-hand side is
-// reduced mod q_j into small int8 planes that the product kernel's
-// workgroups copy into LDS.
-//
-// Two kernels.  skinny_split_kernel reduces r mod every prime into int8
-// planes laid out as the products' MFMA operand wants them: rr[j][kc][g][c]
-// holds the 16 residues of r[64 kc + 16 g + t][c], t < 16 (zero past K and
-// past N), for the KC = ceil(K / 64) chunks.  skinny_kernel: workgroup
-// (j, b) owns rows 64 b .. 64 b + 63 of plane j, four waves of 16 rows (one
-// MFMA block each).  The product is latency-bound at this size, so every
-// load of a wave is issued at once: its row chunks (up to kSkRound of them
-// per round) and its share of rr[j], which the workgroup copies into LDS;
-// small LDS and register footprints keep several workgroups resident per
-// compute unit, which overlaps their memory latencies.
+// X = CRT_j (A_j @ r mod q_j) for A_j the caller's int8 plane j ([n][M][K],
+// row-major, read as an integer matrix mod q_j) and r the int64 right-hand
+// side [K][N], N <= 16, without a separate residue split or reconstruction
+// launch.  The products run on the raw bytes of r rather than on its
+// residues, which are the same for every modulus: with the top bit of every
+// byte but the top one flipped, r = sum_b a_b 256^b + c_1 (a_b the bytes as
+// int8, c_1 = 128 (1 + 256 + ... + 256^6)), so
+//   A_j r = sum_b 256^b P_b + c_1 s,   P_b = A_j a_b,  s = A_j 1 (row sums),
+// nine int8 products whose right-hand sides do not depend on j.  So one MFMA
+// (v_mfma_i32_16x16x64_i8) may mix rows of different moduli: a workgroup
+// takes four output rows for all n moduli, product row 4 j + x (modulus j,
+// row x), against the 16 columns of each byte of r and a column of ones
+// (|P_b| <= K 128 128 <= 2^30 for K <= 2^16).  Then per entry
+//   y = sum_b (256^b mod q) P_b + (c_1 mod q) s     (|y| < 2^41, exact in binary64)
+// and one rounding step gives its balanced residue.  The workgroup holds all
+// n residues of its 64 entries and reconstructs them itself with the
+// rounded-quotient CRT of rns_crt.hip (same constants, same arithmetic).
 //
 // Operand k-order: lane l of an MFMA operand holds row (or column) l % 16 and
 // the 16 bytes k = 64 kc + 16 (l / 16) + t, t < 16, of the 64-wide chunk kc
 // -- the same k for both operands, so the dot products pair every A byte
-// with the r residue of the same k whatever order the instruction adds them
+// with the byte of r at the same k whatever order the instruction adds them
 // in.  The accumulators hold entry (4 (l / 16) + e, l % 16) in element e of
 // lane l.
 #include "rns_device.h"
 
 namespace rns {
 
-constexpr int kSkRows = 64;           // rows of a plane per workgroup
-constexpr int kSkWaves = 4;           // 16 rows per wave
-constexpr int kSkRound = 16;          // 64-wide K chunks per wave loaded at once
+constexpr int kLsRows = 4;                          // output rows per workgroup
+constexpr int kLsWaves = 8;
+constexpr int kLsNB = 9;                            // byte blocks 0..7 of r, then the row sums
+constexpr int kLsPitch = 80;                        // LDS bytes per (byte, column): 64 k + 16 (banks)
+constexpr int kLsChunk = 8 * 16 * kLsPitch;         // one staged 64-wide K chunk of r's bytes
+constexpr int kLsPre = 4;                           // K chunks of A in flight per wave
+constexpr int kLsRAhead = 2;                        // chunks between a load of r and its staging (< 4)
+constexpr int kLsW = 12;                            // doubles per modulus: 256^b mod q (8), c_1, q, 1/q, pad
 
-// The balanced residue of a signed 64-bit value x mod q (q <= 256), exact.
-// With U = x + 2^63 (the top bit flipped; unsigned) and its bytes u_b,
-// x = sum_b u_b 256^b - 2^63, so x = t (mod q) for
-// t = sum_b u_b (256^b mod q) - (2^63 mod q), two four-byte dot products
-// against the packed constants wl (bytes 0..3) and wh (bytes 4..7);
-// 0 <= t + h < 8 * 255 * 256 < 2^21, so one binary32 rounding step balances it.
-struct ResidueConsts {
-    uint32_t wl, wh;                  // packed 256^b mod q, b = 0..3 and 4..7
-    int32_t h;                        // 2^63 mod q
-    float inv;                        // fl(1/q)
+struct LiftArgs {
+    const int8_t *a;                // planes [n][M][K]
+    const int64_t *r;               // [K][N]
+    int64_t *C;                     // [M][N][c_limbs]
+    uint32_t *status;               // the workspace's status header
+    int32_t M, N, K, KC, c_limbs, pair_stores;
 };
-struct ResidueTables {
-    ResidueConsts c[kMaxPrimes];
-};
-__device__ __forceinline__ int residue_i64(int64_t x, int q, const ResidueConsts &c) {
-    const uint32_t lo = (uint32_t)x, hi = (uint32_t)((uint64_t)x >> 32) ^ 0x80000000u;
-    const int t = (int)__builtin_amdgcn_udot4(hi, c.wh, __builtin_amdgcn_udot4(lo, c.wl, 0u, false), false) - c.h;
-    const int k = __float_as_int(__builtin_fmaf((float)t, c.inv, kRoundMagic32)) - 0x4b400000;
-    return __mul24(k, -q) + t;
+
+// the digit table is read as 32-bit words: it starts 4-byte aligned in the kernel arguments
+static_assert(sizeof(LiftArgs) % 8 == 0 && sizeof(StepConsts) % 4 == 0, "argument offsets");
+static_assert((kCrtSlots - 8) * kCrtDigits % 4 == 0, "whole words of digits");
+
+// 4 x 4 byte transpose: out[m] byte i = in[i] byte m
+__device__ __forceinline__ void transpose4(const uint32_t (&in)[4], uint32_t (&out)[4]) {
+    const uint32_t a = __builtin_amdgcn_perm(in[1], in[0], 0x05010400u);
+    const uint32_t b = __builtin_amdgcn_perm(in[3], in[2], 0x05010400u);
+    const uint32_t c = __builtin_amdgcn_perm(in[1], in[0], 0x07030602u);
+    const uint32_t d = __builtin_amdgcn_perm(in[3], in[2], 0x07030602u);
+    out[0] = __builtin_amdgcn_perm(b, a, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(b, a, 0x07060302u);
+    out[2] = __builtin_amdgcn_perm(d, c, 0x05040100u);
+    out[3] = __builtin_amdgcn_perm(d, c, 0x07060302u);
 }
 
-struct SkinnyArgs {
-    const int8_t *a;                  // planes [n][M][K]
-    const int64_t *r;                 // right-hand side [K][N]
-    int8_t *rr;                       // residue planes of r [n][KC][4][16][16]
-    int8_t *y;                        // product planes [n][.][y_pitch]
-    uint32_t *status;                 // the workspace's status header
-    int64_t y_plane, y_pitch;
-    int32_t n, M, N, K, KC;
-    int32_t row_blocks;
-};
+template <int MBW, int KS, int NB>
+__global__ __launch_bounds__(64 * kLsWaves) void lift_step_kernel(LiftArgs g, StepConsts lc, CrtDigits cd) {
+    constexpr int W = 8 * NB;                        // 32-bit words of X'
+    __shared__ __align__(16) uint8_t rT[4][kLsChunk];          // r's bytes of K chunks: [b][column][k]
+    __shared__ __align__(16) int8_t Yl[kLsRows * 16][64];      // residues: [entry][modulus]
+    __shared__ v4i dT[kCrtDigits][kCrtSlots / 16];              // CRT digits, digit-major
+    __shared__ __align__(16) double wt[kMaxPrimes][kLsW];      // per-modulus weights
+    __shared__ v4i fxl[2][2][4];                                // fixed-point fragments
 
-// thread (quad, column, prime): four consecutive k of one column, one 32-bit
-// word of the residue plane
-__global__ __launch_bounds__(256) void skinny_split_kernel(SkinnyArgs g, EpiConsts ec, ResidueTables rt) {
-    const int nq = g.KC * 16;                         // quads per column
-    const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t per_prime = (int64_t)nq * 16;
-    const int j = (int)(id / per_prime);
-    const int rem = (int)(id - (int64_t)j * per_prime);
-    const int quad = rem >> 4, c = rem & 15;
-    if (id == 0) {
-        // no bound is checked on this path: a header of zero blocks (no flags)
-        g.status[0] = 0u;
-        g.status[1] = kStatusCheck;
-    }
-    if (j >= g.n) return;
-    const int q = ec.q[j];
-    const ResidueConsts rc = rt.c[j];
-    const int k0 = 4 * quad;
-    const int cc = min(c, g.N - 1);
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int k = k0 + i;
-        const int64_t x = g.r[(uint32_t)(min(k, g.K - 1) * g.N + cc)];
-        const int res = residue_i64(x, q, rc);
-        word |= (uint32_t)((k < g.K && c < g.N) ? (res & 0xff) : 0) << (8 * i);
-    }
-    const int kc = k0 >> 6, grp = (k0 >> 4) & 3, t = k0 & 15;
-    uint32_t *dst = (uint32_t *)(g.rr + (int64_t)j * g.KC * 1024);
-    dst[(((kc * 4 + grp) * 16 + c) * 16 + t) >> 2] = word;
-}
-
-// KCP: 64-wide chunks of K, padded (a multiple of kSkRound, or less than it)
-template <int KCP>
-__global__ __launch_bounds__(64 * kSkWaves) void skinny_kernel(SkinnyArgs g, EpiConsts ec) {
-    constexpr int R = KCP < kSkRound ? KCP : kSkRound;         // chunks per round
-    static_assert(KCP % R == 0, "whole rounds");
-    constexpr int kPieces = KCP * 64 / (64 * kSkWaves);       // 16-byte pieces of rr per thread
-    static_assert(kPieces * 64 * kSkWaves == KCP * 64, "rr pieces spread evenly");
-    __shared__ v4i rl[KCP][4][16];                             // residues of r mod q_j: [chunk][lane group][column]
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = blockIdx.x / g.row_blocks, rb = blockIdx.x - j * g.row_blocks;
-    const int q = ec.q[j];
-    const double inv = ec.inv[j];
-    const int KC = g.KC;                               // chunks holding data (K is a multiple of 16)
+    const int h = lane >> 5, l32 = lane & 31, g16 = lane >> 4, c16 = lane & 15;
+    const int n = lc.n, M = g.M, N = g.N, K = g.K, KC = g.KC;
+    const int MB = (4 * n + 15) >> 4;                // 16-row blocks of (modulus, row) pairs
+    const int i0 = blockIdx.x * kLsRows;
 
-    // this lane's A row (clamped into the plane; rows past M are computed and dropped)
-    const int row = min(rb * kSkRows + wave * 16 + (lane & 15), g.M - 1);
-    const int8_t *pa = g.a + (int64_t)j * g.M * g.K + (int64_t)row * g.K + 16 * (lane >> 4);
-    // Loads are unconditional, so that the counter waits stay exact: a chunk
-    // past the last re-reads the last, and within the last chunk a lane group
-    // past K re-reads the row's last 16 bytes; the zero residues of those k
-    // cancel whatever they read.
-    auto load = [&](int kc) {
-        const int off = min(min(kc, KC - 1) * 64, g.K - 16 - 16 * (lane >> 4));
-        return *(const v4i *)(pa + off);
+    // this lane's A rows: block m = wave + 8 i, product row 16 m + c16 = 4 j + x
+    const int8_t *arow[MBW];
+#pragma unroll
+    for (int i = 0; i < MBW; i++) {
+        const int mi = 16 * (wave + kLsWaves * i) + c16;
+        const int j = min(mi >> 2, n - 1);
+        const int row = min(i0 + (mi & 3), M - 1);
+        arow[i] = g.a + ((int64_t)j * M + row) * K + 16 * g16;
+    }
+    // Each workgroup walks the K chunks from its own first chunk (the sums are
+    // exact in any order), so that the workgroups do not all read the same
+    // rows of r at once; steps past KC stay in place (they carry no data).
+    const int rot = blockIdx.x % KC;
+    auto cmap = [&](int kc) { return kc >= KC ? kc : (kc + rot >= KC ? kc + rot - KC : kc + rot); };
+    // unconditional loads: a step past the last re-reads the last chunk, and a
+    // lane group past K re-reads the row's last 16 bytes (r's bytes there are zero)
+    auto aload = [&](int i, int kc) {
+        const int off = min(cmap(min(kc, KC - 1)) * 64, K - 16 - 16 * g16);
+        return *(const v4i *)(arow[i] + off);
+    };
+    // every thread stages a quarter column of r per chunk: column t % 16,
+    // k = 64 kc + 4 ((t / 16) % 16) + u (u < 4), the low (t < 256) or high
+    // 32-bit half of each value.  The raw words are loaded ahead (a k past
+    // K reads row K - 1, a column past N column N - 1: 32-bit offsets, no
+    // branch) and flipped and masked only when staged, so no load is waited
+    // for early; every wave issues the same loads.  K is a multiple of 16,
+    // so a thread's four k are all below K or all past it.
+    const int sc = tid & 15, sk = 4 * ((tid >> 4) & 15), half = tid >> 8;
+    const uint32_t rrow = 8u * (uint32_t)N;                          // bytes per k of r
+    const uint32_t rcol = 8u * (uint32_t)min(sc, N - 1) + 4u * (uint32_t)half;
+    const uint32_t rflip = half ? 0x00808080u : 0x80808080u;
+    const uint32_t rcmask = sc < N ? 0xffffffffu : 0u;
+    const char *rbase = (const char *)g.r;
+    auto rload = [&](int kc, uint32_t (&v)[4]) {
+        const int k0 = 64 * cmap(kc) + sk;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint32_t kk = (uint32_t)min(k0 + u, K - 1);
+            v[u] = *(const uint32_t *)(rbase + (__umul24(kk, rrow) + rcol));
+        }
+    };
+    auto rstage = [&](const uint32_t (&v)[4], int kc, int buf) {
+        const uint32_t m = 64 * cmap(kc) + sk < K ? rcmask : 0u;
+        uint32_t x[4], w[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) x[u] = (v[u] ^ rflip) & m;
+        transpose4(x, w);
+#pragma unroll
+        for (int b = 0; b < 4; b++) *(uint32_t *)&rT[buf][((4 * half + b) * 16 + sc) * kLsPitch + sk] = w[b];
     };
 
-    // rr[j] pieces first (a piece past KC chunks re-reads one of them and is
-    // replaced by zero), then the first round of row chunks
-    const v4i *src = (const v4i *)(g.rr + (int64_t)j * KC * 1024);
-    v4i rv[kPieces];
+    // The first loads go out before the constants.  Chunk c of r is staged
+    // in LDS buffer c % 4 two steps before its products, and loaded kLsRAhead
+    // steps before that (rv[c % 4] holds it); the B fragments of a chunk are
+    // read one step ahead, so the LDS reads overlap the products; A is
+    // loaded kLsPre steps ahead of its use.  The step count is rounded up to
+    // whole groups of kLsPre (steps past KC have zero bytes of r and no
+    // ones), so the unrolled loop has no early exit and the counter waits
+    // stay exact.
+    static_assert(kLsPre % 4 == 0 && kLsRAhead >= 1 && kLsRAhead <= 2, "ring indices are compile-time");
+    const int KCR = (KC + kLsPre - 1) / kLsPre * kLsPre;
+    uint32_t rv[4][4];
+    rload(0, rv[0]);
+    rload(1, rv[1]);
+    v4i abuf[kLsPre][MBW];
 #pragma unroll
-    for (int i = 0; i < kPieces; i++) {
-        const int piece = tid + i * 64 * kSkWaves;
-        rv[i] = src[piece < KC * 64 ? piece : piece % (KC * 64)];
-    }
-    v4i abuf[R];
+    for (int p = 0; p < kLsPre; p++)
 #pragma unroll
-    for (int c = 0; c < R; c++) abuf[c] = load(c);
-    __builtin_amdgcn_s_waitcnt(0x0f70 | (R & 15) | ((R >> 4) << 14));   // rr pieces in; row chunks may pend
+        for (int i = 0; i < MBW; i++) abuf[p][i] = aload(i, p);
 #pragma unroll
-    for (int i = 0; i < kPieces; i++) {
-        const int piece = tid + i * 64 * kSkWaves;
-        (&rl[0][0][0])[piece] = piece < KC * 64 ? rv[i] : v4i{0, 0, 0, 0};
-    }
-    __syncthreads();
+    for (int c = 2; c < 2 + kLsRAhead; c++) rload(c, rv[c]);
 
-    v4i acc = {0, 0, 0, 0};
+    // the constants are loaded now and laid out in LDS after the products:
+    // the CRT digits (as 32-bit words of the slot-major table), the weights
+    // of modulus tid, the fixed-point fragments
+    constexpr int kWords = (kCrtSlots - 8) * kCrtDigits / 4;
+    uint32_t cwd[2], ctb[2] = {0u, 0u}, cfx = 0u;
+    int cq = 3, cc1 = 0;
+    {
+        const uint32_t *src = (const uint32_t *)&cd.d[0][0];
 #pragma unroll
-    for (int r0 = 0; r0 < KCP; r0 += R) {
+        for (int x = 0; x < 2; x++) cwd[x] = src[min(tid + 512 * x, kWords - 1)];
+        if (tid < n) {
+            ctb[0] = lc.tb[tid][0];
+            ctb[1] = lc.tb[tid][1];
+            cq = lc.q[tid];
+            cc1 = lc.c1[tid];
+        }
+        if (tid < 64) cfx = (&lc.fx[0][0][0][0])[tid];
+    }
+    if (blockIdx.x == 0 && tid == 0) {
+        g.status[0] = 0u;                            // no bound is checked: no blocks, no flags
+        g.status[1] = kStatusCheck;
+    }
+
+    rstage(rv[0], 0, 0);
+    rstage(rv[1], 1, 1);
+
+    v4i acc[MBW][kLsNB];
 #pragma unroll
-        for (int c = 0; c < R; c++) {
-            const v4i bv = rl[r0 + c][lane >> 4][lane & 15];
-            acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(abuf[c], bv, acc, 0, 0, 0);
-            if (r0 + R < KCP) abuf[c] = load(r0 + R + c);
+    for (int i = 0; i < MBW; i++)
+#pragma unroll
+        for (int nb = 0; nb < kLsNB; nb++) acc[i][nb] = v4i{0, 0, 0, 0};
+    auto lds_barrier = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    v4i bf[2][8];
+    lds_barrier();
+#pragma unroll
+    for (int b = 0; b < 8; b++) bf[0][b] = *(const v4i *)&rT[0][(b * 16 + c16) * kLsPitch + 16 * g16];
+
+    for (int kc0 = 0; kc0 < KCR; kc0 += kLsPre) {
+#pragma unroll
+        for (int p = 0; p < kLsPre; p++) {
+            const int kc = kc0 + p;
+            // no instruction crosses into another chunk's step: the staging
+            // of r stays behind its loads
+            __builtin_amdgcn_sched_barrier(0);
+            // chunk kc + 1 is staged, and buffer (kc + 2) % 4 is no longer read
+            lds_barrier();
+#pragma unroll
+            for (int b = 0; b < 8; b++)
+                bf[(p + 1) & 1][b] = *(const v4i *)&rT[(p + 1) & 3][(b * 16 + c16) * kLsPitch + 16 * g16];
+            __builtin_amdgcn_sched_barrier(0);      // the reads go out before this step's products
+            rstage(rv[(p + 2) & 3], kc + 2, (p + 2) & 3);
+            rload(kc + 2 + kLsRAhead, rv[(p + 2 + kLsRAhead) & 3]);
+            // the row-sum column: ones for k < K (K is a multiple of 16)
+            const int one = K - (64 * cmap(kc) + 16 * g16) > 0 ? 0x01010101 : 0;
+            const v4i ones = v4i{one, one, one, one};
+            // the products read abuf[p] before the load of chunk kc + kLsPre
+            // replaces it, so the loop carries A in fixed registers
+#pragma unroll
+            for (int i = 0; i < MBW; i++) {
+#pragma unroll
+                for (int nb = 0; nb < 8; nb++)
+                    acc[i][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(abuf[p][i], bf[p & 1][nb], acc[i][nb], 0, 0, 0);
+                acc[i][8] = __builtin_amdgcn_mfma_i32_16x16x64_i8(abuf[p][i], ones, acc[i][8], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < MBW; i++) abuf[p][i] = aload(i, kc + kLsPre);
         }
     }
 
-    // balanced residues mod q, one byte per entry (q = 2: the low bit)
-    const int col = lane & 15;
-    if (col < g.N) {
-        int8_t *yp = g.y + (int64_t)j * g.y_plane + col;
+    // (the values are only used from here on, so no wait for them is hoisted into the loads' shadow)
+    asm volatile("" : "+v"(cwd[0]), "+v"(cwd[1]), "+v"(ctb[0]), "+v"(ctb[1]), "+v"(cq), "+v"(cc1), "+v"(cfx));
+    {
+        int8_t *t = (int8_t *)&dT[0][0];
+#pragma unroll
+        for (int x = 0; x < 2; x++) {
+            const int w = tid + 512 * x;
+            if (w < kWords)
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    const int i = 4 * w + e, k = i / kCrtDigits, c = i - k * kCrtDigits;
+                    t[c * kCrtSlots + k] = (int8_t)(cwd[x] >> (8 * e));
+                }
+        }
+        if (tid < kCrtDigits * 8) t[(tid >> 3) * kCrtSlots + kCrtSlots - 8 + (tid & 7)] = 0;
+        if (tid < n) {
+#pragma unroll
+            for (int b = 0; b < 8; b++) wt[tid][b] = (double)(int8_t)(ctb[b >> 2] >> (8 * (b & 3)));
+            wt[tid][8] = (double)cc1;
+            wt[tid][9] = (double)cq;
+            wt[tid][10] = 1.0 / (double)cq;
+            wt[tid][11] = 0.0;
+        }
+        if (tid < 64) ((uint32_t *)&fxl[0][0][0])[tid] = cfx;
+        ((uint32_t *)&Yl[0][0])[tid] = 0u;
+        ((uint32_t *)&Yl[0][0])[tid + 512] = 0u;
+    }
+    __syncthreads();
+
+    // residues: element e of lane (g16, c16) in block m is product row
+    // 16 m + 4 g16 + e, i.e. modulus j = 4 m + g16, row e, column c16
+#pragma unroll
+    for (int i = 0; i < MBW; i++) {
+        const int m = wave + kLsWaves * i;
+        const int j = 4 * m + g16;
+        if (m >= MB || j >= n) continue;
+        double w[kLsW];
+#pragma unroll
+        for (int x = 0; x < kLsW; x += 2) {
+            const auto v = *(const double2 *)&wt[j][x];
+            w[x] = v.x;
+            w[x + 1] = v.y;
+        }
 #pragma unroll
         for (int e = 0; e < 4; e++) {
-            const int rw = rb * kSkRows + wave * 16 + 4 * (lane >> 4) + e;
-            if (rw < g.M) {
-                const int s = acc[e];
-                yp[(int64_t)rw * g.y_pitch] = (int8_t)(q == 2 ? (s & 1) : reduce_low_byte(s, q, inv));
+            double y = w[8] * (double)acc[i][8][e];
+#pragma unroll
+            for (int b = 0; b < 8; b++) y = __builtin_fma(w[b], (double)acc[i][b][e], y);
+            // |y| < 2^41: y w[10] is within 2^-12 of y / q, so the rounding
+            // to an integer (the 1.5 * 2^52 sum) gives round(y / q)
+            const double kq = __builtin_fma(y, w[10], kRoundMagic) - kRoundMagic;
+            Yl[e * 16 + c16][j] = (int8_t)(int)__builtin_fma(-w[9], kq, y);
+        }
+    }
+    __syncthreads();
+
+    // the CRT of the workgroup's 64 entries: wave cw < 2 takes entries
+    // 32 cw + l32 (row 2 cw + l32 / 16, column l32 % 16)
+    if (wave >= 2) return;
+    const int ent = 32 * wave + l32;
+    v4i dig[KS][NB], fx[KS], ua[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) {
+#pragma unroll
+        for (int nb = 0; nb < NB; nb++) {
+            const int c = 32 * nb + l32;
+            dig[ks][nb] = c < kCrtDigits ? dT[c][2 * ks + h] : v4i{0, 0, 0, 0};
+        }
+        fx[ks] = l32 < 8 ? fxl[ks][h][l32 & 3] : v4i{0, 0, 0, 0};
+        ua[ks] = *(const v4i *)&Yl[ent][32 * ks + 16 * h];
+    }
+    // F = sum_k y_k c_k from the four digit sums (rows 0-3, repeated in 4-7)
+    v16i fs = v16i{0};
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) fs = __builtin_amdgcn_mfma_i32_32x32x32_i8(fx[ks], ua[ks], fs, 0, 0, 0);
+    const int64_t F = (int64_t)fs[0] + (int64_t)fs[1] * 256 + (int64_t)fs[2] * 65536 + (int64_t)fs[3] * 16777216;
+    const int64_t r64 = (F + (1ll << 30)) >> 31;
+    const int64_t fr = F - r64 * (1ll << 31);
+    const bool near_half = fr < -(1ll << 30) + (1ll << 21) || fr >= (1ll << 30) - (1ll << 21);
+    const int r = (int)r64;
+    const int rlo = ((r + 127) & 255) - 127;
+    const int rhi = (r - rlo) >> 8;
+#pragma unroll
+    for (int t = 0; t < 2; t++) {
+        const int k = n + t, val = t ? -rhi : -rlo;
+        const int ks_k = k >> 5, h_k = (k >> 4) & 1, x_k = (k >> 2) & 3, sh = 8 * (k & 3);
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+            for (int x = 0; x < 4; x++)
+                if (ks == ks_k && x == x_k && h == h_k)
+                    ua[ks][x] = (int)(((uint32_t)ua[ks][x] & ~(0xffu << sh)) | ((uint32_t)(val & 0xff) << sh));
+    }
+    v16i accd[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++) {
+        accd[nb] = v16i{0};
+#pragma unroll
+        for (int ks = 0; ks < KS; ks++)
+            accd[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[ks][nb], ua[ks], accd[nb], 0, 0, 0);
+    }
+    int part[2 * W];
+#pragma unroll
+    for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) {
+            const v16i &a = accd[nb];
+            const int lo = a[4 * gq] + (a[4 * gq + 1] << 8);
+            const int hi = a[4 * gq + 2] + (a[4 * gq + 3] << 8);
+            const auto sl = __builtin_amdgcn_permlane32_swap((uint32_t)lo, (uint32_t)lo, false, false);
+            const auto sh = __builtin_amdgcn_permlane32_swap((uint32_t)hi, (uint32_t)hi, false, false);
+            const int w0 = 8 * nb + 2 * gq;
+            part[2 * w0] = (int)sl[0];
+            part[2 * w0 + 1] = (int)sh[0];
+            part[2 * w0 + 2] = (int)sl[1];
+            part[2 * w0 + 3] = (int)sh[1];
+        }
+    uint32_t wv[W];
+    int c16c = 0;
+#pragma unroll
+    for (int w = 0; w < W; w++) {
+        const int t0 = part[2 * w] + c16c;
+        const int t1 = part[2 * w + 1] + (t0 >> 16);
+        c16c = t1 >> 16;
+        wv[w] = __builtin_amdgcn_perm((uint32_t)t1, (uint32_t)t0, 0x05040100u);
+    }
+    int64_t carry = c16c;
+    if (near_half) {
+        int64_t bm = 0, bp = 0;
+        uint32_t nzm = 0, nzp = 0;
+#pragma unroll
+        for (int w = 0; w < W; w++) {
+            const uint32_t two = (wv[w] << 1) | (w ? (wv[w - 1] >> 31) : 0u);
+            const uint32_t pw = w < 16 ? lc.P[w] : 0u;
+            const int64_t dm = (int64_t)two - pw + bm;
+            const int64_t dp = (int64_t)two + pw + bp;
+            nzm |= (uint32_t)dm;
+            nzp |= (uint32_t)dp;
+            bm = dm >> 32;
+            bp = dp >> 32;
+        }
+        const int64_t top2 = 2 * carry + (int64_t)(wv[W - 1] >> 31);
+        const int64_t tm = top2 + bm, tp = top2 + bp;
+        const bool above = tm > 0 || (tm == 0 && nzm != 0);
+        const bool below = tp < 0 || (tp == 0 && nzp == 0);
+        if (above || below) {
+            int64_t c2 = 0;
+#pragma unroll
+            for (int w = 0; w < W; w++) {
+                const int64_t pw = w < 16 ? (int64_t)lc.P[w] : 0;
+                c2 += (int64_t)wv[w] + (above ? -pw : pw);
+                wv[w] = (uint32_t)c2;
+                c2 >>= 32;
+            }
+            carry += c2;
+        }
+    }
+    const int row = i0 + (ent >> 4), col = ent & 15;
+    if (row < M && col < N) {
+        int64_t *ce = g.C + ((int64_t)row * N + col) * g.c_limbs;
+        const uint32_t sign = (uint32_t)carry;
+#pragma unroll
+        for (int t = 0; t < RNS_MAX_OUT_LIMBS / 4; t++) {
+            uint32_t wd[4];
+#pragma unroll
+            for (int ii = 0; ii < 4; ii++) {
+                const int ia = 8 * t + ii, ib = 8 * t + 4 + ii;
+                const uint32_t a0 = ia < W ? wv[ia] : sign, a1 = ib < W ? wv[ib] : sign;
+                wd[ii] = h ? a1 : a0;
+            }
+            const int l = 4 * t + 2 * h;
+            if (g.pair_stores) {
+                if (l < g.c_limbs) *(v4u *)(ce + l) = v4u{wd[0], wd[1], wd[2], wd[3]};
+            } else {
+                if (l < g.c_limbs) ce[l] = (int64_t)(((uint64_t)wd[1] << 32) | wd[0]);
+                if (l + 1 < g.c_limbs) ce[l + 1] = (int64_t)(((uint64_t)wd[3] << 32) | wd[2]);
             }
         }
     }
 }
 
-int64_t skinny_rr_bytes(int n, int64_t K) { return (int64_t)n * ((K + 63) / 64) * 1024; }
-
-int launch_skinny(int n, const int8_t *a, const int64_t *r, int64_t M, int64_t N, int64_t K, int8_t *rr,
-                  int8_t *y, int64_t y_plane, int64_t y_pitch, uint32_t *status, const EpiConsts &c,
-                  hipStream_t s) {
-    if (n < 1 || n > kMaxPrimes || M < 1 || N < 1 || N > 16 || K < 16 || K % 16 || K > RNS_SKINNY_K_MAX ||
-        M > (1 << 24) || (reinterpret_cast<uintptr_t>(a) & 15) || (reinterpret_cast<uintptr_t>(rr) & 15))
+int launch_lift_step(const StepConsts &lc, const CrtDigits &cd, int ksteps, int nblocks, const int8_t *a,
+                     const int64_t *r, int64_t M, int64_t N, int64_t K, int64_t *C, int32_t c_limbs,
+                     uint32_t *status, hipStream_t s) {
+    const int n = lc.n;
+    if (n < 1 || n > kMaxPrimes || M < 1 || N < 1 || N > 16 || K < 16 || K % 16 || K > RNS_LIFT_K_MAX ||
+        M > (1 << 30) || (reinterpret_cast<uintptr_t>(a) & 15) || !r || !C || !status || c_limbs < 1 ||
+        c_limbs > RNS_MAX_OUT_LIMBS || ksteps < 1 || ksteps > 2 || nblocks < 1 || nblocks > 2 ||
+        n + 2 > 32 * ksteps)
         return RNS_E_ARG;
-    const int64_t row_blocks = (M + kSkRows - 1) / kSkRows;
-    const int64_t grid = row_blocks * n;
-    if (grid > 0x7fffffff || (int64_t)n * M * K > ((int64_t)1 << 40)) return RNS_E_ARG;
-    const int64_t kc = (K + 63) / 64;
-    SkinnyArgs g{a, r, rr, y, status, y_plane, y_pitch, (int32_t)n, (int32_t)M, (int32_t)N, (int32_t)K, (int32_t)kc,
-                 (int32_t)row_blocks};
-    // per prime: the packed byte weights 256^b mod q, 2^63 mod q and fl(1/q)
-    ResidueTables rt;
-    for (int jj = 0; jj < n; jj++) {
-        const uint32_t q = (uint32_t)c.q[jj];
-        uint32_t p = 1, w[2] = {0, 0};
-        for (int b = 0; b < 8; b++) {
-            w[b >> 2] |= (p % q) << (8 * (b & 3));
-            p = (p * 256u) % q;
-        }
-        rt.c[jj].wl = w[0];
-        rt.c[jj].wh = w[1];
-        rt.c[jj].h = (int32_t)((((w[1] >> 24) & 0xffu) * 128u) % q);   // 2^63 = 256^7 * 128
-        rt.c[jj].inv = 1.0f / (float)q;
+    LiftArgs g{};
+    g.a = a;
+    g.r = r;
+    g.C = C;
+    g.status = status;
+    g.M = (int32_t)M;
+    g.N = (int32_t)N;
+    g.K = (int32_t)K;
+    g.KC = (int32_t)((K + 63) / 64);
+    g.c_limbs = c_limbs;
+    g.pair_stores = (reinterpret_cast<uintptr_t>(C) % 16 == 0 && c_limbs % 2 == 0) ? 1 : 0;
+    const int mb = (4 * n + 15) / 16, mbw = (mb + kLsWaves - 1) / kLsWaves;
+    const dim3 grid((unsigned)((M + kLsRows - 1) / kLsRows)), block(64 * kLsWaves);
+#define RNS_LS(MBW_, KS_, NB_) hipLaunchKernelGGL((lift_step_kernel<MBW_, KS_, NB_>), grid, block, 0, s, g, lc, cd)
+    if (mbw == 1) {
+        if (ksteps == 1) { if (nblocks == 1) RNS_LS(1, 1, 1); else RNS_LS(1, 1, 2); }
+        else { if (nblocks == 1) RNS_LS(1, 2, 1); else RNS_LS(1, 2, 2); }
+    } else {
+        if (ksteps == 1) { if (nblocks == 1) RNS_LS(2, 1, 1); else RNS_LS(2, 1, 2); }
+        else { if (nblocks == 1) RNS_LS(2, 2, 1); else RNS_LS(2, 2, 2); }
     }
-    const int64_t split_threads = (int64_t)n * kc * 16 * 16;
-    hipLaunchKernelGGL(skinny_split_kernel, dim3((unsigned)((split_threads + 255) / 256)), dim3(256), 0, s, g, c, rt);
-    if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
-    const dim3 gr((unsigned)grid), bl(64 * kSkWaves);
-    if (kc <= 4)
-        hipLaunchKernelGGL((skinny_kernel<4>), gr, bl, 0, s, g, c);
-    else if (kc <= 8)
-        hipLaunchKernelGGL((skinny_kernel<8>), gr, bl, 0, s, g, c);
-    else if (kc <= 16)
-        hipLaunchKernelGGL((skinny_kernel<16>), gr, bl, 0, s, g, c);
-    else if (kc <= 32)
-        hipLaunchKernelGGL((skinny_kernel<32>), gr, bl, 0, s, g, c);
-    else
-        hipLaunchKernelGGL((skinny_kernel<64>), gr, bl, 0, s, g, c);
+#undef RNS_LS
     return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
 }
 

@@ -187,6 +187,12 @@ int rns_gemm(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
  * B: device int64 [K][N][b_limbs], reduced per prime by the split kernel.
  * C: device int64 [M][N][c_limbs]: the unique X in the plan's representative
  *   range with X = A_res[j] @ B (mod primes[j]) for every j.
+ * When N <= 16, b_limbs == 1, K is a multiple of 16 up to 2^16, the plan
+ * declares no bound for B (b_bits < 0 or >= 63) and A_res is 16-byte
+ * aligned, the whole call is one kernel: the products run on the bytes of
+ * B, which every prime shares, and each workgroup reconstructs its own
+ * entries; the workspace then holds only the status header (zero blocks)
+ * afterwards, not residue planes.  Otherwise the three stage kernels run.
  * Returns as rns_gemm.
  */
 int rns_gemm_batched_residue(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,

@@ -58,11 +58,13 @@ int launch_zero(int64_t *, int64_t count, hipStream_t) {
     return RNS_OK;
 }
 
-int64_t skinny_rr_bytes(int n, int64_t K) { return (int64_t)n * ((K + 63) / 64) * 1024; }
-
-int launch_skinny(int n, const int8_t *, const int64_t *, int64_t M, int64_t N, int64_t K, int8_t *, int8_t *,
-                  int64_t, int64_t, uint32_t *status, const EpiConsts &, hipStream_t) {
-    require(n >= 1 && M >= 1 && N >= 1 && N <= 16 && K % 16 == 0 && status != nullptr, "skinny arguments");
+int launch_lift_step(const StepConsts &lc, const CrtDigits &, int ksteps, int nblocks, const int8_t *a,
+                     const int64_t *r, int64_t M, int64_t N, int64_t K, int64_t *C, int32_t c_limbs,
+                     uint32_t *status, hipStream_t) {
+    require(lc.n >= 1 && a && r && C && M >= 1 && N >= 1 && N <= 16 && K % 16 == 0 && K <= RNS_LIFT_K_MAX &&
+                status != nullptr && lc.n + 2 <= 32 * ksteps && nblocks >= 1 && nblocks <= 2 && c_limbs >= 1,
+            "lift step arguments");
+    for (int j = 0; j < lc.n; j++) require(lc.q[j] >= 2 && lc.q[j] <= 256 && lc.c1[j] < lc.q[j], "lift tables");
     return RNS_OK;
 }
 

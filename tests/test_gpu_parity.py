@@ -449,10 +449,12 @@ def test_batched_residue_any_int8_and_extremes():
 
 
 # The skinny right-hand side (N <= 16, one limb, K a multiple of 16 up to
-# 4096) takes the fused split-and-products kernel: ragged rows (not a
-# multiple of the 256-row blocks), every column count, K not a multiple of
-# the 64-wide chunks, all 54 primes or a few, the prime-power moduli (256
-# included), any int8 plane values and right-hand sides at the int64 ends.
+# 2^16) takes the one-kernel step (products on r's bytes, residues, CRT):
+# ragged rows (not a multiple of the 4-row workgroups), every column count,
+# K not a multiple of the 64-wide chunks nor of the 4-chunk loop groups,
+# more K chunks than workgroups and the reverse, all 54 primes or a few,
+# the prime-power moduli (256 included), any int8 plane values and
+# right-hand sides at the int64 ends.
 SKINNY = [
     # M, N, K, n, prime_powers, seed
     (1, 1, 16, 1, False, 91),
@@ -462,6 +464,8 @@ SKINNY = [
     (256, 3, 4096, 54, False, 95),
     (777, 16, 208, 54, True, 96),
     (64, 1, 4096, 6, True, 97),
+    (33, 5, 4112, 20, True, 98),
+    (6, 16, 12352, 54, False, 99),
 ]
 
 
@@ -488,6 +492,23 @@ def test_batched_residue_skinny_fused(M, N, K, n, pp, seed):
     rg.residue_products(p, M, N, K, ws, A_res=Ad)
     rg.reconstruct(p, M, N, K, ws, out, batched=True)
     assert np.array_equal(out.cpu().numpy(), X)
+
+
+def test_batched_residue_skinny_int32_edge():
+    """K = 2^16 with every plane entry -128 and r = -2^63 (every flipped byte
+    -128): each of the nine int32 byte products reaches 2^30."""
+    K = 2 ** 16
+    p = rg.plan_n(54)
+    M, N = 5, 3
+    A_res = np.full((54, M, K), -128, dtype=np.int8)
+    A_res[:, 2, :] = 127
+    r = np.full((K, N), -(2 ** 63), dtype=np.int64)
+    r[:, 1] = 2 ** 63 - 1
+    ws0 = rg.new_workspace(p, M, N, K, True)
+    X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
+    ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
+    assert np.array_equal(O.decode_array(X), ref)
+    assert rg.status(ws0) == 0
 
 
 # ---------------------------------------------------------------------------
