@@ -34,10 +34,10 @@ namespace rns {
 constexpr int kLsRows = 4;                          // output rows per workgroup
 constexpr int kLsWaves = 8;
 constexpr int kLsNB = 9;                            // byte blocks 0..7 of r, then the row sums
-constexpr int kLsPitch = 80;                        // LDS bytes per (byte, column): 64 k + 16 (banks)
-constexpr int kLsChunk = 8 * 16 * kLsPitch;         // one staged 64-wide K chunk of r's bytes
+constexpr int kLsPhase = 16;                        // 64-wide K chunks of r held in LDS at once
+constexpr int kLsRowPitch = 64 * kLsPhase + 16;     // LDS bytes per (column, byte) row: a phase of k, + 16
+constexpr int kLsColPitch = 8 * kLsRowPitch + 16;   // LDS bytes per column (its eight byte rows), + 16
 constexpr int kLsPre = 4;                           // K chunks of A in flight per wave
-constexpr int kLsRAhead = 2;                        // chunks between a load of r and its staging (< 4)
 constexpr int kLsW = 12;                            // doubles per modulus: 256^b mod q (8), c_1, q, 1/q, pad
 
 struct LiftArgs {
@@ -51,6 +51,13 @@ struct LiftArgs {
 // the digit table is read as 32-bit words: it starts 4-byte aligned in the kernel arguments
 static_assert(sizeof(LiftArgs) % 8 == 0 && sizeof(StepConsts) % 4 == 0, "argument offsets");
 static_assert((kCrtSlots - 8) * kCrtDigits % 4 == 0, "whole words of digits");
+static_assert(kLsPhase % kLsPre == 0 && kLsRowPitch % 16 == 0 && kLsColPitch % 16 == 0,
+              "phases of whole loop groups, aligned rows");
+// the 16 columns of a fragment read fall in distinct groups of four banks
+static_assert((kLsColPitch / 4) % 64 % 8 == 4, "column pitch: an odd multiple of 16 bytes modulo 256");
+// one base register per lane reaches all eight byte rows of a column within a
+// phase through the 16-bit offset of an LDS instruction
+static_assert(8 * kLsRowPitch < 65536, "byte rows within the offset range");
 
 // 4 x 4 byte transpose: out[m] byte i = in[i] byte m
 __device__ __forceinline__ void transpose4(const uint32_t (&in)[4], uint32_t (&out)[4]) {
@@ -64,10 +71,13 @@ __device__ __forceinline__ void transpose4(const uint32_t (&in)[4], uint32_t (&o
     out[3] = __builtin_amdgcn_perm(d, c, 0x07060302u);
 }
 
+// r's bytes for up to kLsPhase chunks are staged in LDS at once ([column][byte][k]:
+// kLsRowPitch bytes per row, kLsColPitch per column), so the products run with no
+// barrier inside a phase: one phase for K <= 1024, a new staging per further 1024.
 template <int MBW, int KS, int NB>
 __global__ __launch_bounds__(64 * kLsWaves) void lift_step_kernel(LiftArgs g, StepConsts lc, CrtDigits cd) {
     constexpr int W = 8 * NB;                        // 32-bit words of X'
-    __shared__ __align__(16) uint8_t rT[4][kLsChunk];          // r's bytes of K chunks: [b][column][k]
+    __shared__ __align__(16) uint8_t rT[16 * kLsColPitch];     // r's bytes of a phase: [column][b][k]
     __shared__ __align__(16) int8_t Yl[kLsRows * 16][64];      // residues: [entry][modulus]
     __shared__ v4i dT[kCrtDigits][kCrtSlots / 16];              // CRT digits, digit-major
     __shared__ __align__(16) double wt[kMaxPrimes][kLsW];      // per-modulus weights
@@ -80,6 +90,51 @@ __global__ __launch_bounds__(64 * kLsWaves) void lift_step_kernel(LiftArgs g, St
     const int MB = (4 * n + 15) >> 4;                // 16-row blocks of (modulus, row) pairs
     const int i0 = blockIdx.x * kLsRows;
 
+    // r: thread t stages column t % 16, k = 64 c + 4 ((t / 16) % 16) + u (u < 4) of
+    // the phase's chunks c = 2 x + t / 256 (x < kLsPhase / 2).  A k past K reads row
+    // K - 1 and a column past N column N - 1 (no branch); both are zeroed when
+    // staged.  K is a multiple of 16, so a thread's four k are all below K or all
+    // past it.  The top bit of bytes 0..6 is flipped.
+    const int sc = tid & 15, sk = 4 * ((tid >> 4) & 15), spar = tid >> 8;
+    const uint32_t rrow = 8u * (uint32_t)N;
+    const uint32_t rcol = 8u * (uint32_t)min(sc, N - 1);
+    const uint32_t rcmask = sc < N ? 0xffffffffu : 0u;
+    const char *rbase = (const char *)g.r;
+    constexpr int kRx = kLsPhase / 2;                // chunk pairs per phase
+    uint2 rv[kRx][4];
+    // (x0, x1): the chunk pairs x0 <= x < x1 of phase ph
+    auto rload = [&](int ph, int x0, int x1) {
+#pragma unroll
+        for (int x = x0; x < x1; x++) {
+            const int k0 = 64 * (ph * kLsPhase + 2 * x + spar) + sk;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const uint32_t kk = (uint32_t)min(k0 + u, K - 1);
+                rv[x][u] = *(const uint2 *)(rbase + (__umul24(kk, rrow) + rcol));
+            }
+        }
+    };
+    auto rstage = [&](int ph, int x0, int x1) {
+#pragma unroll
+        for (int x = x0; x < x1; x++) {
+            const int c = 2 * x + spar;
+            const uint32_t m = 64 * (ph * kLsPhase + c) + sk < K ? rcmask : 0u;
+            uint32_t lo[4], hi[4], wl[4], wh[4];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                lo[u] = (rv[x][u].x ^ 0x80808080u) & m;
+                hi[u] = (rv[x][u].y ^ 0x00808080u) & m;
+            }
+            transpose4(lo, wl);
+            transpose4(hi, wh);
+#pragma unroll
+            for (int b = 0; b < 4; b++) {
+                *(uint32_t *)&rT[sc * kLsColPitch + b * kLsRowPitch + 64 * c + sk] = wl[b];
+                *(uint32_t *)&rT[sc * kLsColPitch + (b + 4) * kLsRowPitch + 64 * c + sk] = wh[b];
+            }
+        }
+    };
+
     // this lane's A rows: block m = wave + 8 i, product row 16 m + c16 = 4 j + x
     const int8_t *arow[MBW];
 #pragma unroll
@@ -89,72 +144,19 @@ __global__ __launch_bounds__(64 * kLsWaves) void lift_step_kernel(LiftArgs g, St
         const int row = min(i0 + (mi & 3), M - 1);
         arow[i] = g.a + ((int64_t)j * M + row) * K + 16 * g16;
     }
-    // Each workgroup walks the K chunks from its own first chunk (the sums are
-    // exact in any order), so that the workgroups do not all read the same
-    // rows of r at once; steps past KC stay in place (they carry no data).
-    const int rot = blockIdx.x % KC;
-    auto cmap = [&](int kc) { return kc >= KC ? kc : (kc + rot >= KC ? kc + rot - KC : kc + rot); };
-    // unconditional loads: a step past the last re-reads the last chunk, and a
-    // lane group past K re-reads the row's last 16 bytes (r's bytes there are zero)
+    // unconditional loads: a chunk past the last re-reads the last, and a lane
+    // group past K re-reads the row's last 16 bytes (r's bytes there are zero)
     auto aload = [&](int i, int kc) {
-        const int off = min(cmap(min(kc, KC - 1)) * 64, K - 16 - 16 * g16);
+        const int off = min(min(kc, KC - 1) * 64, K - 16 - 16 * g16);
         return *(const v4i *)(arow[i] + off);
     };
-    // every thread stages a quarter column of r per chunk: column t % 16,
-    // k = 64 kc + 4 ((t / 16) % 16) + u (u < 4), the low (t < 256) or high
-    // 32-bit half of each value.  The raw words are loaded ahead (a k past
-    // K reads row K - 1, a column past N column N - 1: 32-bit offsets, no
-    // branch) and flipped and masked only when staged, so no load is waited
-    // for early; every wave issues the same loads.  K is a multiple of 16,
-    // so a thread's four k are all below K or all past it.
-    const int sc = tid & 15, sk = 4 * ((tid >> 4) & 15), half = tid >> 8;
-    const uint32_t rrow = 8u * (uint32_t)N;                          // bytes per k of r
-    const uint32_t rcol = 8u * (uint32_t)min(sc, N - 1) + 4u * (uint32_t)half;
-    const uint32_t rflip = half ? 0x00808080u : 0x80808080u;
-    const uint32_t rcmask = sc < N ? 0xffffffffu : 0u;
-    const char *rbase = (const char *)g.r;
-    auto rload = [&](int kc, uint32_t (&v)[4]) {
-        const int k0 = 64 * cmap(kc) + sk;
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const uint32_t kk = (uint32_t)min(k0 + u, K - 1);
-            v[u] = *(const uint32_t *)(rbase + (__umul24(kk, rrow) + rcol));
-        }
-    };
-    auto rstage = [&](const uint32_t (&v)[4], int kc, int buf) {
-        const uint32_t m = 64 * cmap(kc) + sk < K ? rcmask : 0u;
-        uint32_t x[4], w[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++) x[u] = (v[u] ^ rflip) & m;
-        transpose4(x, w);
-#pragma unroll
-        for (int b = 0; b < 4; b++) *(uint32_t *)&rT[buf][((4 * half + b) * 16 + sc) * kLsPitch + sk] = w[b];
-    };
 
-    // The first loads go out before the constants.  Chunk c of r is staged
-    // in LDS buffer c % 4 two steps before its products, and loaded kLsRAhead
-    // steps before that (rv[c % 4] holds it); the B fragments of a chunk are
-    // read one step ahead, so the LDS reads overlap the products; A is
-    // loaded kLsPre steps ahead of its use.  The step count is rounded up to
-    // whole groups of kLsPre (steps past KC have zero bytes of r and no
-    // ones), so the unrolled loop has no early exit and the counter waits
-    // stay exact.
-    static_assert(kLsPre % 4 == 0 && kLsRAhead >= 1 && kLsRAhead <= 2, "ring indices are compile-time");
+    // The loads go out first: r's first phase, the constants, then A kLsPre
+    // chunks ahead of its use.  The chunk count is rounded up to whole groups
+    // of kLsPre (chunks past KC have zero bytes of r and no ones), so the
+    // unrolled loop has no early exit and the counter waits stay exact.
     const int KCR = (KC + kLsPre - 1) / kLsPre * kLsPre;
-    uint32_t rv[4][4];
-    rload(0, rv[0]);
-    rload(1, rv[1]);
-    v4i abuf[kLsPre][MBW];
-#pragma unroll
-    for (int p = 0; p < kLsPre; p++)
-#pragma unroll
-        for (int i = 0; i < MBW; i++) abuf[p][i] = aload(i, p);
-#pragma unroll
-    for (int c = 2; c < 2 + kLsRAhead; c++) rload(c, rv[c]);
-
-    // the constants are loaded now and laid out in LDS after the products:
-    // the CRT digits (as 32-bit words of the slot-major table), the weights
-    // of modulus tid, the fixed-point fragments
+    rload(0, 0, kRx);
     constexpr int kWords = (kCrtSlots - 8) * kCrtDigits / 4;
     uint32_t cwd[2], ctb[2] = {0u, 0u}, cfx = 0u;
     int cq = 3, cc1 = 0;
@@ -170,63 +172,22 @@ __global__ __launch_bounds__(64 * kLsWaves) void lift_step_kernel(LiftArgs g, St
         }
         if (tid < 64) cfx = (&lc.fx[0][0][0][0])[tid];
     }
+    v4i abuf[kLsPre][MBW];
+#pragma unroll
+    for (int p = 0; p < kLsPre; p++)
+#pragma unroll
+        for (int i = 0; i < MBW; i++) abuf[p][i] = aload(i, p);
     if (blockIdx.x == 0 && tid == 0) {
         g.status[0] = 0u;                            // no bound is checked: no blocks, no flags
         g.status[1] = kStatusCheck;
     }
 
-    rstage(rv[0], 0, 0);
-    rstage(rv[1], 1, 1);
-
-    v4i acc[MBW][kLsNB];
-#pragma unroll
-    for (int i = 0; i < MBW; i++)
-#pragma unroll
-        for (int nb = 0; nb < kLsNB; nb++) acc[i][nb] = v4i{0, 0, 0, 0};
-    auto lds_barrier = [] {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-    };
-    v4i bf[2][8];
-    lds_barrier();
-#pragma unroll
-    for (int b = 0; b < 8; b++) bf[0][b] = *(const v4i *)&rT[0][(b * 16 + c16) * kLsPitch + 16 * g16];
-
-    for (int kc0 = 0; kc0 < KCR; kc0 += kLsPre) {
-#pragma unroll
-        for (int p = 0; p < kLsPre; p++) {
-            const int kc = kc0 + p;
-            // no instruction crosses into another chunk's step: the staging
-            // of r stays behind its loads
-            __builtin_amdgcn_sched_barrier(0);
-            // chunk kc + 1 is staged, and buffer (kc + 2) % 4 is no longer read
-            lds_barrier();
-#pragma unroll
-            for (int b = 0; b < 8; b++)
-                bf[(p + 1) & 1][b] = *(const v4i *)&rT[(p + 1) & 3][(b * 16 + c16) * kLsPitch + 16 * g16];
-            __builtin_amdgcn_sched_barrier(0);      // the reads go out before this step's products
-            rstage(rv[(p + 2) & 3], kc + 2, (p + 2) & 3);
-            rload(kc + 2 + kLsRAhead, rv[(p + 2 + kLsRAhead) & 3]);
-            // the row-sum column: ones for k < K (K is a multiple of 16)
-            const int one = K - (64 * cmap(kc) + 16 * g16) > 0 ? 0x01010101 : 0;
-            const v4i ones = v4i{one, one, one, one};
-            // the products read abuf[p] before the load of chunk kc + kLsPre
-            // replaces it, so the loop carries A in fixed registers
-#pragma unroll
-            for (int i = 0; i < MBW; i++) {
-#pragma unroll
-                for (int nb = 0; nb < 8; nb++)
-                    acc[i][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(abuf[p][i], bf[p & 1][nb], acc[i][nb], 0, 0, 0);
-                acc[i][8] = __builtin_amdgcn_mfma_i32_16x16x64_i8(abuf[p][i], ones, acc[i][8], 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < MBW; i++) abuf[p][i] = aload(i, kc + kLsPre);
-        }
-    }
-
-    // (the values are only used from here on, so no wait for them is hoisted into the loads' shadow)
+    // constants into LDS while A is in flight: the CRT digits (the slot-major
+    // table's words scattered digit-major), the weights of modulus tid, the
+    // fixed-point fragments, zero residues past the moduli.  (The values are
+    // only used from here on, so no wait for them is hoisted above the loads of A.)
     asm volatile("" : "+v"(cwd[0]), "+v"(cwd[1]), "+v"(ctb[0]), "+v"(ctb[1]), "+v"(cq), "+v"(cc1), "+v"(cfx));
+    rstage(0, 0, kRx);
     {
         int8_t *t = (int8_t *)&dT[0][0];
 #pragma unroll
@@ -252,7 +213,58 @@ __global__ __launch_bounds__(64 * kLsWaves) void lift_step_kernel(LiftArgs g, St
         ((uint32_t *)&Yl[0][0])[tid] = 0u;
         ((uint32_t *)&Yl[0][0])[tid + 512] = 0u;
     }
-    __syncthreads();
+    auto lds_barrier = [] {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+    };
+    lds_barrier();
+
+    v4i acc[MBW][kLsNB];
+#pragma unroll
+    for (int i = 0; i < MBW; i++)
+#pragma unroll
+        for (int nb = 0; nb < kLsNB; nb++) acc[i][nb] = v4i{0, 0, 0, 0};
+
+    // one group of kLsPre chunks from kc0 (within a staged phase, no barrier)
+    auto group = [&](int kc0) {
+        const int lc0 = kc0 % kLsPhase;
+#pragma unroll
+        for (int p = 0; p < kLsPre; p++) {
+            const int kc = kc0 + p;
+            v4i bf[8];
+#pragma unroll
+            for (int b = 0; b < 8; b++)
+                bf[b] = *(const v4i *)&rT[c16 * kLsColPitch + b * kLsRowPitch + 64 * (lc0 + p) + 16 * g16];
+            // the row-sum column: ones for k < K (K is a multiple of 16)
+            const int one = K - (64 * kc + 16 * g16) > 0 ? 0x01010101 : 0;
+            const v4i ones = v4i{one, one, one, one};
+            // the products read abuf[p] before the load of chunk kc + kLsPre
+            // replaces it, so the loop carries A in fixed registers
+#pragma unroll
+            for (int i = 0; i < MBW; i++) {
+#pragma unroll
+                for (int nb = 0; nb < 8; nb++)
+                    acc[i][nb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(abuf[p][i], bf[nb], acc[i][nb], 0, 0, 0);
+                acc[i][8] = __builtin_amdgcn_mfma_i32_16x16x64_i8(abuf[p][i], ones, acc[i][8], 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < MBW; i++) abuf[p][i] = aload(i, kc + kLsPre);
+        }
+    };
+    // per phase of r: staged (after a barrier: every wave is done with the
+    // last phase), then its groups of chunks with no barrier
+    for (int c0 = 0; c0 < KCR; c0 += kLsPhase) {
+        if (c0 > 0) {
+            const int ph = c0 / kLsPhase;
+            rload(ph, 0, kRx);
+            lds_barrier();
+            rstage(ph, 0, kRx);
+            lds_barrier();
+        }
+        const int c1 = min(c0 + kLsPhase, KCR);
+        for (int kc0 = c0; kc0 < c1; kc0 += kLsPre) group(kc0);
+    }
 
     // residues: element e of lane (g16, c16) in block m is product row
     // 16 m + 4 g16 + e, i.e. modulus j = 4 m + g16, row e, column c16
