@@ -651,6 +651,24 @@ def dixon_bench(args, rg, wl, plan, A_res, B, C, ws, stream):
     same_as_eager = bool(torch.equal(C, eager_out))
     digest = output_digest(args.workload, C)
 
+    # cold steps: before each, a read pass over 1 GiB (a max reduction) evicts
+    # the 256 MB last-level cache (MALL) and the L2s, leaving clean lines.
+    # Everything is queued ahead, so the GPU never idles between the flush and
+    # the call; events around the call alone time it.
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
+    sink = torch.zeros((), dtype=torch.int32, device="cuda")
+    n_cold = min(args.steps, 40)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_cold)]
+    torch.cuda.synchronize()
+    for c0, c1 in cev:
+        sink.copy_(flush.max())
+        c0.record(stream)
+        call()
+        c1.record(stream)
+    torch.cuda.synchronize()
+    cold = [c0.elapsed_time(c1) for c0, c1 in cev]
+    del flush, sink
+
     logical = 2.0 * M * N * K * n
     step_bytes = n * M * K + K * N * 8 * B.shape[-1] + M * N * 8 * lc
     out = {
@@ -671,6 +689,7 @@ def dixon_bench(args, rg, wl, plan, A_res, B, C, ws, stream):
                      "int8_mfma_frac": 2.0 * n * M * 9 * 16 * K / (ms_step * 1e-3) / 1e12 / PEAK_INT8_TOPS},
         "output": digest,
         "stages": {"step_us_spread_per_replay": spread(per), "eager_call_us": eager_ms * 1e3,
+                   "cold_step_us": spread(cold),
                    "graph_output_equals_eager": same_as_eager},
         "status_flags": rg.status(ws),
     }
