@@ -287,6 +287,10 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
     const int h = lane >> 5, l32 = lane & 31;
 
     __shared__ v4i dT[kCrtDigits][kCrtSlots / 16];
+    // each wave's 128 output entries, as they lie in C, in 16-byte units
+    // (unit u at u ^ ((u >> 4) & 15): conflict-free for the entry-strided
+    // writes and the contiguous reads)
+    __shared__ v4u outs[4][128 * RNS_MAX_OUT_LIMBS / 2];
     {
         int8_t *t = (int8_t *)&dT[0][0];
         for (int i = threadIdx.x; i < kCrtDigits * kCrtSlots; i += blockDim.x) {
@@ -337,10 +341,14 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
     const int64_t drow = stride / cgs, dcg = stride - drow * cgs;
     for (int64_t grp = g0; grp < groups; grp += stride) {
         int64_t i, j0, lim;                   // entries j0 + m < lim (columns, or flat indices) are real
+        int64_t base;                         // the group's first entry (flat); `count` of them are real
+        int count;
         if (ROWS) {
             i = row;
             j0 = cg * 128 + 4 * l32;          // within the plane's row pitch (a multiple of 128)
             lim = N;
+            base = i * N + cg * 128;
+            count = (int)min((int64_t)128, N - cg * 128);
             row += drow;
             cg += dcg;
             if (cg >= cgs) {
@@ -354,6 +362,8 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
             i = ff / N;
             j0 = ff - i * N;
             lim = f0 < total ? j0 + (total - f0) : 0;
+            base = grp * 128;
+            count = (int)min((int64_t)128, total - base);
         }
         uint32_t q[KS][16];
         const uint32_t yo = OFF32 ? (uint32_t)(i * y_pitch + j0) : 0u;
@@ -475,27 +485,45 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
                     carry += c2;
                 }
             }
-            if (j0 + m < lim) {
-                int64_t *ce = C + (i * N + j0 + m) * c_limbs;
-                const uint32_t sign = (uint32_t)carry;
+            const uint32_t sign = (uint32_t)carry;
 #pragma unroll
-                for (int t = 0; t < RNS_MAX_OUT_LIMBS / 4; t++) {
-                    uint32_t wd[4];
+            for (int t = 0; t < RNS_MAX_OUT_LIMBS / 4; t++) {
+                uint32_t wd[4];
 #pragma unroll
-                    for (int ii = 0; ii < 4; ii++) {
-                        const int i0 = 8 * t + ii, i1 = 8 * t + 4 + ii;
-                        const uint32_t a0 = i0 < W ? wv[i0] : sign, a1 = i1 < W ? wv[i1] : sign;
-                        wd[ii] = h ? a1 : a0;
-                    }
-                    const int l = 4 * t + 2 * h;
-                    if (pair_stores) {
-                        if (l < c_limbs) *(v4u *)(ce + l) = v4u{wd[0], wd[1], wd[2], wd[3]};
-                    } else {
-                        if (l < c_limbs) ce[l] = (int64_t)(((uint64_t)wd[1] << 32) | wd[0]);
-                        if (l + 1 < c_limbs) ce[l + 1] = (int64_t)(((uint64_t)wd[3] << 32) | wd[2]);
-                    }
+                for (int ii = 0; ii < 4; ii++) {
+                    const int i0 = 8 * t + ii, i1 = 8 * t + 4 + ii;
+                    const uint32_t a0 = i0 < W ? wv[i0] : sign, a1 = i1 < W ? wv[i1] : sign;
+                    wd[ii] = h ? a1 : a0;
+                }
+                const int l = 4 * t + 2 * h;
+                if (pair_stores) {
+                    // into the wave's staging area: entry 4 l32 + m, limbs l, l + 1
+                    const int u = (4 * l32 + m) * (c_limbs >> 1) + (l >> 1);
+                    if (l < c_limbs) outs[wave][u ^ ((u >> 4) & 15)] = v4u{wd[0], wd[1], wd[2], wd[3]};
+                } else if (j0 + m < lim) {
+                    int64_t *ce = C + (i * N + j0 + m) * c_limbs;
+                    if (l < c_limbs) ce[l] = (int64_t)(((uint64_t)wd[1] << 32) | wd[0]);
+                    if (l + 1 < c_limbs) ce[l + 1] = (int64_t)(((uint64_t)wd[3] << 32) | wd[2]);
                 }
             }
+        }
+        if (pair_stores) {
+            // the group's entries leave in 1 KiB runs (2 c_limbs of them): lane x
+            // of run r stores unit 64 r + x (entry (64 r + x) / (c_limbs / 2)) if
+            // that entry is real
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+            const int upe = c_limbs >> 1;     // units per entry
+            v4u *cu = (v4u *)(C + base * c_limbs);
+#pragma unroll
+            for (int r = 0; r < RNS_MAX_OUT_LIMBS; r++) {
+                const int u = 64 * r + lane;
+                if (r < 2 * upe && u < count * upe) cu[u] = outs[wave][u ^ ((u >> 4) & 15)];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
         }
     }
 }
