@@ -528,6 +528,34 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
     }
 }
 
+// Workgroups of `kernel` (256 threads) resident on the device at once,
+// cached per kernel: grid-stride launches take no more, so that no
+// workgroup waits for a second round while others finish.
+template <typename Kern>
+static int64_t crt_resident_blocks(Kern kernel) {
+    static const int64_t cached = [&] {
+        int dev = 0, cus = 0, per = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+            cus = 1;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, 256, 0) != hipSuccess || per < 1) per = 1;
+        return (int64_t)cus * per;
+    }();
+    return cached;
+}
+
+template <int KS, int NB, bool OFF32, bool ROWS>
+static void launch_crt4(int64_t groups, const CrtConsts &c, const CrtDigits &d, const int8_t *y, int64_t y_plane,
+                        int64_t y_pitch, int64_t M, int64_t N, int64_t *C, int32_t c_limbs, int pairs,
+                        hipStream_t s) {
+    auto kernel = crt4_kernel<KS, NB, OFF32, ROWS>;
+    const int64_t cap = crt_resident_blocks(kernel);
+    int64_t grid = (groups + 3) / 4;
+    if (grid > cap) grid = cap;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(256), 0, s, c, d, y, y_plane, y_pitch, M, N, C, c_limbs,
+                       pairs);
+}
+
 int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
                const int8_t *y, int64_t y_plane, int64_t y_pitch, int64_t M, int64_t N, int64_t *C,
                int32_t c_limbs, hipStream_t s) {
@@ -547,23 +575,16 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
         const int rows4 = (N % 128 == 0 || N >= 1024) ? 1 : 0;
         if (!rows4 && N % 4) return RNS_E_ARG;
         const int64_t groups4 = rows4 ? M * ((N + 127) / 128) : (total + 127) / 128;
-        int64_t grid4 = (groups4 + 3) / 4;
-        if (grid4 > 1536) grid4 = 1536;
-        const dim3 g4((unsigned)grid4), b4(256);
 #define RNS_CRT4_LAUNCH(KS, NB)                                                                             \
     do {                                                                                                    \
         if (off32 && rows4)                                                                                 \
-            hipLaunchKernelGGL((crt4_kernel<KS, NB, true, true>), g4, b4, 0, s, c, d, y, y_plane, y_pitch, M, \
-                               N, C, c_limbs, pairs);                                                       \
+            launch_crt4<KS, NB, true, true>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s);  \
         else if (off32)                                                                                     \
-            hipLaunchKernelGGL((crt4_kernel<KS, NB, true, false>), g4, b4, 0, s, c, d, y, y_plane, y_pitch,  \
-                               M, N, C, c_limbs, pairs);                                                    \
+            launch_crt4<KS, NB, true, false>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s); \
         else if (rows4)                                                                                     \
-            hipLaunchKernelGGL((crt4_kernel<KS, NB, false, true>), g4, b4, 0, s, c, d, y, y_plane, y_pitch,  \
-                               M, N, C, c_limbs, pairs);                                                    \
+            launch_crt4<KS, NB, false, true>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s); \
         else                                                                                                \
-            hipLaunchKernelGGL((crt4_kernel<KS, NB, false, false>), g4, b4, 0, s, c, d, y, y_plane, y_pitch, \
-                               M, N, C, c_limbs, pairs);                                                    \
+            launch_crt4<KS, NB, false, false>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s);\
     } while (0)
         if (ksteps == 1 && nblocks == 1)
             RNS_CRT4_LAUNCH(1, 1);
