@@ -8,7 +8,7 @@ device kernels, with shared device helpers in
 (big integers through the system's libgmp.so.10, opened at run time);
 ``csrc/rns_sliced.hip`` products beyond the residue capacity by operand slices;
 ``csrc/rns_noalloc.hip`` the product with the workspace in a fixed device array;
-``csrc/rns_skinny.hip`` the batched-residue product for skinny right-hand sides.
+``csrc/rns_skinny.hip`` the batched-residue step for skinny right-hand sides in one kernel.
 """
 from __future__ import annotations
 

@@ -297,7 +297,7 @@ def test_batched_residue_small(M, N, K, n, seed):
     X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
     ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
     assert np.array_equal(O.decode_array(X), ref)
-    assert rg.status(ws0) == 0          # the fused path leaves a readable status (no bound on r)
+    assert rg.status(ws0) == 0          # a readable status header: no bound on r, no flags
 
 
 def _planted(n, values, prime_powers=False):
@@ -413,7 +413,7 @@ def test_prime_power_int32_edge():
     X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
     ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
     assert np.array_equal(O.decode_array(X), ref)
-    assert rg.status(ws0) == 0          # the fused path leaves a readable status (no bound on r)
+    assert rg.status(ws0) == 0          # a readable status header: no bound on r, no flags
 
 
 @pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", [SMALL[1], SMALL[3], SMALL[7],
@@ -445,7 +445,7 @@ def test_batched_residue_any_int8_and_extremes():
     X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
     ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
     assert np.array_equal(O.decode_array(X), ref)
-    assert rg.status(ws0) == 0          # the fused path leaves a readable status (no bound on r)
+    assert rg.status(ws0) == 0          # a readable status header: no bound on r, no flags
 
 
 # The skinny right-hand side (N <= 16, one limb, K a multiple of 16 up to
@@ -483,7 +483,7 @@ def test_batched_residue_skinny_fused(M, N, K, n, pp, seed):
     X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
     ref = O.residue_gemm_via_crt(A_res, r, list(p.primes))
     assert np.array_equal(O.decode_array(X), ref)
-    assert rg.status(ws0) == 0          # the fused path leaves a readable status (no bound on r)
+    assert rg.status(ws0) == 0          # a readable status header: no bound on r, no flags
     # the stage calls (split, general product kernel, reconstruction) agree bit for bit
     ws = rg.new_workspace(p, M, N, K, True)
     Ad, rd = dev(A_res), dev(r[..., None])
