@@ -494,6 +494,31 @@ def test_batched_residue_skinny_fused(M, N, K, n, pp, seed):
     assert np.array_equal(out.cpu().numpy(), X)
 
 
+# The fused step on r of every width from 1 to 8 signed bytes, with both
+# ends of the width present, and on a one-byte r with a single entry of that
+# width anywhere: the byte products of r's sign-extension bytes carry the
+# sign whatever the width.
+@pytest.mark.parametrize("B", range(1, 9))
+def test_batched_residue_skinny_byte_widths(B):
+    print(f"skinny fused, r of {B} signed bytes", flush=True)
+    rng = np.random.default_rng(300 + B)
+    lo, hi = -(2 ** (8 * B - 1)), 2 ** (8 * B - 1) - 1
+    for M, N, K, n, pp in ((130, 16, 1024, 54, False), (37, 5, 208, 20, True)):
+        p = rg.plan_n(n, prime_powers=pp)
+        A_res = rng.integers(-128, 128, size=(n, M, K), dtype=np.int64).astype(np.int8)
+        r = rng.integers(lo, hi, size=(K, N), dtype=np.int64)
+        r[0, 0], r[K - 1, N - 1] = lo, hi
+        ws0 = rg.new_workspace(p, M, N, K, True)
+        X = rg.gemm_batched_residue(p, dev(A_res), dev(r[..., None]), workspace=ws0).cpu().numpy()
+        assert np.array_equal(O.decode_array(X), O.residue_gemm_via_crt(A_res, r, list(p.primes)))
+        # one entry of this width in an otherwise one-byte r
+        r1 = rng.integers(-128, 128, size=(K, N), dtype=np.int64)
+        r1[rng.integers(0, K), rng.integers(0, N)] = lo if B % 2 else hi
+        X1 = rg.gemm_batched_residue(p, dev(A_res), dev(r1[..., None]), workspace=ws0).cpu().numpy()
+        assert np.array_equal(O.decode_array(X1), O.residue_gemm_via_crt(A_res, r1, list(p.primes)))
+        assert rg.status(ws0) == 0
+
+
 def test_batched_residue_skinny_int32_edge():
     """K = 2^16 with every plane entry -128 and r = -2^63 (every flipped byte
     -128): each of the nine int32 byte products reaches 2^30."""
