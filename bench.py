@@ -46,6 +46,8 @@ def parse():
                     help="target wall time of the CPU oracle sample")
     ap.add_argument("--no-clock", action="store_true",
                     help="skip sampling the shader clock with amd-smi (profiler runs)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="only the int8 matrix-core ceiling (random and zero operand bytes)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -155,6 +157,47 @@ def gfx_clock_during(run, seconds=1.5):
     if not samples:
         return None, None
     return float(np.median([c for c, _ in samples])), float(np.median([p for _, p in samples]))
+
+
+def mfma_ceiling(no_clock=False, iters=3000, reps=10):
+    """What the int8 matrix cores sustain with no memory traffic: one wave per
+    SIMD on every compute unit runs rns_probe_int8_mfma (32 MFMAs of 32x32x32
+    per iteration, 16 accumulator chains) on random operand bytes and on zero
+    bytes, timed with HIP events on the launch stream; the shader clock and
+    socket power amd-smi reports while each runs back to back.  The dense
+    peak assumes the full clock; the clock falls under the power limit with
+    the switching of the operand bits, which the two data sets bracket."""
+    import torch
+    import exact_integer_gemm_amd as rg
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    ops = 2.0 * 32 ** 3 * 32 * iters * 4 * cus
+    res = {"probe": "rns_probe_int8_mfma", "workgroups": cus, "iters": iters, "ops_per_launch": ops}
+    for kind in ("random", "zero"):
+        if kind == "random":
+            src = torch.randint(-128, 128, (cus * 256 * 128,), dtype=torch.int8, device="cuda")
+        else:
+            src = torch.zeros(cus * 256 * 128, dtype=torch.int8, device="cuda")
+
+        def run():
+            rg.probe_int8_mfma(src, cus, iters)
+        for _ in range(2):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            run()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms = float(np.median(ts))
+        clk, pw = (None, None) if no_clock else gfx_clock_during(run)
+        res[kind] = {"us": ms * 1e3, "TOPs": ops / (ms * 1e-3) / 1e12,
+                     "frac_of_peak": ops / (ms * 1e-3) / 1e12 / PEAK_INT8_TOPS,
+                     "clock_MHz": clk, "socket_power_W": pw}
+    return res
 
 
 def copy_probe():
@@ -446,6 +489,9 @@ def main():
     if args.copy_probe:
         copy_probe()
         return
+    if args.mfma_probe:
+        print(json.dumps({"int8_mfma_ceiling": mfma_ceiling(args.no_clock)}), flush=True)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
@@ -532,6 +578,10 @@ def main():
     clk_mhz, power_w = (None, None) if args.no_clock else gfx_clock_during(
         lambda: rg.residue_products(plan, M, N, K, ws, A_res=A_res))
 
+    # the matrix cores' own rate on random and zero operand bytes (no memory
+    # traffic), next to which the products' fraction of the dense peak reads
+    ceiling = mfma_ceiling(args.no_clock) if args.workload == "wide" else None
+
     # Garner reconstruction (same output) timed outside the step, for its
     # O(p^2) share next to the CRT that the step uses
     C2 = torch.empty_like(C)
@@ -581,7 +631,10 @@ def main():
                      "algorithmic_ops_per_launch": gemm_ops,
                      "clock_MHz_during_products": clk_mhz, "socket_power_W_during_products": power_w,
                      "frac_at_measured_clock": (gemm_tops / (PEAK_INT8_TOPS * clk_mhz / 2400.0)
-                                                if clk_mhz else None)},
+                                                if clk_mhz else None),
+                     "int8_mfma_ceiling": ceiling,
+                     "frac_of_random_operand_ceiling": (gemm_tops / ceiling["random"]["TOPs"]
+                                                        if ceiling else None)},
         "output": digest,
         "stages": {
             "split_us_spread": spread(st[:, 0]), "products_us_spread": spread(st[:, 1]),

@@ -115,6 +115,7 @@ def load() -> ctypes.CDLL:
         "rns_reconstruct_garner": (ctypes.c_int, [P, I64, I64, I64, I32, VP, I32, VP, SZ, VP]),
         "rns_status": (ctypes.c_int, [VP, VP, ctypes.POINTER(ctypes.c_uint32)]),
         "rns_error_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "rns_probe_int8_mfma": (ctypes.c_int, [VP, SZ, I32, I32, VP, VP]),
         "rns_fp64_stats": (ctypes.c_int, [VP, I64, VP, VP, SZ, VP]),
         "rns_enclose_plan": (ctypes.c_int, [I64, ctypes.POINTER(_FpStats), ctypes.POINTER(_FpStats), I32,
                                             ctypes.POINTER(_EnclosePlan)]),
@@ -412,6 +413,21 @@ def status(workspace: torch.Tensor) -> int:
         rc = load().rns_status(workspace.data_ptr(), _stream_ptr(workspace), ctypes.byref(flags))
     _check(rc, "rns_status")
     return flags.value
+
+
+def probe_int8_mfma(src: torch.Tensor, workgroups: int, iters: int) -> torch.Tensor:
+    """Measurement aid (rns_probe_int8_mfma): ``workgroups`` x 4 waves run
+    ``iters`` x 32 v_mfma_i32_32x32x32_i8 on operand bytes read once from
+    ``src`` (int8, at least workgroups * 32 KiB, on the device), with no
+    memory traffic in the loop.  Returns the int32 [workgroups * 256]
+    accumulator sums (asynchronously, on the current stream)."""
+    _need(src, torch.int8, 1, "src")
+    out = torch.empty(workgroups * 256, dtype=torch.int32, device=src.device)
+    with torch.cuda.device(src.device):
+        rc = load().rns_probe_int8_mfma(src.data_ptr(), src.numel(), workgroups, iters, out.data_ptr(),
+                                        _stream_ptr(src))
+    _check(rc, "rns_probe_int8_mfma")
+    return out
 
 
 def workspace_planes(p: Plan, workspace: torch.Tensor, M: int, N: int, K: int,

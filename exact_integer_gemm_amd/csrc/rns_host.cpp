@@ -681,6 +681,13 @@ int rns_plan_moduli(int64_t K, int32_t a_bits, int32_t b_bits, int32_t kind, rns
     return RNS_E_CAPACITY;
 }
 
+int rns_probe_int8_mfma(const void *src, size_t src_bytes, int32_t workgroups, int32_t iters, int32_t *out,
+                        hipStream_t stream) {
+    if (!src || !out || workgroups < 1 || workgroups > (1 << 20) || iters < 1) return RNS_E_ARG;
+    if (src_bytes < (size_t)workgroups * 256 * 128 || reinterpret_cast<uintptr_t>(src) % 16) return RNS_E_ARG;
+    return launch_mfma_probe((const int8_t *)src, workgroups, iters, out, stream);
+}
+
 int rns_plan(int64_t K, int32_t a_bits, int32_t b_bits, rns_plan_t *out) {
     return rns_plan_moduli(K, a_bits, b_bits, RNS_MODULI_PRIMES, out);
 }

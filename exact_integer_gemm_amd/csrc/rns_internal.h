@@ -176,6 +176,7 @@ int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
                 int64_t a_plane, int64_t b_plane, int64_t y_plane,
                 int64_t a_row, int64_t a_kstep, int64_t b_row, int64_t b_kstep, int64_t y_pitch,
                 int8_t *partial, const EpiConsts &c, hipStream_t s);
+int launch_mfma_probe(const int8_t *src, int workgroups, int iters, int32_t *out, hipStream_t s);
 int launch_garner(const GarnerConsts &g, const int8_t *y, int64_t y_plane, int64_t y_pitch,
                   int64_t M, int64_t N, int64_t *C, int32_t c_limbs, hipStream_t s);
 int launch_zero(int64_t *C, int64_t count, hipStream_t s);

@@ -307,6 +307,22 @@ typedef struct rns_layout {
 int rns_workspace_layout(const rns_plan_t *plan, int64_t M, int64_t N, int64_t K,
                          int32_t batched_residue, rns_layout_t *out);
 
+/* Measurement aid, not a step of the product: the int8 matrix-core rate the
+ * device sustains on given operand bytes, against which the products'
+ * roofline fraction can be read (the dense peak assumes the full clock; the
+ * clock falls under the power limit by how much the operand bits switch).
+ * `workgroups` workgroups of four waves (one per SIMD) each run `iters`
+ * iterations of 32 v_mfma_i32_32x32x32_i8 on fragments read once from
+ * `src` (device, 16-byte aligned, at least workgroups * 32 KiB; thread t
+ * reads bytes 128 t .. 128 t + 127) and XORed with one another between
+ * iterations, with 16 accumulator chains per wave and no memory traffic in
+ * the loop: 2 * 32^3 * 32 * iters * 4 * workgroups int8 ops.  out (device,
+ * workgroups * 256 int32) receives each thread's accumulator sum.
+ * Asynchronous on `stream`; RNS_E_ARG for a null or short buffer or a count
+ * below 1. */
+int rns_probe_int8_mfma(const void *src, size_t src_bytes, int32_t workgroups, int32_t iters, int32_t *out,
+                        hipStream_t stream);
+
 /* A constant string naming an RNS_* code. */
 const char *rns_error_string(int code);
 

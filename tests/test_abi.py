@@ -338,3 +338,17 @@ def test_noalloc_rejects_before_any_device_work(lib):
     assert lib.rns_gemm_noalloc(None, 8, 8, 8, None, 1, None, 1, None, 1, None) == -1
     assert lib.rns_gemm_noalloc(ctypes.byref(c), 8, 8, 2 ** 17 + 1, None, 1, None, 1, None, 4, None) == -2
     assert "scratch" in lib.rns_error_string(-10).decode()
+
+
+def test_mfma_probe_rejects_before_any_device_work(lib):
+    """The measurement aid checks its buffer and counts before it launches."""
+    E_ARG = -1
+    out = ctypes.c_void_p(256)
+    fake = ctypes.c_void_p(4096)            # never dereferenced: every call below is rejected
+    assert lib.rns_probe_int8_mfma(None, 1 << 20, 1, 1, out, None) == E_ARG
+    assert lib.rns_probe_int8_mfma(fake, 1 << 20, 1, 1, None, None) == E_ARG
+    assert lib.rns_probe_int8_mfma(fake, 32 * 1024 - 1, 1, 1, out, None) == E_ARG   # one workgroup needs 32 KiB
+    assert lib.rns_probe_int8_mfma(fake, 1 << 20, 0, 1, out, None) == E_ARG
+    assert lib.rns_probe_int8_mfma(fake, 1 << 20, 1, 0, out, None) == E_ARG
+    assert lib.rns_probe_int8_mfma(ctypes.c_void_p(4100), 1 << 20, 1, 1, out, None) == E_ARG   # unaligned
+
