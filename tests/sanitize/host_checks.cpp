@@ -171,9 +171,26 @@ static void bigint() {
     CHECK(rns_reduce_fractions(nullptr, 1, 1, &dd, 1, nullptr, nullptr, 0) == RNS_E_ARG);
 }
 
+// the measurement aid's argument checks, then one accepted call (the stand-in
+// launcher checks what it receives)
+static void probe() {
+    alignas(16) static int8_t src[2 * 256 * 128];
+    static int32_t out[2 * 256];
+    int ok = rns_probe_int8_mfma(src, sizeof src, 2, 3, out, nullptr) == RNS_OK;
+    ok &= rns_probe_int8_mfma(src, sizeof src - 1, 2, 3, out, nullptr) == RNS_E_ARG;
+    ok &= rns_probe_int8_mfma(src + 1, sizeof src - 1, 1, 3, out, nullptr) == RNS_E_ARG;
+    ok &= rns_probe_int8_mfma(nullptr, sizeof src, 1, 3, out, nullptr) == RNS_E_ARG;
+    ok &= rns_probe_int8_mfma(src, sizeof src, 1, 0, out, nullptr) == RNS_E_ARG;
+    if (!ok) {
+        std::fprintf(stderr, "probe argument checks\n");
+        fails++;
+    }
+}
+
 int main() {
     plans();
     stages();
+    probe();
     bigint();
     if (fails) std::fprintf(stderr, "%d checks failed\n", fails);
     else std::printf("host checks passed\n");

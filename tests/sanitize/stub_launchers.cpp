@@ -53,6 +53,12 @@ int launch_garner(const GarnerConsts &g, const int8_t *, int64_t, int64_t, int64
     return RNS_OK;
 }
 
+int launch_mfma_probe(const int8_t *src, int workgroups, int iters, int32_t *out, hipStream_t) {
+    require(src != nullptr && out != nullptr && workgroups >= 1 && iters >= 1, "probe arguments");
+    require(reinterpret_cast<uintptr_t>(src) % 16 == 0, "probe source alignment");
+    return RNS_OK;
+}
+
 int launch_zero(int64_t *, int64_t count, hipStream_t) {
     require(count >= 0, "zero count");
     return RNS_OK;
