@@ -8,7 +8,8 @@ device kernels, with shared device helpers in
 (big integers through the system's libgmp.so.10, opened at run time);
 ``csrc/rns_sliced.hip`` products beyond the residue capacity by operand slices;
 ``csrc/rns_noalloc.hip`` the product with the workspace in a fixed device array;
-``csrc/rns_skinny.hip`` the batched-residue step for skinny right-hand sides in one kernel.
+``csrc/rns_skinny.hip`` the batched-residue step for skinny right-hand sides in one kernel;
+``csrc/rns_probe.hip`` a measurement aid (the int8 matrix-core rate with no memory traffic).
 """
 from __future__ import annotations
 
@@ -20,7 +21,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "librns_gemm.so")
 SOURCES = [os.path.join(CSRC, f) for f in ("rns_host.cpp", "rns_split.hip", "rns_gemm.hip", "rns_crt.hip", "rns_garner.hip",
                                                     "rns_enclose.hip", "rns_solve.hip", "rns_ratrec.cpp",
-                                                    "rns_sliced.hip", "rns_noalloc.hip", "rns_skinny.hip")]
+                                                    "rns_sliced.hip", "rns_noalloc.hip", "rns_skinny.hip",
+                                                    "rns_probe.hip")]
 HEADERS = [os.path.join(CSRC, "rns_internal.h"), os.path.join(CSRC, "rns_device.h"),
            os.path.join(os.path.dirname(HERE), "include", "rns_gemm.h"),
            os.path.join(os.path.dirname(HERE), "include", "rns_enclose.h"),
