@@ -92,7 +92,7 @@ def gemm_kernel_name(tile_config, n, M, N):
     tiles = n * ((M + 255) // 256) * ((N + 255) // 256)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if tiles > cus and cus % 8 == 0:
-        return ("gemm_ps_kernel<4> (persistent, one workgroup per CU) + gemm_tail_kernel<8> "
+        return ("gemm_ps_kernel<4> (persistent, one workgroup per CU) + gemm_tail4_kernel<8> "
                 "when tiles past the last whole round are split over K")
     return "gemm_pp_kernel<4> (one 256x256 tile per workgroup)"
 

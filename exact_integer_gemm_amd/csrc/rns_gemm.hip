@@ -35,7 +35,7 @@ struct GemmArgs {
     // Large tiling only: the first full_tiles workgroups each run a whole
     // tile; each later workgroup runs 1/split of the K steps of one of the
     // remaining tiles and leaves its residues in `partial` (kTailUnitBytes
-    // per workgroup), which gemm_tail_kernel combines.
+    // per workgroup), which gemm_tail4_kernel combines.
     int32_t full_tiles, split;
     int8_t *partial;
     int32_t tiles;                       // all tiles of all primes
@@ -245,7 +245,7 @@ __device__ __forceinline__ void store_big_tile(v16i (&acc)[4][16 / NW], int q, d
     }
 }
 
-// A part of a split tile leaves its residues for gemm_tail_kernel: thread
+// A part of a split tile leaves its residues for gemm_tail4_kernel: thread
 // tid's 64 * FN values as 4 * FN runs of 16 bytes, run c = i * FN + j at
 // [c][tid][16] of the part's kTailUnitBytes slot.
 // For q = 2 the rounding step leaves s - 2 round(s / 2) in {-1, 0, 1}, whose
@@ -701,39 +701,65 @@ __global__ __launch_bounds__(512) void gemm_ps_kernel(GemmArgs g, EpiConsts ec) 
     if (group == 0) __builtin_amdgcn_s_barrier();
 }
 
-// The split tiles: block b sums the residues the `split` parts of tile
-// full_tiles + b left in their slots (|sum| <= split * 128, exact in int32),
-// reduces the sum mod q and stores the tile like the product kernel does.
-// NW matches the product kernel's wave count (the slots' layout).
+// The split tiles: the residues the `split` parts of a tile left in their
+// slots are added up (|sum| <= split * 128, exact in int32), reduced again
+// mod q and stored like the product kernel stores a tile; NW matches the
+// product kernel's wave count (the slots' layout).  Four workgroups per
+// split tile, so the combine spreads over four times as many compute units:
+// workgroup 4 t + i takes accumulator row block i of tile full_tiles + t
+// (rows wm * 128 + 32 i + l32, all 256 columns: two runs of each part's
+// slot).  Its 64 rows go through LDS and leave in 16-byte row chunks.
 template <int NW>
-__global__ __launch_bounds__(64 * NW) void gemm_tail_kernel(GemmArgs g, EpiConsts ec) {
+__global__ __launch_bounds__(64 * NW) void gemm_tail4_kernel(GemmArgs g, EpiConsts ec) {
     constexpr int FN = 16 / NW;
-    __shared__ v4i out[256 * kOutPitch / 16];
+    __shared__ v4i out[64 * kOutPitch / 16];
     const int tid = threadIdx.x;
-    const int tile = g.full_tiles + blockIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1, half = lane >> 5, l32 = lane & 31;
+    const int t = blockIdx.x >> 2, i = blockIdx.x & 3;
+    const int tile = g.full_tiles + t;
     const int per_prime = g.tiles_m * g.tiles_n;
     const int p = tile / per_prime;
-    const int t = tile - p * per_prime;
-    const int tm = t / g.tiles_n, tn = t - tm * g.tiles_n;
-    v16i acc[4][FN];
+    const int tt = tile - p * per_prime;
+    const int tm = tt / g.tiles_n, tn = tt - tm * g.tiles_n;
+    v16i acc[FN];
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < FN; j++) acc[i][j] = v16i{0};
-    const int8_t *slots = g.partial + (int64_t)blockIdx.x * g.split * kTailUnitBytes;
+    for (int j = 0; j < FN; j++) acc[j] = v16i{0};
+    const int8_t *slots = g.partial + (int64_t)t * g.split * kTailUnitBytes;
     for (int o = 0; o < g.split; o++) {
 #pragma unroll
-        for (int i = 0; i < 4; i++)
+        for (int j = 0; j < FN; j++) {
+            const v4i v = *(const v4i *)(slots + (int64_t)o * kTailUnitBytes + ((i * FN + j) * 64 * NW + tid) * 16);
 #pragma unroll
-            for (int j = 0; j < FN; j++) {
-                const v4i v = *(const v4i *)(slots + (int64_t)o * kTailUnitBytes +
-                                             ((i * FN + j) * 64 * NW + tid) * 16);
-#pragma unroll
-                for (int e = 0; e < 16; e++) acc[i][j][e] += (int)(int8_t)(v[e >> 2] >> (8 * (e & 3)));
-            }
+            for (int e = 0; e < 16; e++) acc[j][e] += (int)(int8_t)(v[e >> 2] >> (8 * (e & 3)));
+        }
     }
-    store_big_tile<NW>(acc, ec.q[p], ec.inv[p], (int8_t *)out,
-                       g.y + p * g.y_plane + (int64_t)(tm * 256) * g.y_pitch + tn * 256, g.y_pitch, tid);
+    const int q = ec.q[p];
+    const double inv = ec.inv[p];
+    const uint32_t keep = residue_keep_mask(q);
+    int8_t *ob = (int8_t *)out;
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) {
+            const int row = wm * 32 + l32;                       // local row
+            const int col = wn * 32 * FN + j * 32 + 8 * gq + 4 * half;
+            const v16i &a = acc[j];
+            *(uint32_t *)(ob + row * kOutPitch + col) =
+                pack4(reduce_low_byte(a[4 * gq], q, inv), reduce_low_byte(a[4 * gq + 1], q, inv),
+                      reduce_low_byte(a[4 * gq + 2], q, inv), reduce_low_byte(a[4 * gq + 3], q, inv)) & keep;
+        }
+    __syncthreads();
+    // 64 rows x 256 bytes: 16 lanes per row, 4 * NW rows per pass; local row
+    // r is row (r / 32) * 128 + 32 i + r % 32 of the tile
+    int8_t *Yp = g.y + p * g.y_plane + (int64_t)(tm * 256) * g.y_pitch + tn * 256;
+#pragma unroll
+    for (int pass = 0; pass < 16 / NW; pass++) {
+        const int r = pass * 4 * NW + (tid >> 4);
+        const int c = (tid & 15) * 16;
+        const int row = (r >> 5) * 128 + 32 * i + (r & 31);
+        *(v4i *)(Yp + (int64_t)row * g.y_pitch + c) = *(const v4i *)(ob + r * kOutPitch + c);
+    }
 }
 
 // Compute units of the current device (cached per device).
@@ -802,8 +828,8 @@ int launch_gemm(int cfg, int n, const int8_t *a, const int8_t *b, int8_t *y,
                 hipLaunchKernelGGL((gemm_pp_kernel<4>), dim3((unsigned)grid), dim3(512), 0, s, g, c);
             if (g.split > 1) {
                 if (hipGetLastError() != hipSuccess) return RNS_E_HIP;
-                hipLaunchKernelGGL((gemm_tail_kernel<8>), dim3((unsigned)(tiles - g.full_tiles)), dim3(512), 0,
-                                   s, g, c);
+                hipLaunchKernelGGL((gemm_tail4_kernel<8>), dim3((unsigned)(4 * (tiles - g.full_tiles))), dim3(512),
+                                   0, s, g, c);
             }
             break;
         case kTileSmall:
