@@ -146,6 +146,33 @@ def test_split_tail_tiles():
         assert np.array_equal(out.cpu().numpy(), ref)
 
 
+# Shapes whose 256 x 256 tiles exceed a whole round over 256 compute units by
+# 14, 26 and 94 tiles: the products split those tiles over K into 16, 8 and
+# 2 parts, and the combine adds the parts of each tile's row blocks.  Small
+# entries keep the product far inside the capacity of the n primes.
+SPLIT_PARTS = [
+    # M, N, K, n primes, parts expected on 256 compute units, seed
+    (256, 1280, 4096, 54, 16, 41),
+    (256, 1536, 2048, 47, 8, 42),
+    (256, 1792, 1024, 50, 2, 43),
+]
+
+
+@pytest.mark.parametrize("M,N,K,n,parts,seed", SPLIT_PARTS)
+def test_split_tail_part_counts(M, N, K, n, parts, seed):
+    tiles = n * (M // 256) * (N // 256)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    print(f"split tail parts: M={M} N={N} K={K} n={n} tiles={tiles} cus={cus} "
+          f"(parts {parts} on 256 compute units)", flush=True)
+    p = rg.plan_n(n)
+    ws = rg.new_workspace(p, M, N, K)
+    for s_ in (seed, seed + 100):
+        A, B = W.random_operands(s_, M, N, K, 1, 1, 20, 20)
+        C = rg.gemm(p, dev(A), dev(B), workspace=ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy(), oracle_c(A, B, p.out_limbs_min))
+
+
 def test_persistent_rounds():
     """Two whole rounds of 256 x 256 tiles per compute unit, then K parts of
     the remaining tiles: each workgroup walks its list of tiles with the
