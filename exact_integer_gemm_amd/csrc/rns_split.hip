@@ -339,15 +339,15 @@ __device__ __forceinline__ void products(const v4i (&a)[F], const SplitLds &lds,
 //               single, row r0 + f / 2, entry k = 64 kb + 32 (f % 2) + lane % 32.
 template <int L, bool FP, int NB>
 __device__ void split_rows(const SplitOperand &op, const SplitConsts &c, int sidx, SplitLds &lds,
-                           uint8_t *ostage, int64_t units, uint32_t &flag) {
+                           uint8_t *ostage, int64_t units, uint32_t &flag, int64_t bid, int64_t nblk) {
     constexpr bool PAIR = L <= 2;
     constexpr int R = PAIR ? kRowsPair : kRowsSingle;
     constexpr int F = PAIR ? R : 2 * R;
     constexpr int W = EntryWords<L, FP, !PAIR>::W;
     const int lane = threadIdx.x & 63, h = lane >> 5;
     const int64_t groups = op.r_pad / R;
-    const int64_t stride = (int64_t)gridDim.x * kSplitWaves;
-    int64_t unit = (int64_t)blockIdx.x * kSplitWaves + (threadIdx.x >> 6);
+    const int64_t stride = nblk * kSplitWaves;
+    int64_t unit = bid * kSplitWaves + (threadIdx.x >> 6);
 
     // all loads are unconditional: an entry outside the operand (or of a
     // unit past the end) reads entry 0 and is then taken as zero
@@ -408,7 +408,8 @@ constexpr int kColsLdsBytes = ColsTile<true>::BYTES > ColsTile<false>::BYTES ? C
 
 template <int L, bool FP, int NB>
 __device__ void split_cols(const SplitOperand &op, const SplitConsts &c, int sidx, SplitLds &lds,
-                           uint8_t *stage, uint8_t *ostage, int64_t tiles, uint32_t &flag) {
+                           uint8_t *stage, uint8_t *ostage, int64_t tiles, uint32_t &flag, int64_t bid,
+                           int64_t nblk) {
     constexpr bool PAIR = L <= 2;
     using T = ColsTile<PAIR>;
     constexpr int F = 8;                               // fragments per wave and tile
@@ -429,7 +430,7 @@ __device__ void split_cols(const SplitOperand &op, const SplitConsts &c, int sid
             load_entry<L, FP, false>(op.x, ok[j] ? k * op.rows + n : 0, h, xs[j]);
         }
     };
-    int64_t tile = blockIdx.x;
+    int64_t tile = bid;
     const TableWords tw = table_load(c, sidx);
     load_tile(tile < tiles ? tile : 0, tile < tiles);
     table_commit(tw, lds);
@@ -471,7 +472,7 @@ __device__ void split_cols(const SplitOperand &op, const SplitConsts &c, int sid
             a[f] = *(const v4i *)(stage + rl * T::PITCH + eo);
             off[f] = (PAIR ? f : f >> 1) * kKBlock + (PAIR ? 0 : 32 * (f & 1));
         }
-        const int64_t next = t + gridDim.x;
+        const int64_t next = t + nblk;
         load_tile(next < tiles ? next : t, next < tiles);
         int8_t *dst = op.planes + kb * (op.r_pad * kKBlock) + (n0 + RW * wv) * kKBlock;
         products<PAIR, NB, F>(a, lds, c.n, lane, dst, plane, off, ostage);
@@ -479,7 +480,22 @@ __device__ void split_cols(const SplitOperand &op, const SplitConsts &c, int sid
     // the first tile runs outside the loop (exact waits, as on the row path)
     if (tile < tiles) {
         body(tile, true);
-        for (tile += gridDim.x; tile < tiles; tile += gridDim.x) body(tile, false);
+        for (tile += nblk; tile < tiles; tile += nblk) body(tile, false);
+    }
+}
+
+// One status word per block, written unconditionally (no clearing pass);
+// the first block of the first launch also writes the header: the block
+// count of the whole split and its check word.  Every thread of the block
+// calls it (the flag is reduced over the block).
+__device__ __forceinline__ void write_status(const SplitStatus &st, uint32_t flag, int64_t bid) {
+    const bool any = __syncthreads_or(flag != 0);
+    if (threadIdx.x == 0) {
+        st.status[kStatusHeader + st.first + bid] = any ? st.flag_bit : 0u;
+        if (st.first == 0 && bid == 0) {
+            st.status[0] = (uint32_t)st.total;
+            st.status[1] = (uint32_t)st.total ^ kStatusCheck;
+        }
     }
 }
 
@@ -491,20 +507,33 @@ __global__ __launch_bounds__(kSplitThreads, 2) void split_kernel(SplitOperand op
     uint32_t flag = 0;
     if constexpr (COLS) {
         __shared__ __align__(16) uint8_t stage[kColsLdsBytes];
-        split_cols<L, FP, NB>(op, c, st.b_start, lds, stage, mine, st.work, flag);
+        split_cols<L, FP, NB>(op, c, st.b_start, lds, stage, mine, st.work, flag, blockIdx.x, gridDim.x);
     } else {
-        split_rows<L, FP, NB>(op, c, st.b_start, lds, mine, st.work, flag);
+        split_rows<L, FP, NB>(op, c, st.b_start, lds, mine, st.work, flag, blockIdx.x, gridDim.x);
     }
-    // one status word per block, written unconditionally (no clearing pass);
-    // the first block of the first launch also writes the header: the block
-    // count of the whole split and its check word
-    const bool any = __syncthreads_or(flag != 0);
-    if (threadIdx.x == 0) {
-        st.status[kStatusHeader + st.first + blockIdx.x] = any ? st.flag_bit : 0u;
-        if (st.first == 0 && blockIdx.x == 0) {
-            st.status[0] = (uint32_t)st.total;
-            st.status[1] = (uint32_t)st.total ^ kStatusCheck;
-        }
+    write_status(st, flag, blockIdx.x);
+}
+
+// Both operands in one launch, for shapes whose two grids fit on the device
+// at once: blocks below ga run A on the row path, the others B on the column
+// path (integer entries of L limbs both).  One launch instead of two, and
+// the two operands' blocks run side by side.
+template <int L, int NB>
+__global__ __launch_bounds__(kSplitThreads, 2) void split_ab_kernel(SplitOperand a, SplitOperand b, SplitConsts c,
+                                                                    SplitStatus sa, SplitStatus sb, int32_t ga) {
+    __shared__ SplitLds lds;
+    __shared__ __align__(16) uint8_t ostage[kSplitWaves][kOutStageBytes];
+    __shared__ __align__(16) uint8_t stage[kColsLdsBytes];
+    uint8_t *mine = ostage[threadIdx.x >> 6];
+    uint32_t flag = 0;
+    const int64_t bid = blockIdx.x;
+    if (bid < ga) {
+        split_rows<L, false, NB>(a, c, sa.b_start, lds, mine, sa.work, flag, bid, ga);
+        write_status(sa, flag, bid);
+    } else {
+        split_cols<L, false, NB>(b, c, sb.b_start, lds, stage, mine, sb.work, flag, bid - ga,
+                                 (int64_t)gridDim.x - ga);
+        write_status(sb, flag, bid - ga);
     }
 }
 
@@ -602,6 +631,40 @@ static int64_t launch_operand(const SplitOperand &op, const SplitConsts &c, cons
                 : launch_kind<false, false>(nb, op, c, st, blocks, dry, s);
 }
 
+// The fused launch of both operands (split_ab_kernel), or -1 where no
+// instance exists.  dry: only the resident-block count of that instance.
+template <int L, int NB>
+static int64_t launch_ab_one(const SplitOperand &a, const SplitOperand &b, const SplitConsts &c,
+                             const SplitStatus &sa, const SplitStatus &sb, int64_t ga, int64_t gb, bool dry,
+                             hipStream_t s) {
+    auto kernel = split_ab_kernel<L, NB>;
+    if (dry) return resident_blocks(kernel);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(ga + gb)), dim3(kSplitThreads), 0, s, a, b, c, sa, sb, (int32_t)ga);
+    return ga + gb;
+}
+template <int L>
+static int64_t launch_ab_nb(int nb, const SplitOperand &a, const SplitOperand &b, const SplitConsts &c,
+                            const SplitStatus &sa, const SplitStatus &sb, int64_t ga, int64_t gb, bool dry,
+                            hipStream_t s) {
+    switch (nb) {
+        case 1: return launch_ab_one<L, 1>(a, b, c, sa, sb, ga, gb, dry, s);
+        case 2: return launch_ab_one<L, 2>(a, b, c, sa, sb, ga, gb, dry, s);
+        case 3: if constexpr (L <= 2) return launch_ab_one<L, 3>(a, b, c, sa, sb, ga, gb, dry, s); else return -1;
+        case 4: if constexpr (L <= 2) return launch_ab_one<L, 4>(a, b, c, sa, sb, ga, gb, dry, s); else return -1;
+        default: return -1;
+    }
+}
+static int64_t launch_ab(const SplitOperand &a, const SplitOperand &b, const SplitConsts &c, const SplitStatus &sa,
+                         const SplitStatus &sb, int64_t ga, int64_t gb, bool dry, hipStream_t s) {
+    const int nb = (c.n + (a.limbs <= 2 ? 16 : 32) - 1) / (a.limbs <= 2 ? 16 : 32);
+    switch (a.limbs) {
+        case 1: return launch_ab_nb<1>(nb, a, b, c, sa, sb, ga, gb, dry, s);
+        case 2: return launch_ab_nb<2>(nb, a, b, c, sa, sb, ga, gb, dry, s);
+        case 3: return launch_ab_nb<3>(nb, a, b, c, sa, sb, ga, gb, dry, s);
+        default: return launch_ab_nb<4>(nb, a, b, c, sa, sb, ga, gb, dry, s);
+    }
+}
+
 int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts &c,
                  uint32_t *status, int64_t status_slots, hipStream_t s) {
     if (c.n < 1 || c.n > kMaxPrimes) return RNS_E_ARG;
@@ -626,6 +689,33 @@ int launch_split(const SplitOperand *a, const SplitOperand *b, const SplitConsts
     const int64_t total = grid[0] + grid[1];
     if (total <= 0) return RNS_OK;
     if (total + kStatusHeader > status_slots || total > 0x7fffffff) return RNS_E_ARG;
+    // Small shapes: both operands in one launch when A (row path) and B
+    // (column path, B given as [K][N]) have integer entries of the same limb
+    // count and their blocks need at most two rounds of the fused kernel's
+    // resident blocks (each block then runs one or two units); the blocks
+    // are shared in proportion to the work.  Larger shapes keep a launch per
+    // operand, each with its own kernel's full grid.
+    if (grid[0] > 0 && grid[1] > 0 && !a->fp64 && !b->fp64 && a->limbs == b->limbs && !a->transposed &&
+        b->transposed) {
+        const bool pair = a->limbs <= 2;
+        const int64_t ba = split_blocks(*a, pair, false), bb = split_blocks(*b, pair, true);
+        const int64_t cap = launch_ab(*a, *b, c, st[0], st[1], 0, 0, true, s);
+        if (cap > 1 && ba + bb <= 2 * cap) {
+            int64_t ga = ba, gb = bb;
+            if (ba + bb > cap) {
+                ga = ba * cap / (ba + bb);
+                ga = ga < 1 ? 1 : (ga > ba ? ba : ga);
+                gb = cap - ga;
+                gb = gb < 1 ? 1 : (gb > bb ? bb : gb);
+            }
+            if (ga + gb + kStatusHeader > status_slots) return RNS_E_ARG;
+            st[0].first = 0;
+            st[1].first = (int32_t)ga;
+            st[0].total = st[1].total = (int32_t)(ga + gb);
+            if (launch_ab(*a, *b, c, st[0], st[1], ga, gb, false, s) < 0) return RNS_E_ARG;
+            return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
+        }
+    }
     int64_t first = 0;
     for (int i = 0; i < 2; i++) {
         if (grid[i] == 0) continue;
