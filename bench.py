@@ -596,6 +596,35 @@ def main():
     garner_ms = g_ev[0].elapsed_time(g_ev[1]) / g_reps
     same_as_garner = bool(torch.equal(C, C2))
 
+    # the same step replayed from a HIP graph (G steps per graph): the
+    # kernels' own pace, which the host's per-call dispatch hides on small
+    # shapes.  `value` stays the eager step above.  Each of three further
+    # replays follows eager work that overwrites C and is checked against
+    # the eager output.
+    eager_C = C.clone()
+    G = 5
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(G):
+            step()
+    graph.replay()
+    torch.cuda.synchronize()
+    g_reps = max(2, args.steps // G)
+    g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(g_reps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = g0.elapsed_time(g1) / (g_reps * G)
+    graph_same = True
+    for _ in range(3):
+        C.fill_(-1)
+        graph.replay()
+        torch.cuda.synchronize()
+        graph_same = graph_same and bool(torch.equal(C, eager_C))
+    del graph
+
     # rates
     mnk2 = 2.0 * M * N * K
     logical = mnk2 * (n if batched else 1)        # the lift step has no single product
@@ -649,6 +678,8 @@ def main():
             "garner_share_if_used": garner_ms / (split_ms + gemm_ms + garner_ms),
             "garner_bit_identical": same_as_garner,
             "hbm_peak_GBps": PEAK_HBM_GBPS,
+            "graph_step_us": graph_ms * 1e3, "graph_steps_per_replay": G,
+            "graph_output_equals_eager": graph_same,
         },
         "status_flags": flags,
     }
