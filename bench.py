@@ -686,6 +686,8 @@ def main():
 
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, plan, C, batched, args.cpu_seconds)
+        if args.workload == "square":
+            out["cpu_baseline_one_thread"] = cpu_one_thread(args.workload, C.shape[-1], 64, M, N, K)
     print(json.dumps(out), flush=True)
 
 
@@ -780,6 +782,26 @@ def dixon_bench(args, rg, wl, plan, A_res, B, C, ws, stream):
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, plan, C, True, args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def cpu_one_thread(workload, lc, rows, M, N, K):
+    """The C oracle with one OpenMP thread on the first `rows` rows of the
+    workload (a child process: the thread count is fixed when the library
+    starts), next to the all-cores figure."""
+    import subprocess
+    code = ("import time, workloads as W; from oracle import cgemm; "
+            f"wl = W.make({workload!r}); cgemm.build(); "
+            f"t = time.perf_counter(); cgemm.gemm(wl.A[:{rows}], wl.B, {lc}); print(time.perf_counter() - t)")
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    try:
+        r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=300,
+                           cwd=os.path.dirname(os.path.abspath(__file__)))
+        dt = float(r.stdout.strip().splitlines()[-1])
+    except Exception as e:              # reported, never fatal to the benchmark line
+        return {"error": str(e)[:200]}
+    return {"value": 2.0 * rows * N * K / dt, "unit": "ops/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {M} rows of C (all of B), C schoolbook oracle, one thread",
+            "seconds": dt}
 
 
 def cpu_baseline(wl, plan, C_gpu, batched, target_s):
