@@ -391,13 +391,24 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
                 ua[3][ks][wd] = (int)__builtin_amdgcn_perm(d, c, 0x07060302u);
             }
 
+        // the four entries of each lane in stages, so that the matrix-core
+        // products of one entry run while the others' scalar work issues:
+        // the quotient products of all four, then their quotients and -r
+        // slots, then the value products of all four, then carries and stores
+        v16i fsq[4];
 #pragma unroll
         for (int m = 0; m < 4; m++) {
             // F = sum_k y_k c_k from the four digit sums
-            v16i fs = v16i{0};
+            fsq[m] = v16i{0};
 #pragma unroll
             for (int ks = 0; ks < KS; ks++)
-                fs = __builtin_amdgcn_mfma_i32_32x32x32_i8(fx[ks], ua[m][ks], fs, 0, 0, 0);
+                fsq[m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fx[ks], ua[m][ks], fsq[m], 0, 0, 0);
+        }
+        v4i um[4][KS];
+        bool nhm[4];
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const v16i &fs = fsq[m];
             const int64_t F = (int64_t)fs[0] + (int64_t)fs[1] * 256 + (int64_t)fs[2] * 65536 +
                               (int64_t)fs[3] * 16777216;
             // F / 2^31 is within 2^-19 of S / P; r = floor(F / 2^31 + 1/2)
@@ -407,7 +418,8 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
             const int r = (int)r64;
             const int rlo = ((r + 127) & 255) - 127;
             const int rhi = (r - rlo) >> 8;
-            v4i u[KS];
+            nhm[m] = near_half;
+            v4i (&u)[KS] = um[m];
 #pragma unroll
             for (int ks = 0; ks < KS; ks++) u[ks] = ua[m][ks];
 #pragma unroll
@@ -421,14 +433,21 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
                         if (ks == ks_k && x == x_k && h == h_k)
                             u[ks][x] = (int)(((uint32_t)u[ks][x] & ~(0xffu << sh)) | ((uint32_t)(val & 0xff) << sh));
             }
-            v16i acc[NB];
+        }
+        v16i accm[4][NB];
+#pragma unroll
+        for (int m = 0; m < 4; m++)
 #pragma unroll
             for (int nb = 0; nb < NB; nb++) {
-                acc[nb] = v16i{0};
+                accm[m][nb] = v16i{0};
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++)
-                    acc[nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[ks][nb], u[ks], acc[nb], 0, 0, 0);
+                    accm[m][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[ks][nb], um[m][ks], accm[m][nb], 0, 0, 0);
             }
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const v16i (&acc)[NB] = accm[m];
+            const bool near_half = nhm[m];
             int part[2 * W];
 #pragma unroll
             for (int nb = 0; nb < NB; nb++)
