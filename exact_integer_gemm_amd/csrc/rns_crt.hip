@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256) void crt_kernel(CrtConsts cc, CrtDigits cd,
 // balanced base-256 digits of c_k (rows 0-3, repeated in rows 4-7 so that
 // both half-waves receive them) leaves F in four partial sums
 // (|partial| <= 64 * 128 * 128 < 2^20).
-template <int KS, int NB, bool OFF32, bool ROWS>
+template <int KS, int NB, bool OFF32, bool ROWS, int G>
 __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd,
                                                    const int8_t *__restrict__ y, int64_t y_plane,
                                                    int64_t y_pitch, int64_t M, int64_t N,
@@ -391,138 +391,143 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
                 ua[3][ks][wd] = (int)__builtin_amdgcn_perm(d, c, 0x07060302u);
             }
 
-        // the four entries of each lane in stages, so that the matrix-core
-        // products of one entry run while the others' scalar work issues:
-        // the quotient products of all four, then their quotients and -r
-        // slots, then the value products of all four, then carries and stores
-        v16i fsq[4];
+        // the four entries of each lane in groups of G, each group in stages
+        // so that the matrix-core products of one entry run while the others'
+        // scalar work issues: the group's quotient products, then their
+        // quotients and -r slots, then its value products, then carries and
+        // stores.  G = 4 hides the most latency; G = 2 holds half as many
+        // accumulators, which leaves room for 4 waves per SIMD instead of 3.
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            // F = sum_k y_k c_k from the four digit sums
-            fsq[m] = v16i{0};
+        for (int m0 = 0; m0 < 4; m0 += G) {
+            v16i fsq[4];
 #pragma unroll
-            for (int ks = 0; ks < KS; ks++)
-                fsq[m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fx[ks], ua[m][ks], fsq[m], 0, 0, 0);
-        }
-        v4i um[4][KS];
-        bool nhm[4];
-#pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const v16i &fs = fsq[m];
-            const int64_t F = (int64_t)fs[0] + (int64_t)fs[1] * 256 + (int64_t)fs[2] * 65536 +
-                              (int64_t)fs[3] * 16777216;
-            // F / 2^31 is within 2^-19 of S / P; r = floor(F / 2^31 + 1/2)
-            const int64_t r64 = (F + (1ll << 30)) >> 31;
-            const int64_t fr = F - r64 * (1ll << 31);
-            const bool near_half = fr < -(1ll << 30) + (1ll << 21) || fr >= (1ll << 30) - (1ll << 21);
-            const int r = (int)r64;
-            const int rlo = ((r + 127) & 255) - 127;
-            const int rhi = (r - rlo) >> 8;
-            nhm[m] = near_half;
-            v4i (&u)[KS] = um[m];
-#pragma unroll
-            for (int ks = 0; ks < KS; ks++) u[ks] = ua[m][ks];
-#pragma unroll
-            for (int t = 0; t < 2; t++) {
-                const int k = cc.n + t, val = t ? -rhi : -rlo;
-                const int ks_k = k >> 5, h_k = (k >> 4) & 1, x_k = (k >> 2) & 3, sh = 8 * (k & 3);
+            for (int m = m0; m < m0 + G; m++) {
+                // F = sum_k y_k c_k from the four digit sums
+                fsq[m] = v16i{0};
 #pragma unroll
                 for (int ks = 0; ks < KS; ks++)
-#pragma unroll
-                    for (int x = 0; x < 4; x++)
-                        if (ks == ks_k && x == x_k && h == h_k)
-                            u[ks][x] = (int)(((uint32_t)u[ks][x] & ~(0xffu << sh)) | ((uint32_t)(val & 0xff) << sh));
+                    fsq[m] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fx[ks], ua[m][ks], fsq[m], 0, 0, 0);
             }
-        }
-        v16i accm[4][NB];
+            v4i um[4][KS];
+            bool nhm[4];
 #pragma unroll
-        for (int m = 0; m < 4; m++)
+            for (int m = m0; m < m0 + G; m++) {
+                const v16i &fs = fsq[m];
+                const int64_t F = (int64_t)fs[0] + (int64_t)fs[1] * 256 + (int64_t)fs[2] * 65536 +
+                                  (int64_t)fs[3] * 16777216;
+                // F / 2^31 is within 2^-19 of S / P; r = floor(F / 2^31 + 1/2)
+                const int64_t r64 = (F + (1ll << 30)) >> 31;
+                const int64_t fr = F - r64 * (1ll << 31);
+                const bool near_half = fr < -(1ll << 30) + (1ll << 21) || fr >= (1ll << 30) - (1ll << 21);
+                const int r = (int)r64;
+                const int rlo = ((r + 127) & 255) - 127;
+                const int rhi = (r - rlo) >> 8;
+                nhm[m] = near_half;
+                v4i (&u)[KS] = um[m];
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++) {
-                accm[m][nb] = v16i{0};
+                for (int ks = 0; ks < KS; ks++) u[ks] = ua[m][ks];
 #pragma unroll
-                for (int ks = 0; ks < KS; ks++)
-                    accm[m][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[ks][nb], um[m][ks], accm[m][nb], 0, 0, 0);
-            }
+                for (int t = 0; t < 2; t++) {
+                    const int k = cc.n + t, val = t ? -rhi : -rlo;
+                    const int ks_k = k >> 5, h_k = (k >> 4) & 1, x_k = (k >> 2) & 3, sh = 8 * (k & 3);
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            const v16i (&acc)[NB] = accm[m];
-            const bool near_half = nhm[m];
-            int part[2 * W];
+                    for (int ks = 0; ks < KS; ks++)
 #pragma unroll
-            for (int nb = 0; nb < NB; nb++)
-#pragma unroll
-                for (int gq = 0; gq < 4; gq++) {
-                    const v16i &a = acc[nb];
-                    const int lo = a[4 * gq] + (a[4 * gq + 1] << 8);
-                    const int hi = a[4 * gq + 2] + (a[4 * gq + 3] << 8);
-                    const auto sl = __builtin_amdgcn_permlane32_swap((uint32_t)lo, (uint32_t)lo, false, false);
-                    const auto sh = __builtin_amdgcn_permlane32_swap((uint32_t)hi, (uint32_t)hi, false, false);
-                    const int w0 = 8 * nb + 2 * gq;
-                    part[2 * w0] = (int)sl[0];
-                    part[2 * w0 + 1] = (int)sh[0];
-                    part[2 * w0 + 2] = (int)sl[1];
-                    part[2 * w0 + 3] = (int)sh[1];
+                        for (int x = 0; x < 4; x++)
+                            if (ks == ks_k && x == x_k && h == h_k)
+                                u[ks][x] = (int)(((uint32_t)u[ks][x] & ~(0xffu << sh)) | ((uint32_t)(val & 0xff) << sh));
                 }
-            uint32_t wv[W];
-            int c16 = 0;
-#pragma unroll
-            for (int w = 0; w < W; w++) {
-                const int t0 = part[2 * w] + c16;
-                const int t1 = part[2 * w + 1] + (t0 >> 16);
-                c16 = t1 >> 16;
-                wv[w] = __builtin_amdgcn_perm((uint32_t)t1, (uint32_t)t0, 0x05040100u);
             }
-            int64_t carry = c16;
-            if (near_half) {
-                int64_t bm = 0, bp = 0;
-                uint32_t nzm = 0, nzp = 0;
+            v16i accm[4][NB];
+#pragma unroll
+            for (int m = m0; m < m0 + G; m++)
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++) {
+                    accm[m][nb] = v16i{0};
+#pragma unroll
+                    for (int ks = 0; ks < KS; ks++)
+                        accm[m][nb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(dig[ks][nb], um[m][ks], accm[m][nb], 0, 0, 0);
+                }
+#pragma unroll
+            for (int m = m0; m < m0 + G; m++) {
+                const v16i (&acc)[NB] = accm[m];
+                const bool near_half = nhm[m];
+                int part[2 * W];
+#pragma unroll
+                for (int nb = 0; nb < NB; nb++)
+#pragma unroll
+                    for (int gq = 0; gq < 4; gq++) {
+                        const v16i &a = acc[nb];
+                        const int lo = a[4 * gq] + (a[4 * gq + 1] << 8);
+                        const int hi = a[4 * gq + 2] + (a[4 * gq + 3] << 8);
+                        const auto sl = __builtin_amdgcn_permlane32_swap((uint32_t)lo, (uint32_t)lo, false, false);
+                        const auto sh = __builtin_amdgcn_permlane32_swap((uint32_t)hi, (uint32_t)hi, false, false);
+                        const int w0 = 8 * nb + 2 * gq;
+                        part[2 * w0] = (int)sl[0];
+                        part[2 * w0 + 1] = (int)sh[0];
+                        part[2 * w0 + 2] = (int)sl[1];
+                        part[2 * w0 + 3] = (int)sh[1];
+                    }
+                uint32_t wv[W];
+                int c16 = 0;
 #pragma unroll
                 for (int w = 0; w < W; w++) {
-                    const uint32_t two = (wv[w] << 1) | (w ? (wv[w - 1] >> 31) : 0u);
-                    const uint32_t pw = w < 16 ? cc.P[w] : 0u;
-                    const int64_t dm = (int64_t)two - pw + bm;
-                    const int64_t dp = (int64_t)two + pw + bp;
-                    nzm |= (uint32_t)dm;
-                    nzp |= (uint32_t)dp;
-                    bm = dm >> 32;
-                    bp = dp >> 32;
+                    const int t0 = part[2 * w] + c16;
+                    const int t1 = part[2 * w + 1] + (t0 >> 16);
+                    c16 = t1 >> 16;
+                    wv[w] = __builtin_amdgcn_perm((uint32_t)t1, (uint32_t)t0, 0x05040100u);
                 }
-                const int64_t top2 = 2 * carry + (int64_t)(wv[W - 1] >> 31);
-                const int64_t tm = top2 + bm, tp = top2 + bp;
-                const bool above = tm > 0 || (tm == 0 && nzm != 0);
-                const bool below = tp < 0 || (tp == 0 && nzp == 0);
-                if (above || below) {
-                    int64_t c2 = 0;
+                int64_t carry = c16;
+                if (near_half) {
+                    int64_t bm = 0, bp = 0;
+                    uint32_t nzm = 0, nzp = 0;
 #pragma unroll
                     for (int w = 0; w < W; w++) {
-                        const int64_t pw = w < 16 ? (int64_t)cc.P[w] : 0;
-                        c2 += (int64_t)wv[w] + (above ? -pw : pw);
-                        wv[w] = (uint32_t)c2;
-                        c2 >>= 32;
+                        const uint32_t two = (wv[w] << 1) | (w ? (wv[w - 1] >> 31) : 0u);
+                        const uint32_t pw = w < 16 ? cc.P[w] : 0u;
+                        const int64_t dm = (int64_t)two - pw + bm;
+                        const int64_t dp = (int64_t)two + pw + bp;
+                        nzm |= (uint32_t)dm;
+                        nzp |= (uint32_t)dp;
+                        bm = dm >> 32;
+                        bp = dp >> 32;
                     }
-                    carry += c2;
-                }
-            }
-            const uint32_t sign = (uint32_t)carry;
+                    const int64_t top2 = 2 * carry + (int64_t)(wv[W - 1] >> 31);
+                    const int64_t tm = top2 + bm, tp = top2 + bp;
+                    const bool above = tm > 0 || (tm == 0 && nzm != 0);
+                    const bool below = tp < 0 || (tp == 0 && nzp == 0);
+                    if (above || below) {
+                        int64_t c2 = 0;
 #pragma unroll
-            for (int t = 0; t < RNS_MAX_OUT_LIMBS / 4; t++) {
-                uint32_t wd[4];
-#pragma unroll
-                for (int ii = 0; ii < 4; ii++) {
-                    const int i0 = 8 * t + ii, i1 = 8 * t + 4 + ii;
-                    const uint32_t a0 = i0 < W ? wv[i0] : sign, a1 = i1 < W ? wv[i1] : sign;
-                    wd[ii] = h ? a1 : a0;
+                        for (int w = 0; w < W; w++) {
+                            const int64_t pw = w < 16 ? (int64_t)cc.P[w] : 0;
+                            c2 += (int64_t)wv[w] + (above ? -pw : pw);
+                            wv[w] = (uint32_t)c2;
+                            c2 >>= 32;
+                        }
+                        carry += c2;
+                    }
                 }
-                const int l = 4 * t + 2 * h;
-                if (pair_stores) {
-                    // into the wave's staging area: entry 4 l32 + m, limbs l, l + 1
-                    const int u = (4 * l32 + m) * (c_limbs >> 1) + (l >> 1);
-                    if (l < c_limbs) outs[wave][u ^ ((u >> 4) & 15)] = v4u{wd[0], wd[1], wd[2], wd[3]};
-                } else if (j0 + m < lim) {
-                    int64_t *ce = C + (i * N + j0 + m) * c_limbs;
-                    if (l < c_limbs) ce[l] = (int64_t)(((uint64_t)wd[1] << 32) | wd[0]);
-                    if (l + 1 < c_limbs) ce[l + 1] = (int64_t)(((uint64_t)wd[3] << 32) | wd[2]);
+                const uint32_t sign = (uint32_t)carry;
+#pragma unroll
+                for (int t = 0; t < RNS_MAX_OUT_LIMBS / 4; t++) {
+                    uint32_t wd[4];
+#pragma unroll
+                    for (int ii = 0; ii < 4; ii++) {
+                        const int i0 = 8 * t + ii, i1 = 8 * t + 4 + ii;
+                        const uint32_t a0 = i0 < W ? wv[i0] : sign, a1 = i1 < W ? wv[i1] : sign;
+                        wd[ii] = h ? a1 : a0;
+                    }
+                    const int l = 4 * t + 2 * h;
+                    if (pair_stores) {
+                        // into the wave's staging area: entry 4 l32 + m, limbs l, l + 1
+                        const int u = (4 * l32 + m) * (c_limbs >> 1) + (l >> 1);
+                        if (l < c_limbs) outs[wave][u ^ ((u >> 4) & 15)] = v4u{wd[0], wd[1], wd[2], wd[3]};
+                    } else if (j0 + m < lim) {
+                        int64_t *ce = C + (i * N + j0 + m) * c_limbs;
+                        if (l < c_limbs) ce[l] = (int64_t)(((uint64_t)wd[1] << 32) | wd[0]);
+                        if (l + 1 < c_limbs) ce[l + 1] = (int64_t)(((uint64_t)wd[3] << 32) | wd[2]);
+                    }
                 }
             }
         }
@@ -563,11 +568,11 @@ static int64_t crt_resident_blocks(Kern kernel) {
     return cached;
 }
 
-template <int KS, int NB, bool OFF32, bool ROWS>
+template <int KS, int NB, bool OFF32, bool ROWS, int G>
 static void launch_crt4(int64_t groups, const CrtConsts &c, const CrtDigits &d, const int8_t *y, int64_t y_plane,
                         int64_t y_pitch, int64_t M, int64_t N, int64_t *C, int32_t c_limbs, int pairs,
                         hipStream_t s) {
-    auto kernel = crt4_kernel<KS, NB, OFF32, ROWS>;
+    auto kernel = crt4_kernel<KS, NB, OFF32, ROWS, G>;
     const int64_t cap = crt_resident_blocks(kernel);
     int64_t grid = (groups + 3) / 4;
     if (grid > cap) grid = cap;
@@ -594,25 +599,32 @@ int launch_crt(const CrtConsts &c, const CrtDigits &d, int ksteps, int nblocks,
         const int rows4 = (N % 128 == 0 || N >= 1024) ? 1 : 0;
         if (!rows4 && N % 4) return RNS_E_ARG;
         const int64_t groups4 = rows4 ? M * ((N + 127) / 128) : (total + 127) / 128;
-#define RNS_CRT4_LAUNCH(KS, NB)                                                                             \
-    do {                                                                                                    \
-        if (off32 && rows4)                                                                                 \
-            launch_crt4<KS, NB, true, true>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s);  \
-        else if (off32)                                                                                     \
-            launch_crt4<KS, NB, true, false>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s); \
-        else if (rows4)                                                                                     \
-            launch_crt4<KS, NB, false, true>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s); \
-        else                                                                                                \
-            launch_crt4<KS, NB, false, false>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s);\
+#define RNS_CRT4_LAUNCH(KS, NB, G)                                                                          \
+    do {                                                                                                      \
+        if (off32 && rows4)                                                                                   \
+            launch_crt4<KS, NB, true, true, G>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s);  \
+        else if (off32)                                                                                       \
+            launch_crt4<KS, NB, true, false, G>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s); \
+        else if (rows4)                                                                                       \
+            launch_crt4<KS, NB, false, true, G>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs, s); \
+        else                                                                                                  \
+            launch_crt4<KS, NB, false, false, G>(groups4, c, d, y, y_plane, y_pitch, M, N, C, c_limbs, pairs,  \
+                                                 s);                                                          \
     } while (0)
-        if (ksteps == 1 && nblocks == 1)
-            RNS_CRT4_LAUNCH(1, 1);
+        // one K step and one digit block: with few bytes per entry (square,
+        // 10 primes and 2 limbs: 26) the latency the four-entry stages hide
+        // counts most; with many (wide, 29 primes and 4 limbs: 61) the extra
+        // waves of pairs keep more loads in flight
+        if (ksteps == 1 && nblocks == 1 && c.n + 8 * c_limbs < 40)
+            RNS_CRT4_LAUNCH(1, 1, 4);
+        else if (ksteps == 1 && nblocks == 1)
+            RNS_CRT4_LAUNCH(1, 1, 2);
         else if (ksteps == 1)
-            RNS_CRT4_LAUNCH(1, 2);
+            RNS_CRT4_LAUNCH(1, 2, 2);
         else if (nblocks == 1)
-            RNS_CRT4_LAUNCH(2, 1);
+            RNS_CRT4_LAUNCH(2, 1, 2);
         else
-            RNS_CRT4_LAUNCH(2, 2);
+            RNS_CRT4_LAUNCH(2, 2, 2);
 #undef RNS_CRT4_LAUNCH
         return hipGetLastError() == hipSuccess ? RNS_OK : RNS_E_HIP;
     }
