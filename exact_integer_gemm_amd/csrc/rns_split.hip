@@ -79,10 +79,23 @@ __device__ __forceinline__ v4i as_v4i(u64 lo, u64 hi) {
     return v4i{(int)(uint32_t)lo, (int)(uint32_t)(lo >> 32), (int)(uint32_t)hi, (int)(uint32_t)(hi >> 32)};
 }
 
-// W consecutive words from an 8-byte aligned address (one wide load)
+typedef unsigned long long u64x2 __attribute__((ext_vector_type(2), aligned(8)));
+
+// W consecutive words from an 8-byte aligned address, in 16-byte loads.
+// Every entry is read once, so the loads carry the non-temporal hint: on
+// the wide workload the split takes 160 us with it against 165 without.
 template <int W>
 __device__ __forceinline__ void load_words(const int64_t *p, u64 (&w)[W]) {
-    __builtin_memcpy(w, p, sizeof(w));
+    if constexpr (W % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < W / 2; i++) {
+            const u64x2 v = __builtin_nontemporal_load((const u64x2 *)p + i);
+            w[2 * i] = v.x;
+            w[2 * i + 1] = v.y;
+        }
+    } else {
+        __builtin_memcpy(w, p, sizeof(w));
+    }
 }
 
 // The limbs of an entry from its loaded words (binary64: floor(x * 2^scale));
