@@ -540,10 +540,13 @@ __global__ __launch_bounds__(256, 2) void crt4_kernel(CrtConsts cc, CrtDigits cd
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
             const int upe = c_limbs >> 1;     // units per entry
             v4u *cu = (v4u *)(C + base * c_limbs);
+            // nothing in the path reads C back: the stores carry the
+            // non-temporal hint (square 19.8 -> 18.8 us, wide 63.2 -> 62.5 us)
 #pragma unroll
             for (int r = 0; r < RNS_MAX_OUT_LIMBS; r++) {
                 const int u = 64 * r + lane;
-                if (r < 2 * upe && u < count * upe) cu[u] = outs[wave][u ^ ((u >> 4) & 15)];
+                if (r < 2 * upe && u < count * upe)
+                    __builtin_nontemporal_store(outs[wave][u ^ ((u >> 4) & 15)], cu + u);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
             __builtin_amdgcn_wave_barrier();
