@@ -397,6 +397,57 @@ def test_reconstruct_planted_values_prime_powers(n):
         assert [int(v) for v in got] == vals, method
 
 
+# The quad form of the CRT kernel takes outputs of at least 1024 x 128
+# entries: row groups of 128 columns (N = 1024) or flat quads (N = 1000).  It
+# stages a lane's four entries in groups of G = 4 below 40 bytes per entry
+# (n + 8 c_limbs) and of G = 2 from there; n + 2 > 32 slots take two K steps,
+# more than 32 balanced base-256 digits of 256 P two digit blocks; c_limbs
+# even stores 1 KiB runs, odd stores each limb directly.
+QUAD_PLANTED = [
+    # n, N, extra output limbs beyond the fewest
+    (1, 1024, 0),      # G = 4, rows, direct stores
+    (6, 1000, 1),      # G = 4, flat, runs
+    (16, 1024, 0),     # G = 4 (32 bytes), rows, runs
+    (16, 1000, 1),     # G = 2 (40 bytes), flat, direct stores
+    (29, 1024, 0),     # G = 2, rows, runs
+    (29, 1000, 1),     # G = 2, flat, direct stores
+    (31, 1024, 1),     # two K steps
+    (33, 1000, 0),     # two K steps, 32 digits (one block)
+    (54, 1024, 0),     # all 54 primes (P even): two K steps, two digit blocks
+    (54, 1000, 1),
+]
+
+
+@pytest.mark.parametrize("n,N,extra", QUAD_PLANTED)
+def test_reconstruct_planted_values_quad_form(n, N, extra):
+    """The planted values through the quad form: column j holds s_j times
+    the planted value of its row, s_j = +1 or -1 at random (+1 throughout
+    when P is even, where the negated lower end would leave (-P/2, P/2]), so
+    both ends of the range and their neighbours reach every entry position of
+    a lane.  Expected limbs come from the oracle's encoding of the values."""
+    rng = np.random.default_rng(3000 + n)
+    p = rg.plan_n(n)
+    ps = list(p.primes)
+    vals = _boundary_values(ps, rng)
+    M = len(vals)
+    assert M * N >= 1024 * 128
+    signs = rng.choice([-1, 1], size=N) if O.prod(ps) % 2 else np.ones(N, dtype=np.int64)
+    L = p.out_limbs_min + extra
+    print(f"planted quad form n={n} M={M} N={N} limbs={L}", flush=True)
+    _, _, A_res, _ = _planted(n, vals)
+    B = dev(signs.astype(np.int64).reshape(1, N, 1))
+    ws = rg.new_workspace(p, M, N, 1, True, B.device)
+    rg.split(p, None, B, ws, M=M)
+    rg.residue_products(p, M, N, 1, ws, A_res=A_res)
+    out = torch.full((M, N, L), 7, dtype=torch.int64, device=B.device)
+    rg.reconstruct(p, M, N, 1, ws, out, batched=True)
+    got = out.cpu().numpy()
+    pos = O.encode_array(np.array(vals, dtype=object), L)
+    neg = O.encode_array(np.array([-v for v in vals], dtype=object), L)
+    want = np.where((signs > 0)[None, :, None], pos[:, None, :], neg[:, None, :])
+    assert np.array_equal(got, want)
+
+
 @pytest.mark.parametrize("M,N,K,la,lb,ab,bb,seed", [(40, 33, 512, 3, 3, 170, 170, 81),
                                                     (300, 270, 200, 3, 3, 172, 168, 82),
                                                     (64, 64, 64, 2, 2, 100, 100, 83)])
