@@ -185,11 +185,17 @@ class Plan:
     primes: tuple
 
     def _c(self) -> _Plan:
-        c = _Plan()
-        c.n_primes, c.out_limbs_min = self.n_primes, self.out_limbs_min
-        c.a_bits, c.b_bits, c.k_max, c.log2_P = self.a_bits, self.b_bits, self.k_max, self.log2_P
-        for i in range(RNS_MAX_PRIMES):
-            c.primes[i] = self.primes[i] if i < len(self.primes) else 0
+        """The plan as the C struct, built on first use and kept: every entry
+        point takes it as const, and filling its 54 moduli from Python costs
+        more than a kernel launch."""
+        c = self.__dict__.get("_cstruct")
+        if c is None:
+            c = _Plan()
+            c.n_primes, c.out_limbs_min = self.n_primes, self.out_limbs_min
+            c.a_bits, c.b_bits, c.k_max, c.log2_P = self.a_bits, self.b_bits, self.k_max, self.log2_P
+            for i in range(RNS_MAX_PRIMES):
+                c.primes[i] = self.primes[i] if i < len(self.primes) else 0
+            object.__setattr__(self, "_cstruct", c)
         return c
 
     @staticmethod
