@@ -82,8 +82,9 @@ __device__ __forceinline__ v4i as_v4i(u64 lo, u64 hi) {
 typedef unsigned long long u64x2 __attribute__((ext_vector_type(2), aligned(8)));
 
 // W consecutive words from an 8-byte aligned address, in 16-byte loads.
-// Every entry is read once, so the loads carry the non-temporal hint: on
-// the wide workload the split takes 160 us with it against 165 without.
+// Every entry is read once, so the loads carry the non-temporal hint (on
+// the wide workload, measured with one launch per operand: 160 us with it,
+// 165 us without).
 template <int W>
 __device__ __forceinline__ void load_words(const int64_t *p, u64 (&w)[W]) {
     if constexpr (W % 2 == 0) {
